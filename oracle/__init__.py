@@ -1,0 +1,212 @@
+"""CPU oracle for the HISA indexer and the flat DSA indexer (numpy front end).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the bench's
+CPU-baseline leg are the only callers.  The product path never imports this
+package, and this package imports nothing from the product package.
+
+The arithmetic lives in ``hisa_oracle.c`` (plain C, fp64, OpenMP over
+queries); this module compiles it with gcc on first use and marshals numpy
+arrays.  See the header of ``hisa_oracle.c`` for the passages of the pages
+each step follows and for the readings taken where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hisa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle into ``oracle/liboracle.so`` (IEEE semantics kept:
+    no fast-math, no FMA contraction)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-fno-fast-math", "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            lib.oracle_pool.argtypes = [_P, _I64, _I32, _I32, _P, _P]
+            lib.oracle_pool_range.argtypes = [_P, _I64, _I32, _I32, _I64, _I64, _P, _P]
+            lib.oracle_block_scores.argtypes = [_P, _P, _I64, _I32, _P]
+            lib.oracle_select_blocks.argtypes = [_P, _P, _I64, _I32, _I32, _I32, _P, _P]
+            lib.oracle_tokens_on_blocks.argtypes = [_P, _P, _I64, _I64, _I32, _I32, _P, _I32,
+                                                    _I32, _P, _P, _P]
+            lib.oracle_hisa_query.argtypes = [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32,
+                                              _P, _P, _P, _P]
+            lib.oracle_flat_query.argtypes = [_P, _P, _I64, _I64, _I32, _I32, _P, _P, _P]
+            lib.oracle_index_batch.argtypes = [_I32, _P, _P, _P, _I64, _P, _P, _P, _P, _P,
+                                               _I32, _I32, _I32, _I32, _I32, _P, _P, _P]
+            lib.oracle_bf16_round.argtypes = [ctypes.c_double]
+            lib.oracle_bf16_round.restype = ctypes.c_uint16
+            lib.oracle_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 arrays are passed as their uint16 bit patterns")
+    return a
+
+
+def threads() -> int:
+    return int(_load().oracle_threads())
+
+
+def bf16_round(v: float) -> int:
+    """Round-to-nearest-even of a double to bf16 bits (the representative
+    rounding rule)."""
+    return int(_load().oracle_bf16_round(float(v)))
+
+
+def pool(keys, B: int, return_flag: bool = False):
+    """Block representatives of one sequence: keys [L, d] bf16 bits ->
+    reps [ceil(L/B), d] bf16 bits."""
+    keys = _u16(keys)
+    L, d = keys.shape
+    M = (L + B - 1) // B
+    reps = np.zeros((M, d), np.uint16)
+    flag = ctypes.c_int(0)
+    rc = _load().oracle_pool(_ptr(keys), L, d, B, _ptr(reps), ctypes.byref(flag))
+    if rc != 0:
+        raise ValueError("oracle_pool: bad arguments")
+    return (reps, bool(flag.value)) if return_flag else reps
+
+
+def pool_range(keys, B: int, b0: int, b1: int, reps: np.ndarray) -> bool:
+    """Re-pool blocks [b0, b1) in place (the incremental update at append)."""
+    keys = _u16(keys)
+    L, d = keys.shape
+    assert reps.dtype == np.uint16 and reps.flags.c_contiguous
+    flag = ctypes.c_int(0)
+    rc = _load().oracle_pool_range(_ptr(keys), L, d, B, b0, b1, _ptr(reps), ctypes.byref(flag))
+    if rc != 0:
+        raise ValueError("oracle_pool_range: bad arguments")
+    return bool(flag.value)
+
+
+def block_scores(q, reps) -> np.ndarray:
+    q = _u16(q)
+    reps = _u16(reps)
+    out = np.zeros(reps.shape[0], np.float64)
+    _load().oracle_block_scores(_ptr(q), _ptr(reps), reps.shape[0], reps.shape[1], _ptr(out))
+    return out
+
+
+def select_blocks(q, reps, t: int, B: int, m: int):
+    """Ascending block ids a query at position t keeps, and how many block
+    scores that took."""
+    q = _u16(q)
+    reps = _u16(reps)
+    sel = np.zeros(m, np.int64)
+    nb = ctypes.c_int64(0)
+    n = _load().oracle_select_blocks(_ptr(q), _ptr(reps), t, reps.shape[1], B, m,
+                                     _ptr(sel), ctypes.byref(nb))
+    if n < 0:
+        raise ValueError("oracle_select_blocks: bad arguments")
+    return sel[:n].copy(), int(nb.value)
+
+
+def tokens_on_blocks(q, keys, t: int, B: int, blocks, k: int):
+    """Stage 2 on a given block set: (idx[k], scores[k])."""
+    q = _u16(q)
+    keys = _u16(keys)
+    blocks = np.ascontiguousarray(blocks, np.int64)
+    idx = np.zeros(k, np.int32)
+    sc = np.zeros(k, np.float64)
+    rc = _load().oracle_tokens_on_blocks(_ptr(q), _ptr(keys), keys.shape[0], t, keys.shape[1],
+                                         B, _ptr(blocks), len(blocks), k, _ptr(idx), _ptr(sc),
+                                         None)
+    if rc != 0:
+        raise ValueError("oracle_tokens_on_blocks: bad arguments")
+    return idx, sc
+
+
+def hisa_query(q, keys, reps, t: int, B: int, m: int, k: int):
+    """One HISA query: (idx[k], scores[k], blocks[m], (n_block_scores,
+    n_token_scores))."""
+    q = _u16(q)
+    keys = _u16(keys)
+    reps = _u16(reps)
+    idx = np.zeros(k, np.int32)
+    sc = np.zeros(k, np.float64)
+    blk = np.zeros(m, np.int32)
+    counts = np.zeros(2, np.int64)
+    rc = _load().oracle_hisa_query(_ptr(q), _ptr(keys), _ptr(reps), keys.shape[0], t,
+                                   keys.shape[1], B, m, k, _ptr(idx), _ptr(sc), _ptr(blk),
+                                   _ptr(counts))
+    if rc != 0:
+        raise ValueError("oracle_hisa_query: bad arguments")
+    return idx, sc, blk, (int(counts[0]), int(counts[1]))
+
+
+def flat_query(q, keys, t: int, k: int):
+    q = _u16(q)
+    keys = _u16(keys)
+    idx = np.zeros(k, np.int32)
+    sc = np.zeros(k, np.float64)
+    counts = np.zeros(2, np.int64)
+    rc = _load().oracle_flat_query(_ptr(q), _ptr(keys), keys.shape[0], t, keys.shape[1], k,
+                                   _ptr(idx), _ptr(sc), _ptr(counts))
+    if rc != 0:
+        raise ValueError("oracle_flat_query: bad arguments")
+    return idx, sc, (int(counts[0]), int(counts[1]))
+
+
+def index_batch(flat: bool, queries, q_pos, keys, k: int, *, reps=None, q_seq=None,
+                seq_key_off=None, seq_rep_off=None, seq_len=None, B: int = 128, m: int = 3):
+    """Batched HISA (flat=False) or flat (flat=True) over packed sequences.
+    Returns (idx[nq,k] int32, scores[nq,k] fp64, blocks[nq,m] int32 or
+    None)."""
+    queries = _u16(queries)
+    keys = _u16(keys)
+    nq, d = queries.shape
+    q_pos = np.ascontiguousarray(q_pos, np.int64)
+    if seq_key_off is None:
+        seq_key_off = np.zeros(1, np.int64)
+        seq_rep_off = np.zeros(1, np.int64)
+        seq_len = np.array([keys.shape[0]], np.int64)
+    seq_key_off = np.ascontiguousarray(seq_key_off, np.int64)
+    seq_len = np.ascontiguousarray(seq_len, np.int64)
+    seq_rep_off = None if seq_rep_off is None else np.ascontiguousarray(seq_rep_off, np.int64)
+    q_seq = None if q_seq is None else np.ascontiguousarray(q_seq, np.int32)
+    if reps is not None:
+        reps = _u16(reps)
+    idx = np.zeros((nq, k), np.int32)
+    sc = np.zeros((nq, k), np.float64)
+    blk = None if flat else np.zeros((nq, m), np.int32)
+    rc = _load().oracle_index_batch(int(flat), _ptr(queries), _ptr(q_pos), _ptr(q_seq), nq,
+                                    _ptr(keys), _ptr(reps), _ptr(seq_key_off), _ptr(seq_rep_off),
+                                    _ptr(seq_len), len(seq_len), d, B, m, k, _ptr(idx), _ptr(sc),
+                                    _ptr(blk))
+    if rc != 0:
+        raise ValueError("oracle_index_batch: bad arguments")
+    return idx, sc, blk
