@@ -1,0 +1,192 @@
+/*
+ * hisa.h -- C ABI of libhisa, the MI355X (gfx950) HISA hierarchical indexer
+ * and flat DSA indexer.
+ *
+ * What is computed (pages cited by title and passage):
+ *   "HISA: Efficient Hierarchical Indexing for Fine-Grained Sparse
+ *   Attention" (aitrends.kr summary of the HISA paper):
+ *     structure paragraph   -- the L index keys of a sequence are split into
+ *                              contiguous blocks of B; a block's
+ *                              representative is the mean of its keys;
+ *     stage-1 paragraph     -- each query scores the representatives by
+ *                              inner product under a causal mask and keeps
+ *                              the top m blocks, always including the first
+ *                              block and the last two;
+ *     stage-2 paragraph     -- the token-level score is applied only to the
+ *                              m*B tokens of the kept blocks and the top k
+ *                              token indices are returned for the sparse
+ *                              attention operator;
+ *     maintenance paragraph -- representatives are updated incrementally
+ *                              when keys are appended to the cache; the
+ *                              output layout is the flat indexer's;
+ *     kernel paragraph      -- no loss once m*B >= k.
+ *   "Why long-context LLMs slow down and how sparse attention fixes it"
+ *   (idea.jsleekr.com), section "DSA": the flat indexer scores every key
+ *   with a light dot product and keeps the best few.
+ *
+ * Conventions shared by every call
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *   - d (index-key dimension) must be 64.
+ *   - Every array pointer is a DEVICE pointer owned by the caller, unless a
+ *     parameter says "host".  The library allocates nothing and keeps no
+ *     mutable global state; calls on different streams are independent.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work and returns; the library never synchronises.  A device
+ *     fault shows up at the caller's next synchronisation.
+ *   - Return value: HISA_OK or a negative HISA_ERR_* code.  Arguments are
+ *     validated on the host before anything is enqueued; on error nothing
+ *     is written.  HISA_ERR_HIP means a launch was rejected by the runtime
+ *     (earlier launches of the same call may have run).
+ *
+ * Representatives (the readings taken where the pages are silent):
+ *   R_b = RNE_bf16( fp64( S_b / n_b ) ), S_b the fp64 sum of the n_b keys
+ *   of block b (n_b = B except for a partial last block), added exactly
+ *   whenever every nonzero |key| >= 2^-34 and |S_b| < 2^10, so that the
+ *   result is independent of summation order.
+ *
+ * Selection (readings): key j is visible to a query at position t iff
+ *   j <= t; block b is causal iff b*B <= t; with c = t / B the forced blocks
+ *   are 0, c-1 and c, counted among the m kept blocks; if c+1 <= m every
+ *   causal block is kept.  Scores are fp32 sums of exact bf16 products.
+ *   Ties at the m-th block / k-th token go to the lower block / token index.
+ *
+ * Output layout (identical for HISA and flat):
+ *   out_idx[i*k + r]: the selected token indices of query i, relative to the
+ *   start of its sequence, in ascending order, then -1 up to k.  A row holds
+ *   min(k, number of candidate tokens) valid entries.
+ *   out_scores[i*k + r] (optional): the fp32 score of out_idx[i*k + r]
+ *   (NaN where out_idx is -1).
+ *   out_blocks[i*m + r] (optional, HISA only): the kept block ids of query
+ *   i in ascending order, then -1 up to m.
+ *   A query whose sequence id is outside [0, nseq) or whose position is
+ *   outside [0, seq_len) gets an all -1 row (NaN scores); that is not an
+ *   error the host can see, since positions live on the device.
+ */
+#ifndef HISA_H
+#define HISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HISA_ABI_VERSION 1
+
+enum {
+    HISA_OK = 0,
+    HISA_ERR_INVALID_ARG = -1,  /* null required pointer, bad size, m < 3, m*B < k, ... */
+    HISA_ERR_UNSUPPORTED = -2,  /* d != 64, B not a power of two in [16, 256], limits */
+    HISA_ERR_WORKSPACE = -3,    /* workspace smaller than one query needs */
+    HISA_ERR_HIP = -4           /* the HIP runtime rejected a launch */
+};
+
+/* Largest k and largest m*B the index calls accept. */
+#define HISA_MAX_K 16384
+#define HISA_MAX_CANDIDATES 16384
+/* Largest sequence length (token indices are int32). */
+#define HISA_MAX_LEN ((int64_t)1 << 30)
+
+/* Host-side description of one sequence in a packed key cache, for the
+ * append call.  key rows [key_off, key_off + capacity) belong to the
+ * sequence, of which the first `len` are filled; its representatives occupy
+ * rows [rep_off, rep_off + ceil(capacity / B)). */
+typedef struct hisa_seq {
+    int64_t key_off;
+    int64_t rep_off;
+    int64_t len;
+    int64_t capacity;
+} hisa_seq;
+
+/*
+ * hisa_pool_blocks -- mean-pool one sequence's keys into representatives
+ * (structure paragraph of the HISA summary).
+ *   keys  [L, d] bf16, read.
+ *   reps  [ceil(L / B), d] bf16, written.
+ *   L >= 0 (0 is a no-op), d == 64, B a power of two in [16, 256].
+ * Errors: INVALID_ARG (null pointer with L > 0, L < 0 or L > HISA_MAX_LEN),
+ *         UNSUPPORTED (d, B).
+ */
+int hisa_pool_blocks(const uint16_t* keys, int64_t L, int d, int B, uint16_t* reps,
+                     void* stream);
+
+/*
+ * hisa_append_keys -- append n_new keys to each of nseq sequences and bring
+ * the representatives of every block the new keys touch up to date
+ * (maintenance paragraph of the HISA summary).  The result equals pooling
+ * the grown sequences from scratch, bit for bit.
+ *   keys      packed key cache, rows written at [key_off + len, + n_new).
+ *   reps      packed representatives, rows of the touched blocks written.
+ *   seqs      HOST array of nseq descriptors (len = length before the call;
+ *             the library does not update it).
+ *   new_keys  [nseq, n_new, d] bf16, read.
+ *   n_new >= 0 (0 is a no-op), nseq >= 0.
+ * Errors: INVALID_ARG (null pointer, negative sizes, len + n_new > capacity,
+ *         capacity > HISA_MAX_LEN), UNSUPPORTED (d, B).
+ */
+int hisa_append_keys(uint16_t* keys, uint16_t* reps, const hisa_seq* seqs, int nseq,
+                     const uint16_t* new_keys, int64_t n_new, int d, int B, void* stream);
+
+/* Arguments of the two index calls. */
+typedef struct hisa_index_args {
+    const uint16_t* queries;     /* [nq, d] bf16 index queries */
+    const int64_t* q_pos;        /* [nq] position of each query in its sequence */
+    const int32_t* q_seq;        /* [nq] sequence id of each query; NULL: all in sequence 0 */
+    int64_t nq;                  /* number of queries, >= 0 (0 is a no-op) */
+    const uint16_t* keys;        /* packed keys, [*, d] bf16 */
+    const uint16_t* reps;        /* packed representatives, [*, d] bf16 (HISA only) */
+    const int64_t* seq_key_off;  /* [nseq] first key row of each sequence; NULL if nseq == 1: 0 */
+    const int64_t* seq_rep_off;  /* [nseq] first rep row of each sequence; NULL if nseq == 1: 0 */
+    const int64_t* seq_len;      /* [nseq] keys in each sequence; NULL if nseq == 1: max_len */
+    int32_t nseq;                /* >= 1 */
+    int64_t max_len;             /* HOST bound: every seq_len <= max_len <= HISA_MAX_LEN */
+    int32_t d;                   /* 64 */
+    int32_t B;                   /* block size (HISA), power of two in [16, 256] */
+    int32_t m;                   /* kept blocks (HISA), 3 <= m, m*B <= HISA_MAX_CANDIDATES */
+    int32_t k;                   /* tokens returned, 1 <= k <= HISA_MAX_K; HISA: k <= m*B */
+    int32_t* out_idx;            /* [nq, k] */
+    float* out_scores;           /* [nq, k] or NULL */
+    int32_t* out_blocks;         /* [nq, m] or NULL (HISA only) */
+    void* workspace;             /* device scratch owned by the caller */
+    size_t workspace_bytes;      /* its size; see hisa_workspace_bytes */
+} hisa_index_args;
+
+/*
+ * hisa_workspace_bytes -- workspace an index call wants for these
+ * arguments (flat != 0: the flat indexer).  Only the sizes in `a` are
+ * read.  Any workspace of at least the one-query size is accepted: the call
+ * then works through the queries in as many chunks as it needs; the
+ * returned size is what processes up to 4096 queries per chunk.
+ * *min_bytes (nullable) receives the one-query size.
+ */
+int hisa_workspace_bytes(const hisa_index_args* a, int flat, size_t* bytes, size_t* min_bytes);
+
+/*
+ * hisa_index -- HISA: block scores, causal + forced top-m, token scores in
+ * the kept blocks, top-k (stage-1 and stage-2 paragraphs of the HISA
+ * summary).
+ * Errors: INVALID_ARG (null required pointer, nq < 0, nseq < 1, m < 3,
+ *         k < 1, m*B < k, max_len < 1), UNSUPPORTED (d, B, k, m*B or
+ *         max_len beyond the limits above), WORKSPACE.
+ */
+int hisa_index(const hisa_index_args* a, void* stream);
+
+/*
+ * hisa_flat_index -- the flat DSA indexer: every visible key scored, top-k
+ * ("DSA" section of the video summary).  B, m, reps and out_blocks are
+ * ignored.  Same errors as hisa_index, less those about B and m.
+ */
+int hisa_flat_index(const hisa_index_args* a, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* hisa_status_str(int status);
+
+/* HISA_ABI_VERSION of the built library. */
+int hisa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HISA_H */

@@ -1,0 +1,249 @@
+// C ABI of libhisa: host-side validation, workspace layout, query chunking
+// and kernel launches.  The contract of every entry point is documented in
+// include/hisa.h.
+#include "../../include/hisa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "kernels.h"
+
+using namespace hisa;
+
+namespace {
+
+constexpr int64_t kChunkDefault = 4096;   // queries per chunk in the recommended workspace
+constexpr int64_t kChunkMax = 65535;      // grid.y limit
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline bool valid_B(int B) { return B >= 16 && B <= 256 && (B & (B - 1)) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? HISA_OK : HISA_ERR_HIP; }
+
+// Validation shared by both index calls.  flat selects which rules apply.
+int validate_index(const hisa_index_args* a, int flat)
+{
+    if (!a) return HISA_ERR_INVALID_ARG;
+    if (a->nq < 0 || a->nseq < 1 || a->k < 1 || a->max_len < 1) return HISA_ERR_INVALID_ARG;
+    if (a->d != 64) return HISA_ERR_UNSUPPORTED;
+    if (a->max_len > HISA_MAX_LEN || a->k > HISA_MAX_K) return HISA_ERR_UNSUPPORTED;
+    if (a->nseq > 1 && (!a->seq_key_off || !a->seq_len)) return HISA_ERR_INVALID_ARG;
+    if (!flat) {
+        if (a->m < 3) return HISA_ERR_INVALID_ARG;
+        if (!valid_B(a->B)) return HISA_ERR_UNSUPPORTED;
+        if ((int64_t)a->m * a->B < a->k) return HISA_ERR_INVALID_ARG;
+        if ((int64_t)a->m * a->B > HISA_MAX_CANDIDATES) return HISA_ERR_UNSUPPORTED;
+        if ((a->max_len + a->B - 1) / a->B > HISA_MAX_CANDIDATES) return HISA_ERR_UNSUPPORTED;
+        if (a->nseq > 1 && !a->seq_rep_off) return HISA_ERR_INVALID_ARG;
+    }
+    if (a->nq == 0) return HISA_OK;
+    if (!a->queries || !a->q_pos || !a->keys || !a->out_idx) return HISA_ERR_INVALID_ARG;
+    if (!flat && !a->reps) return HISA_ERR_INVALID_ARG;
+    return HISA_OK;
+}
+
+// Workspace regions of one chunk of `chunk` queries.
+struct Layout {
+    // HISA
+    size_t sigma = 0, sel = 0, ukeys = 0;
+    // flat
+    size_t hist = 0, state = 0, counts = 0;
+    size_t total = 0;
+};
+
+int64_t hisa_Mmax(const hisa_index_args* a) { return (a->max_len + a->B - 1) / a->B; }
+
+bool flat_uses_radix(const hisa_index_args* a) { return a->max_len > HISA_MAX_CANDIDATES; }
+
+Layout layout_for(const hisa_index_args* a, int flat, int64_t chunk)
+{
+    Layout L;
+    size_t off = 0;
+    if (!flat) {
+        const int64_t Mmax = hisa_Mmax(a);
+        L.sigma = off;
+        off += align_up((size_t)chunk * Mmax * sizeof(float));
+        L.sel = off;
+        off += align_up((size_t)chunk * a->m * sizeof(int32_t));
+        L.ukeys = off;
+        off += align_up((size_t)chunk * a->m * a->B * sizeof(uint32_t));
+    } else {
+        L.ukeys = off;
+        off += align_up((size_t)chunk * a->max_len * sizeof(uint32_t));
+        if (flat_uses_radix(a)) {
+            const size_t S = radix_slices(1, a->max_len);   // the largest slice count any chunk uses
+            L.hist = off;
+            off += align_up((size_t)chunk * 256 * sizeof(int));
+            L.state = off;
+            off += align_up((size_t)chunk * 4 * sizeof(uint32_t));
+            L.counts = off;
+            off += align_up((size_t)chunk * S * 2 * sizeof(int));
+        }
+    }
+    L.total = off;
+    return L;
+}
+
+// Largest chunk whose layout fits in the given workspace (0 if none).
+int64_t chunk_for(const hisa_index_args* a, int flat, size_t bytes)
+{
+    const int64_t cap = std::min<int64_t>(std::max<int64_t>(a->nq, 1), kChunkMax);
+    if (layout_for(a, flat, 1).total > bytes) return 0;
+    int64_t lo = 1, hi = cap;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) / 2;
+        if (layout_for(a, flat, mid).total <= bytes) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+QueryMeta meta_of(const hisa_index_args* a)
+{
+    QueryMeta qm;
+    qm.queries = a->queries;
+    qm.q_pos = a->q_pos;
+    qm.q_seq = a->q_seq;
+    qm.seq_key_off = a->seq_key_off;
+    qm.seq_rep_off = a->seq_rep_off;
+    qm.seq_len = a->seq_len;
+    qm.nseq = a->nseq;
+    qm.max_len = a->max_len;
+    return qm;
+}
+
+template <class T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+
+}  // namespace
+
+extern "C" {
+
+int hisa_abi_version(void) { return HISA_ABI_VERSION; }
+
+const char* hisa_status_str(int status)
+{
+    switch (status) {
+        case HISA_OK: return "ok";
+        case HISA_ERR_INVALID_ARG: return "invalid argument";
+        case HISA_ERR_UNSUPPORTED: return "unsupported size or shape";
+        case HISA_ERR_WORKSPACE: return "workspace too small";
+        case HISA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int hisa_pool_blocks(const uint16_t* keys, int64_t L, int d, int B, uint16_t* reps, void* stream)
+{
+    if (L < 0 || L > HISA_MAX_LEN) return HISA_ERR_INVALID_ARG;
+    if (d != 64 || !valid_B(B)) return HISA_ERR_UNSUPPORTED;
+    if (L == 0) return HISA_OK;
+    if (!keys || !reps) return HISA_ERR_INVALID_ARG;
+    PoolJob job{0, 0, L, L, 0, 0, (L + B - 1) / B};
+    return status_of(launch_pool(const_cast<uint16_t*>(keys), reps, nullptr, B, &job, 1,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+int hisa_append_keys(uint16_t* keys, uint16_t* reps, const hisa_seq* seqs, int nseq, const uint16_t* new_keys,
+                     int64_t n_new, int d, int B, void* stream)
+{
+    if (nseq < 0 || n_new < 0) return HISA_ERR_INVALID_ARG;
+    if (d != 64 || !valid_B(B)) return HISA_ERR_UNSUPPORTED;
+    if (nseq == 0 || n_new == 0) return HISA_OK;
+    if (!keys || !reps || !seqs || !new_keys) return HISA_ERR_INVALID_ARG;
+    for (int s = 0; s < nseq; ++s) {
+        const hisa_seq& q = seqs[s];
+        if (q.key_off < 0 || q.rep_off < 0 || q.len < 0 || q.capacity > HISA_MAX_LEN) return HISA_ERR_INVALID_ARG;
+        if (q.len + n_new > q.capacity) return HISA_ERR_INVALID_ARG;
+    }
+    PoolJob jobs[kPoolJobsPerLaunch];
+    for (int base = 0; base < nseq; base += kPoolJobsPerLaunch) {
+        const int n = std::min(kPoolJobsPerLaunch, nseq - base);
+        for (int i = 0; i < n; ++i) {
+            const hisa_seq& q = seqs[base + i];
+            const int64_t first = q.len / B;
+            const int64_t last = (q.len + n_new - 1) / B;
+            jobs[i] = PoolJob{q.key_off, q.rep_off, q.len, q.len + n_new, (int64_t)(base + i) * n_new, first,
+                              last - first + 1};
+        }
+        const hipError_t err = launch_pool(keys, reps, new_keys, B, jobs, n, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return HISA_ERR_HIP;
+    }
+    return HISA_OK;
+}
+
+int hisa_workspace_bytes(const hisa_index_args* a, int flat, size_t* bytes, size_t* min_bytes)
+{
+    if (!bytes) return HISA_ERR_INVALID_ARG;
+    const int rc = validate_index(a, flat);
+    if (rc != HISA_OK) return rc;
+    const int64_t chunk = std::max<int64_t>(1, std::min<int64_t>(a->nq, kChunkDefault));
+    *bytes = layout_for(a, flat, chunk).total;
+    if (min_bytes) *min_bytes = layout_for(a, flat, 1).total;
+    return HISA_OK;
+}
+
+int hisa_index(const hisa_index_args* a, void* stream_)
+{
+    const int rc = validate_index(a, 0);
+    if (rc != HISA_OK) return rc;
+    if (a->nq == 0) return HISA_OK;
+    if (!a->workspace) return HISA_ERR_WORKSPACE;
+    const int64_t chunk = chunk_for(a, 0, a->workspace_bytes);
+    if (chunk < 1) return HISA_ERR_WORKSPACE;
+    const Layout L = layout_for(a, 0, chunk);
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const QueryMeta qm = meta_of(a);
+    const int64_t Mmax = hisa_Mmax(a);
+    float* sigma = at<float>(a->workspace, L.sigma);
+    int32_t* sel = at<int32_t>(a->workspace, L.sel);
+    uint32_t* ukeys = at<uint32_t>(a->workspace, L.ukeys);
+    for (int64_t q0 = 0; q0 < a->nq; q0 += chunk) {
+        const int64_t nc = std::min(chunk, a->nq - q0);
+        hipError_t err = launch_block_scores(qm, a->reps, q0, nc, a->B, Mmax, sigma, stream);
+        if (err == hipSuccess)
+            err = launch_select_blocks(qm, q0, nc, a->B, a->m, Mmax, sigma, sel, a->out_blocks, stream);
+        if (err == hipSuccess) err = launch_token_scores(qm, a->keys, q0, nc, a->B, a->m, sel, ukeys, stream);
+        if (err == hipSuccess)
+            err = launch_topk_small(ukeys, nc, a->m * a->B, a->k, sel, a->m, a->B, a->out_idx + q0 * a->k,
+                                    a->out_scores ? a->out_scores + q0 * a->k : nullptr, stream);
+        if (err != hipSuccess) return HISA_ERR_HIP;
+    }
+    return HISA_OK;
+}
+
+int hisa_flat_index(const hisa_index_args* a, void* stream_)
+{
+    const int rc = validate_index(a, 1);
+    if (rc != HISA_OK) return rc;
+    if (a->nq == 0) return HISA_OK;
+    if (!a->workspace) return HISA_ERR_WORKSPACE;
+    const int64_t chunk = chunk_for(a, 1, a->workspace_bytes);
+    if (chunk < 1) return HISA_ERR_WORKSPACE;
+    const Layout L = layout_for(a, 1, chunk);
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const QueryMeta qm = meta_of(a);
+    uint32_t* ukeys = at<uint32_t>(a->workspace, L.ukeys);
+    for (int64_t q0 = 0; q0 < a->nq; q0 += chunk) {
+        const int64_t nc = std::min(chunk, a->nq - q0);
+        int32_t* oi = a->out_idx + q0 * a->k;
+        float* os = a->out_scores ? a->out_scores + q0 * a->k : nullptr;
+        hipError_t err = launch_flat_scores(qm, a->keys, q0, nc, a->max_len, ukeys, stream);
+        if (err == hipSuccess) {
+            if (!flat_uses_radix(a)) {
+                err = launch_topk_small(ukeys, nc, (int)a->max_len, a->k, nullptr, 0, 1, oi, os, stream);
+            } else {
+                RadixWorkspace ws{at<int>(a->workspace, L.hist), at<uint32_t>(a->workspace, L.state),
+                                  at<int>(a->workspace, L.counts)};
+                err = launch_topk_radix(ukeys, nc, a->max_len, a->k, ws, oi, os, stream);
+            }
+        }
+        if (err != hipSuccess) return HISA_ERR_HIP;
+    }
+    return HISA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Host-side launchers of the libhisa kernels (internal; the public C ABI is
+// include/hisa.h).  Every launcher only enqueues on `stream` and returns the
+// launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hisa {
+
+// One sequence's part of a pool / append launch.
+struct PoolJob {
+    int64_t key_off;    // first key row of the sequence
+    int64_t rep_off;    // first representative row
+    int64_t len_old;    // keys already in the cache
+    int64_t len_new;    // keys after the append (== len_old for plain pooling)
+    int64_t new_row;    // row of this sequence's first key in new_keys
+    int64_t blk_first;  // first block to (re)compute
+    int64_t nblk;       // blocks to (re)compute
+};
+
+constexpr int kPoolJobsPerLaunch = 16;
+
+hipError_t launch_pool(uint16_t* keys, uint16_t* reps, const uint16_t* new_keys, int B, const PoolJob* jobs,
+                       int njobs, hipStream_t stream);
+
+// Query metadata as passed through the C ABI (device pointers).
+struct QueryMeta {
+    const uint16_t* queries;
+    const int64_t* q_pos;
+    const int32_t* q_seq;
+    const int64_t* seq_key_off;
+    const int64_t* seq_rep_off;
+    const int64_t* seq_len;
+    int32_t nseq;
+    int64_t max_len;
+};
+
+// HISA stage 1: block scores of queries [q0, q0+nq) into sigma [nq, Mmax].
+hipError_t launch_block_scores(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int B,
+                               int64_t Mmax, float* sigma, hipStream_t stream);
+
+// HISA stage 1: causal + forced top-m.  sel [nq, m]; out_blocks (nullable)
+// gets the same rows at query offset q0.
+hipError_t launch_select_blocks(const QueryMeta& qm, int64_t q0, int64_t nq, int B, int m, int64_t Mmax,
+                                const float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream);
+
+// HISA stage 2: token ranking keys of the kept blocks into ukeys [nq, m*B].
+hipError_t launch_token_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int B,
+                               int m, const int32_t* sel, uint32_t* ukeys, hipStream_t stream);
+
+// Flat: ranking keys of every key position into ukeys [nq, Lmax].
+hipError_t launch_flat_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq,
+                              int64_t Lmax, uint32_t* ukeys, hipStream_t stream);
+
+// Top-k of rows of N ranking keys held by one workgroup (N <= 16384).
+// sel == NULL: slot s is token s; otherwise slot s is token
+// sel[row*m + s/B]*B + s%B.
+hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel, int m,
+                             int B, int32_t* out_idx, float* out_scores, hipStream_t stream);
+
+// Top-k of long rows (slot s is token s) with several workgroups per row.
+struct RadixWorkspace {
+    int* hist;        // [nrows, 256]
+    uint32_t* state;  // [nrows, 4]
+    int* counts;      // [nrows, S, 2]
+};
+size_t radix_slices(int64_t nrows, int64_t N);
+hipError_t launch_topk_radix(const uint32_t* ukeys, int64_t nrows, int64_t N, int k, const RadixWorkspace& ws,
+                             int32_t* out_idx, float* out_scores, hipStream_t stream);
+
+}  // namespace hisa

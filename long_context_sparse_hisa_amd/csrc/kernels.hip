@@ -1,0 +1,549 @@
+// libhisa kernels for gfx950: mean pooling / append, HISA stage 1 (block
+// scores, causal + forced top-m), HISA stage 2 (token scores in the kept
+// blocks), the flat indexer's scores, and top-k selection.
+//
+// What each kernel computes follows "HISA: Efficient Hierarchical Indexing
+// for Fine-Grained Sparse Attention" (aitrends.kr summary): structure
+// paragraph (blocks of B, mean-pooled representatives), stage-1 paragraph
+// (inner-product block scores, causal mask, first and last two blocks
+// forced, top-m), stage-2 paragraph (token scores only inside the kept
+// blocks, top-k out), maintenance paragraph (representatives updated at
+// append); and the "DSA" section of "Why long-context LLMs slow down and
+// how sparse attention fixes it" (idea.jsleekr.com) for the flat indexer.
+#include "kernels.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "select.h"
+
+namespace hisa {
+
+// ---- pooling and append ---------------------------------------------------
+// One workgroup per block: 8 threads cover one 128-byte key row (16 bytes,
+// 8 dims each), 32 rows in flight per step, so every load is a fully used
+// 16-byte vector.  The sum is taken in fp64, where adding bf16 values is
+// exact (see the precondition in hisa.h), so the partial-sum order does not
+// change the result.
+
+struct PoolJobs {
+    PoolJob j[kPoolJobsPerLaunch];
+};
+
+__global__ __launch_bounds__(kThreads) void pool_kernel(uint16_t* keys, uint16_t* reps, const uint16_t* new_keys,
+                                                        int B, PoolJobs jobs)
+{
+    const PoolJob& job = jobs.j[blockIdx.y];
+    if ((int64_t)blockIdx.x >= job.nblk) return;
+    const int64_t blk = job.blk_first + blockIdx.x;
+    const int64_t start = blk * B;
+    const int count = (int)min((int64_t)B, job.len_new - start);
+    const int col = threadIdx.x & 7;
+    const int grp = threadIdx.x >> 3;
+
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    for (int r = grp; r < count; r += 32) {
+        const int64_t j = start + r;
+        uint4 v;
+        if (j < job.len_old) {
+            v = reinterpret_cast<const uint4*>(keys + (job.key_off + j) * kDim)[col];
+        } else {
+            v = reinterpret_cast<const uint4*>(new_keys + (job.new_row + (j - job.len_old)) * kDim)[col];
+            reinterpret_cast<uint4*>(keys + (job.key_off + j) * kDim)[col] = v;
+        }
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e + 0] += (double)bf16_lo(w[e]);
+            acc[2 * e + 1] += (double)bf16_hi(w[e]);
+        }
+    }
+    __shared__ double part[32][kDim];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[grp][col * 8 + e] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < kDim) {
+        double s = 0.0;
+        for (int g = 0; g < 32; ++g) s += part[g][threadIdx.x];
+        const double mean = s / (double)count;
+        reps[(job.rep_off + blk) * kDim + threadIdx.x] = f64_to_bf16_rne(mean);
+    }
+}
+
+hipError_t launch_pool(uint16_t* keys, uint16_t* reps, const uint16_t* new_keys, int B, const PoolJob* jobs,
+                       int njobs, hipStream_t stream)
+{
+    for (int base = 0; base < njobs; base += kPoolJobsPerLaunch) {
+        const int n = std::min(kPoolJobsPerLaunch, njobs - base);
+        PoolJobs pj;
+        int64_t maxblk = 0;
+        for (int i = 0; i < kPoolJobsPerLaunch; ++i) {
+            pj.j[i] = i < n ? jobs[base + i] : PoolJob{0, 0, 0, 0, 0, 0, 0};
+            if (i < n) maxblk = std::max(maxblk, pj.j[i].nblk);
+        }
+        if (maxblk == 0) continue;
+        hipLaunchKernelGGL(pool_kernel, dim3((unsigned)maxblk, (unsigned)n), dim3(kThreads), 0, stream, keys, reps,
+                           new_keys, B, pj);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+// ---- HISA stage 1: block scores --------------------------------------------
+// One thread per (query, causal block): a 128-byte representative row
+// against the query held in registers.
+
+__global__ __launch_bounds__(kThreads) void block_score_kernel(QueryMeta qm, const uint16_t* reps, int64_t q0,
+                                                               int B, int64_t Mmax, float* sigma)
+{
+    const int64_t row = blockIdx.y;
+    const int64_t i = q0 + row;
+    const QueryInfo qi =
+        query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
+    if (!qi.valid) return;
+    const int64_t c = qi.t / B;
+    const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (b > c) return;
+    uint32_t q[32];
+    load_query(qm.queries + i * kDim, q);
+    const uint4* rp = reinterpret_cast<const uint4*>(reps + (qi.rep_off + b) * kDim);
+    sigma[row * Mmax + b] = dot64_packed(q, rp);
+}
+
+hipError_t launch_block_scores(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int B,
+                               int64_t Mmax, float* sigma, hipStream_t stream)
+{
+    dim3 grid((unsigned)((Mmax + kThreads - 1) / kThreads), (unsigned)nq);
+    hipLaunchKernelGGL(block_score_kernel, grid, dim3(kThreads), 0, stream, qm, reps, q0, B, Mmax, sigma);
+    return hipGetLastError();
+}
+
+// ---- HISA stage 1: causal + forced top-m -----------------------------------
+// One workgroup per query.  Block b sits in slot b; the free candidates are
+// blocks 1 .. c-2, from which m-3 are chosen; blocks 0, c-1, c are added.
+
+template <int ITEMS>
+__global__ __launch_bounds__(kThreads) void select_blocks_kernel(QueryMeta qm, int64_t q0, int B, int m,
+                                                                 int64_t Mmax, const float* sigma, int32_t* sel,
+                                                                 int32_t* out_blocks)
+{
+    __shared__ SelectSmem<ITEMS> sm;
+    const int64_t row = blockIdx.x;
+    const int64_t i = q0 + row;
+    const QueryInfo qi =
+        query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
+    int32_t* srow = sel + row * m;
+    int32_t* orow = out_blocks ? out_blocks + i * m : nullptr;
+    if (!qi.valid) {
+        for (int r = threadIdx.x; r < m; r += kThreads) {
+            srow[r] = -1;
+            if (orow) orow[r] = -1;
+        }
+        return;
+    }
+    const int64_t c = qi.t / B;
+    if (c + 1 <= m) {
+        for (int r = threadIdx.x; r < m; r += kThreads) {
+            const int32_t v = r <= c ? r : -1;
+            srow[r] = v;
+            if (orow) orow[r] = v;
+        }
+        return;
+    }
+    const float* sg = sigma + row * Mmax;
+    uint32_t key[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int64_t b = (int64_t)it * kThreads + threadIdx.x;
+        key[it] = (b >= 1 && b <= c - 2) ? score_key(sg[b]) : 0u;
+    }
+    const Threshold th = wg_radix_select(key, m - 3, sm);
+    wg_emit_selected(key, th, sm, [&](int slot, uint32_t, int rank) {
+        srow[1 + rank] = slot;
+        if (orow) orow[1 + rank] = slot;
+    });
+    if (threadIdx.x == 0) {
+        srow[0] = 0;
+        srow[m - 2] = (int32_t)(c - 1);
+        srow[m - 1] = (int32_t)c;
+        if (orow) {
+            orow[0] = 0;
+            orow[m - 2] = (int32_t)(c - 1);
+            orow[m - 1] = (int32_t)c;
+        }
+    }
+}
+
+template <int ITEMS>
+static hipError_t launch_select_items(const QueryMeta& qm, int64_t q0, int64_t nq, int B, int m, int64_t Mmax,
+                                      const float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL(select_blocks_kernel<ITEMS>, dim3((unsigned)nq), dim3(kThreads), 0, stream, qm, q0, B, m,
+                       Mmax, sigma, sel, out_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_blocks(const QueryMeta& qm, int64_t q0, int64_t nq, int B, int m, int64_t Mmax,
+                                const float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream)
+{
+    const int64_t per = (Mmax + kThreads - 1) / kThreads;
+    if (per <= 1) return launch_select_items<1>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
+    if (per <= 2) return launch_select_items<2>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
+    if (per <= 4) return launch_select_items<4>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
+    if (per <= 8) return launch_select_items<8>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
+    if (per <= 16) return launch_select_items<16>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
+    if (per <= 32) return launch_select_items<32>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
+    if (per <= 64) return launch_select_items<64>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
+    return hipErrorInvalidValue;
+}
+
+// ---- HISA stage 2: token scores in the kept blocks -------------------------
+// Candidate slot s of a query is row s % B of kept block s / B; slots of
+// padding blocks and keys after the query get key 0.
+
+__global__ __launch_bounds__(kThreads) void token_score_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0,
+                                                               int B, int m, const int32_t* sel, uint32_t* ukeys)
+{
+    const int64_t row = blockIdx.y;
+    const int64_t i = q0 + row;
+    const int64_t N = (int64_t)m * B;
+    const int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (s >= N) return;
+    uint32_t* out = ukeys + row * N + s;
+    const QueryInfo qi =
+        query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
+    if (!qi.valid) {
+        *out = 0u;
+        return;
+    }
+    const int32_t blk = sel[row * m + s / B];
+    const int64_t j = (int64_t)blk * B + s % B;
+    if (blk < 0 || j > qi.t) {
+        *out = 0u;
+        return;
+    }
+    uint32_t q[32];
+    load_query(qm.queries + i * kDim, q);
+    *out = score_key(dot64_packed(q, reinterpret_cast<const uint4*>(keys + (qi.key_off + j) * kDim)));
+}
+
+hipError_t launch_token_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int B, int m,
+                               const int32_t* sel, uint32_t* ukeys, hipStream_t stream)
+{
+    const int64_t N = (int64_t)m * B;
+    dim3 grid((unsigned)((N + kThreads - 1) / kThreads), (unsigned)nq);
+    hipLaunchKernelGGL(token_score_kernel, grid, dim3(kThreads), 0, stream, qm, keys, q0, B, m, sel, ukeys);
+    return hipGetLastError();
+}
+
+// ---- flat indexer: every key ------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void flat_score_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0,
+                                                              int64_t Lmax, uint32_t* ukeys)
+{
+    const int64_t row = blockIdx.y;
+    const int64_t i = q0 + row;
+    const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (j >= Lmax) return;
+    uint32_t* out = ukeys + row * Lmax + j;
+    const QueryInfo qi =
+        query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
+    if (!qi.valid || j > qi.t) {
+        *out = 0u;
+        return;
+    }
+    uint32_t q[32];
+    load_query(qm.queries + i * kDim, q);
+    *out = score_key(dot64_packed(q, reinterpret_cast<const uint4*>(keys + (qi.key_off + j) * kDim)));
+}
+
+hipError_t launch_flat_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int64_t Lmax,
+                              uint32_t* ukeys, hipStream_t stream)
+{
+    dim3 grid((unsigned)((Lmax + kThreads - 1) / kThreads), (unsigned)nq);
+    hipLaunchKernelGGL(flat_score_kernel, grid, dim3(kThreads), 0, stream, qm, keys, q0, Lmax, ukeys);
+    return hipGetLastError();
+}
+
+// ---- top-k of short rows: one workgroup per row ----------------------------
+
+template <int ITEMS>
+__global__ __launch_bounds__(kThreads) void topk_small_kernel(const uint32_t* ukeys, int N, int k, const int32_t* sel,
+                                                              int m, int B, int32_t* out_idx, float* out_scores)
+{
+    __shared__ SelectSmem<ITEMS> sm;
+    const int64_t row = blockIdx.x;
+    const uint32_t* src = ukeys + row * N;
+    uint32_t key[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int s = it * kThreads + threadIdx.x;
+        key[it] = s < N ? src[s] : 0u;
+    }
+    const Threshold th = wg_radix_select(key, k, sm);
+    int32_t* orow = out_idx + row * k;
+    float* srow = out_scores ? out_scores + row * k : nullptr;
+    const int32_t* selrow = sel ? sel + row * m : nullptr;
+    const int total = wg_emit_selected(key, th, sm, [&](int slot, uint32_t kk, int rank) {
+        orow[rank] = selrow ? selrow[slot / B] * B + slot % B : slot;
+        if (srow) srow[rank] = key_score(kk);
+    });
+    for (int r = total + threadIdx.x; r < k; r += kThreads) {
+        orow[r] = -1;
+        if (srow) srow[r] = __builtin_nanf("");
+    }
+}
+
+template <int ITEMS>
+static hipError_t launch_topk_items(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel, int m,
+                                    int B, int32_t* out_idx, float* out_scores, hipStream_t stream)
+{
+    hipLaunchKernelGGL(topk_small_kernel<ITEMS>, dim3((unsigned)nrows), dim3(kThreads), 0, stream, ukeys, N, k, sel,
+                       m, B, out_idx, out_scores);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel, int m, int B,
+                             int32_t* out_idx, float* out_scores, hipStream_t stream)
+{
+    const int per = (N + kThreads - 1) / kThreads;
+    if (per <= 1) return launch_topk_items<1>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
+    if (per <= 2) return launch_topk_items<2>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
+    if (per <= 4) return launch_topk_items<4>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
+    if (per <= 8) return launch_topk_items<8>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
+    if (per <= 16) return launch_topk_items<16>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
+    if (per <= 32) return launch_topk_items<32>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
+    if (per <= 64) return launch_topk_items<64>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
+    return hipErrorInvalidValue;
+}
+
+// ---- top-k of long rows: S workgroups per row --------------------------------
+// Four histogram passes of 8 bits (partial histograms merged with global
+// atomics, one small kernel per pass picking the digit), then a count pass
+// and an emit pass that writes each slice's selection at the offset given by
+// the counts of the slices before it, so rows come out in ascending order.
+// state[row] = {prefix, mask, remaining, all}.
+
+constexpr int64_t kSliceMin = 4096;
+constexpr int64_t kRadixTargetWgs = 1024;
+
+size_t radix_slices(int64_t nrows, int64_t N)
+{
+    const int64_t max_s = (N + kSliceMin - 1) / kSliceMin;
+    int64_t want = (kRadixTargetWgs + nrows - 1) / std::max<int64_t>(nrows, 1);
+    if (want < 1) want = 1;
+    return (size_t)std::min(want, std::max<int64_t>(max_s, 1));
+}
+
+static int64_t slice_len_of(int64_t N, int64_t S)
+{
+    const int64_t per = (N + S - 1) / S;
+    return (per + kThreads - 1) / kThreads * kThreads;
+}
+
+__global__ __launch_bounds__(kThreads) void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(kThreads) void radix_hist_kernel(const uint32_t* ukeys, int64_t N, int64_t slice_len,
+                                                              int pass, int* hist, const uint32_t* state)
+{
+    __shared__ int h[256];
+    const int64_t row = blockIdx.y;
+    uint32_t prefix = 0u, mask = 0u;
+    if (pass > 0) {
+        const uint32_t* st = state + row * 4;
+        if (st[3]) return;
+        prefix = st[0];
+        mask = st[1];
+    }
+    h[threadIdx.x] = 0;
+    __syncthreads();
+    const int shift = 24 - 8 * pass;
+    const int64_t beg = (int64_t)blockIdx.x * slice_len;
+    const int64_t end = min(N, beg + slice_len);
+    const uint32_t* src = ukeys + row * N;
+    for (int64_t e = beg + threadIdx.x; e < end; e += kThreads) {
+        const uint32_t kk = src[e];
+        if (kk != 0u && (kk & mask) == prefix) atomicAdd(&h[(kk >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    const int v = h[threadIdx.x];
+    if (v) atomicAdd(&hist[row * 256 + threadIdx.x], v);
+}
+
+__global__ __launch_bounds__(kThreads) void radix_digit_kernel(int* hist, uint32_t* state, int k, int pass)
+{
+    __shared__ int scratch[kWaves];
+    __shared__ int pick[2];
+    const int64_t row = blockIdx.x;
+    uint32_t* st = state + row * 4;
+    if (pass > 0 && st[3]) return;
+    int* hr = hist + row * 256;
+    const int h = hr[255 - threadIdx.x];
+    hr[255 - threadIdx.x] = 0;   // ready for the next pass
+    const uint32_t prefix = pass ? st[0] : 0u;
+    const uint32_t mask = pass ? st[1] : 0u;
+    const int rem = pass ? (int)st[2] : k;
+    if (pass == 0) {
+        const int total = block_sum(h, scratch);
+        if (total <= k) {
+            if (threadIdx.x == 0) {
+                st[0] = 0u;
+                st[1] = 0u;
+                st[2] = 0u;
+                st[3] = 1u;
+            }
+            return;
+        }
+    }
+    const int cum = block_incl_scan(h, scratch);
+    if (cum >= rem && cum - h < rem) {
+        pick[0] = 255 - (int)threadIdx.x;
+        pick[1] = cum - h;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int shift = 24 - 8 * pass;
+        st[0] = prefix | ((uint32_t)pick[0] << shift);
+        st[1] = mask | (0xffu << shift);
+        st[2] = (uint32_t)(rem - pick[1]);
+        st[3] = 0u;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void radix_count_kernel(const uint32_t* ukeys, int64_t N, int64_t slice_len,
+                                                               const uint32_t* state, int* counts, int64_t S)
+{
+    __shared__ int scratch[kWaves];
+    const int64_t row = blockIdx.y;
+    const uint32_t* st = state + row * 4;
+    const bool all = st[3] != 0u;
+    const uint32_t T = all ? 0u : st[0];
+    const int64_t beg = (int64_t)blockIdx.x * slice_len;
+    const int64_t end = min(N, beg + slice_len);
+    const uint32_t* src = ukeys + row * N;
+    int g = 0, q = 0;
+    for (int64_t e = beg + threadIdx.x; e < end; e += kThreads) {
+        const uint32_t kk = src[e];
+        g += kk > T;
+        q += !all && kk == T;
+    }
+    g = block_sum(g, scratch);
+    q = block_sum(q, scratch);
+    if (threadIdx.x == 0) {
+        counts[(row * S + blockIdx.x) * 2 + 0] = g;
+        counts[(row * S + blockIdx.x) * 2 + 1] = q;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void radix_emit_kernel(const uint32_t* ukeys, int64_t N, int64_t slice_len,
+                                                              const uint32_t* state, const int* counts, int64_t S,
+                                                              int k, int32_t* out_idx, float* out_scores)
+{
+    __shared__ int scratch[kWaves];
+    __shared__ int wc[2][kWaves];
+    const int64_t row = blockIdx.y;
+    const int64_t slice = blockIdx.x;
+    const uint32_t* st = state + row * 4;
+    const bool all = st[3] != 0u;
+    const uint32_t T = all ? 0u : st[0];
+    const int need_eq = all ? 0 : (int)st[2];
+    int bg = 0, be = 0, tg = 0, te = 0;
+    for (int64_t s = threadIdx.x; s < S; s += kThreads) {
+        const int g = counts[(row * S + s) * 2 + 0];
+        const int q = counts[(row * S + s) * 2 + 1];
+        if (s < slice) {
+            bg += g;
+            be += q;
+        }
+        tg += g;
+        te += q;
+    }
+    bg = block_sum(bg, scratch);
+    be = block_sum(be, scratch);
+    tg = block_sum(tg, scratch);
+    te = block_sum(te, scratch);
+    int32_t* orow = out_idx + row * k;
+    float* srow = out_scores ? out_scores + row * k : nullptr;
+    if (slice == 0) {
+        const int total = tg + min(te, need_eq);
+        for (int r = total + threadIdx.x; r < k; r += kThreads) {
+            orow[r] = -1;
+            if (srow) srow[r] = __builtin_nanf("");
+        }
+    }
+    const int64_t beg = slice * slice_len;
+    const int64_t end = min(N, beg + slice_len);
+    const uint32_t* src = ukeys + row * N;
+    const int w = wave_id();
+    for (int64_t base = beg; base < end; base += kThreads) {
+        const int64_t e = base + threadIdx.x;
+        const uint32_t kk = e < end ? src[e] : 0u;
+        const bool gt = kk > T;
+        const bool eq = !all && e < end && kk == T;
+        const uint64_t mg = __ballot(gt);
+        const uint64_t me = __ballot(eq);
+        if (lane_id() == 0) {
+            wc[0][w] = __popcll(mg);
+            wc[1][w] = __popcll(me);
+        }
+        __syncthreads();
+        int og = bg, oe = be, sg = 0, se = 0;
+        for (int v = 0; v < kWaves; ++v) {
+            if (v < w) {
+                og += wc[0][v];
+                oe += wc[1][v];
+            }
+            sg += wc[0][v];
+            se += wc[1][v];
+        }
+        const int pg = og + __popcll(mg & lanemask_lt());
+        const int pe = oe + __popcll(me & lanemask_lt());
+        int pos = -1;
+        if (gt) pos = pg + min(pe, need_eq);
+        else if (eq && pe < need_eq) pos = pg + pe;
+        if (pos >= 0) {
+            orow[pos] = (int32_t)e;
+            if (srow) srow[pos] = key_score(kk);
+        }
+        bg += sg;
+        be += se;
+        __syncthreads();
+    }
+}
+
+hipError_t launch_topk_radix(const uint32_t* ukeys, int64_t nrows, int64_t N, int k, const RadixWorkspace& ws,
+                             int32_t* out_idx, float* out_scores, hipStream_t stream)
+{
+    const int64_t S = (int64_t)radix_slices(nrows, N);
+    const int64_t slice_len = slice_len_of(N, S);
+    const int64_t nh = nrows * 256;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nh + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
+                       reinterpret_cast<uint32_t*>(ws.hist), nh, 0u);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const dim3 grid((unsigned)S, (unsigned)nrows);
+    for (int pass = 0; pass < 4; ++pass) {
+        hipLaunchKernelGGL(radix_hist_kernel, grid, dim3(kThreads), 0, stream, ukeys, N, slice_len, pass, ws.hist,
+                           ws.state);
+        hipLaunchKernelGGL(radix_digit_kernel, dim3((unsigned)nrows), dim3(kThreads), 0, stream, ws.hist, ws.state,
+                           k, pass);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(radix_count_kernel, grid, dim3(kThreads), 0, stream, ukeys, N, slice_len, ws.state, ws.counts,
+                       S);
+    hipLaunchKernelGGL(radix_emit_kernel, grid, dim3(kThreads), 0, stream, ukeys, N, slice_len, ws.state, ws.counts,
+                       S, k, out_idx, out_scores);
+    return hipGetLastError();
+}
+
+}  // namespace hisa

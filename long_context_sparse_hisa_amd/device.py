@@ -1,0 +1,118 @@
+"""Device-side state of a workload: packed keys, representatives, lengths,
+and the buffers the index calls write.  Marshalling only: every computation
+is a libhisa call.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import hisa
+from .synth import D, Workload
+
+
+def to_dev(a: np.ndarray, device) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+class DeviceCache:
+    """Packed key cache and block representatives of a workload's sequences."""
+
+    def __init__(self, w: Workload, B: int | None = None, device: str = "cuda:0", stream=None):
+        self.w = w
+        self.B = B or w.B
+        self.device = torch.device(device)
+        self.stream = stream
+        self.keys = to_dev(w.keys, self.device)
+        self.seq_key_off = np.asarray(w.seq_key_off, np.int64)
+        self.seq_rep_off = w.seq_rep_off(self.B)
+        self.seq_cap = np.asarray(w.seq_cap, np.int64)
+        self.seq_len = np.asarray(w.seq_len, np.int64).copy()
+        self.reps = torch.zeros((w.total_rep_rows(self.B), D), dtype=torch.int16, device=self.device)
+        self.d_key_off = to_dev(self.seq_key_off, self.device)
+        self.d_rep_off = to_dev(self.seq_rep_off, self.device)
+        self.d_len = to_dev(self.seq_len, self.device)
+        self._ws = {}
+
+    @property
+    def nseq(self) -> int:
+        return len(self.seq_len)
+
+    def pool(self):
+        for s in range(self.nseq):
+            o, n, r = int(self.seq_key_off[s]), int(self.seq_len[s]), int(self.seq_rep_off[s])
+            nb = (n + self.B - 1) // self.B
+            hisa.hisa_pool_blocks(self.keys[o:o + n], self.B, self.reps[r:r + max(nb, 1)], self.stream)
+
+    def append(self, new_keys: np.ndarray | torch.Tensor, update_lengths: bool = True):
+        """Append new_keys [nseq, n_new, D] (bf16 bits) to every sequence."""
+        nk = new_keys if isinstance(new_keys, torch.Tensor) else to_dev(new_keys, self.device)
+        seqs = [(self.seq_key_off[s], self.seq_rep_off[s], self.seq_len[s], self.seq_cap[s])
+                for s in range(self.nseq)]
+        hisa.hisa_append_keys(self.keys, self.reps, seqs, nk, self.B, self.stream)
+        if update_lengths:
+            self.seq_len += nk.shape[1]
+            self.d_len.copy_(torch.from_numpy(self.seq_len))
+
+    def set_lengths(self, lengths):
+        self.seq_len = np.asarray(lengths, np.int64).copy()
+        self.d_len.copy_(torch.from_numpy(self.seq_len))
+
+    def workspace(self, nbytes: int, tag: str = "") -> torch.Tensor:
+        ws = self._ws.get(tag)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            self._ws[tag] = ws
+        return ws
+
+
+class IndexCall:
+    """Buffers and arguments of one index call, reusable across launches."""
+
+    def __init__(self, cache: DeviceCache, queries, q_pos, q_seq, k: int, m: int | None = None,
+                 flat: bool = False, scores: bool = True, blocks: bool = True,
+                 max_len: int | None = None, workspace_bytes: int | None = None):
+        dev = cache.device
+        self.cache = cache
+        self.flat = flat
+        self.queries = queries if isinstance(queries, torch.Tensor) else to_dev(queries, dev)
+        self.q_pos = q_pos if isinstance(q_pos, torch.Tensor) else to_dev(np.asarray(q_pos, np.int64), dev)
+        self.q_seq = q_seq if isinstance(q_seq, torch.Tensor) else to_dev(np.asarray(q_seq, np.int32), dev)
+        nq = self.queries.shape[0]
+        self.k = k
+        self.m = m if m is not None else cache.w.m
+        self.out_idx = torch.empty((nq, k), dtype=torch.int32, device=dev)
+        self.out_scores = torch.empty((nq, k), dtype=torch.float32, device=dev) if scores else None
+        self.out_blocks = (torch.empty((nq, self.m), dtype=torch.int32, device=dev)
+                           if (blocks and not flat) else None)
+        self.max_len = int(max_len if max_len is not None else cache.seq_cap.max())
+        args = self._args(None)
+        want, _ = hisa.hisa_workspace_bytes(args, flat)
+        nbytes = want if workspace_bytes is None else workspace_bytes
+        self.workspace = cache.workspace(nbytes, "flat" if flat else "hisa")
+        self.args = self._args(self.workspace)
+        self.args.workspace_bytes = nbytes
+
+    def _args(self, ws):
+        c = self.cache
+        return hisa.make_args(self.queries, self.q_pos, c.keys, self.k, reps=c.reps, q_seq=self.q_seq,
+                              seq_key_off=c.d_key_off, seq_rep_off=c.d_rep_off, seq_len=c.d_len,
+                              max_len=self.max_len, B=c.B, m=self.m, out_idx=self.out_idx,
+                              out_scores=self.out_scores, out_blocks=self.out_blocks, workspace=ws)
+
+    def run(self, stream=None):
+        if self.flat:
+            hisa.hisa_flat_index(self.args, stream or self.cache.stream)
+        else:
+            hisa.hisa_index(self.args, stream or self.cache.stream)
+
+    def results(self):
+        """(idx, scores or None, blocks or None) as numpy arrays."""
+        torch.cuda.synchronize()
+        idx = self.out_idx.cpu().numpy()
+        sc = None if self.out_scores is None else self.out_scores.cpu().numpy()
+        blk = None if self.out_blocks is None else self.out_blocks.cpu().numpy()
+        return idx, sc, blk

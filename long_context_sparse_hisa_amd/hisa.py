@@ -1,0 +1,168 @@
+"""Thin ctypes binding of libhisa (include/hisa.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the indexer runs in the HIP library.
+The library must have been built (``python -m long_context_sparse_hisa_amd.build``);
+if it is missing, or a tensor is not on the GPU, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libhisa.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "hisa.h")
+
+HISA_OK = 0
+HISA_ERR_INVALID_ARG = -1
+HISA_ERR_UNSUPPORTED = -2
+HISA_ERR_WORKSPACE = -3
+HISA_ERR_HIP = -4
+
+_P = ctypes.c_void_p
+_lib = None
+
+
+class HisaError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__("%s: %s (%d)" % (call, status_str(status), status))
+
+
+class hisa_seq(ctypes.Structure):
+    _fields_ = [("key_off", ctypes.c_int64), ("rep_off", ctypes.c_int64), ("len", ctypes.c_int64),
+                ("capacity", ctypes.c_int64)]
+
+
+class hisa_index_args(ctypes.Structure):
+    _fields_ = [
+        ("queries", _P), ("q_pos", _P), ("q_seq", _P), ("nq", ctypes.c_int64),
+        ("keys", _P), ("reps", _P), ("seq_key_off", _P), ("seq_rep_off", _P), ("seq_len", _P),
+        ("nseq", ctypes.c_int32), ("max_len", ctypes.c_int64),
+        ("d", ctypes.c_int32), ("B", ctypes.c_int32), ("m", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("out_idx", _P), ("out_scores", _P), ("out_blocks", _P),
+        ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+def lib():
+    """The loaded libhisa (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libhisa.so is not built: run python -m long_context_sparse_hisa_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        L.hisa_pool_blocks.argtypes = [_P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _P, _P]
+        L.hisa_append_keys.argtypes = [_P, _P, ctypes.POINTER(hisa_seq), ctypes.c_int, _P,
+                                       ctypes.c_int64, ctypes.c_int, ctypes.c_int, _P]
+        L.hisa_workspace_bytes.argtypes = [ctypes.POINTER(hisa_index_args), ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_size_t),
+                                           ctypes.POINTER(ctypes.c_size_t)]
+        L.hisa_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
+        L.hisa_flat_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
+        L.hisa_status_str.restype = ctypes.c_char_p
+        L.hisa_status_str.argtypes = [ctypes.c_int]
+        L.hisa_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/hisa.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(hisa_\w+)\s*\(", text, re.M)))
+
+
+def status_str(status: int) -> str:
+    return lib().hisa_status_str(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().hisa_abi_version())
+
+
+def _check(rc: int, call: str):
+    if rc != HISA_OK:
+        raise HisaError(rc, call)
+
+
+def _dev(t, what: str, nbytes_per_elem=None):
+    """Device pointer of a contiguous GPU tensor (or None)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % what)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % what)
+    if nbytes_per_elem is not None and t.element_size() != nbytes_per_elem:
+        raise ValueError("%s must have %d-byte elements" % (what, nbytes_per_elem))
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def hisa_pool_blocks(keys, B: int, reps, stream=None):
+    """reps[:ceil(L/B)] = block means of keys [L, 64] (bf16 bits)."""
+    rc = lib().hisa_pool_blocks(_dev(keys, "keys", 2), keys.shape[0], keys.shape[1], B,
+                                _dev(reps, "reps", 2), _stream(stream))
+    _check(rc, "hisa_pool_blocks")
+
+
+def hisa_append_keys(keys, reps, seqs, new_keys, B: int, stream=None):
+    """Append new_keys [nseq, n_new, 64] to each sequence; seqs is a list of
+    (key_off, rep_off, len, capacity) with the lengths before the append."""
+    arr = (hisa_seq * max(1, len(seqs)))(*[hisa_seq(*map(int, s)) for s in seqs])
+    n_new = new_keys.shape[1] if new_keys.dim() == 3 else new_keys.shape[0]
+    rc = lib().hisa_append_keys(_dev(keys, "keys", 2), _dev(reps, "reps", 2), arr, len(seqs),
+                                _dev(new_keys, "new_keys", 2), n_new, keys.shape[-1], B,
+                                _stream(stream))
+    _check(rc, "hisa_append_keys")
+
+
+def make_args(queries, q_pos, keys, k: int, *, reps=None, q_seq=None, seq_key_off=None,
+              seq_rep_off=None, seq_len=None, max_len=None, B: int = 128, m: int = 64,
+              out_idx=None, out_scores=None, out_blocks=None, workspace=None) -> hisa_index_args:
+    a = hisa_index_args()
+    a.queries = _dev(queries, "queries", 2)
+    a.q_pos = _dev(q_pos, "q_pos", 8)
+    a.q_seq = _dev(q_seq, "q_seq", 4)
+    a.nq = queries.shape[0]
+    a.keys = _dev(keys, "keys", 2)
+    a.reps = _dev(reps, "reps", 2)
+    a.seq_key_off = _dev(seq_key_off, "seq_key_off", 8)
+    a.seq_rep_off = _dev(seq_rep_off, "seq_rep_off", 8)
+    a.seq_len = _dev(seq_len, "seq_len", 8)
+    a.nseq = 1 if seq_len is None else seq_len.shape[0]
+    a.max_len = keys.shape[0] if max_len is None else int(max_len)
+    a.d = queries.shape[1]
+    a.B, a.m, a.k = B, m, k
+    a.out_idx = _dev(out_idx, "out_idx", 4)
+    a.out_scores = _dev(out_scores, "out_scores", 4)
+    a.out_blocks = _dev(out_blocks, "out_blocks", 4)
+    if workspace is not None:
+        a.workspace = _dev(workspace, "workspace")
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def hisa_workspace_bytes(args: hisa_index_args, flat: bool = False):
+    """(recommended bytes, minimum bytes) of workspace for these args."""
+    b = ctypes.c_size_t(0)
+    mb = ctypes.c_size_t(0)
+    rc = lib().hisa_workspace_bytes(ctypes.byref(args), int(flat), ctypes.byref(b), ctypes.byref(mb))
+    _check(rc, "hisa_workspace_bytes")
+    return int(b.value), int(mb.value)
+
+
+def hisa_index(args: hisa_index_args, stream=None):
+    _check(lib().hisa_index(ctypes.byref(args), _stream(stream)), "hisa_index")
+
+
+def hisa_flat_index(args: hisa_index_args, stream=None):
+    _check(lib().hisa_flat_index(ctypes.byref(args), _stream(stream)), "hisa_flat_index")

@@ -1,0 +1,117 @@
+"""The C-ABI library without a GPU: it loads, exports what include/hisa.h
+declares, and rejects bad arguments on the host before touching a device."""
+import ctypes
+import os
+
+import pytest
+
+from long_context_sparse_hisa_amd import hisa
+
+FAKE = 0x1000          # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hisa.LIB_PATH):
+        from long_context_sparse_hisa_amd import build
+        build.build()
+    return hisa.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = hisa.header_functions()
+    assert {"hisa_pool_blocks", "hisa_append_keys", "hisa_index", "hisa_flat_index",
+            "hisa_workspace_bytes", "hisa_status_str", "hisa_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert hisa.abi_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert hisa.status_str(code) != "unknown status"
+    assert hisa.status_str(7) == "unknown status"
+
+
+def _args(**kw):
+    a = hisa.hisa_index_args()
+    a.queries = FAKE
+    a.q_pos = FAKE
+    a.keys = FAKE
+    a.reps = FAKE
+    a.out_idx = FAKE
+    a.nq = 16
+    a.nseq = 1
+    a.max_len = 32768
+    a.d, a.B, a.m, a.k = 64, 128, 64, 2048
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _rc(fn, a):
+    return fn(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("d", 32, hisa.HISA_ERR_UNSUPPORTED),
+    ("B", 100, hisa.HISA_ERR_UNSUPPORTED),
+    ("B", 512, hisa.HISA_ERR_UNSUPPORTED),
+    ("m", 2, hisa.HISA_ERR_INVALID_ARG),
+    ("k", 0, hisa.HISA_ERR_INVALID_ARG),
+    ("k", 8193, hisa.HISA_ERR_INVALID_ARG),        # m*B < k: the no-loss condition
+    ("m", 200, hisa.HISA_ERR_UNSUPPORTED),         # m*B beyond the candidate limit
+    ("nq", -1, hisa.HISA_ERR_INVALID_ARG),
+    ("nseq", 0, hisa.HISA_ERR_INVALID_ARG),
+    ("nseq", 2, hisa.HISA_ERR_INVALID_ARG),        # several sequences need offsets
+    ("max_len", 0, hisa.HISA_ERR_INVALID_ARG),
+    ("max_len", (1 << 30) + 1, hisa.HISA_ERR_UNSUPPORTED),
+    ("queries", None, hisa.HISA_ERR_INVALID_ARG),
+    ("reps", None, hisa.HISA_ERR_INVALID_ARG),
+    ("out_idx", None, hisa.HISA_ERR_INVALID_ARG),
+])
+def test_index_validation(lib, field, value, code):
+    assert _rc(lib.hisa_index, _args(**{field: value})) == code
+
+
+def test_flat_ignores_block_arguments(lib):
+    a = _args(B=100, m=0, reps=None, workspace=FAKE, workspace_bytes=16)
+    assert _rc(lib.hisa_flat_index, a) == hisa.HISA_ERR_WORKSPACE
+    assert _rc(lib.hisa_flat_index, _args(d=16)) == hisa.HISA_ERR_UNSUPPORTED
+
+
+def test_workspace_checks(lib):
+    a = _args()
+    assert _rc(lib.hisa_index, a) == hisa.HISA_ERR_WORKSPACE          # none given
+    want, least = hisa.hisa_workspace_bytes(a)
+    assert 0 < least <= want
+    a = _args(workspace=FAKE, workspace_bytes=least - 1)
+    assert _rc(lib.hisa_index, a) == hisa.HISA_ERR_WORKSPACE
+    fw, fl = hisa.hisa_workspace_bytes(_args(), flat=True)
+    assert 0 < fl <= fw
+    # one query of a 32K flat row needs its 32768 ranking keys
+    assert fl >= 32768 * 4
+
+
+def test_zero_queries_is_a_no_op(lib):
+    a = _args(nq=0, queries=None, q_pos=None, out_idx=None)
+    assert _rc(lib.hisa_index, a) == hisa.HISA_OK
+    assert _rc(lib.hisa_flat_index, a) == hisa.HISA_OK
+
+
+def test_pool_and_append_validation(lib):
+    P = ctypes.c_void_p
+    assert lib.hisa_pool_blocks(P(FAKE), 0, 64, 128, P(FAKE), None) == hisa.HISA_OK
+    assert lib.hisa_pool_blocks(P(FAKE), -1, 64, 128, P(FAKE), None) == hisa.HISA_ERR_INVALID_ARG
+    assert lib.hisa_pool_blocks(P(FAKE), 10, 32, 128, P(FAKE), None) == hisa.HISA_ERR_UNSUPPORTED
+    assert lib.hisa_pool_blocks(P(FAKE), 10, 64, 96, P(FAKE), None) == hisa.HISA_ERR_UNSUPPORTED
+    assert lib.hisa_pool_blocks(None, 10, 64, 128, P(FAKE), None) == hisa.HISA_ERR_INVALID_ARG
+    seqs = (hisa.hisa_seq * 2)(hisa.hisa_seq(0, 0, 100, 228), hisa.hisa_seq(228, 2, 200, 228))
+    # the second sequence has room for 28 keys only
+    assert lib.hisa_append_keys(P(FAKE), P(FAKE), seqs, 2, P(FAKE), 29, 64, 128, None) == \
+        hisa.HISA_ERR_INVALID_ARG
+    assert lib.hisa_append_keys(P(FAKE), P(FAKE), seqs, 2, P(FAKE), 0, 64, 128, None) == hisa.HISA_OK
+    assert lib.hisa_append_keys(P(FAKE), P(FAKE), seqs, 2, P(FAKE), 8, 64, 48, None) == \
+        hisa.HISA_ERR_UNSUPPORTED
+    assert lib.hisa_append_keys(P(FAKE), P(FAKE), seqs, -1, P(FAKE), 8, 64, 128, None) == \
+        hisa.HISA_ERR_INVALID_ARG

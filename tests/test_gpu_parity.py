@@ -1,0 +1,323 @@
+"""HIP path vs the CPU oracle, through the C ABI, on the GPU."""
+import numpy as np
+import pytest
+
+import oracle
+from long_context_sparse_hisa_amd import synth
+from parity import check_all_rows_properties, check_rows
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_context_sparse_hisa_amd import hisa
+    hisa.lib()                                  # raises if the library is missing
+
+
+def _dev():
+    from long_context_sparse_hisa_amd import device
+    return device
+
+
+def _oracle_reps(w, B, lengths=None):
+    lengths = w.seq_len if lengths is None else lengths
+    out = []
+    for s in range(w.nseq):
+        o = int(w.seq_key_off[s])
+        out.append(oracle.pool(w.keys[o:o + int(lengths[s])], B))
+    return out
+
+
+def _gpu_reps(cache, s, n):
+    r = int(cache.seq_rep_off[s])
+    nb = (n + cache.B - 1) // cache.B
+    return cache.reps[r:r + nb].cpu().numpy().view(np.uint16)
+
+
+# ---- pooling and append -------------------------------------------------------
+
+@pytest.mark.parametrize("L,B", [(1, 16), (100, 16), (128, 128), (1000, 64), (4097, 128), (5000, 256),
+                                 (70000, 128)])
+def test_pool_bitwise(L, B):
+    print("pool L=%d B=%d" % (L, B), flush=True)
+    dv = _dev()
+    w = synth.chunked_prefill(L=L, seed=21, B=B, q_positions=[0])
+    cache = dv.DeviceCache(w, B=B)
+    cache.pool()
+    torch.cuda.synchronize()
+    assert np.array_equal(_gpu_reps(cache, 0, L), oracle.pool(w.keys, B))
+
+
+def test_pool_rounding_ties():
+    print("pool ties", flush=True)
+    dv = _dev()
+    B = 16
+    vals = []
+    for x in (1.0625, 1.1875, -1.0625, -1.1875, 3.0, 0.0):   # the first four give exact midpoints
+        blk = np.full((B, synth.D), 1.0 if x >= 0 else -1.0, np.float32)
+        blk[0] = x
+        vals.append(blk)
+    keys = synth.to_bf16(np.concatenate(vals + [np.full((5, synth.D), 2.5, np.float32)]))
+    w = synth.Workload("ties", keys, np.zeros(1, np.int64), np.array([len(keys)], np.int64),
+                       np.array([len(keys)], np.int64), B, 3, 1)
+    cache = dv.DeviceCache(w, B=B)
+    cache.pool()
+    torch.cuda.synchronize()
+    got = _gpu_reps(cache, 0, len(keys))
+    want = oracle.pool(keys, B)
+    assert np.array_equal(got, want)
+    assert got[0, 0] == 0x3F80 and got[1, 0] == 0x3F82            # ties to even
+
+
+def test_append_matches_one_shot_pooling():
+    print("append", flush=True)
+    dv = _dev()
+    B = 64
+    g = np.random.default_rng(22)
+    caps = np.array([900, 700, 1000], np.int64)
+    init = np.array([0, 77, 128], np.int64)
+    offs = np.concatenate([[0], np.cumsum(caps)[:-1]]).astype(np.int64)
+    full = synth.to_bf16(g.standard_normal((int(caps.sum()), synth.D)).astype(np.float32))
+    keys = np.zeros_like(full)
+    for s in range(3):
+        keys[offs[s]:offs[s] + init[s]] = full[offs[s]:offs[s] + init[s]]
+    w = synth.Workload("append", keys, offs, init.copy(), caps, B, 3, 1)
+    cache = dv.DeviceCache(w, B=B)
+    cache.pool()
+    lens = init.copy()
+    for n_new in (1, 37, 64, 128, 200, 5):
+        new = np.stack([full[offs[s] + lens[s]: offs[s] + lens[s] + n_new] for s in range(3)])
+        cache.append(new)
+        lens += n_new
+        torch.cuda.synchronize()
+        kk = cache.keys.cpu().numpy().view(np.uint16)
+        for s in range(3):
+            o = int(offs[s])
+            assert np.array_equal(kk[o:o + lens[s]], full[o:o + lens[s]])
+            assert np.array_equal(_gpu_reps(cache, s, int(lens[s])), oracle.pool(full[o:o + lens[s]], B))
+
+
+# ---- index: small grids checked row by row ----------------------------------------
+
+def _run(cache, ph, k, m, flat, **kw):
+    call = _dev().IndexCall(cache, ph.queries, ph.q_pos, ph.q_seq, k=k, m=m, flat=flat, **kw)
+    call.run()
+    return call.results()
+
+
+def _check_phase(w, cache, ph, k, m, flat, rows=None, label="", props=True, **kw):
+    idx, sc, blk = _run(cache, ph, k, m, flat, **kw)
+    B = cache.B
+    lens = cache.seq_len
+    reps = None if flat else _oracle_reps(w, B, lens)
+    if props:
+        check_all_rows_properties(idx, blk, ph.q_pos, B, m, k, flat)
+
+    def K_of(i):                       # host keys: nothing the oracle reads comes from the GPU
+        s = int(ph.q_seq[i])
+        o = int(w.seq_key_off[s])
+        return w.keys[o:o + int(lens[s])]
+
+    def R_of(i):
+        return reps[int(ph.q_seq[i])]
+
+    rows = range(len(ph.q_pos)) if rows is None else rows
+    counts = check_rows(rows, ph.queries, ph.q_pos, K_of, R_of, B, m, k, idx, sc, blk, flat, label)
+    print(label, "flat" if flat else "hisa", counts, flush=True)
+    return idx, sc, blk
+
+
+@pytest.mark.parametrize("L,B,m,k,iid", [
+    (300, 16, 3, 1, True), (300, 16, 5, 17, False), (1000, 64, 4, 100, False),
+    (1000, 128, 8, 256, True), (2500, 32, 6, 150, False), (4097, 128, 8, 300, False),
+    (3000, 256, 3, 700, False), (1500, 16, 64, 1024, False)])
+def test_index_small_grid(L, B, m, k, iid):
+    print("grid L=%d B=%d m=%d k=%d iid=%s" % (L, B, m, k, iid), flush=True)
+    dv = _dev()
+    if iid:
+        w = synth.tiny_prefill(L=L, seed=23, B=B, m=m, k=k)
+    else:
+        w = synth.chunked_prefill(L=L, seed=23, B=B, m=m, k=k)
+    cache = dv.DeviceCache(w, B=B)
+    cache.pool()
+    ph = w.phases[0]
+    for flat in (False, True):
+        _check_phase(w, cache, ph, k, m, flat, label="grid%d" % L)
+
+
+def test_small_workspace_forces_chunks():
+    print("chunked workspace", flush=True)
+    dv = _dev()
+    w = synth.chunked_prefill(L=2000, seed=24, B=64, m=6, k=200)
+    cache = dv.DeviceCache(w, B=64)
+    cache.pool()
+    ph = w.phases[0]
+    full_h, _, full_b = _run(cache, ph, 200, 6, False)
+    from long_context_sparse_hisa_amd import hisa
+    probe = dv.IndexCall(cache, ph.queries, ph.q_pos, ph.q_seq, k=200, m=6)
+    _, least = hisa.hisa_workspace_bytes(probe.args)
+    small_h, _, small_b = _run(cache, ph, 200, 6, False, workspace_bytes=least * 7 + 100)
+    assert np.array_equal(full_h, small_h) and np.array_equal(full_b, small_b)
+    full_f, _, _ = _run(cache, ph, 200, 6, True)
+    probe = dv.IndexCall(cache, ph.queries, ph.q_pos, ph.q_seq, k=200, m=6, flat=True)
+    _, least = hisa.hisa_workspace_bytes(probe.args, True)
+    small_f, _, _ = _run(cache, ph, 200, 6, True, workspace_bytes=least * 3)
+    assert np.array_equal(full_f, small_f)
+
+
+def test_packed_sequences_and_invalid_queries():
+    print("packed", flush=True)
+    dv = _dev()
+    w = synth.decode_batch(nseq=5, L=3000, seed=25, B=64, m=5, k=300, spare=100)
+    cache = dv.DeviceCache(w, B=64)
+    cache.set_lengths([3000, 1, 640, 2999, 1500])
+    cache.pool()
+    ph = w.phases[0]
+    q_pos = np.array([2999, 0, 639, 2000, 1500], np.int64)      # the last is past its end
+    q_seq = np.array([0, 1, 2, 3, 4], np.int32)
+    ph2 = synth.Phase("p", ph.queries, q_pos, q_seq)
+    for flat in (False, True):
+        idx, sc, blk = _run(cache, ph2, 300, 5, flat)
+        assert np.all(idx[4] == -1) and np.all(np.isnan(sc[4]))
+        if not flat:
+            assert np.all(blk[4] == -1)
+        _check_phase(w, cache, ph2, 300, 5, flat, rows=[0, 1, 2, 3], label="packed", props=False)
+    bad = synth.Phase("bad", ph.queries[:2], np.array([5, 5], np.int64), np.array([-1, 7], np.int32))
+    for flat in (False, True):
+        idx, _, _ = _run(cache, bad, 300, 5, flat)
+        assert np.all(idx == -1)
+
+
+def test_degenerate_ties_pick_lowest_indices():
+    print("ties", flush=True)
+    dv = _dev()
+    L, B = 3000, 64
+    keys = np.tile(synth.to_bf16(np.linspace(-1, 1, synth.D).astype(np.float32)), (L, 1))
+    q = synth.to_bf16(np.ones((3, synth.D), np.float32))
+    q[2] = 0                                               # zero query: every score is 0
+    w = synth.Workload("ties", keys, np.zeros(1, np.int64), np.array([L], np.int64),
+                       np.array([L], np.int64), B, 6, 100)
+    ph = synth.Phase("p", q, np.array([2999, 1234, 2500], np.int64), np.zeros(3, np.int32))
+    cache = dv.DeviceCache(w, B=B)
+    cache.pool()
+    for flat in (False, True):
+        idx, _, blk = _check_phase(w, cache, ph, 100, 6, flat, label="ties")
+        if flat:
+            assert np.array_equal(idx[0], np.arange(100))
+
+
+def test_hisa_with_m_covering_every_block_equals_flat():
+    print("m covers all", flush=True)
+    dv = _dev()
+    w = synth.chunked_prefill(L=2048, seed=26, B=128, m=16, k=512)
+    cache = dv.DeviceCache(w, B=128)
+    cache.pool()
+    ph = w.phases[0]
+    h_idx, h_sc, _ = _run(cache, ph, 512, 16, False)
+    f_idx, f_sc, _ = _run(cache, ph, 512, 16, True)
+    assert np.array_equal(h_idx, f_idx)
+    assert np.array_equal(np.nan_to_num(h_sc, nan=-7.0), np.nan_to_num(f_sc, nan=-7.0))
+
+
+@pytest.mark.parametrize("L", [20000, 70000])
+def test_flat_long_rows(L):
+    """Rows longer than one workgroup's selection go through the
+    several-workgroup radix path."""
+    print("flat long L=%d" % L, flush=True)
+    dv = _dev()
+    pos = np.array([0, 5, 2047, 2048, 9999, L // 2, L - 2, L - 1], np.int64)
+    w = synth.chunked_prefill(L=L, seed=27, B=128, m=16, k=2048, q_positions=pos)
+    cache = dv.DeviceCache(w, B=128)
+    cache.pool()
+    _check_phase(w, cache, w.phases[0], 2048, 16, True, label="flatlong")
+    # ties across slices: a run of equal keys longer than k
+    keys = w.keys.copy()
+    keys[1000:9000] = keys[1000]
+    w2 = synth.Workload("ties", keys, w.seq_key_off, w.seq_len, w.seq_cap, 128, 16, 2048)
+    cache2 = dv.DeviceCache(w2, B=128)
+    q = np.repeat(keys[1000:1001], 2, axis=0)
+    ph = synth.Phase("p", q, np.array([L - 1, 8999], np.int64), np.zeros(2, np.int32))
+    _check_phase(w2, cache2, ph, 2048, 16, True, label="flatties")
+
+
+# ---- the five workloads at full size ----------------------------------------------
+
+def test_tiny_prefill_4k_full():
+    print("tiny prefill 4K", flush=True)
+    dv = _dev()
+    w = synth.tiny_prefill()
+    cache = dv.DeviceCache(w)
+    cache.pool()
+    torch.cuda.synchronize()
+    assert np.array_equal(_gpu_reps(cache, 0, 4096), oracle.pool(w.keys, 128))
+    for flat in (False, True):
+        _check_phase(w, cache, w.phases[0], w.k, w.m, flat, label="cfg1")
+
+
+def test_decode_32k_x16_full():
+    print("decode 32K x16", flush=True)
+    dv = _dev()
+    w = synth.decode_batch()
+    cache = dv.DeviceCache(w)
+    cache.pool()
+    for flat in (False, True):
+        _check_phase(w, cache, w.phases[0], w.k, w.m, flat, label="cfg2")
+
+
+def test_chunked_prefill_32k_sampled():
+    print("chunked prefill 32K", flush=True)
+    dv = _dev()
+    w = synth.chunked_prefill()
+    cache = dv.DeviceCache(w)
+    cache.pool()
+    g = np.random.default_rng(28)
+    rows = sorted(set([0, 1, 127, 128, 8191, 32767] + list(g.choice(32768, 120, replace=False))))
+    for flat in (False, True):
+        _check_phase(w, cache, w.phases[0], w.k, w.m, flat, rows=rows, label="cfg3")
+
+
+def test_long_context_128k():
+    print("long context 128K", flush=True)
+    dv = _dev()
+    w = synth.long_context()
+    cache = dv.DeviceCache(w)
+    cache.pool()
+    g = np.random.default_rng(29)
+    chunk, dec = w.phases
+    rows = sorted(set([0, 4095] + list(g.choice(4096, 40, replace=False))))
+    for flat in (False, True):
+        _check_phase(w, cache, chunk, w.k, w.m, flat, rows=rows, label="cfg4chunk")
+        idx, _, _ = _check_phase(w, cache, dec, w.k, w.m, flat, label="cfg4decode")
+        if flat:
+            assert set(w.needles.tolist()) <= set(idx[0].tolist())
+
+
+def test_long_decode_1m_with_appends():
+    print("1M decode + append", flush=True)
+    dv = _dev()
+    w = synth.long_decode_append()
+    cache = dv.DeviceCache(w)
+    cache.pool()
+    full = w.keys.copy()
+    L = int(w.seq_len[0])
+    want_reps = oracle.pool(full[:L], 128)
+    torch.cuda.synchronize()
+    assert np.array_equal(_gpu_reps(cache, 0, L), want_reps)
+    for ph in w.phases:
+        cache.append(ph.append)
+        n_new = ph.append.shape[1]
+        full[L:L + n_new] = ph.append[0]
+        L += n_new
+        torch.cuda.synchronize()
+        got = _gpu_reps(cache, 0, L)
+        b0 = (L - n_new) // 128
+        want = oracle.pool(full[b0 * 128:L], 128)
+        assert np.array_equal(got[b0:], want)
+        w.keys = full                                    # the oracle reads the grown cache
+        for flat in (False, True):
+            _check_phase(w, cache, ph, w.k, w.m, flat, label="cfg5 " + ph.name, props=True)
