@@ -1,0 +1,396 @@
+#!/usr/bin/env python3
+"""Indexer throughput on one MI355X: HISA against the flat DSA indexer.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line on stdout.  The default workload is the 32K decode
+batch: 16 sequences of 32768 keys (d = 64, bf16, mixture-of-Gaussians keys),
+B = 128, m = 64, k = 2048.  One step is one decode step of the whole path:
+each sequence appends its newest key (position 32767, with the in-place
+update of that block's representative) and its query at 32767 is indexed.
+The flat indexer runs the same steps on the same bytes.
+
+Inputs are resident in HBM before the timed region.  To keep the 256 MB
+last-level cache from serving repeated steps, the step rotates over
+`--replicas` copies of the key cache and representatives (cold-cache
+numbers); `--replicas 1` gives the warm-cache figure.
+
+The timed region replays one captured HIP graph per step (per replica):
+the step's kernels without host work in between.  Per-stage durations come
+from HIP events recorded on the launch stream around every stage of a
+separate run of eager steps queued behind a sleep kernel, so that they run
+back to back; the roofline object is computed from the stage with the
+largest average duration.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+
+WORKLOADS = ("decode_32k_x16", "chunked_prefill_32k", "long_context_128k", "long_decode_1m",
+             "tiny_prefill_4k")
+
+STAGES_HISA = ("block_stage", "token_stage")
+STAGES_FLAT = ("flat_scores", "flat_topk")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---- algorithmic traffic per stage ------------------------------------------------
+
+def hisa_stage_bytes(q_pos, B, m, k):
+    """Algorithmic HBM bytes of the two HISA stages for queries at q_pos
+    (d = 64: a key or representative row is 128 bytes).  Block stage: the
+    query, its causal representatives, the kept-block list out.  Token
+    stage: the query, the kept list, the candidate keys, indices and scores
+    out."""
+    q_pos = np.asarray(q_pos, np.int64)
+    nb = q_pos // B + 1                                  # causal blocks
+    kept = np.minimum(nb, m)
+    cand = np.minimum(kept * B, q_pos + 1)                # <= m*B candidate tokens
+    return {
+        "block_stage": float((128 + nb * 128 + 2 * m * 4).sum()),
+        "token_stage": float((128 + m * 4 + cand * 128 + k * 8).sum()),
+    }
+
+
+def flat_stage_bytes(q_pos, k):
+    """Flat: the scores stage reads every visible key and writes its score;
+    the top-k stage reads the scores and writes indices and scores."""
+    q_pos = np.asarray(q_pos, np.int64)
+    n = q_pos + 1
+    return {
+        "flat_scores": float((n * 128 + 128 + n * 4).sum()),
+        "flat_topk": float((n * 4 + k * 8).sum()),
+    }
+
+
+# ---- setup -----------------------------------------------------------------------
+
+class Setup:
+    """Device-resident workload: R replicas of keys + reps, the query
+    batches of one step, and reusable argument blocks."""
+
+    def __init__(self, name, replicas, hisa_mod, synth, device_mod, torch):
+        self.name = name
+        self.torch = torch
+        self.h = hisa_mod
+        dev = "cuda:0"
+        if name == "decode_32k_x16":
+            w = synth.decode_batch()
+            self.desc = ("16 sequences x 32768 keys, d=64 bf16 MoG; B=128 m=64 k=2048; per step: append "
+                         "the key at 32767 of every sequence (rep update) + index its query at 32767")
+        elif name == "chunked_prefill_32k":
+            w = synth.chunked_prefill()
+            self.desc = "32768 keys, all 32768 causal queries (MoG), d=64 bf16; B=128 m=64 k=2048"
+        elif name == "long_context_128k":
+            w = synth.long_context()
+            self.desc = ("131072 keys (MoG + 64 needles), prefill chunk of 4096 queries + decode batch "
+                         "of 32 at 131071; B=128 m=64 k=2048")
+        elif name == "long_decode_1m":
+            w = synth.long_decode_append(steps=1)
+            self.desc = ("1,048,576-key cache (MoG), d=64 bf16; B=128 m=64 k=2048; per step: append 128 "
+                         "keys (rep update) + index one query at the last position")
+        elif name == "tiny_prefill_4k":
+            w = synth.tiny_prefill()
+            self.desc = "4096 i.i.d. N(0,1) keys, all 4096 causal queries, d=64 bf16; B=128 m=8 k=256"
+        else:
+            raise ValueError(name)
+        self.w = w
+        self.cache = device_mod.DeviceCache(w, device=dev)
+        c = self.cache
+        # decode workloads: the cache holds L-n_new keys, the step appends n_new
+        self.append_src = None
+        if name == "decode_32k_x16":
+            c.set_lengths(w.seq_len - 1)
+            last = np.stack([w.keys[int(o) + int(L) - 1] for o, L in zip(w.seq_key_off, w.seq_len)])
+            self.append_src = device_mod.to_dev(last[:, None, :], dev)
+        elif name == "long_decode_1m":
+            ph = w.phases[0]
+            self.append_src = device_mod.to_dev(ph.append, dev)
+        c.pool()
+        if self.append_src is not None:
+            self.seqs = [(c.seq_key_off[s], c.seq_rep_off[s], c.seq_len[s], c.seq_cap[s])
+                         for s in range(c.nseq)]
+            c.append(self.append_src, update_lengths=True)   # lengths the queries see
+        torch.cuda.synchronize()
+        self.phases = w.phases if name != "long_decode_1m" else w.phases[:1]
+        self.B, self.m, self.k = w.B, w.m, w.k
+        # replicas (cold-cache rotation)
+        self.keys = [c.keys] + [c.keys.clone() for _ in range(replicas - 1)]
+        self.reps = [c.reps] + [c.reps.clone() for _ in range(replicas - 1)]
+        self.calls = {}
+        for flat in (False, True):
+            calls = []
+            for ph in self.phases:
+                ic = device_mod.IndexCall(c, ph.queries, ph.q_pos, ph.q_seq, k=self.k, m=self.m,
+                                          flat=flat, scores=True, blocks=not flat)
+                per_rep = []
+                for r in range(replicas):
+                    a = hisa_mod.make_args(ic.queries, ic.q_pos, self.keys[r], self.k, reps=self.reps[r],
+                                           q_seq=ic.q_seq, seq_key_off=c.d_key_off,
+                                           seq_rep_off=c.d_rep_off, seq_len=c.d_len,
+                                           max_len=ic.max_len, B=self.B, m=self.m,
+                                           out_idx=ic.out_idx, out_scores=ic.out_scores,
+                                           out_blocks=ic.out_blocks, workspace=ic.workspace)
+                    a.workspace_bytes = ic.args.workspace_bytes
+                    per_rep.append(a)
+                calls.append((ic, per_rep))
+            self.calls[flat] = calls
+        self.replicas = replicas
+        self.q_per_step = sum(len(ph.q_pos) for ph in self.phases)
+
+    def step(self, r, flat, stream, events=None, append_events=None):
+        """One step on replica r; events: one StageEvents per phase."""
+        h = self.h
+        if self.append_src is not None:
+            if append_events is not None:
+                h._hiprt().hipEventRecord(append_events[0], stream)
+            h.hisa_append_keys(self.keys[r], self.reps[r], self.seqs, self.append_src, self.B,
+                               self.torch.cuda.current_stream())
+            if append_events is not None:
+                h._hiprt().hipEventRecord(append_events[1], stream)
+        for p, (ic, per_rep) in enumerate(self.calls[flat]):
+            a = per_rep[r]
+            if events is not None:
+                events[p].attach(a)
+            else:
+                a.stage_events = None
+            (h.hisa_flat_index if flat else h.hisa_index)(a)
+
+
+def capture_graphs(S, flat, torch):
+    """One HIP graph per replica holding one whole step (kernels only: no
+    events, no allocation, no memset nodes)."""
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                   # warm the path once outside capture
+        S.step(0, flat, side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(S.replicas):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            S.step(r, flat, torch.cuda.current_stream().cuda_stream)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_method(S, flat, steps, warmup, torch):
+    """Wall time of `steps` graph replays (one step each, rotating over the
+    replicas), bracketed by device synchronisation."""
+    graphs = capture_graphs(S, flat, torch)
+    for i in range(warmup):
+        graphs[i % S.replicas].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[(warmup + i) % S.replicas].replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def stage_times(S, flat, nsteps, torch):
+    """Average duration of every stage, from HIP events recorded on the
+    launch stream around each stage of `nsteps` eager steps.  A sleep kernel
+    holds the GPU while the host queues the steps, so the queued kernels run
+    back to back and the event gaps are the kernels' own durations."""
+    h = S.h
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    nph = len(S.phases)
+    evs = [[h.StageEvents() for _ in range(nph)] for _ in range(nsteps)]
+    hr = h._hiprt()
+    app = []
+    if S.append_src is not None:
+        for _ in range(nsteps):
+            pair = []
+            for _ in range(2):
+                e = ctypes.c_void_p()
+                hr.hipEventCreate(ctypes.byref(e))
+                pair.append(e)
+            app.append(pair)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.0e7))                   # ~10 ms of spinning while the host queues
+    for i in range(nsteps):
+        S.step(i % S.replicas, flat, sp, evs[i], app[i] if app else None)
+    torch.cuda.synchronize()
+    names = STAGES_FLAT if flat else STAGES_HISA
+    out = {}
+    for p in range(nph):
+        for s_, nm in enumerate(names, start=1):
+            vals = [evs[i][p].elapsed_ms(s_ - 1, s_) for i in range(nsteps)]
+            out["%s/%s" % (S.phases[p].name, nm)] = float(np.mean(vals))
+    if app:
+        vals = []
+        for a0, a1 in app:
+            f = ctypes.c_float()
+            hr.hipEventElapsedTime(ctypes.byref(f), a0, a1)
+            vals.append(f.value)
+            hr.hipEventDestroy(a0)
+            hr.hipEventDestroy(a1)
+        out["append"] = float(np.mean(vals))
+    return out
+
+
+def cpu_baseline(S, seconds, oracle):
+    """The oracle on the same step, repeated for about `seconds`."""
+    w = S.w
+    B, m, k = S.B, S.m, S.k
+    lens = S.cache.seq_len
+    reps = np.zeros((w.total_rep_rows(B), 64), np.uint16)
+    rep_off = w.seq_rep_off(B)
+    for s in range(w.nseq):
+        o = int(w.seq_key_off[s])
+        r = oracle.pool(w.keys[o:o + int(lens[s])], B)
+        reps[rep_off[s]:rep_off[s] + len(r)] = r
+    # prefill steps are far beyond a few seconds of CPU work: time an evenly
+    # spaced sample of at most 256 queries per phase instead
+    sample = []
+    for ph in S.phases:
+        nq = len(ph.q_pos)
+        pick = np.unique(np.linspace(0, nq - 1, min(nq, 256)).astype(np.int64))
+        sample.append((ph, pick))
+    nsample = sum(len(p) for _, p in sample)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        if S.append_src is not None:                   # re-pool the blocks the append touches
+            n_new = S.append_src.shape[1]
+            for s in range(w.nseq):
+                o = int(w.seq_key_off[s])
+                L = int(lens[s])
+                oracle.pool_range(w.keys[o:o + L], B, (L - n_new) // B, (L + B - 1) // B,
+                                  reps[rep_off[s]:rep_off[s] + (L + B - 1) // B])
+        for ph, pick in sample:
+            oracle.index_batch(False, ph.queries[pick], ph.q_pos[pick], w.keys, k, reps=reps,
+                               q_seq=ph.q_seq[pick], seq_key_off=w.seq_key_off, seq_rep_off=rep_off,
+                               seq_len=lens, B=B, m=m)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    whole = nsample == S.q_per_step
+    what = ("the whole step" if whole else "%d evenly spaced queries of the step" % nsample)
+    return {"value": n * nsample / el, "unit": "queries/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": "%d repetitions of %s (%s), HISA oracle, %.1f s" % (n, what, S.desc, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_32k_x16", choices=WORKLOADS)
+    ap.add_argument("--replicas", type=int, default=None,
+                    help="key-cache copies rotated over (default: enough to exceed the 256 MB cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--stage-steps", type=int, default=32,
+                    help="eager steps whose stages are timed with HIP events")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the indexer here runs on a single MI355X and has no "
+              "multi-GPU path (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from long_context_sparse_hisa_amd import device, hisa, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    hisa.lib()
+    default_rep = {"decode_32k_x16": 64, "long_decode_1m": 256, "chunked_prefill_32k": 1,
+                   "long_context_128k": 1, "tiny_prefill_4k": 1}
+    R = args.replicas or default_rep[args.workload]
+    log("setting up %s with %d replicas" % (args.workload, R))
+    S = Setup(args.workload, R, hisa, synth, device, torch)
+    log("timing HISA: %d warmup + %d graph-replayed steps" % (args.warmup, args.steps))
+    h_el = time_method(S, False, args.steps, args.warmup, torch)
+    log("timing flat: %d warmup + %d graph-replayed steps" % (args.warmup, args.steps))
+    f_el = time_method(S, True, args.steps, args.warmup, torch)
+    nst = max(4, min(args.stage_steps, S.replicas * 4))
+    log("per-stage HIP-event timing over %d eager steps each" % nst)
+    h_stage = stage_times(S, False, nst, torch)
+    f_stage = stage_times(S, True, nst, torch)
+    h_ms = h_el / args.steps * 1e3
+    f_ms = f_el / args.steps * 1e3
+    qps = S.q_per_step * args.steps / h_el
+    fqps = S.q_per_step * args.steps / f_el
+
+    # roofline of the dominant HISA kernel
+    stage_bytes = {}
+    for ph in S.phases:
+        for nm, b in hisa_stage_bytes(ph.q_pos, S.B, S.m, S.k).items():
+            stage_bytes["%s/%s" % (ph.name, nm)] = b
+        for nm, b in flat_stage_bytes(ph.q_pos, S.k).items():
+            stage_bytes["%s/%s" % (ph.name, nm)] = b
+    kern = max((n for n in h_stage if n in stage_bytes), key=lambda n: h_stage[n])
+    achieved = stage_bytes[kern] / (h_stage[kern] * 1e-3) / 1e9
+    fkern = max((n for n in f_stage if n in stage_bytes), key=lambda n: f_stage[n])
+    f_achieved = stage_bytes[fkern] / (f_stage[fkern] * 1e-3) / 1e9
+    # algorithmic bytes of a whole step: every stage's per-query traffic plus
+    # the append (new rows written, touched blocks re-read, reps written)
+    append_rows = 0 if S.append_src is None else S.append_src.shape[0] * S.append_src.shape[1]
+    h_step_bytes = sum(b for n, b in stage_bytes.items() if n.split("/")[-1] in STAGES_HISA)
+    f_step_bytes = sum(b for n, b in stage_bytes.items() if n.split("/")[-1] in STAGES_FLAT)
+    h_step_bytes += append_rows * 128 * 2
+    f_step_bytes += append_rows * 128 * 2
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("timing the CPU oracle for about %.0f s" % args.cpu_seconds)
+        cpu = cpu_baseline(S, args.cpu_seconds, oracle)
+
+    out = {
+        "metric": "indexer queries/s + HBM GB/s at 32K/128K/1M ctx; HISA vs flat-DSA speedup",
+        "value": qps,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": h_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "description": S.desc, "queries_per_step": S.q_per_step,
+                   "replicas": R, "B": S.B, "m": S.m, "k": S.k},
+        "roofline": {"bound": "hbm", "kernel": kern, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": stage_bytes[kern],
+                     "avg_launch_ms": h_stage[kern]},
+        "cpu_baseline": cpu,
+        "step_bytes": h_step_bytes,
+        "hbm_gbps_step": h_step_bytes / (h_ms * 1e-3) / 1e9,
+        "stage_ms": h_stage,
+        "flat": {"value": fqps, "unit": "queries/s", "ms_per_step": f_ms, "stage_ms": f_stage,
+                 "step_bytes": f_step_bytes,
+                 "hbm_gbps_step": f_step_bytes / (f_ms * 1e-3) / 1e9,
+                 "dominant": {"kernel": fkern, "achieved_gbps": f_achieved,
+                              "frac": f_achieved / HBM_PEAK_GBPS}},
+        "speedup_vs_flat": f_ms / h_ms,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -150,7 +150,15 @@ typedef struct hisa_index_args {
     int32_t* out_blocks;         /* [nq, m] or NULL (HISA only) */
     void* workspace;             /* device scratch owned by the caller */
     size_t workspace_bytes;      /* its size; see hisa_workspace_bytes */
+    void* const* stage_events;   /* NULL, or HISA_STAGE_EVENTS hipEvent_t handles (profiling
+                                    aid): event 0 is recorded on the stream before the first
+                                    kernel of the call's last query chunk, event s right after
+                                    stage s of that chunk.  HISA stages: 1 block scores and
+                                    top-m, 2 token scores and top-k.  Flat stages: 1 scores,
+                                    2 top-k.  Events 3 and 4 are not recorded. */
 } hisa_index_args;
+
+#define HISA_STAGE_EVENTS 5
 
 /*
  * hisa_workspace_bytes -- workspace an index call wants for these

@@ -56,6 +56,19 @@ struct Layout {
 
 int64_t hisa_Mmax(const hisa_index_args* a) { return (a->max_len + a->B - 1) / a->B; }
 
+// Below this many queries the token stage splits every query over several
+// workgroups (decode); above it one workgroup per query fills the chip.
+constexpr int64_t kSplitBelow = 512;
+
+bool hisa_split(const hisa_index_args* a) { return a->nq < kSplitBelow; }
+
+int log2_of(int B)
+{
+    int lb = 0;
+    while ((1 << lb) < B) ++lb;
+    return lb;
+}
+
 bool flat_uses_radix(const hisa_index_args* a) { return a->max_len > HISA_MAX_CANDIDATES; }
 
 Layout layout_for(const hisa_index_args* a, int flat, int64_t chunk)
@@ -64,12 +77,16 @@ Layout layout_for(const hisa_index_args* a, int flat, int64_t chunk)
     size_t off = 0;
     if (!flat) {
         const int64_t Mmax = hisa_Mmax(a);
-        L.sigma = off;
-        off += align_up((size_t)chunk * Mmax * sizeof(float));
         L.sel = off;
         off += align_up((size_t)chunk * a->m * sizeof(int32_t));
-        L.ukeys = off;
-        off += align_up((size_t)chunk * a->m * a->B * sizeof(uint32_t));
+        if (Mmax > kStage1FusedMax) {
+            L.sigma = off;
+            off += align_up((size_t)chunk * Mmax * sizeof(float));
+        }
+        if (hisa_split(a)) {
+            L.ukeys = off;
+            off += align_up((size_t)chunk * a->m * a->B * sizeof(uint32_t));
+        }
     } else {
         L.ukeys = off;
         off += align_up((size_t)chunk * a->max_len * sizeof(uint32_t));
@@ -117,6 +134,17 @@ QueryMeta meta_of(const hisa_index_args* a)
 
 template <class T>
 T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+
+// Records stage event s of the last chunk when the caller asked for them.
+struct StageMarks {
+    void* const* ev;
+    hipStream_t stream;
+    hipError_t mark(bool last_chunk, int s) const
+    {
+        if (!ev || !last_chunk || !ev[s]) return hipSuccess;
+        return hipEventRecord(static_cast<hipEvent_t>(ev[s]), stream);
+    }
+};
 
 }  // namespace
 
@@ -198,18 +226,23 @@ int hisa_index(const hisa_index_args* a, void* stream_)
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     const QueryMeta qm = meta_of(a);
     const int64_t Mmax = hisa_Mmax(a);
-    float* sigma = at<float>(a->workspace, L.sigma);
+    const int lb = log2_of(a->B);
+    const bool split = hisa_split(a);
+    float* sigma = Mmax > kStage1FusedMax ? at<float>(a->workspace, L.sigma) : nullptr;
     int32_t* sel = at<int32_t>(a->workspace, L.sel);
-    uint32_t* ukeys = at<uint32_t>(a->workspace, L.ukeys);
+    uint32_t* ukeys = split ? at<uint32_t>(a->workspace, L.ukeys) : nullptr;
+    const StageMarks marks{a->stage_events, stream};
     for (int64_t q0 = 0; q0 < a->nq; q0 += chunk) {
         const int64_t nc = std::min(chunk, a->nq - q0);
-        hipError_t err = launch_block_scores(qm, a->reps, q0, nc, a->B, Mmax, sigma, stream);
+        const bool last = q0 + nc >= a->nq;
+        hipError_t err = marks.mark(last, 0);
         if (err == hipSuccess)
-            err = launch_select_blocks(qm, q0, nc, a->B, a->m, Mmax, sigma, sel, a->out_blocks, stream);
-        if (err == hipSuccess) err = launch_token_scores(qm, a->keys, q0, nc, a->B, a->m, sel, ukeys, stream);
+            err = launch_stage1(qm, a->reps, q0, nc, lb, a->m, Mmax, sigma, sel, a->out_blocks, stream);
+        if (err == hipSuccess) err = marks.mark(last, 1);
         if (err == hipSuccess)
-            err = launch_topk_small(ukeys, nc, a->m * a->B, a->k, sel, a->m, a->B, a->out_idx + q0 * a->k,
-                                    a->out_scores ? a->out_scores + q0 * a->k : nullptr, stream);
+            err = launch_stage2(qm, a->keys, q0, nc, lb, a->m, a->k, sel, ukeys, a->out_idx, a->out_scores, split,
+                                stream);
+        if (err == hipSuccess) err = marks.mark(last, 2);
         if (err != hipSuccess) return HISA_ERR_HIP;
     }
     return HISA_OK;
@@ -227,20 +260,25 @@ int hisa_flat_index(const hisa_index_args* a, void* stream_)
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     const QueryMeta qm = meta_of(a);
     uint32_t* ukeys = at<uint32_t>(a->workspace, L.ukeys);
+    const StageMarks marks{a->stage_events, stream};
     for (int64_t q0 = 0; q0 < a->nq; q0 += chunk) {
         const int64_t nc = std::min(chunk, a->nq - q0);
+        const bool last = q0 + nc >= a->nq;
         int32_t* oi = a->out_idx + q0 * a->k;
         float* os = a->out_scores ? a->out_scores + q0 * a->k : nullptr;
-        hipError_t err = launch_flat_scores(qm, a->keys, q0, nc, a->max_len, ukeys, stream);
+        hipError_t err = marks.mark(last, 0);
+        if (err == hipSuccess) err = launch_flat_scores(qm, a->keys, q0, nc, a->max_len, ukeys, stream);
+        if (err == hipSuccess) err = marks.mark(last, 1);
         if (err == hipSuccess) {
             if (!flat_uses_radix(a)) {
-                err = launch_topk_small(ukeys, nc, (int)a->max_len, a->k, nullptr, 0, 1, oi, os, stream);
+                err = launch_topk_small(ukeys, nc, (int)a->max_len, a->k, nullptr, 0, 0, oi, os, stream);
             } else {
                 RadixWorkspace ws{at<int>(a->workspace, L.hist), at<uint32_t>(a->workspace, L.state),
                                   at<int>(a->workspace, L.counts)};
                 err = launch_topk_radix(ukeys, nc, a->max_len, a->k, ws, oi, os, stream);
             }
         }
+        if (err == hipSuccess) err = marks.mark(last, 2);
         if (err != hipSuccess) return HISA_ERR_HIP;
     }
     return HISA_OK;

@@ -97,22 +97,47 @@ __device__ __forceinline__ float key_score(uint32_t key)
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// Cross-lane steps through DPP (data-parallel primitives on the VALU):
+// row_shr:n moves values n lanes up inside each row of 16 lanes; row_bcast
+// 15 / 31 carry the last lane of a row into the following row(s).  Lanes
+// with no source read 0.  Every lane of the wave must be active.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v)
 {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int n = __shfl_up(v, o, 64);
-        if (lane_id() >= o) v += n;
-    }
-    return v;
+    uint32_t x = (uint32_t)v;
+    x += dpp_u32<0x111>(x);          // row_shr:1
+    x += dpp_u32<0x112>(x);          // row_shr:2
+    x += dpp_u32<0x114>(x);          // row_shr:4
+    x += dpp_u32<0x118>(x);          // row_shr:8
+    x += dpp_u32<0x142, 0xa>(x);     // row_bcast:15 into rows 1 and 3
+    x += dpp_u32<0x143, 0xc>(x);     // row_bcast:31 into rows 2 and 3
+    return (int)x;
 }
 
 __device__ __forceinline__ int wave_sum(int v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
 }
+
+// Largest value over the wave (unsigned), the same ladder with max.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x)
+{
+    x = max(x, dpp_u32<0x111>(x));
+    x = max(x, dpp_u32<0x112>(x));
+    x = max(x, dpp_u32<0x114>(x));
+    x = max(x, dpp_u32<0x118>(x));
+    x = max(x, dpp_u32<0x142, 0xa>(x));
+    x = max(x, dpp_u32<0x143, 0xc>(x));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return ~wave_max_u32(~x); }
 
 // Inclusive scan over the workgroup in thread order; scratch holds kWaves
 // ints.  Contains barriers: every thread must call it.

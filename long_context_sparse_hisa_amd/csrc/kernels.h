@@ -37,18 +37,23 @@ struct QueryMeta {
     int64_t max_len;
 };
 
-// HISA stage 1: block scores of queries [q0, q0+nq) into sigma [nq, Mmax].
-hipError_t launch_block_scores(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int B,
-                               int64_t Mmax, float* sigma, hipStream_t stream);
+// HISA stage 1: block scores, causal + forced top-m.  sel [nq, m] (the
+// chunk's rows); out_blocks (nullable) gets the same rows at query offset
+// q0.  Queries with at most kStage1FusedMax blocks are scored by the
+// selecting workgroup; longer ones go through sigma [nq, Mmax].
+// lb = log2(B).
+constexpr int64_t kStage1FusedMax = 2048;
+hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
+                         int64_t Mmax, float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream);
 
-// HISA stage 1: causal + forced top-m.  sel [nq, m]; out_blocks (nullable)
-// gets the same rows at query offset q0.
-hipError_t launch_select_blocks(const QueryMeta& qm, int64_t q0, int64_t nq, int B, int m, int64_t Mmax,
-                                const float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream);
-
-// HISA stage 2: token ranking keys of the kept blocks into ukeys [nq, m*B].
-hipError_t launch_token_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int B,
-                               int m, const int32_t* sel, uint32_t* ukeys, hipStream_t stream);
+// HISA stage 2: token scores in the kept blocks and the top-k, written at
+// query offset q0 of out_idx / out_scores.  split: several workgroups per
+// query score into ukeys [nq, m*B], then one workgroup per query selects;
+// otherwise one workgroup per query does both.
+constexpr int kStage2SlotsPerWg = 512;
+hipError_t launch_stage2(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m, int k,
+                         const int32_t* sel, uint32_t* ukeys, int32_t* out_idx, float* out_scores, bool split,
+                         hipStream_t stream);
 
 // Flat: ranking keys of every key position into ukeys [nq, Lmax].
 hipError_t launch_flat_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq,
@@ -56,9 +61,10 @@ hipError_t launch_flat_scores(const QueryMeta& qm, const uint16_t* keys, int64_t
 
 // Top-k of rows of N ranking keys held by one workgroup (N <= 16384).
 // sel == NULL: slot s is token s; otherwise slot s is token
-// sel[row*m + s/B]*B + s%B.
+// sel[row*m + s/B]*B + s%B (lb = log2(B)).  Output row r starts at
+// out_idx + r*k.
 hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel, int m,
-                             int B, int32_t* out_idx, float* out_scores, hipStream_t stream);
+                             int lb, int32_t* out_idx, float* out_scores, hipStream_t stream);
 
 // Top-k of long rows (slot s is token s) with several workgroups per row.
 struct RadixWorkspace {

@@ -94,19 +94,20 @@ hipError_t launch_pool(uint16_t* keys, uint16_t* reps, const uint16_t* new_keys,
     return hipSuccess;
 }
 
-// ---- HISA stage 1: block scores --------------------------------------------
+// ---- HISA stage 1: block scores ----------------------------------------------
 // One thread per (query, causal block): a 128-byte representative row
-// against the query held in registers.
+// against the query held in registers.  Used when a query has too many
+// blocks for one workgroup to score (long contexts).
 
 __global__ __launch_bounds__(kThreads) void block_score_kernel(QueryMeta qm, const uint16_t* reps, int64_t q0,
-                                                               int B, int64_t Mmax, float* sigma)
+                                                               int lb, int64_t Mmax, float* sigma)
 {
     const int64_t row = blockIdx.y;
     const int64_t i = q0 + row;
     const QueryInfo qi =
         query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
     if (!qi.valid) return;
-    const int64_t c = qi.t / B;
+    const int64_t c = qi.t >> lb;
     const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (b > c) return;
     uint32_t q[32];
@@ -115,24 +116,18 @@ __global__ __launch_bounds__(kThreads) void block_score_kernel(QueryMeta qm, con
     sigma[row * Mmax + b] = dot64_packed(q, rp);
 }
 
-hipError_t launch_block_scores(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int B,
-                               int64_t Mmax, float* sigma, hipStream_t stream)
-{
-    dim3 grid((unsigned)((Mmax + kThreads - 1) / kThreads), (unsigned)nq);
-    hipLaunchKernelGGL(block_score_kernel, grid, dim3(kThreads), 0, stream, qm, reps, q0, B, Mmax, sigma);
-    return hipGetLastError();
-}
-
 // ---- HISA stage 1: causal + forced top-m -----------------------------------
 // One workgroup per query.  Block b sits in slot b; the free candidates are
-// blocks 1 .. c-2, from which m-3 are chosen; blocks 0, c-1, c are added.
+// blocks 1 .. c-2, from which m-3 are chosen; blocks 0, c-1, c are added and
+// the kept list comes out ascending.  FUSED: the workgroup scores the
+// representatives itself; otherwise it reads the scores from sigma.
 
-template <int ITEMS>
-__global__ __launch_bounds__(kThreads) void select_blocks_kernel(QueryMeta qm, int64_t q0, int B, int m,
-                                                                 int64_t Mmax, const float* sigma, int32_t* sel,
-                                                                 int32_t* out_blocks)
+template <int NT, int ITEMS, bool FUSED>
+__global__ __launch_bounds__(NT) void stage1_select_kernel(QueryMeta qm, const uint16_t* reps, int64_t q0, int lb,
+                                                           int m, int64_t Mmax, const float* sigma, int32_t* sel,
+                                                           int32_t* out_blocks)
 {
-    __shared__ SelectSmem<ITEMS> sm;
+    __shared__ BucketSmem<NT, ITEMS> sm;
     const int64_t row = blockIdx.x;
     const int64_t i = q0 + row;
     const QueryInfo qi =
@@ -140,30 +135,42 @@ __global__ __launch_bounds__(kThreads) void select_blocks_kernel(QueryMeta qm, i
     int32_t* srow = sel + row * m;
     int32_t* orow = out_blocks ? out_blocks + i * m : nullptr;
     if (!qi.valid) {
-        for (int r = threadIdx.x; r < m; r += kThreads) {
+        for (int r = threadIdx.x; r < m; r += NT) {
             srow[r] = -1;
             if (orow) orow[r] = -1;
         }
         return;
     }
-    const int64_t c = qi.t / B;
+    const int64_t c = qi.t >> lb;
     if (c + 1 <= m) {
-        for (int r = threadIdx.x; r < m; r += kThreads) {
+        for (int r = threadIdx.x; r < m; r += NT) {
             const int32_t v = r <= c ? r : -1;
             srow[r] = v;
             if (orow) orow[r] = v;
         }
         return;
     }
-    const float* sg = sigma + row * Mmax;
     uint32_t key[ITEMS];
+    if (FUSED) {
+        uint32_t q[32];
+        load_query(qm.queries + i * kDim, q);
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-        const int64_t b = (int64_t)it * kThreads + threadIdx.x;
-        key[it] = (b >= 1 && b <= c - 2) ? score_key(sg[b]) : 0u;
+        for (int it = 0; it < ITEMS; ++it) {
+            const int64_t b = (int64_t)it * NT + threadIdx.x;
+            key[it] = (b >= 1 && b <= c - 2)
+                          ? score_key(dot64_packed(q, reinterpret_cast<const uint4*>(reps + (qi.rep_off + b) * kDim)))
+                          : 0u;
+        }
+    } else {
+        const float* sg = sigma + row * Mmax;
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int64_t b = (int64_t)it * NT + threadIdx.x;
+            key[it] = (b >= 1 && b <= c - 2) ? score_key(sg[b]) : 0u;
+        }
     }
-    const Threshold th = wg_radix_select(key, m - 3, sm);
-    wg_emit_selected(key, th, sm, [&](int slot, uint32_t, int rank) {
+    const Threshold th = wg_bucket_select<NT, ITEMS>(key, m - 3, sm);
+    wg_emit_selected<NT, ITEMS>(key, th, sm.radix, [&](int slot, uint32_t, int rank) {
         srow[1 + rank] = slot;
         if (orow) orow[1 + rank] = slot;
     });
@@ -179,66 +186,232 @@ __global__ __launch_bounds__(kThreads) void select_blocks_kernel(QueryMeta qm, i
     }
 }
 
-template <int ITEMS>
-static hipError_t launch_select_items(const QueryMeta& qm, int64_t q0, int64_t nq, int B, int m, int64_t Mmax,
-                                      const float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream)
+template <int NT, int ITEMS, bool FUSED>
+static hipError_t launch_stage1_items(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb,
+                                      int m, int64_t Mmax, const float* sigma, int32_t* sel, int32_t* out_blocks,
+                                      hipStream_t stream)
 {
-    hipLaunchKernelGGL(select_blocks_kernel<ITEMS>, dim3((unsigned)nq), dim3(kThreads), 0, stream, qm, q0, B, m,
-                       Mmax, sigma, sel, out_blocks);
+    hipLaunchKernelGGL((stage1_select_kernel<NT, ITEMS, FUSED>), dim3((unsigned)nq), dim3(NT), 0, stream, qm, reps,
+                       q0, lb, m, Mmax, sigma, sel, out_blocks);
     return hipGetLastError();
 }
 
-hipError_t launch_select_blocks(const QueryMeta& qm, int64_t q0, int64_t nq, int B, int m, int64_t Mmax,
-                                const float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream)
+hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
+                         int64_t Mmax, float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream)
 {
-    const int64_t per = (Mmax + kThreads - 1) / kThreads;
-    if (per <= 1) return launch_select_items<1>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
-    if (per <= 2) return launch_select_items<2>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
-    if (per <= 4) return launch_select_items<4>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
-    if (per <= 8) return launch_select_items<8>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
-    if (per <= 16) return launch_select_items<16>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
-    if (per <= 32) return launch_select_items<32>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
-    if (per <= 64) return launch_select_items<64>(qm, q0, nq, B, m, Mmax, sigma, sel, out_blocks, stream);
+    if (Mmax <= kStage1FusedMax) {
+        // 256 threads score up to 2048 representatives, 8 per thread
+        const int64_t per = (Mmax + 255) / 256;
+#define HISA_S1F(N) \
+    if (per <= N) return launch_stage1_items<256, N, true>(qm, reps, q0, nq, lb, m, Mmax, nullptr, sel, out_blocks, stream)
+        HISA_S1F(1);
+        HISA_S1F(2);
+        HISA_S1F(4);
+        HISA_S1F(8);
+#undef HISA_S1F
+        return hipErrorInvalidValue;
+    }
+    dim3 grid((unsigned)((Mmax + kThreads - 1) / kThreads), (unsigned)nq);
+    hipLaunchKernelGGL(block_score_kernel, grid, dim3(kThreads), 0, stream, qm, reps, q0, lb, Mmax, sigma);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // 1024 threads select among up to 16384 scores, 16 per thread
+    const int64_t per = (Mmax + 1023) / 1024;
+#define HISA_S1S(N) \
+    if (per <= N) return launch_stage1_items<1024, N, false>(qm, reps, q0, nq, lb, m, Mmax, sigma, sel, out_blocks, stream)
+    HISA_S1S(2);
+    HISA_S1S(4);
+    HISA_S1S(8);
+    HISA_S1S(16);
+#undef HISA_S1S
     return hipErrorInvalidValue;
 }
 
-// ---- HISA stage 2: token scores in the kept blocks -------------------------
+// ---- HISA stage 2: token scores in the kept blocks and top-k ---------------
 // Candidate slot s of a query is row s % B of kept block s / B; slots of
 // padding blocks and keys after the query get key 0.
 
-__global__ __launch_bounds__(kThreads) void token_score_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0,
-                                                               int B, int m, const int32_t* sel, uint32_t* ukeys)
+HISA_INLINE uint32_t token_key(const uint32_t (&q)[32], const uint16_t* keys, const QueryInfo& qi,
+                               const int32_t* srow, int lb, int s)
 {
-    const int64_t row = blockIdx.y;
-    const int64_t i = q0 + row;
-    const int64_t N = (int64_t)m * B;
-    const int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (s >= N) return;
-    uint32_t* out = ukeys + row * N + s;
-    const QueryInfo qi =
-        query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
-    if (!qi.valid) {
-        *out = 0u;
-        return;
-    }
-    const int32_t blk = sel[row * m + s / B];
-    const int64_t j = (int64_t)blk * B + s % B;
-    if (blk < 0 || j > qi.t) {
-        *out = 0u;
-        return;
-    }
-    uint32_t q[32];
-    load_query(qm.queries + i * kDim, q);
-    *out = score_key(dot64_packed(q, reinterpret_cast<const uint4*>(keys + (qi.key_off + j) * kDim)));
+    const int32_t blk = srow[s >> lb];
+    const int64_t j = ((int64_t)blk << lb) + (s & ((1 << lb) - 1));
+    if (blk < 0 || j > qi.t) return 0u;
+    return score_key(dot64_packed(q, reinterpret_cast<const uint4*>(keys + (qi.key_off + j) * kDim)));
 }
 
-hipError_t launch_token_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int B, int m,
-                               const int32_t* sel, uint32_t* ukeys, hipStream_t stream)
+// Select the k best slots of one row and write them (ascending token index)
+// with their scores, then the -1 padding.  srow == NULL: slot s is token s.
+template <int NT, int ITEMS>
+HISA_INLINE void select_and_write(const uint32_t (&key)[ITEMS], int k, int lb, const int32_t* srow, int32_t* orow,
+                                  float* scrow, BucketSmem<NT, ITEMS>& sm)
 {
-    const int64_t N = (int64_t)m * B;
-    dim3 grid((unsigned)((N + kThreads - 1) / kThreads), (unsigned)nq);
-    hipLaunchKernelGGL(token_score_kernel, grid, dim3(kThreads), 0, stream, qm, keys, q0, B, m, sel, ukeys);
+    const Threshold th = wg_bucket_select<NT, ITEMS>(key, k, sm);
+    const int total = wg_emit_selected<NT, ITEMS>(key, th, sm.radix, [&](int slot, uint32_t kk, int rank) {
+        orow[rank] = srow ? (srow[slot >> lb] << lb) + (slot & ((1 << lb) - 1)) : slot;
+        if (scrow) scrow[rank] = key_score(kk);
+    });
+    for (int r = total + threadIdx.x; r < k; r += NT) {
+        orow[r] = -1;
+        if (scrow) scrow[r] = __builtin_nanf("");
+    }
+}
+
+// One workgroup per query: gather, score and select without leaving the
+// workgroup (many queries in flight).
+template <int NT, int ITEMS>
+__global__ __launch_bounds__(NT) void stage2_fused_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0, int lb,
+                                                          int m, int k, const int32_t* sel, int32_t* out_idx,
+                                                          float* out_scores)
+{
+    __shared__ BucketSmem<NT, ITEMS> sm;
+    const int64_t row = blockIdx.x;
+    const int64_t i = q0 + row;
+    const QueryInfo qi =
+        query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
+    const int N = m << lb;
+    const int32_t* srow = sel + row * m;
+    uint32_t key[ITEMS];
+    if (qi.valid) {
+        uint32_t q[32];
+        load_query(qm.queries + i * kDim, q);
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int s = it * NT + threadIdx.x;
+            key[it] = s < N ? token_key(q, keys, qi, srow, lb, s) : 0u;
+        }
+    } else {
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) key[it] = 0u;
+    }
+    select_and_write<NT, ITEMS>(key, k, lb, srow, out_idx + i * k, out_scores ? out_scores + i * k : nullptr, sm);
+}
+
+// Several workgroups per query, each scoring `per_wg` slots into ukeys;
+// few queries still fill the chip.  The top-k follows in topk_rows_kernel.
+__global__ __launch_bounds__(kThreads) void stage2_score_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0,
+                                                                int lb, int m, int per_wg, const int32_t* sel,
+                                                                uint32_t* ukeys)
+{
+    const int64_t row = blockIdx.x;
+    const int64_t i = q0 + row;
+    const QueryInfo qi =
+        query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
+    const int N = m << lb;
+    const int32_t* srow = sel + row * m;
+    uint32_t* urow = ukeys + row * N;
+    const int beg = blockIdx.y * per_wg;
+    const int end = min(N, beg + per_wg);
+    if (qi.valid) {
+        uint32_t q[32];
+        load_query(qm.queries + i * kDim, q);
+        for (int s = beg + threadIdx.x; s < end; s += kThreads) urow[s] = token_key(q, keys, qi, srow, lb, s);
+    } else {
+        for (int s = beg + threadIdx.x; s < end; s += kThreads) urow[s] = 0u;
+    }
+}
+
+// Top-k of rows of N ranking keys, one workgroup per row; out rows start at
+// out_idx / out_scores (the caller offsets them).  sel: slot -> token map.
+template <int NT, int ITEMS>
+__global__ __launch_bounds__(NT) void topk_rows_kernel(const uint32_t* ukeys, int N, int k, const int32_t* sel, int m,
+                                                       int lb, int32_t* out_idx, float* out_scores)
+{
+    __shared__ BucketSmem<NT, ITEMS> sm;
+    const int64_t row = blockIdx.x;
+    const uint32_t* src = ukeys + row * N;
+    uint32_t key[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int s = it * NT + threadIdx.x;
+        key[it] = s < N ? src[s] : 0u;
+    }
+    select_and_write<NT, ITEMS>(key, k, lb, sel ? sel + row * m : nullptr, out_idx + row * k,
+                                out_scores ? out_scores + row * k : nullptr, sm);
+}
+
+template <int NT, int ITEMS>
+static hipError_t launch_topk_rows_items(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel,
+                                         int m, int lb, int32_t* out_idx, float* out_scores, hipStream_t stream)
+{
+    hipLaunchKernelGGL((topk_rows_kernel<NT, ITEMS>), dim3((unsigned)nrows), dim3(NT), 0, stream, ukeys, N, k, sel, m,
+                       lb, out_idx, out_scores);
     return hipGetLastError();
+}
+
+hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel, int m, int lb,
+                             int32_t* out_idx, float* out_scores, hipStream_t stream)
+{
+    if (N <= 2048) {
+        const int per = (N + 255) / 256;
+#define HISA_TK(N_) \
+    if (per <= N_) return launch_topk_rows_items<256, N_>(ukeys, nrows, N, k, sel, m, lb, out_idx, out_scores, stream)
+        HISA_TK(1);
+        HISA_TK(2);
+        HISA_TK(4);
+        HISA_TK(8);
+#undef HISA_TK
+    }
+    const int per = (N + 1023) / 1024;
+#define HISA_TK(N_) \
+    if (per <= N_) return launch_topk_rows_items<1024, N_>(ukeys, nrows, N, k, sel, m, lb, out_idx, out_scores, stream)
+    HISA_TK(2);
+    HISA_TK(4);
+    HISA_TK(8);
+    HISA_TK(16);
+#undef HISA_TK
+    return hipErrorInvalidValue;
+}
+
+template <int NT, int ITEMS>
+static hipError_t launch_stage2_fused(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m,
+                                      int k, const int32_t* sel, int32_t* out_idx, float* out_scores,
+                                      hipStream_t stream)
+{
+    hipLaunchKernelGGL((stage2_fused_kernel<NT, ITEMS>), dim3((unsigned)nq), dim3(NT), 0, stream, qm, keys, q0, lb, m,
+                       k, sel, out_idx, out_scores);
+    return hipGetLastError();
+}
+
+hipError_t launch_stage2(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m, int k,
+                         const int32_t* sel, uint32_t* ukeys, int32_t* out_idx, float* out_scores, bool split,
+                         hipStream_t stream)
+{
+    const int N = m << lb;
+    if (split) {
+        const int per_wg = kStage2SlotsPerWg;
+        dim3 grid((unsigned)nq, (unsigned)((N + per_wg - 1) / per_wg));
+        hipLaunchKernelGGL(stage2_score_kernel, grid, dim3(kThreads), 0, stream, qm, keys, q0, lb, m, per_wg, sel,
+                           ukeys);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        return launch_topk_small(ukeys, nq, N, k, sel, m, lb, out_idx + q0 * k,
+                                 out_scores ? out_scores + q0 * k : nullptr, stream);
+    }
+    if (N <= 2048) {
+        const int per = (N + 255) / 256;
+#define HISA_S2(N_) \
+    if (per <= N_) return launch_stage2_fused<256, N_>(qm, keys, q0, nq, lb, m, k, sel, out_idx, out_scores, stream)
+        HISA_S2(1);
+        HISA_S2(2);
+        HISA_S2(4);
+        HISA_S2(8);
+#undef HISA_S2
+    }
+    if (N <= 8192) {
+        const int per = (N + 511) / 512;
+#define HISA_S2(N_) \
+    if (per <= N_) return launch_stage2_fused<512, N_>(qm, keys, q0, nq, lb, m, k, sel, out_idx, out_scores, stream)
+        HISA_S2(8);
+        HISA_S2(16);
+#undef HISA_S2
+    }
+    const int per = (N + 1023) / 1024;
+#define HISA_S2(N_) \
+    if (per <= N_) return launch_stage2_fused<1024, N_>(qm, keys, q0, nq, lb, m, k, sel, out_idx, out_scores, stream)
+    HISA_S2(16);
+#undef HISA_S2
+    return hipErrorInvalidValue;
 }
 
 // ---- flat indexer: every key ------------------------------------------------
@@ -268,58 +441,6 @@ hipError_t launch_flat_scores(const QueryMeta& qm, const uint16_t* keys, int64_t
     dim3 grid((unsigned)((Lmax + kThreads - 1) / kThreads), (unsigned)nq);
     hipLaunchKernelGGL(flat_score_kernel, grid, dim3(kThreads), 0, stream, qm, keys, q0, Lmax, ukeys);
     return hipGetLastError();
-}
-
-// ---- top-k of short rows: one workgroup per row ----------------------------
-
-template <int ITEMS>
-__global__ __launch_bounds__(kThreads) void topk_small_kernel(const uint32_t* ukeys, int N, int k, const int32_t* sel,
-                                                              int m, int B, int32_t* out_idx, float* out_scores)
-{
-    __shared__ SelectSmem<ITEMS> sm;
-    const int64_t row = blockIdx.x;
-    const uint32_t* src = ukeys + row * N;
-    uint32_t key[ITEMS];
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-        const int s = it * kThreads + threadIdx.x;
-        key[it] = s < N ? src[s] : 0u;
-    }
-    const Threshold th = wg_radix_select(key, k, sm);
-    int32_t* orow = out_idx + row * k;
-    float* srow = out_scores ? out_scores + row * k : nullptr;
-    const int32_t* selrow = sel ? sel + row * m : nullptr;
-    const int total = wg_emit_selected(key, th, sm, [&](int slot, uint32_t kk, int rank) {
-        orow[rank] = selrow ? selrow[slot / B] * B + slot % B : slot;
-        if (srow) srow[rank] = key_score(kk);
-    });
-    for (int r = total + threadIdx.x; r < k; r += kThreads) {
-        orow[r] = -1;
-        if (srow) srow[r] = __builtin_nanf("");
-    }
-}
-
-template <int ITEMS>
-static hipError_t launch_topk_items(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel, int m,
-                                    int B, int32_t* out_idx, float* out_scores, hipStream_t stream)
-{
-    hipLaunchKernelGGL(topk_small_kernel<ITEMS>, dim3((unsigned)nrows), dim3(kThreads), 0, stream, ukeys, N, k, sel,
-                       m, B, out_idx, out_scores);
-    return hipGetLastError();
-}
-
-hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel, int m, int B,
-                             int32_t* out_idx, float* out_scores, hipStream_t stream)
-{
-    const int per = (N + kThreads - 1) / kThreads;
-    if (per <= 1) return launch_topk_items<1>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
-    if (per <= 2) return launch_topk_items<2>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
-    if (per <= 4) return launch_topk_items<4>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
-    if (per <= 8) return launch_topk_items<8>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
-    if (per <= 16) return launch_topk_items<16>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
-    if (per <= 32) return launch_topk_items<32>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
-    if (per <= 64) return launch_topk_items<64>(ukeys, nrows, N, k, sel, m, B, out_idx, out_scores, stream);
-    return hipErrorInvalidValue;
 }
 
 // ---- top-k of long rows: S workgroups per row --------------------------------

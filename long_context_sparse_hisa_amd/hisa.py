@@ -44,13 +44,18 @@ class hisa_index_args(ctypes.Structure):
         ("d", ctypes.c_int32), ("B", ctypes.c_int32), ("m", ctypes.c_int32), ("k", ctypes.c_int32),
         ("out_idx", _P), ("out_scores", _P), ("out_blocks", _P),
         ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+        ("stage_events", ctypes.POINTER(_P)),
     ]
+
+
+HISA_STAGE_EVENTS = 5
 
 
 def lib():
     """The loaded libhisa (raises if it was not built)."""
     global _lib
     if _lib is None:
+        import torch  # noqa: F401  (one HIP runtime: libhisa binds to the one torch loaded)
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("libhisa.so is not built: run python -m long_context_sparse_hisa_amd.build")
         L = ctypes.CDLL(LIB_PATH)
@@ -166,3 +171,54 @@ def hisa_index(args: hisa_index_args, stream=None):
 
 def hisa_flat_index(args: hisa_index_args, stream=None):
     _check(lib().hisa_flat_index(ctypes.byref(args), _stream(stream)), "hisa_flat_index")
+
+
+# ---- HIP events (stage timing) -------------------------------------------------
+
+_hip = None
+
+
+def _hiprt():
+    global _hip
+    if _hip is None:
+        lib()                                  # the HIP runtime torch loaded
+        h = ctypes.CDLL("libamdhip64.so.7")
+        h.hipEventCreate.argtypes = [ctypes.POINTER(_P)]
+        h.hipEventDestroy.argtypes = [_P]
+        h.hipEventSynchronize.argtypes = [_P]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _P, _P]
+        h.hipEventRecord.argtypes = [_P, _P]
+        _hip = h
+    return _hip
+
+
+class StageEvents:
+    """HISA_STAGE_EVENTS hipEvent_t handles to hang on hisa_index_args."""
+
+    def __init__(self):
+        h = _hiprt()
+        self.handles = (_P * HISA_STAGE_EVENTS)()
+        for i in range(HISA_STAGE_EVENTS):
+            e = _P()
+            if h.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles[i] = e
+
+    def attach(self, args: hisa_index_args):
+        args.stage_events = ctypes.cast(self.handles, ctypes.POINTER(_P))
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        h = _hiprt()
+        h.hipEventSynchronize(self.handles[b])
+        f = ctypes.c_float(0.0)
+        if h.hipEventElapsedTime(ctypes.byref(f), self.handles[a], self.handles[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(f.value)
+
+    def __del__(self):
+        try:
+            h = _hiprt()
+            for i in range(HISA_STAGE_EVENTS):
+                h.hipEventDestroy(self.handles[i])
+        except Exception:
+            pass

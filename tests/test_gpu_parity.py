@@ -321,3 +321,48 @@ def test_long_decode_1m_with_appends():
         w.keys = full                                    # the oracle reads the grown cache
         for flat in (False, True):
             _check_phase(w, cache, ph, w.k, w.m, flat, label="cfg5 " + ph.name, props=True)
+
+
+def test_graph_replays_match_eager():
+    """A decode step (append + HISA + flat) captured in a HIP graph gives the
+    eager result on every replay, with other eager work in between."""
+    print("graph replay", flush=True)
+    dv = _dev()
+    w = synth.decode_batch(nseq=4, L=20000, seed=30, B=128, m=16, k=512, spare=8)
+    cache = dv.DeviceCache(w)
+    cache.set_lengths(w.seq_len - 1)
+    cache.pool()
+    last = np.stack([w.keys[int(o) + int(L) - 1] for o, L in zip(w.seq_key_off, w.seq_len)])[:, None]
+    new = dv.to_dev(last, cache.device)
+    seqs = [(cache.seq_key_off[s], cache.seq_rep_off[s], cache.seq_len[s], cache.seq_cap[s])
+            for s in range(cache.nseq)]
+    cache.append(new)                        # lengths the queries see
+    ph = w.phases[0]
+    hcall = dv.IndexCall(cache, ph.queries, ph.q_pos, ph.q_seq, k=512, m=16)
+    fcall = dv.IndexCall(cache, ph.queries, ph.q_pos, ph.q_seq, k=512, m=16, flat=True)
+    from long_context_sparse_hisa_amd import hisa
+
+    def step():
+        hisa.hisa_append_keys(cache.keys, cache.reps, seqs, new, cache.B)
+        hcall.run()
+        fcall.run()
+
+    step()
+    want = [x.copy() for x in hcall.results() + fcall.results() if x is not None]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in [hcall.out_idx, fcall.out_idx, hcall.out_scores, fcall.out_scores, hcall.out_blocks]:
+            t.fill_(7)                        # eager work that the replay must overwrite
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [x for x in hcall.results() + fcall.results() if x is not None]
+        for a, b in zip(got, want):
+            assert np.array_equal(np.nan_to_num(a, nan=-9), np.nan_to_num(b, nan=-9)), "replay %d" % rep
