@@ -16,11 +16,11 @@ last-level cache from serving repeated steps, the step rotates over
 numbers); `--replicas 1` gives the warm-cache figure.
 
 The timed region replays one captured HIP graph per step (per replica):
-the step's kernels without host work in between.  Per-stage durations come
-from HIP events recorded on the launch stream around every stage of a
-separate run of eager steps queued behind a sleep kernel, so that they run
-back to back; the roofline object is computed from the stage with the
-largest average duration.
+the step's kernels without host work in between.  Per-kernel durations come
+from HIP start / stop events attached to the kernel dispatches of a
+separate run of eager steps (queued behind a sleep kernel so they run back
+to back); the roofline object is computed from the kernel with the largest
+average duration.
 """
 from __future__ import annotations
 
@@ -38,7 +38,11 @@ HBM_PEAK_GBPS = 8000.0
 WORKLOADS = ("decode_32k_x16", "chunked_prefill_32k", "long_context_128k", "long_decode_1m",
              "tiny_prefill_4k")
 
-STAGES_HISA = ("block_stage", "token_stage")
+STAGES_HISA = ("block_stage", "token_scores", "token_topk")
+STAGES_HISA_FUSED = ("block_stage", "token_fused")
+# the library splits the token stage over several workgroups per query
+# (scores, then a separate top-k kernel) for calls with fewer queries
+SPLIT_BELOW = 512
 STAGES_FLAT = ("flat_scores", "flat_topk")
 
 
@@ -60,7 +64,11 @@ def hisa_stage_bytes(q_pos, B, m, k):
     cand = np.minimum(kept * B, q_pos + 1)                # <= m*B candidate tokens
     return {
         "block_stage": float((128 + nb * 128 + 2 * m * 4).sum()),
-        "token_stage": float((128 + m * 4 + cand * 128 + k * 8).sum()),
+        # few queries: scores go to a workspace row, then the top-k reads it
+        "token_scores": float((128 + m * 4 + cand * 128 + m * B * 4).sum()),
+        "token_topk": float(len(q_pos) * (m * B * 4 + m * 4 + k * 8)),
+        # one workgroup per query: both in one kernel
+        "token_fused": float((128 + m * 4 + cand * 128 + k * 8).sum()),
     }
 
 
@@ -71,8 +79,45 @@ def flat_stage_bytes(q_pos, k):
     n = q_pos + 1
     return {
         "flat_scores": float((n * 128 + 128 + n * 4).sum()),
-        "flat_topk": float((n * 4 + k * 8).sum()),
+        "flat_topk": float((n * 4).sum() + len(n) * k * 8),
     }
+
+
+# ---- measured HBM traffic ----------------------------------------------------------
+
+# kernel symbol that carries each stage
+STAGE_KERNEL = {"block_stage": "stage1_select_kernel", "token_scores": "stage2_score_kernel",
+                "token_topk": "topk_rows_kernel", "token_fused": "stage2_fused_kernel",
+                "flat_scores": "flat_score_kernel"}
+
+
+def kernel_source_hash(root):
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(root, "long_context_sparse_hisa_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(root, workload, stage):
+    """HBM bytes per dispatch of a stage's kernel from the PMC summary under
+    profiles/ (FETCH_SIZE and WRITE_SIZE scaled by a known-size copy), or
+    None when there is none or the kernel sources changed since."""
+    import glob
+    sym = STAGE_KERNEL.get(stage.split("/")[-1])
+    if sym is None:
+        return None
+    for path in glob.glob(os.path.join(root, "profiles", "*_hbm_traffic.md")):
+        lines = open(path).read().splitlines()
+        sha = [l.split("=", 1)[1].strip() for l in lines if l.startswith("source_sha256")]
+        if not sha or sha[0] != kernel_source_hash(root):
+            continue
+        for l in lines:
+            f = l.split("\t")
+            if len(f) == 4 and f[0] == "traffic" and f[1] == workload and sym in f[2]:
+                return float(f[3])
+    return None
 
 
 # ---- setup -----------------------------------------------------------------------
@@ -203,10 +248,11 @@ def time_method(S, flat, steps, warmup, torch):
 
 
 def stage_times(S, flat, nsteps, torch):
-    """Average duration of every stage, from HIP events recorded on the
-    launch stream around each stage of `nsteps` eager steps.  A sleep kernel
-    holds the GPU while the host queues the steps, so the queued kernels run
-    back to back and the event gaps are the kernels' own durations."""
+    """Average duration of every stage over `nsteps` eager steps, from the
+    start / stop HIP events the library records with each stage's kernel
+    dispatches (the kernels' own execution time).  A sleep kernel holds the
+    GPU while the host queues the steps, so the kernels run back to back as
+    in the graph-replayed steps."""
     h = S.h
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -227,11 +273,14 @@ def stage_times(S, flat, nsteps, torch):
     for i in range(nsteps):
         S.step(i % S.replicas, flat, sp, evs[i], app[i] if app else None)
     torch.cuda.synchronize()
-    names = STAGES_FLAT if flat else STAGES_HISA
     out = {}
     for p in range(nph):
-        for s_, nm in enumerate(names, start=1):
-            vals = [evs[i][p].elapsed_ms(s_ - 1, s_) for i in range(nsteps)]
+        if flat:
+            names = STAGES_FLAT
+        else:
+            names = STAGES_HISA if len(S.phases[p].q_pos) < SPLIT_BELOW else STAGES_HISA_FUSED
+        for s_, nm in enumerate(names):
+            vals = [evs[i][p].stage_ms(s_) for i in range(nsteps)]
             out["%s/%s" % (S.phases[p].name, nm)] = float(np.mean(vals))
     if app:
         vals = []
@@ -301,6 +350,8 @@ def main():
     ap.add_argument("--stage-steps", type=int, default=32,
                     help="eager steps whose stages are timed with HIP events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device (a known-size reference for HBM counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -315,6 +366,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
+        return
     hisa.lib()
     default_rep = {"decode_32k_x16": 64, "long_decode_1m": 256, "chunked_prefill_32k": 1,
                    "long_context_128k": 1, "tiny_prefill_4k": 1}
@@ -345,13 +405,19 @@ def main():
     achieved = stage_bytes[kern] / (h_stage[kern] * 1e-3) / 1e9
     fkern = max((n for n in f_stage if n in stage_bytes), key=lambda n: f_stage[n])
     f_achieved = stage_bytes[fkern] / (f_stage[fkern] * 1e-3) / 1e9
-    # algorithmic bytes of a whole step: every stage's per-query traffic plus
-    # the append (new rows written, touched blocks re-read, reps written)
+    # algorithmic bytes of a whole step: every stage's per-query traffic
+    # (no workspace round trips) plus the append (new rows written, touched
+    # blocks re-read, representatives written)
     append_rows = 0 if S.append_src is None else S.append_src.shape[0] * S.append_src.shape[1]
-    h_step_bytes = sum(b for n, b in stage_bytes.items() if n.split("/")[-1] in STAGES_HISA)
+    h_step_bytes = sum(b for n, b in stage_bytes.items() if n.split("/")[-1] in STAGES_HISA_FUSED)
     f_step_bytes = sum(b for n, b in stage_bytes.items() if n.split("/")[-1] in STAGES_FLAT)
     h_step_bytes += append_rows * 128 * 2
     f_step_bytes += append_rows * 128 * 2
+
+    def per_kernel(stage):
+        return {n: {"avg_ms": v, "algorithmic_bytes": stage_bytes.get(n),
+                    "gbps": (stage_bytes[n] / (v * 1e-3) / 1e9) if n in stage_bytes and v > 0 else None}
+                for n, v in stage.items()}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -375,14 +441,15 @@ def main():
         "config": {"workload": args.workload, "description": S.desc, "queries_per_step": S.q_per_step,
                    "replicas": R, "B": S.B, "m": S.m, "k": S.k},
         "roofline": {"bound": "hbm", "kernel": kern, "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)), args.workload, kern),
                      "algorithmic_bytes_per_launch": stage_bytes[kern],
                      "avg_launch_ms": h_stage[kern]},
         "cpu_baseline": cpu,
         "step_bytes": h_step_bytes,
         "hbm_gbps_step": h_step_bytes / (h_ms * 1e-3) / 1e9,
-        "stage_ms": h_stage,
-        "flat": {"value": fqps, "unit": "queries/s", "ms_per_step": f_ms, "stage_ms": f_stage,
+        "kernels": per_kernel(h_stage),
+        "flat": {"value": fqps, "unit": "queries/s", "ms_per_step": f_ms, "kernels": per_kernel(f_stage),
                  "step_bytes": f_step_bytes,
                  "hbm_gbps_step": f_step_bytes / (f_ms * 1e-3) / 1e9,
                  "dominant": {"kernel": fkern, "achieved_gbps": f_achieved,

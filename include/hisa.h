@@ -150,15 +150,19 @@ typedef struct hisa_index_args {
     int32_t* out_blocks;         /* [nq, m] or NULL (HISA only) */
     void* workspace;             /* device scratch owned by the caller */
     size_t workspace_bytes;      /* its size; see hisa_workspace_bytes */
-    void* const* stage_events;   /* NULL, or HISA_STAGE_EVENTS hipEvent_t handles (profiling
-                                    aid): event 0 is recorded on the stream before the first
-                                    kernel of the call's last query chunk, event s right after
-                                    stage s of that chunk.  HISA stages: 1 block scores and
-                                    top-m, 2 token scores and top-k.  Flat stages: 1 scores,
-                                    2 top-k.  Events 3 and 4 are not recorded. */
+    void* const* stage_events;   /* NULL, or 2 * HISA_STAGES hipEvent_t handles (profiling aid,
+                                    created with timing enabled).  Events 2s and 2s+1 record
+                                    when the first kernel of stage s starts and its last kernel
+                                    ends, for the call's last query chunk, from the dispatch
+                                    itself.  HISA stages: 0 block scores and top-m; 1 token
+                                    scores (fewer than 512 queries) or token scores and top-k
+                                    (one workgroup per query); 2 token top-k (fewer than 512
+                                    queries, else not recorded).  Flat stages: 0 scores,
+                                    1 top-k (2 not recorded). */
 } hisa_index_args;
 
-#define HISA_STAGE_EVENTS 5
+#define HISA_STAGES 3
+
 
 /*
  * hisa_workspace_bytes -- workspace an index call wants for these

@@ -135,16 +135,16 @@ QueryMeta meta_of(const hisa_index_args* a)
 template <class T>
 T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
 
-// Records stage event s of the last chunk when the caller asked for them.
-struct StageMarks {
-    void* const* ev;
-    hipStream_t stream;
-    hipError_t mark(bool last_chunk, int s) const
-    {
-        if (!ev || !last_chunk || !ev[s]) return hipSuccess;
-        return hipEventRecord(static_cast<hipEvent_t>(ev[s]), stream);
+// Start / stop events of stage s for the last query chunk, if asked for.
+Timing stage_timing(const hisa_index_args* a, bool last_chunk, int s)
+{
+    Timing t;
+    if (a->stage_events && last_chunk) {
+        t.start = static_cast<hipEvent_t>(a->stage_events[2 * s]);
+        t.stop = static_cast<hipEvent_t>(a->stage_events[2 * s + 1]);
     }
-};
+    return t;
+}
 
 }  // namespace
 
@@ -231,18 +231,22 @@ int hisa_index(const hisa_index_args* a, void* stream_)
     float* sigma = Mmax > kStage1FusedMax ? at<float>(a->workspace, L.sigma) : nullptr;
     int32_t* sel = at<int32_t>(a->workspace, L.sel);
     uint32_t* ukeys = split ? at<uint32_t>(a->workspace, L.ukeys) : nullptr;
-    const StageMarks marks{a->stage_events, stream};
     for (int64_t q0 = 0; q0 < a->nq; q0 += chunk) {
         const int64_t nc = std::min(chunk, a->nq - q0);
         const bool last = q0 + nc >= a->nq;
-        hipError_t err = marks.mark(last, 0);
-        if (err == hipSuccess)
-            err = launch_stage1(qm, a->reps, q0, nc, lb, a->m, Mmax, sigma, sel, a->out_blocks, stream);
-        if (err == hipSuccess) err = marks.mark(last, 1);
-        if (err == hipSuccess)
-            err = launch_stage2(qm, a->keys, q0, nc, lb, a->m, a->k, sel, ukeys, a->out_idx, a->out_scores, split,
-                                stream);
-        if (err == hipSuccess) err = marks.mark(last, 2);
+        hipError_t err = launch_stage1(qm, a->reps, q0, nc, lb, a->m, Mmax, sigma, sel, a->out_blocks, stream,
+                                       stage_timing(a, last, 0));
+        if (err == hipSuccess && split) {
+            err = launch_stage2_split_scores(qm, a->keys, q0, nc, lb, a->m, sel, ukeys, stream,
+                                             stage_timing(a, last, 1));
+            if (err == hipSuccess)
+                err = launch_topk_small(ukeys, nc, a->m << lb, a->k, sel, a->m, lb, a->out_idx + q0 * a->k,
+                                        a->out_scores ? a->out_scores + q0 * a->k : nullptr, stream,
+                                        stage_timing(a, last, 2));
+        } else if (err == hipSuccess) {
+            err = launch_stage2_fused(qm, a->keys, q0, nc, lb, a->m, a->k, sel, a->out_idx, a->out_scores, stream,
+                                      stage_timing(a, last, 1));
+        }
         if (err != hipSuccess) return HISA_ERR_HIP;
     }
     return HISA_OK;
@@ -260,25 +264,22 @@ int hisa_flat_index(const hisa_index_args* a, void* stream_)
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     const QueryMeta qm = meta_of(a);
     uint32_t* ukeys = at<uint32_t>(a->workspace, L.ukeys);
-    const StageMarks marks{a->stage_events, stream};
     for (int64_t q0 = 0; q0 < a->nq; q0 += chunk) {
         const int64_t nc = std::min(chunk, a->nq - q0);
         const bool last = q0 + nc >= a->nq;
         int32_t* oi = a->out_idx + q0 * a->k;
         float* os = a->out_scores ? a->out_scores + q0 * a->k : nullptr;
-        hipError_t err = marks.mark(last, 0);
-        if (err == hipSuccess) err = launch_flat_scores(qm, a->keys, q0, nc, a->max_len, ukeys, stream);
-        if (err == hipSuccess) err = marks.mark(last, 1);
+        hipError_t err = launch_flat_scores(qm, a->keys, q0, nc, a->max_len, ukeys, stream, stage_timing(a, last, 0));
         if (err == hipSuccess) {
             if (!flat_uses_radix(a)) {
-                err = launch_topk_small(ukeys, nc, (int)a->max_len, a->k, nullptr, 0, 0, oi, os, stream);
+                err = launch_topk_small(ukeys, nc, (int)a->max_len, a->k, nullptr, 0, 0, oi, os, stream,
+                                        stage_timing(a, last, 1));
             } else {
                 RadixWorkspace ws{at<int>(a->workspace, L.hist), at<uint32_t>(a->workspace, L.state),
                                   at<int>(a->workspace, L.counts)};
-                err = launch_topk_radix(ukeys, nc, a->max_len, a->k, ws, oi, os, stream);
+                err = launch_topk_radix(ukeys, nc, a->max_len, a->k, ws, oi, os, stream, stage_timing(a, last, 1));
             }
         }
-        if (err == hipSuccess) err = marks.mark(last, 2);
         if (err != hipSuccess) return HISA_ERR_HIP;
     }
     return HISA_OK;

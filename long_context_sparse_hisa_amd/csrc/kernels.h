@@ -9,6 +9,14 @@
 
 namespace hisa {
 
+// Optional kernel timing: when set, the first kernel of a launcher records
+// `start` when it begins and the last records `stop` when it ends (the
+// dispatch packet's own timestamps, as a profiler sees them).
+struct Timing {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 // One sequence's part of a pool / append launch.
 struct PoolJob {
     int64_t key_off;    // first key row of the sequence
@@ -44,27 +52,31 @@ struct QueryMeta {
 // lb = log2(B).
 constexpr int64_t kStage1FusedMax = 2048;
 hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
-                         int64_t Mmax, float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream);
+                         int64_t Mmax, float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream,
+                         Timing t = {});
 
-// HISA stage 2: token scores in the kept blocks and the top-k, written at
-// query offset q0 of out_idx / out_scores.  split: several workgroups per
-// query score into ukeys [nq, m*B], then one workgroup per query selects;
-// otherwise one workgroup per query does both.
+// HISA stage 2, one workgroup per query: token scores in the kept blocks
+// and the top-k, written at query offset q0 of out_idx / out_scores.
+hipError_t launch_stage2_fused(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m, int k,
+                               const int32_t* sel, int32_t* out_idx, float* out_scores, hipStream_t stream,
+                               Timing t = {});
+
+// HISA stage 2 for few queries: kStage2SlotsPerWg candidate slots per
+// workgroup scored into ukeys [nq, m*B]; launch_topk_small then selects.
 constexpr int kStage2SlotsPerWg = 512;
-hipError_t launch_stage2(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m, int k,
-                         const int32_t* sel, uint32_t* ukeys, int32_t* out_idx, float* out_scores, bool split,
-                         hipStream_t stream);
+hipError_t launch_stage2_split_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb,
+                                      int m, const int32_t* sel, uint32_t* ukeys, hipStream_t stream, Timing t = {});
 
 // Flat: ranking keys of every key position into ukeys [nq, Lmax].
 hipError_t launch_flat_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq,
-                              int64_t Lmax, uint32_t* ukeys, hipStream_t stream);
+                              int64_t Lmax, uint32_t* ukeys, hipStream_t stream, Timing t = {});
 
 // Top-k of rows of N ranking keys held by one workgroup (N <= 16384).
 // sel == NULL: slot s is token s; otherwise slot s is token
 // sel[row*m + s/B]*B + s%B (lb = log2(B)).  Output row r starts at
 // out_idx + r*k.
 hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel, int m,
-                             int lb, int32_t* out_idx, float* out_scores, hipStream_t stream);
+                             int lb, int32_t* out_idx, float* out_scores, hipStream_t stream, Timing t = {});
 
 // Top-k of long rows (slot s is token s) with several workgroups per row.
 struct RadixWorkspace {
@@ -74,6 +86,6 @@ struct RadixWorkspace {
 };
 size_t radix_slices(int64_t nrows, int64_t N);
 hipError_t launch_topk_radix(const uint32_t* ukeys, int64_t nrows, int64_t N, int k, const RadixWorkspace& ws,
-                             int32_t* out_idx, float* out_scores, hipStream_t stream);
+                             int32_t* out_idx, float* out_scores, hipStream_t stream, Timing t = {});
 
 }  // namespace hisa

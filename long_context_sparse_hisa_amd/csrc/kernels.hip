@@ -12,6 +12,7 @@
 // how sparse attention fixes it" (idea.jsleekr.com) for the flat indexer.
 #include "kernels.h"
 
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include <algorithm>
@@ -20,6 +21,21 @@
 #include "select.h"
 
 namespace hisa {
+
+template <class T>
+struct exact {
+    using type = T;
+};
+
+// Launch `kernel` with arguments converted to its exact parameter types,
+// recording the optional start / stop events from the dispatch itself.
+template <typename... P>
+static hipError_t launch_k(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, hipEvent_t ev0,
+                           hipEvent_t ev1, typename exact<P>::type... args)
+{
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev0, ev1, 0, args...);
+    return hipGetLastError();
+}
 
 // ---- pooling and append ---------------------------------------------------
 // One workgroup per block: 8 threads cover one 128-byte key row (16 bytes,
@@ -86,9 +102,8 @@ hipError_t launch_pool(uint16_t* keys, uint16_t* reps, const uint16_t* new_keys,
             if (i < n) maxblk = std::max(maxblk, pj.j[i].nblk);
         }
         if (maxblk == 0) continue;
-        hipLaunchKernelGGL(pool_kernel, dim3((unsigned)maxblk, (unsigned)n), dim3(kThreads), 0, stream, keys, reps,
-                           new_keys, B, pj);
-        hipError_t err = hipGetLastError();
+        const hipError_t err = launch_k(pool_kernel, dim3((unsigned)maxblk, (unsigned)n), dim3(kThreads), stream,
+                                        nullptr, nullptr, keys, reps, new_keys, B, pj);
         if (err != hipSuccess) return err;
     }
     return hipSuccess;
@@ -189,21 +204,20 @@ __global__ __launch_bounds__(NT) void stage1_select_kernel(QueryMeta qm, const u
 template <int NT, int ITEMS, bool FUSED>
 static hipError_t launch_stage1_items(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb,
                                       int m, int64_t Mmax, const float* sigma, int32_t* sel, int32_t* out_blocks,
-                                      hipStream_t stream)
+                                      hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1)
 {
-    hipLaunchKernelGGL((stage1_select_kernel<NT, ITEMS, FUSED>), dim3((unsigned)nq), dim3(NT), 0, stream, qm, reps,
-                       q0, lb, m, Mmax, sigma, sel, out_blocks);
-    return hipGetLastError();
+    return launch_k(stage1_select_kernel<NT, ITEMS, FUSED>, dim3((unsigned)nq), dim3(NT), stream, ev0, ev1, qm, reps,
+                    q0, lb, m, Mmax, sigma, sel, out_blocks);
 }
 
 hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
-                         int64_t Mmax, float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream)
+                         int64_t Mmax, float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream, Timing t)
 {
     if (Mmax <= kStage1FusedMax) {
         // 256 threads score up to 2048 representatives, 8 per thread
         const int64_t per = (Mmax + 255) / 256;
 #define HISA_S1F(N) \
-    if (per <= N) return launch_stage1_items<256, N, true>(qm, reps, q0, nq, lb, m, Mmax, nullptr, sel, out_blocks, stream)
+    if (per <= N) return launch_stage1_items<256, N, true>(qm, reps, q0, nq, lb, m, Mmax, nullptr, sel, out_blocks, stream, t.start, t.stop)
         HISA_S1F(1);
         HISA_S1F(2);
         HISA_S1F(4);
@@ -212,13 +226,13 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
         return hipErrorInvalidValue;
     }
     dim3 grid((unsigned)((Mmax + kThreads - 1) / kThreads), (unsigned)nq);
-    hipLaunchKernelGGL(block_score_kernel, grid, dim3(kThreads), 0, stream, qm, reps, q0, lb, Mmax, sigma);
-    hipError_t err = hipGetLastError();
+    const hipError_t err =
+        launch_k(block_score_kernel, grid, dim3(kThreads), stream, t.start, nullptr, qm, reps, q0, lb, Mmax, sigma);
     if (err != hipSuccess) return err;
     // 1024 threads select among up to 16384 scores, 16 per thread
     const int64_t per = (Mmax + 1023) / 1024;
 #define HISA_S1S(N) \
-    if (per <= N) return launch_stage1_items<1024, N, false>(qm, reps, q0, nq, lb, m, Mmax, sigma, sel, out_blocks, stream)
+    if (per <= N) return launch_stage1_items<1024, N, false>(qm, reps, q0, nq, lb, m, Mmax, sigma, sel, out_blocks, stream, nullptr, t.stop)
     HISA_S1S(2);
     HISA_S1S(4);
     HISA_S1S(8);
@@ -332,20 +346,20 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(const uint32_t* ukeys, in
 
 template <int NT, int ITEMS>
 static hipError_t launch_topk_rows_items(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel,
-                                         int m, int lb, int32_t* out_idx, float* out_scores, hipStream_t stream)
+                                         int m, int lb, int32_t* out_idx, float* out_scores, hipStream_t stream,
+                                         Timing t)
 {
-    hipLaunchKernelGGL((topk_rows_kernel<NT, ITEMS>), dim3((unsigned)nrows), dim3(NT), 0, stream, ukeys, N, k, sel, m,
-                       lb, out_idx, out_scores);
-    return hipGetLastError();
+    return launch_k(topk_rows_kernel<NT, ITEMS>, dim3((unsigned)nrows), dim3(NT), stream, t.start, t.stop, ukeys, N, k,
+                    sel, m, lb, out_idx, out_scores);
 }
 
 hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel, int m, int lb,
-                             int32_t* out_idx, float* out_scores, hipStream_t stream)
+                             int32_t* out_idx, float* out_scores, hipStream_t stream, Timing t)
 {
     if (N <= 2048) {
         const int per = (N + 255) / 256;
 #define HISA_TK(N_) \
-    if (per <= N_) return launch_topk_rows_items<256, N_>(ukeys, nrows, N, k, sel, m, lb, out_idx, out_scores, stream)
+    if (per <= N_) return launch_topk_rows_items<256, N_>(ukeys, nrows, N, k, sel, m, lb, out_idx, out_scores, stream, t)
         HISA_TK(1);
         HISA_TK(2);
         HISA_TK(4);
@@ -354,7 +368,7 @@ hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k,
     }
     const int per = (N + 1023) / 1024;
 #define HISA_TK(N_) \
-    if (per <= N_) return launch_topk_rows_items<1024, N_>(ukeys, nrows, N, k, sel, m, lb, out_idx, out_scores, stream)
+    if (per <= N_) return launch_topk_rows_items<1024, N_>(ukeys, nrows, N, k, sel, m, lb, out_idx, out_scores, stream, t)
     HISA_TK(2);
     HISA_TK(4);
     HISA_TK(8);
@@ -364,34 +378,32 @@ hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k,
 }
 
 template <int NT, int ITEMS>
-static hipError_t launch_stage2_fused(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m,
-                                      int k, const int32_t* sel, int32_t* out_idx, float* out_scores,
-                                      hipStream_t stream)
+static hipError_t launch_stage2_fused_items(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq,
+                                            int lb, int m, int k, const int32_t* sel, int32_t* out_idx,
+                                            float* out_scores, hipStream_t stream, Timing t)
 {
-    hipLaunchKernelGGL((stage2_fused_kernel<NT, ITEMS>), dim3((unsigned)nq), dim3(NT), 0, stream, qm, keys, q0, lb, m,
-                       k, sel, out_idx, out_scores);
-    return hipGetLastError();
+    return launch_k(stage2_fused_kernel<NT, ITEMS>, dim3((unsigned)nq), dim3(NT), stream, t.start, t.stop, qm, keys,
+                    q0, lb, m, k, sel, out_idx, out_scores);
 }
 
-hipError_t launch_stage2(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m, int k,
-                         const int32_t* sel, uint32_t* ukeys, int32_t* out_idx, float* out_scores, bool split,
-                         hipStream_t stream)
+hipError_t launch_stage2_split_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb,
+                                      int m, const int32_t* sel, uint32_t* ukeys, hipStream_t stream, Timing t)
 {
     const int N = m << lb;
-    if (split) {
-        const int per_wg = kStage2SlotsPerWg;
-        dim3 grid((unsigned)nq, (unsigned)((N + per_wg - 1) / per_wg));
-        hipLaunchKernelGGL(stage2_score_kernel, grid, dim3(kThreads), 0, stream, qm, keys, q0, lb, m, per_wg, sel,
-                           ukeys);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-        return launch_topk_small(ukeys, nq, N, k, sel, m, lb, out_idx + q0 * k,
-                                 out_scores ? out_scores + q0 * k : nullptr, stream);
-    }
+    const int per_wg = kStage2SlotsPerWg;
+    dim3 grid((unsigned)nq, (unsigned)((N + per_wg - 1) / per_wg));
+    return launch_k(stage2_score_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm, keys, q0, lb, m, per_wg,
+                    sel, ukeys);
+}
+
+hipError_t launch_stage2_fused(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m, int k,
+                               const int32_t* sel, int32_t* out_idx, float* out_scores, hipStream_t stream, Timing t)
+{
+    const int N = m << lb;
     if (N <= 2048) {
         const int per = (N + 255) / 256;
 #define HISA_S2(N_) \
-    if (per <= N_) return launch_stage2_fused<256, N_>(qm, keys, q0, nq, lb, m, k, sel, out_idx, out_scores, stream)
+    if (per <= N_) return launch_stage2_fused_items<256, N_>(qm, keys, q0, nq, lb, m, k, sel, out_idx, out_scores, stream, t)
         HISA_S2(1);
         HISA_S2(2);
         HISA_S2(4);
@@ -401,14 +413,14 @@ hipError_t launch_stage2(const QueryMeta& qm, const uint16_t* keys, int64_t q0, 
     if (N <= 8192) {
         const int per = (N + 511) / 512;
 #define HISA_S2(N_) \
-    if (per <= N_) return launch_stage2_fused<512, N_>(qm, keys, q0, nq, lb, m, k, sel, out_idx, out_scores, stream)
+    if (per <= N_) return launch_stage2_fused_items<512, N_>(qm, keys, q0, nq, lb, m, k, sel, out_idx, out_scores, stream, t)
         HISA_S2(8);
         HISA_S2(16);
 #undef HISA_S2
     }
     const int per = (N + 1023) / 1024;
 #define HISA_S2(N_) \
-    if (per <= N_) return launch_stage2_fused<1024, N_>(qm, keys, q0, nq, lb, m, k, sel, out_idx, out_scores, stream)
+    if (per <= N_) return launch_stage2_fused_items<1024, N_>(qm, keys, q0, nq, lb, m, k, sel, out_idx, out_scores, stream, t)
     HISA_S2(16);
 #undef HISA_S2
     return hipErrorInvalidValue;
@@ -436,11 +448,10 @@ __global__ __launch_bounds__(kThreads) void flat_score_kernel(QueryMeta qm, cons
 }
 
 hipError_t launch_flat_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int64_t Lmax,
-                              uint32_t* ukeys, hipStream_t stream)
+                              uint32_t* ukeys, hipStream_t stream, Timing t)
 {
     dim3 grid((unsigned)((Lmax + kThreads - 1) / kThreads), (unsigned)nq);
-    hipLaunchKernelGGL(flat_score_kernel, grid, dim3(kThreads), 0, stream, qm, keys, q0, Lmax, ukeys);
-    return hipGetLastError();
+    return launch_k(flat_score_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm, keys, q0, Lmax, ukeys);
 }
 
 // ---- top-k of long rows: S workgroups per row --------------------------------
@@ -642,29 +653,28 @@ __global__ __launch_bounds__(kThreads) void radix_emit_kernel(const uint32_t* uk
 }
 
 hipError_t launch_topk_radix(const uint32_t* ukeys, int64_t nrows, int64_t N, int k, const RadixWorkspace& ws,
-                             int32_t* out_idx, float* out_scores, hipStream_t stream)
+                             int32_t* out_idx, float* out_scores, hipStream_t stream, Timing t)
 {
     const int64_t S = (int64_t)radix_slices(nrows, N);
     const int64_t slice_len = slice_len_of(N, S);
     const int64_t nh = nrows * 256;
-    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((nh + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
-                       reinterpret_cast<uint32_t*>(ws.hist), nh, 0u);
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_k(fill_u32_kernel, dim3((unsigned)((nh + kThreads - 1) / kThreads)), dim3(kThreads), stream,
+                              t.start, nullptr, reinterpret_cast<uint32_t*>(ws.hist), nh, 0u);
     if (err != hipSuccess) return err;
     const dim3 grid((unsigned)S, (unsigned)nrows);
     for (int pass = 0; pass < 4; ++pass) {
-        hipLaunchKernelGGL(radix_hist_kernel, grid, dim3(kThreads), 0, stream, ukeys, N, slice_len, pass, ws.hist,
-                           ws.state);
-        hipLaunchKernelGGL(radix_digit_kernel, dim3((unsigned)nrows), dim3(kThreads), 0, stream, ws.hist, ws.state,
-                           k, pass);
-        err = hipGetLastError();
+        err = launch_k(radix_hist_kernel, grid, dim3(kThreads), stream, nullptr, nullptr, ukeys, N, slice_len, pass,
+                       ws.hist, ws.state);
+        if (err == hipSuccess)
+            err = launch_k(radix_digit_kernel, dim3((unsigned)nrows), dim3(kThreads), stream, nullptr, nullptr, ws.hist,
+                           ws.state, k, pass);
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(radix_count_kernel, grid, dim3(kThreads), 0, stream, ukeys, N, slice_len, ws.state, ws.counts,
-                       S);
-    hipLaunchKernelGGL(radix_emit_kernel, grid, dim3(kThreads), 0, stream, ukeys, N, slice_len, ws.state, ws.counts,
-                       S, k, out_idx, out_scores);
-    return hipGetLastError();
+    err = launch_k(radix_count_kernel, grid, dim3(kThreads), stream, nullptr, nullptr, ukeys, N, slice_len, ws.state,
+                   ws.counts, S);
+    if (err != hipSuccess) return err;
+    return launch_k(radix_emit_kernel, grid, dim3(kThreads), stream, nullptr, t.stop, ukeys, N, slice_len, ws.state,
+                    ws.counts, S, k, out_idx, out_scores);
 }
 
 }  // namespace hisa

@@ -48,7 +48,7 @@ class hisa_index_args(ctypes.Structure):
     ]
 
 
-HISA_STAGE_EVENTS = 5
+HISA_STAGES = 3
 
 
 def lib():
@@ -193,12 +193,14 @@ def _hiprt():
 
 
 class StageEvents:
-    """HISA_STAGE_EVENTS hipEvent_t handles to hang on hisa_index_args."""
+    """2 * HISA_STAGES hipEvent_t handles to hang on hisa_index_args: the
+    start and stop of every stage, taken from the kernel dispatches."""
 
     def __init__(self):
         h = _hiprt()
-        self.handles = (_P * HISA_STAGE_EVENTS)()
-        for i in range(HISA_STAGE_EVENTS):
+        n = 2 * HISA_STAGES
+        self.handles = (_P * n)()
+        for i in range(n):
             e = _P()
             if h.hipEventCreate(ctypes.byref(e)) != 0:
                 raise RuntimeError("hipEventCreate failed")
@@ -207,18 +209,19 @@ class StageEvents:
     def attach(self, args: hisa_index_args):
         args.stage_events = ctypes.cast(self.handles, ctypes.POINTER(_P))
 
-    def elapsed_ms(self, a: int, b: int) -> float:
+    def stage_ms(self, s: int) -> float:
+        """Duration of stage s (start of its first kernel to end of its last)."""
         h = _hiprt()
-        h.hipEventSynchronize(self.handles[b])
+        h.hipEventSynchronize(self.handles[2 * s + 1])
         f = ctypes.c_float(0.0)
-        if h.hipEventElapsedTime(ctypes.byref(f), self.handles[a], self.handles[b]) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
+        if h.hipEventElapsedTime(ctypes.byref(f), self.handles[2 * s], self.handles[2 * s + 1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed (stage %d not recorded?)" % s)
         return float(f.value)
 
     def __del__(self):
         try:
             h = _hiprt()
-            for i in range(HISA_STAGE_EVENTS):
+            for i in range(2 * HISA_STAGES):
                 h.hipEventDestroy(self.handles[i])
         except Exception:
             pass
