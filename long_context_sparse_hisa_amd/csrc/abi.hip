@@ -50,7 +50,7 @@ struct Layout {
     // HISA
     size_t sigma = 0, sel = 0, ukeys = 0;
     // flat
-    size_t hist = 0, state = 0, counts = 0;
+    size_t hist = 0, state = 0, counts = 0, cand_key[2] = {0, 0}, cand_tok[2] = {0, 0};
     size_t total = 0;
 };
 
@@ -69,7 +69,11 @@ int log2_of(int B)
     return lb;
 }
 
-bool flat_uses_radix(const hisa_index_args* a) { return a->max_len > HISA_MAX_CANDIDATES; }
+FlatPlan flat_plan_of(const hisa_index_args* a) { return flat_plan(a->nq, a->max_len, a->k); }
+
+// Flat scores on the matrix cores once a call has enough queries to fill
+// 16-row tiles (the radix top-k needs the masked entries zeroed instead).
+bool flat_mfma(const hisa_index_args* a) { return a->nq >= 32 && !flat_plan_of(a).radix; }
 
 Layout layout_for(const hisa_index_args* a, int flat, int64_t chunk)
 {
@@ -90,7 +94,16 @@ Layout layout_for(const hisa_index_args* a, int flat, int64_t chunk)
     } else {
         L.ukeys = off;
         off += align_up((size_t)chunk * a->max_len * sizeof(uint32_t));
-        if (flat_uses_radix(a)) {
+        const FlatPlan p = flat_plan_of(a);
+        if (!p.radix && p.S > 1) {
+            for (int b = 0; b < 2; ++b) {
+                L.cand_key[b] = off;
+                off += align_up((size_t)chunk * p.S * p.K1 * sizeof(uint32_t));
+                L.cand_tok[b] = off;
+                off += align_up((size_t)chunk * p.S * p.K1 * sizeof(int32_t));
+            }
+        }
+        if (p.radix) {
             const size_t S = radix_slices(1, a->max_len);   // the largest slice count any chunk uses
             L.hist = off;
             off += align_up((size_t)chunk * 256 * sizeof(int));
@@ -269,11 +282,14 @@ int hisa_flat_index(const hisa_index_args* a, void* stream_)
         const bool last = q0 + nc >= a->nq;
         int32_t* oi = a->out_idx + q0 * a->k;
         float* os = a->out_scores ? a->out_scores + q0 * a->k : nullptr;
-        hipError_t err = launch_flat_scores(qm, a->keys, q0, nc, a->max_len, ukeys, stream, stage_timing(a, last, 0));
+        hipError_t err = launch_flat_scores(qm, a->keys, q0, nc, a->max_len, ukeys, flat_mfma(a), stream,
+                                            stage_timing(a, last, 0));
         if (err == hipSuccess) {
-            if (!flat_uses_radix(a)) {
-                err = launch_topk_small(ukeys, nc, (int)a->max_len, a->k, nullptr, 0, 0, oi, os, stream,
-                                        stage_timing(a, last, 1));
+            if (!flat_plan_of(a).radix) {
+                uint32_t* ck[2] = {at<uint32_t>(a->workspace, L.cand_key[0]), at<uint32_t>(a->workspace, L.cand_key[1])};
+                int32_t* ct[2] = {at<int32_t>(a->workspace, L.cand_tok[0]), at<int32_t>(a->workspace, L.cand_tok[1])};
+                err = launch_flat_topk(flat_plan_of(a), qm, q0, nc, ukeys, a->max_len, a->k, ck, ct, a->out_idx,
+                                       a->out_scores, stream, stage_timing(a, last, 1));
             } else {
                 RadixWorkspace ws{at<int>(a->workspace, L.hist), at<uint32_t>(a->workspace, L.state),
                                   at<int>(a->workspace, L.counts)};

@@ -67,9 +67,26 @@ constexpr int kStage2SlotsPerWg = 512;
 hipError_t launch_stage2_split_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb,
                                       int m, const int32_t* sel, uint32_t* ukeys, hipStream_t stream, Timing t = {});
 
-// Flat: ranking keys of every key position into ukeys [nq, Lmax].
+// Flat: ranking keys of the visible keys into ukeys [nq, Lmax].  mfma: 16
+// query rows per tile on the matrix cores, only visible keys written (the
+// levelled top-k reads rows up to t); otherwise one thread per (query,
+// key) and masked keys written as 0 (what the radix top-k needs).
 hipError_t launch_flat_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq,
-                              int64_t Lmax, uint32_t* ukeys, hipStream_t stream, Timing t = {});
+                              int64_t Lmax, uint32_t* ukeys, bool mfma, hipStream_t stream, Timing t = {});
+
+// Flat top-k in levels: slices of SL keys keep their top K1 = min(k, SL),
+// then groups of G = kFlatMergeWidth / K1 slices are merged until one is
+// left.  radix: K1 too large to merge, use launch_topk_radix instead.
+constexpr int kFlatMergeWidth = 16384;
+struct FlatPlan {
+    int SL, S, K1, G, levels;
+    bool radix;
+};
+FlatPlan flat_plan(int64_t nq, int64_t Lmax, int k);
+// p: the plan of the whole call (its workspace was laid out for it).
+hipError_t launch_flat_topk(const FlatPlan& p, const QueryMeta& qm, int64_t q0, int64_t nq, const uint32_t* ukeys,
+                            int64_t Lmax, int k, uint32_t* cand_key[2], int32_t* cand_tok[2], int32_t* out_idx,
+                            float* out_scores, hipStream_t stream, Timing t = {});
 
 // Top-k of rows of N ranking keys held by one workgroup (N <= 16384).
 // sel == NULL: slot s is token s; otherwise slot s is token

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(NT) void stage1_select_kernel(QueryMeta qm, const u
                                                            int m, int64_t Mmax, const float* sigma, int32_t* sel,
                                                            int32_t* out_blocks)
 {
-    __shared__ BucketSmem<NT, ITEMS> sm;
+    __shared__ BucketSmem<NT> sm;
     const int64_t row = blockIdx.x;
     const int64_t i = q0 + row;
     const QueryInfo qi =
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(NT) void stage1_select_kernel(QueryMeta qm, const u
         load_query(qm.queries + i * kDim, q);
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
-            const int64_t b = (int64_t)it * NT + threadIdx.x;
+            const int64_t b = slot_of<ITEMS>(it);
             key[it] = (b >= 1 && b <= c - 2)
                           ? score_key(dot64_packed(q, reinterpret_cast<const uint4*>(reps + (qi.rep_off + b) * kDim)))
                           : 0u;
@@ -180,12 +180,12 @@ __global__ __launch_bounds__(NT) void stage1_select_kernel(QueryMeta qm, const u
         const float* sg = sigma + row * Mmax;
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
-            const int64_t b = (int64_t)it * NT + threadIdx.x;
+            const int64_t b = slot_of<ITEMS>(it);
             key[it] = (b >= 1 && b <= c - 2) ? score_key(sg[b]) : 0u;
         }
     }
     const Threshold th = wg_bucket_select<NT, ITEMS>(key, m - 3, sm);
-    wg_emit_selected<NT, ITEMS>(key, th, sm.radix, [&](int slot, uint32_t, int rank) {
+    wg_emit_selected<NT, ITEMS>(key, th, sm, m - 3, [&](int slot, uint32_t, int rank) {
         srow[1 + rank] = slot;
         if (orow) orow[1 + rank] = slot;
     });
@@ -258,10 +258,10 @@ HISA_INLINE uint32_t token_key(const uint32_t (&q)[32], const uint16_t* keys, co
 // with their scores, then the -1 padding.  srow == NULL: slot s is token s.
 template <int NT, int ITEMS>
 HISA_INLINE void select_and_write(const uint32_t (&key)[ITEMS], int k, int lb, const int32_t* srow, int32_t* orow,
-                                  float* scrow, BucketSmem<NT, ITEMS>& sm)
+                                  float* scrow, BucketSmem<NT>& sm)
 {
     const Threshold th = wg_bucket_select<NT, ITEMS>(key, k, sm);
-    const int total = wg_emit_selected<NT, ITEMS>(key, th, sm.radix, [&](int slot, uint32_t kk, int rank) {
+    const int total = wg_emit_selected<NT, ITEMS>(key, th, sm, k, [&](int slot, uint32_t kk, int rank) {
         orow[rank] = srow ? (srow[slot >> lb] << lb) + (slot & ((1 << lb) - 1)) : slot;
         if (scrow) scrow[rank] = key_score(kk);
     });
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(NT) void stage2_fused_kernel(QueryMeta qm, const ui
                                                           int m, int k, const int32_t* sel, int32_t* out_idx,
                                                           float* out_scores)
 {
-    __shared__ BucketSmem<NT, ITEMS> sm;
+    __shared__ BucketSmem<NT> sm;
     const int64_t row = blockIdx.x;
     const int64_t i = q0 + row;
     const QueryInfo qi =
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(NT) void stage2_fused_kernel(QueryMeta qm, const ui
         load_query(qm.queries + i * kDim, q);
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
-            const int s = it * NT + threadIdx.x;
+            const int s = slot_of<ITEMS>(it);
             key[it] = s < N ? token_key(q, keys, qi, srow, lb, s) : 0u;
         }
     } else {
@@ -331,13 +331,13 @@ template <int NT, int ITEMS>
 __global__ __launch_bounds__(NT) void topk_rows_kernel(const uint32_t* ukeys, int N, int k, const int32_t* sel, int m,
                                                        int lb, int32_t* out_idx, float* out_scores)
 {
-    __shared__ BucketSmem<NT, ITEMS> sm;
+    __shared__ BucketSmem<NT> sm;
     const int64_t row = blockIdx.x;
     const uint32_t* src = ukeys + row * N;
     uint32_t key[ITEMS];
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
-        const int s = it * NT + threadIdx.x;
+        const int s = slot_of<ITEMS>(it);
         key[it] = s < N ? src[s] : 0u;
     }
     select_and_write<NT, ITEMS>(key, k, lb, sel ? sel + row * m : nullptr, out_idx + row * k,
@@ -428,6 +428,8 @@ hipError_t launch_stage2_fused(const QueryMeta& qm, const uint16_t* keys, int64_
 
 // ---- flat indexer: every key ------------------------------------------------
 
+// One thread per (query, key); masked keys get key 0 so that whole rows can
+// be read (few queries, and the radix path).
 __global__ __launch_bounds__(kThreads) void flat_score_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0,
                                                               int64_t Lmax, uint32_t* ukeys)
 {
@@ -447,11 +449,277 @@ __global__ __launch_bounds__(kThreads) void flat_score_kernel(QueryMeta qm, cons
     *out = score_key(dot64_packed(q, reinterpret_cast<const uint4*>(keys + (qi.key_off + j) * kDim)));
 }
 
-hipError_t launch_flat_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int64_t Lmax,
-                              uint32_t* ukeys, hipStream_t stream, Timing t)
+// Many queries: 16 query rows x 256 keys per workgroup on the bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16, two per 16x16 tile since d = 64), so every
+// key row is loaded once per 16 queries.  Lane l feeds query row l%16 and
+// key l%16 with dims 8*(l/16)..+8 of each half of d, and receives the
+// scores of key l%16 for query rows 4*(l/16)..+4.  Only visible keys
+// (j <= t) are written; rows are read back up to t.  A tile whose queries
+// sit in different sequences falls back to one thread per key.
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kTileRows = 16;
+constexpr int kTileKeys = 256;
+
+__global__ __launch_bounds__(kThreads) void flat_score_mfma_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0,
+                                                                   int64_t nq, int64_t Lmax, uint32_t* ukeys)
 {
+    __shared__ int64_t s_t[kTileRows];
+    __shared__ int64_t s_koff[kTileRows];
+    __shared__ int s_seq[kTileRows];
+    const int64_t row0 = (int64_t)blockIdx.y * kTileRows;
+    const int64_t kt0 = (int64_t)blockIdx.x * kTileKeys;
+    if (threadIdx.x < kTileRows) {
+        const int64_t row = row0 + threadIdx.x;
+        QueryInfo qi;
+        qi.valid = false;
+        qi.key_off = 0;
+        if (row < nq)
+            qi = query_info(q0 + row, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq,
+                            qm.max_len);
+        s_t[threadIdx.x] = qi.valid ? qi.t : -1;
+        s_koff[threadIdx.x] = qi.key_off;
+        s_seq[threadIdx.x] = qi.valid ? qi.seq : -1;
+    }
+    __syncthreads();
+    int64_t tmax = -1, koff = 0;
+    int seq0 = -1;
+    bool uniform = true;
+    for (int r = 0; r < kTileRows; ++r) {
+        if (s_t[r] < 0) continue;
+        if (seq0 < 0) {
+            seq0 = s_seq[r];
+            koff = s_koff[r];
+        } else if (s_seq[r] != seq0) {
+            uniform = false;
+        }
+        tmax = max(tmax, s_t[r]);
+    }
+    if (kt0 > tmax) return;                    // no row sees any key of this tile
+    const int lane = lane_id();
+    if (uniform) {
+        const int col = lane & 15, kg = lane >> 4;
+        bf16x8_t a0 = {}, a1 = {};
+        if (s_t[col] >= 0) {
+            const uint16_t* qrow = qm.queries + (q0 + row0 + col) * kDim + 8 * kg;
+            a0 = *reinterpret_cast<const bf16x8_t*>(qrow);
+            a1 = *reinterpret_cast<const bf16x8_t*>(qrow + 32);
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int64_t j = kt0 + 64 * wave_id() + 16 * st + col;
+            bf16x8_t b0 = {}, b1 = {};
+            if (j <= tmax) {
+                const uint16_t* krow = keys + (koff + j) * kDim + 8 * kg;
+                b0 = *reinterpret_cast<const bf16x8_t*>(krow);
+                b1 = *reinterpret_cast<const bf16x8_t*>(krow + 32);
+            }
+            f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, c, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * kg + e;
+                if (j <= s_t[r]) ukeys[(row0 + r) * Lmax + j] = score_key(c[e]);
+            }
+        }
+    } else {
+        const int64_t j = kt0 + threadIdx.x;
+        for (int r = 0; r < kTileRows; ++r) {
+            if (j > s_t[r]) continue;
+            uint32_t q[32];
+            load_query(qm.queries + (q0 + row0 + r) * kDim, q);
+            ukeys[(row0 + r) * Lmax + j] =
+                score_key(dot64_packed(q, reinterpret_cast<const uint4*>(keys + (s_koff[r] + j) * kDim)));
+        }
+    }
+}
+
+hipError_t launch_flat_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int64_t Lmax,
+                              uint32_t* ukeys, bool mfma, hipStream_t stream, Timing t)
+{
+    if (mfma) {
+        dim3 grid((unsigned)((Lmax + kTileKeys - 1) / kTileKeys), (unsigned)((nq + kTileRows - 1) / kTileRows));
+        return launch_k(flat_score_mfma_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm, keys, q0, nq, Lmax,
+                        ukeys);
+    }
     dim3 grid((unsigned)((Lmax + kThreads - 1) / kThreads), (unsigned)nq);
     return launch_k(flat_score_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm, keys, q0, Lmax, ukeys);
+}
+
+// ---- flat top-k in levels -----------------------------------------------------
+// Level 1: workgroup (row, g) selects the top min(k, SL) of slice g of the
+// row's visible keys (slots [g*SL, (g+1)*SL) of [0, t]).  With one slice
+// that is the answer; otherwise each slice leaves K1 candidates (key,
+// token; key 0 pads), in ascending token order, and further levels merge
+// groups of G slices' candidates until one group remains.  Slices and
+// candidates stay in token order, so every output is ascending.
+
+template <int NT, int ITEMS, bool TO_CAND>
+__global__ __launch_bounds__(NT) void flat_select_kernel(QueryMeta qm, int64_t q0, const uint32_t* ukeys,
+                                                         int64_t Lmax, int SL, int k, int K1, uint32_t* cand_key,
+                                                         int32_t* cand_tok, int32_t* out_idx, float* out_scores)
+{
+    __shared__ BucketSmem<NT> sm;
+    const int64_t row = blockIdx.x;
+    const int g = blockIdx.y;
+    const QueryInfo qi =
+        query_info(q0 + row, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
+    const int64_t n_row = qi.valid ? qi.t + 1 : 0;
+    const int64_t beg = (int64_t)g * SL;
+    const int64_t n = max<int64_t>(0, min<int64_t>(SL, n_row - beg));
+    const uint32_t* src = ukeys + row * Lmax + beg;
+    uint32_t key[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int s = slot_of<ITEMS>(it);
+        key[it] = s < n ? src[s] : 0u;
+    }
+    const int want = TO_CAND ? K1 : k;
+    const Threshold th = wg_bucket_select<NT, ITEMS>(key, want, sm);
+    if (TO_CAND) {
+        uint32_t* ck = cand_key + (row * gridDim.y + g) * K1;
+        int32_t* ct = cand_tok + (row * gridDim.y + g) * K1;
+        const int total = wg_emit_selected<NT, ITEMS>(key, th, sm, K1, [&](int slot, uint32_t kk, int rank) {
+            ck[rank] = kk;
+            ct[rank] = (int32_t)(beg + slot);
+        });
+        for (int r = total + threadIdx.x; r < K1; r += NT) {
+            ck[r] = 0u;
+            ct[r] = -1;
+        }
+    } else {
+        int32_t* orow = out_idx + (q0 + row) * k;
+        float* srow = out_scores ? out_scores + (q0 + row) * k : nullptr;
+        const int total = wg_emit_selected<NT, ITEMS>(key, th, sm, k, [&](int slot, uint32_t kk, int rank) {
+            orow[rank] = (int32_t)(beg + slot);
+            if (srow) srow[rank] = key_score(kk);
+        });
+        for (int r = total + threadIdx.x; r < k; r += NT) {
+            orow[r] = -1;
+            if (srow) srow[r] = __builtin_nanf("");
+        }
+    }
+}
+
+// Merge level: workgroup (row, g) takes the candidates of slices
+// [g*G, (g+1)*G) of S_in (G*K1 keys) and keeps the top K1 (TO_CAND) or
+// writes the final top-k.
+template <int NT, int ITEMS, bool TO_CAND>
+__global__ __launch_bounds__(NT) void cand_select_kernel(int64_t q0, const uint32_t* in_key, const int32_t* in_tok,
+                                                         int S_in, int G, int k, int K1, uint32_t* out_key,
+                                                         int32_t* out_tok, int32_t* out_idx, float* out_scores)
+{
+    __shared__ BucketSmem<NT> sm;
+    const int64_t row = blockIdx.x;
+    const int g = blockIdx.y;
+    const int s0 = g * G;
+    const int n = max(0, min(G, S_in - s0)) * K1;
+    const uint32_t* kin = in_key + ((int64_t)row * S_in + s0) * K1;
+    const int32_t* tin = in_tok + ((int64_t)row * S_in + s0) * K1;
+    uint32_t key[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int s = slot_of<ITEMS>(it);
+        key[it] = s < n ? kin[s] : 0u;
+    }
+    const Threshold th = wg_bucket_select<NT, ITEMS>(key, TO_CAND ? K1 : k, sm);
+    if (TO_CAND) {
+        uint32_t* ok = out_key + (row * gridDim.y + g) * K1;
+        int32_t* ot = out_tok + (row * gridDim.y + g) * K1;
+        const int total = wg_emit_selected<NT, ITEMS>(key, th, sm, K1, [&](int slot, uint32_t kk, int rank) {
+            ok[rank] = kk;
+            ot[rank] = tin[slot];
+        });
+        for (int r = total + threadIdx.x; r < K1; r += NT) {
+            ok[r] = 0u;
+            ot[r] = -1;
+        }
+    } else {
+        int32_t* orow = out_idx + (q0 + row) * k;
+        float* srow = out_scores ? out_scores + (q0 + row) * k : nullptr;
+        const int total = wg_emit_selected<NT, ITEMS>(key, th, sm, k, [&](int slot, uint32_t kk, int rank) {
+            orow[rank] = tin[slot];
+            if (srow) srow[rank] = key_score(kk);
+        });
+        for (int r = total + threadIdx.x; r < k; r += NT) {
+            orow[r] = -1;
+            if (srow) srow[r] = __builtin_nanf("");
+        }
+    }
+}
+
+template <int NT, int ITEMS>
+static hipError_t launch_flat_level(const QueryMeta& qm, int64_t q0, int64_t nq, const uint32_t* ukeys, int64_t Lmax,
+                                    int SL, int S, int k, int K1, uint32_t* ck, int32_t* ct, int32_t* out_idx,
+                                    float* out_scores, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1)
+{
+    if (S > 1)
+        return launch_k(flat_select_kernel<NT, ITEMS, true>, dim3((unsigned)nq, (unsigned)S), dim3(NT), stream, ev0,
+                        ev1, qm, q0, ukeys, Lmax, SL, k, K1, ck, ct, out_idx, out_scores);
+    return launch_k(flat_select_kernel<NT, ITEMS, false>, dim3((unsigned)nq, 1u), dim3(NT), stream, ev0, ev1, qm, q0,
+                    ukeys, Lmax, SL, k, K1, ck, ct, out_idx, out_scores);
+}
+
+template <int NT, int ITEMS>
+static hipError_t launch_cand_level(int64_t q0, int64_t nq, const uint32_t* ik, const int32_t* itok, int S_in, int G,
+                                    int S_out, int k, int K1, uint32_t* ok, int32_t* otok, int32_t* out_idx,
+                                    float* out_scores, hipStream_t stream, hipEvent_t ev1)
+{
+    if (S_out > 1)
+        return launch_k(cand_select_kernel<NT, ITEMS, true>, dim3((unsigned)nq, (unsigned)S_out), dim3(NT), stream,
+                        nullptr, ev1, q0, ik, itok, S_in, G, k, K1, ok, otok, out_idx, out_scores);
+    return launch_k(cand_select_kernel<NT, ITEMS, false>, dim3((unsigned)nq, 1u), dim3(NT), stream, nullptr, ev1, q0,
+                    ik, itok, S_in, G, k, K1, ok, otok, out_idx, out_scores);
+}
+
+FlatPlan flat_plan(int64_t nq, int64_t Lmax, int k)
+{
+    FlatPlan p;
+    p.SL = nq < 256 ? 8192 : 16384;
+    p.S = (int)((Lmax + p.SL - 1) / p.SL);
+    p.K1 = std::min<int64_t>(k, p.SL);
+    p.levels = 1;
+    p.radix = false;
+    if (p.S > 1) {
+        if (p.K1 > kFlatMergeWidth / 4) {
+            p.radix = true;                    // too few candidates merge per group
+            return p;
+        }
+        p.G = kFlatMergeWidth / p.K1;
+        int S = p.S;
+        while (S > 1) {
+            S = (S + p.G - 1) / p.G;
+            ++p.levels;
+        }
+    }
+    return p;
+}
+
+hipError_t launch_flat_topk(const FlatPlan& p, const QueryMeta& qm, int64_t q0, int64_t nq, const uint32_t* ukeys,
+                            int64_t Lmax, int k, uint32_t* cand_key[2], int32_t* cand_tok[2], int32_t* out_idx,
+                            float* out_scores, hipStream_t stream, Timing t)
+{
+    hipEvent_t first_stop = p.S > 1 ? nullptr : t.stop;
+    hipError_t err;
+    if (p.SL == 8192)
+        err = launch_flat_level<1024, 8>(qm, q0, nq, ukeys, Lmax, p.SL, p.S, k, p.K1, cand_key[0], cand_tok[0],
+                                         out_idx, out_scores, stream, t.start, first_stop);
+    else
+        err = launch_flat_level<1024, 16>(qm, q0, nq, ukeys, Lmax, p.SL, p.S, k, p.K1, cand_key[0], cand_tok[0],
+                                          out_idx, out_scores, stream, t.start, first_stop);
+    int S = p.S, cur = 0;
+    while (err == hipSuccess && S > 1) {
+        const int S_out = (S + p.G - 1) / p.G;
+        err = launch_cand_level<1024, 16>(q0, nq, cand_key[cur], cand_tok[cur], S, p.G, S_out, k, p.K1,
+                                          cand_key[cur ^ 1], cand_tok[cur ^ 1], out_idx, out_scores, stream,
+                                          S_out > 1 ? nullptr : t.stop);
+        S = S_out;
+        cur ^= 1;
+    }
+    return err;
 }
 
 // ---- top-k of long rows: S workgroups per row --------------------------------

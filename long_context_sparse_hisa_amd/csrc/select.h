@@ -1,11 +1,12 @@
 // Workgroup-level top-n selection on register-held ranking keys.
 //
-// A workgroup of NT threads holds ITEMS keys per thread; key[it] of thread
-// tid belongs to slot it*NT + tid.  Key 0 means "no candidate".  The n
-// largest keys are selected, equal keys going to the lower slot, and handed
-// to a callback with their rank in ascending slot order, so the output of a
-// selection is ordered by slot without a sort.  Everything here is
-// force-inlined so the key arrays stay in registers.
+// A workgroup of NT threads holds ITEMS keys per thread.  Wave w owns the
+// contiguous slots [w*ITEMS*64, (w+1)*ITEMS*64): key[it] of lane l belongs
+// to slot (w*ITEMS + it)*64 + l (see slot_of).  Key 0 means "no
+// candidate".  The n largest keys are selected, equal keys going to the
+// lower slot, and handed to a callback with their rank in ascending slot
+// order, so the output of a selection is ordered by slot without a sort.
+// Everything here is force-inlined so the key arrays stay in registers.
 #pragma once
 
 #include "common.h"
@@ -13,6 +14,12 @@
 #define HISA_INLINE __device__ __attribute__((always_inline)) inline
 
 namespace hisa {
+
+template <int ITEMS>
+HISA_INLINE int slot_of(int it)
+{
+    return ((wave_id() * ITEMS + it) << 6) | lane_id();
+}
 
 // ---- workgroup scans for NT threads ------------------------------------------
 
@@ -44,41 +51,37 @@ HISA_INLINE int wg_sum(int v, int* scratch)
     return tot;
 }
 
-// ---- radix select --------------------------------------------------------------
-
-template <int NT, int ITEMS>
-struct SelectSmem {
-    static constexpr int NW = NT / 64;
-    int hist[256];
-    int cnt[2 * ITEMS * NW];
-    int scratch[NW];
-    int pick[2];
-};
-
 struct Threshold {
     uint32_t T;      // the n-th largest key (0 when every candidate is taken)
     int need_eq;     // how many keys equal to T are taken, lowest slots first
     bool all;        // n >= number of candidates: take every nonzero key
 };
 
+// ---- radix select (exact fallback) ----------------------------------------------
+
+template <int NT>
+struct RadixSmem {
+    int hist[256];
+    int scratch[NT / 64];
+    int pick[2];
+};
+
 // 8 bits per pass from the top: after four passes the exact n-th largest
-// key is known together with how many of its copies to take.
+// key is known together with how many of its copies to take.  Used when
+// the bucket select meets heavy ties or non-finite scores.  may_take_all:
+// when at most n keys are nonzero, answer "take every nonzero key"; a
+// caller that passes a subset of the keys it will emit from must say false
+// (the threshold then stays exact, 1 <= n <= number of nonzero keys).
 template <int NT, int ITEMS>
-HISA_INLINE Threshold wg_radix_select(const uint32_t (&key)[ITEMS], int n, SelectSmem<NT, ITEMS>& sm)
+HISA_INLINE Threshold wg_radix_select(const uint32_t (&key)[ITEMS], int n, RadixSmem<NT>& sm, bool may_take_all)
 {
     static_assert(NT >= 256, "one digit per thread");
     Threshold th;
-    if (n <= 0) {
-        th.T = 0xffffffffu;
-        th.need_eq = 0;
-        th.all = false;
-        return th;
-    }
     int nvalid = 0;
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) nvalid += key[it] != 0u;
     nvalid = wg_sum<NT>(nvalid, sm.scratch);
-    if (nvalid <= n) {
+    if (may_take_all && nvalid <= n) {
         th.T = 0u;
         th.need_eq = 0;
         th.all = true;
@@ -116,82 +119,27 @@ HISA_INLINE Threshold wg_radix_select(const uint32_t (&key)[ITEMS], int n, Selec
     return th;
 }
 
-// Hand every selected key to emit(slot, key, rank), rank = its position in
-// ascending slot order among the selected.  Returns how many were selected.
-template <int NT, int ITEMS, class Emit>
-HISA_INLINE int wg_emit_selected(const uint32_t (&key)[ITEMS], const Threshold& th, SelectSmem<NT, ITEMS>& sm,
-                                 Emit emit)
-{
-    constexpr int NW = NT / 64;
-    constexpr int kEntries = ITEMS * NW;
-    static_assert(kEntries <= NT, "one count entry per thread");
-    const int w = wave_id();
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-        const bool gt = key[it] > th.T;
-        const bool eq = !th.all && key[it] == th.T;
-        const uint64_t bg = __ballot(gt);
-        const uint64_t be = __ballot(eq);
-        if (lane_id() == 0) {
-            sm.cnt[2 * (it * NW + w) + 0] = __popcll(bg);
-            sm.cnt[2 * (it * NW + w) + 1] = __popcll(be);
-        }
-    }
-    __syncthreads();
-    // one scan over both counts, packed 16 + 16 bits (each total < 65536)
-    const int e = threadIdx.x;
-    const int g = e < kEntries ? sm.cnt[2 * e + 0] : 0;
-    const int q = e < kEntries ? sm.cnt[2 * e + 1] : 0;
-    const int packed = g | (q << 16);
-    const int pi = wg_incl_scan<NT>(packed, sm.scratch);
-    const int gi = pi & 0xffff, qi = (int)((uint32_t)pi >> 16);
-    if (e < kEntries) {
-        sm.cnt[2 * e + 0] = gi - g;
-        sm.cnt[2 * e + 1] = qi - q;
-    }
-    if (e == NT - 1) {
-        sm.pick[0] = gi;
-        sm.pick[1] = qi;
-    }
-    __syncthreads();
-    const int total = sm.pick[0] + min(sm.pick[1], th.need_eq);
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-        const bool gt = key[it] > th.T;
-        const bool eq = !th.all && key[it] == th.T;
-        const uint64_t bg = __ballot(gt);
-        const uint64_t be = __ballot(eq);
-        const int pg = sm.cnt[2 * (it * NW + w) + 0] + __popcll(bg & lanemask_lt());
-        const int pe = sm.cnt[2 * (it * NW + w) + 1] + __popcll(be & lanemask_lt());
-        const int slot = it * NT + threadIdx.x;
-        if (gt) emit(slot, key[it], pg + min(pe, th.need_eq));
-        else if (eq && pe < th.need_eq) emit(slot, key[it], pg + pe);
-    }
-    __syncthreads();
-    return total;
-}
-
 // ---- bucket select ---------------------------------------------------------------
-// The same contract as wg_radix_select, in fewer passes for ordinary data:
-// the candidate scores are spread over kBins equal-width bins between their
-// minimum and maximum (a monotone map, so every key in a higher bin is
-// larger than every key in a lower one and equal keys share a bin), one
+// The candidate scores are spread over kBins equal-width bins between their
+// minimum and maximum.  That map is monotone, so every key in a higher bin
+// is larger than every key in a lower one and equal keys share a bin.  One
 // histogram finds the bin holding the n-th largest key, and only that bin's
 // members are ranked exactly.  When the bin holds more than kListCap keys
-// (heavy ties) the radix select finishes the job on that bin alone.
+// (heavy ties), or scores are not finite, the radix select takes over.
 
 constexpr int kBins = 1024;
 constexpr int kListCap = 512;
 
-template <int NT, int ITEMS>
+template <int NT>
 struct BucketSmem {
     static constexpr int NW = NT / 64;
-    int hist[kBins];
+    int hist[kBins + 1];                      // the extra bin counts the empty slots
     uint32_t list_key[kListCap];
     int list_slot[kListCap];
     uint32_t red[3][NW];
+    int wave_tot[2][NW];
     int misc[8];
-    SelectSmem<NT, ITEMS> radix;
+    RadixSmem<NT> radix;
 };
 
 struct Binning {
@@ -205,10 +153,9 @@ struct Binning {
 };
 
 template <int NT, int ITEMS>
-HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, BucketSmem<NT, ITEMS>& sm)
+HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, BucketSmem<NT>& sm)
 {
     constexpr int NW = NT / 64;
-    static_assert(kBins % NT == 0, "whole bins per thread");
     Threshold th;
     if (n <= 0) {
         th.T = 0xffffffffu;
@@ -233,7 +180,7 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
         sm.red[1][wave_id()] = kmin;
         sm.red[2][wave_id()] = kmax;
     }
-    for (int b = threadIdx.x; b < kBins; b += NT) sm.hist[b] = 0;
+    for (int b = threadIdx.x; b <= kBins; b += NT) sm.hist[b] = 0;
     if (threadIdx.x == 0) sm.misc[2] = 0;
     __syncthreads();
     int nvalid = 0;
@@ -260,28 +207,30 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
     const float smin = key_score(kmin), smax = key_score(kmax);
     const float range = smax - smin;
     if (!(range > 0.f) || !__builtin_isfinite(range))
-        return wg_radix_select<NT, ITEMS>(key, n, sm.radix);   // non-finite scores: exact radix path
+        return wg_radix_select<NT, ITEMS>(key, n, sm.radix, true);   // non-finite scores: exact radix path
     const Binning bin{smin, (float)kBins / range};
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it)
-        if (key[it]) atomicAdd(&sm.hist[bin(key[it])], 1);
+    for (int it = 0; it < ITEMS; ++it) atomicAdd(&sm.hist[key[it] ? bin(key[it]) : kBins], 1);   // no branch
     __syncthreads();
-    // thread t owns kPer bins counted down from the top
-    constexpr int kPer = kBins / NT;
-    int own = 0;
+    // one wave finds the bin of the n-th largest key: lane l owns the 16
+    // bins counted down from kBins-1-16l
+    if (wave_id() == 0) {
+        constexpr int kPer = kBins / 64;
+        int own = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) own += sm.hist[kBins - 1 - kPer * threadIdx.x - j];
-    const int cum = wg_incl_scan<NT>(own, sm.radix.scratch);
-    if (cum >= n && cum - own < n) {
-        int above = cum - own;
-        int b = kBins - 1 - kPer * threadIdx.x;
-        for (int j = 0; j < kPer; ++j, --b) {
-            const int h = sm.hist[b];
-            if (above + h >= n) break;
-            above += h;
+        for (int j = 0; j < kPer; ++j) own += sm.hist[kBins - 1 - kPer * lane_id() - j];
+        const int cum = wave_incl_scan(own);
+        if (cum >= n && cum - own < n) {
+            int above = cum - own;
+            int b = kBins - 1 - kPer * lane_id();
+            for (int j = 0; j < kPer; ++j, --b) {
+                const int h = sm.hist[b];
+                if (above + h >= n) break;
+                above += h;
+            }
+            sm.misc[0] = b;
+            sm.misc[1] = above;
         }
-        sm.misc[0] = b;
-        sm.misc[1] = above;
     }
     __syncthreads();
     const int bstar = sm.misc[0];
@@ -292,38 +241,105 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
         uint32_t sub[ITEMS];
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) sub[it] = (key[it] && bin(key[it]) == bstar) ? key[it] : 0u;
-        return wg_radix_select<NT, ITEMS>(sub, need, sm.radix);
+        return wg_radix_select<NT, ITEMS>(sub, need, sm.radix, false);
     }
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
         if (key[it] && bin(key[it]) == bstar) {
             const int p = atomicAdd(&sm.misc[2], 1);
             sm.list_key[p] = key[it];
-            sm.list_slot[p] = it * NT + threadIdx.x;
+            sm.list_slot[p] = slot_of<ITEMS>(it);
         }
     }
     __syncthreads();
     // rank of member j in (key desc, slot asc) order; the member of rank
-    // need-1 is the threshold key
+    // need-1 is the threshold key, and the equal keys before it plus itself
+    // are the copies of it to take
     for (int j = threadIdx.x; j < c; j += NT) {
         const uint32_t kj = sm.list_key[j];
         const int sj = sm.list_slot[j];
-        int r = 0;
+        int r = 0, eq_before = 0;
         for (int i = 0; i < c; ++i) {
             const uint32_t ki = sm.list_key[i];
-            r += (ki > kj) || (ki == kj && sm.list_slot[i] < sj);
+            const bool before = ki == kj && sm.list_slot[i] < sj;
+            r += (ki > kj) || before;
+            eq_before += before;
         }
-        if (r == need - 1) sm.misc[3] = (int)kj;
+        if (r == need - 1) {
+            sm.misc[3] = (int)kj;
+            sm.misc[4] = eq_before + 1;
+        }
     }
     __syncthreads();
-    const uint32_t T = (uint32_t)sm.misc[3];
-    int gt = 0;
-    for (int j = threadIdx.x; j < c; j += NT) gt += sm.list_key[j] > T;
-    gt = wg_sum<NT>(gt, sm.radix.scratch);
-    th.T = T;
-    th.need_eq = need - gt;
+    th.T = (uint32_t)sm.misc[3];
+    th.need_eq = sm.misc[4];
     th.all = false;
     return th;
+}
+
+// Hand every selected key to emit(slot, key, rank), rank = its position in
+// ascending slot order among the selected, for ranks below `limit` (a
+// guard: a consistent threshold never selects more than the n asked for).
+// Returns how many were selected, at most limit.
+// One barrier: each wave knows the counts of its own slots from ballots and
+// only needs the totals of the waves before it.  No barrier at the end:
+// synchronise before reusing the shared memory.
+template <int NT, int ITEMS, class Emit>
+HISA_INLINE int wg_emit_selected(const uint32_t (&key)[ITEMS], const Threshold& th, BucketSmem<NT>& sm, int limit,
+                                 Emit emit)
+{
+    constexpr int NW = NT / 64;
+    const int w = wave_id();
+    int wg = 0, we = 0;
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        wg += __popcll(__ballot(key[it] > th.T));
+        we += __popcll(__ballot(!th.all && key[it] == th.T));
+    }
+    if (lane_id() == 0) {
+        sm.wave_tot[0][w] = wg;
+        sm.wave_tot[1][w] = we;
+    }
+    __syncthreads();
+    int rg = 0, re = 0, tg = 0, te = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        const int g = sm.wave_tot[0][v], q = sm.wave_tot[1][v];
+        rg += v < w ? g : 0;
+        re += v < w ? q : 0;
+        tg += g;
+        te += q;
+    }
+    const uint64_t lt = lanemask_lt();
+    if (th.all || te <= th.need_eq) {
+        // every key equal to the threshold is taken: selected = key >= T
+        // (or every nonzero key), ranked by one ballot per item
+        const uint32_t lo = th.all ? 1u : th.T;
+        int r = rg + re;
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const bool take = key[it] >= lo;
+            const uint64_t b = __ballot(take);
+            const int rank = r + __popcll(b & lt);
+            if (take && rank < limit) emit(slot_of<ITEMS>(it), key[it], rank);
+            r += __popcll(b);
+        }
+        return min(limit, tg + te);
+    }
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const bool gt = key[it] > th.T;
+        const bool eq = key[it] == th.T;
+        const uint64_t bg = __ballot(gt);
+        const uint64_t be = __ballot(eq);
+        const int pg = rg + __popcll(bg & lt);
+        const int pe = re + __popcll(be & lt);
+        const int rank = gt ? pg + min(pe, th.need_eq) : pg + pe;
+        if ((gt || (eq && pe < th.need_eq)) && rank < limit) emit(slot_of<ITEMS>(it), key[it], rank);
+        rg += __popcll(bg);
+        re += __popcll(be);
+    }
+    return min(limit, tg + min(te, th.need_eq));
 }
 
 }  // namespace hisa

@@ -115,7 +115,9 @@ def check_all_rows_properties(g_idx, g_blk, q_pos, B, m, k, flat, seq_len=None):
     # ascending and causal
     big = np.where(valid, g_idx, np.iinfo(np.int32).max)
     assert np.all(np.diff(big, axis=1)[valid[:, 1:]] > 0), "rows not ascending"
-    assert np.all(g_idx.max(1) <= q_pos), "non-causal index"
+    bad = np.nonzero(g_idx.max(1) > q_pos)[0]
+    assert len(bad) == 0, "non-causal index: row %d t=%d idx>t: %s" % (
+        bad[0], q_pos[bad[0]], g_idx[bad[0]][g_idx[bad[0]] > q_pos[bad[0]]][:10])
     if flat:
         assert np.all(nvalid == np.minimum(k, q_pos + 1)), "flat row count"
     else:
