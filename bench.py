@@ -40,9 +40,7 @@ WORKLOADS = ("decode_32k_x16", "chunked_prefill_32k", "long_context_128k", "long
 
 STAGES_HISA = ("block_stage", "token_scores", "token_topk")
 STAGES_HISA_FUSED = ("block_stage", "token_fused")
-# the library splits the token stage over several workgroups per query
-# (scores, then a separate top-k kernel) for calls with fewer queries
-SPLIT_BELOW = 512
+HISA_SPLIT_BELOW = 512          # the library splits the token stage below this many queries
 STAGES_FLAT = ("flat_scores", "flat_topk")
 
 
@@ -179,7 +177,8 @@ class Setup:
             calls = []
             for ph in self.phases:
                 ic = device_mod.IndexCall(c, ph.queries, ph.q_pos, ph.q_seq, k=self.k, m=self.m,
-                                          flat=flat, scores=True, blocks=not flat)
+                                          flat=flat, scores=True, blocks=not flat,
+                                          one_chunk_limit=16 << 30)
                 per_rep = []
                 for r in range(replicas):
                     a = hisa_mod.make_args(ic.queries, ic.q_pos, self.keys[r], self.k, reps=self.reps[r],
@@ -277,8 +276,10 @@ def stage_times(S, flat, nsteps, torch):
     for p in range(nph):
         if flat:
             names = STAGES_FLAT
+        elif len(S.phases[p].q_pos) < HISA_SPLIT_BELOW:
+            names = STAGES_HISA            # scored across workgroups, then selected
         else:
-            names = STAGES_HISA if len(S.phases[p].q_pos) < SPLIT_BELOW else STAGES_HISA_FUSED
+            names = STAGES_HISA_FUSED      # one workgroup per query scores and selects
         for s_, nm in enumerate(names):
             vals = [evs[i][p].stage_ms(s_) for i in range(nsteps)]
             out["%s/%s" % (S.phases[p].name, nm)] = float(np.mean(vals))

@@ -155,10 +155,10 @@ typedef struct hisa_index_args {
                                     when the first kernel of stage s starts and its last kernel
                                     ends, for the call's last query chunk, from the dispatch
                                     itself.  HISA stages: 0 block scores and top-m; 1 token
-                                    scores (fewer than 512 queries) or token scores and top-k
-                                    (one workgroup per query); 2 token top-k (fewer than 512
-                                    queries, else not recorded).  Flat stages: 0 scores,
-                                    1 top-k (2 not recorded). */
+                                    scores; 2 token top-k.  (Stage 1 also selects, and stage 2
+                                    is not recorded, only on the fallback that handles one
+                                    query per workgroup.)  Flat stages: 0 scores, 1 top-k
+                                    (2 not recorded). */
 } hisa_index_args;
 
 #define HISA_STAGES 3
@@ -168,11 +168,14 @@ typedef struct hisa_index_args {
  * hisa_workspace_bytes -- workspace an index call wants for these
  * arguments (flat != 0: the flat indexer).  Only the sizes in `a` are
  * read.  Any workspace of at least the one-query size is accepted: the call
- * then works through the queries in as many chunks as it needs; the
- * returned size is what processes up to 4096 queries per chunk.
- * *min_bytes (nullable) receives the one-query size.
+ * then works through the queries in as many chunks as it needs.
+ *   *bytes          the recommended size: the largest chunk that fits in
+ *                   1 GiB (all queries if they fit);
+ *   *min_bytes      (nullable) the one-query size;
+ *   *all_bytes      (nullable) the size that takes every query in one chunk.
  */
-int hisa_workspace_bytes(const hisa_index_args* a, int flat, size_t* bytes, size_t* min_bytes);
+int hisa_workspace_bytes(const hisa_index_args* a, int flat, size_t* bytes, size_t* min_bytes,
+                         size_t* all_bytes);
 
 /*
  * hisa_index -- HISA: block scores, causal + forced top-m, token scores in

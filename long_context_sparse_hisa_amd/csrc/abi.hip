@@ -13,7 +13,7 @@ using namespace hisa;
 
 namespace {
 
-constexpr int64_t kChunkDefault = 4096;   // queries per chunk in the recommended workspace
+constexpr size_t kRecommendedBytes = size_t(1) << 30;   // the recommended workspace: up to 1 GiB of chunk
 constexpr int64_t kChunkMax = 65535;      // grid.y limit
 constexpr size_t kAlign = 256;
 
@@ -216,14 +216,15 @@ int hisa_append_keys(uint16_t* keys, uint16_t* reps, const hisa_seq* seqs, int n
     return HISA_OK;
 }
 
-int hisa_workspace_bytes(const hisa_index_args* a, int flat, size_t* bytes, size_t* min_bytes)
+int hisa_workspace_bytes(const hisa_index_args* a, int flat, size_t* bytes, size_t* min_bytes, size_t* all_bytes)
 {
     if (!bytes) return HISA_ERR_INVALID_ARG;
     const int rc = validate_index(a, flat);
     if (rc != HISA_OK) return rc;
-    const int64_t chunk = std::max<int64_t>(1, std::min<int64_t>(a->nq, kChunkDefault));
+    const int64_t chunk = std::max<int64_t>(1, chunk_for(a, flat, kRecommendedBytes));
     *bytes = layout_for(a, flat, chunk).total;
     if (min_bytes) *min_bytes = layout_for(a, flat, 1).total;
+    if (all_bytes) *all_bytes = layout_for(a, flat, std::max<int64_t>(1, std::min<int64_t>(a->nq, kChunkMax))).total;
     return HISA_OK;
 }
 

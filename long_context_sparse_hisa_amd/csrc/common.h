@@ -11,6 +11,8 @@ constexpr int kThreads = 256;   // threads per workgroup of every kernel here
 constexpr int kWaves = kThreads / 64;
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;   // one MFMA operand slice per lane
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;     // one 16x16 MFMA result slice per lane
 
 // ---- bf16 ------------------------------------------------------------------
 

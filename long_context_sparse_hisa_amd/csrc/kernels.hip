@@ -37,6 +37,12 @@ static hipError_t launch_k(void (*kernel)(P...), dim3 grid, dim3 block, hipStrea
     return hipGetLastError();
 }
 
+__global__ __launch_bounds__(kThreads) void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
 // ---- pooling and append ---------------------------------------------------
 // One workgroup per block: 8 threads cover one 128-byte key row (16 bytes,
 // 8 dims each), 32 rows in flight per step, so every load is a fully used
@@ -457,9 +463,6 @@ __global__ __launch_bounds__(kThreads) void flat_score_kernel(QueryMeta qm, cons
 // (j <= t) are written; rows are read back up to t.  A tile whose queries
 // sit in different sequences falls back to one thread per key.
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-
 constexpr int kTileRows = 16;
 constexpr int kTileKeys = 256;
 
@@ -744,12 +747,6 @@ static int64_t slice_len_of(int64_t N, int64_t S)
 {
     const int64_t per = (N + S - 1) / S;
     return (per + kThreads - 1) / kThreads * kThreads;
-}
-
-__global__ __launch_bounds__(kThreads) void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
-{
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i < n) p[i] = v;
 }
 
 __global__ __launch_bounds__(kThreads) void radix_hist_kernel(const uint32_t* ukeys, int64_t N, int64_t slice_len,

@@ -74,7 +74,8 @@ class IndexCall:
 
     def __init__(self, cache: DeviceCache, queries, q_pos, q_seq, k: int, m: int | None = None,
                  flat: bool = False, scores: bool = True, blocks: bool = True,
-                 max_len: int | None = None, workspace_bytes: int | None = None):
+                 max_len: int | None = None, workspace_bytes: int | None = None,
+                 one_chunk_limit: int = 0):
         dev = cache.device
         self.cache = cache
         self.flat = flat
@@ -90,7 +91,9 @@ class IndexCall:
                            if (blocks and not flat) else None)
         self.max_len = int(max_len if max_len is not None else cache.seq_cap.max())
         args = self._args(None)
-        want, _ = hisa.hisa_workspace_bytes(args, flat)
+        want, _, whole = hisa.hisa_workspace_bytes(args, flat, all_queries=True)
+        if whole <= one_chunk_limit:           # every query in one chunk
+            want = whole
         nbytes = want if workspace_bytes is None else workspace_bytes
         self.workspace = cache.workspace(nbytes, "flat" if flat else "hisa")
         self.args = self._args(self.workspace)

@@ -64,6 +64,7 @@ def lib():
                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int, _P]
         L.hisa_workspace_bytes.argtypes = [ctypes.POINTER(hisa_index_args), ctypes.c_int,
                                            ctypes.POINTER(ctypes.c_size_t),
+                                           ctypes.POINTER(ctypes.c_size_t),
                                            ctypes.POINTER(ctypes.c_size_t)]
         L.hisa_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
         L.hisa_flat_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
@@ -156,12 +157,17 @@ def make_args(queries, q_pos, keys, k: int, *, reps=None, q_seq=None, seq_key_of
     return a
 
 
-def hisa_workspace_bytes(args: hisa_index_args, flat: bool = False):
-    """(recommended bytes, minimum bytes) of workspace for these args."""
+def hisa_workspace_bytes(args: hisa_index_args, flat: bool = False, all_queries: bool = False):
+    """(recommended bytes, minimum bytes) of workspace for these args, or
+    with all_queries (recommended, minimum, one-chunk bytes)."""
     b = ctypes.c_size_t(0)
     mb = ctypes.c_size_t(0)
-    rc = lib().hisa_workspace_bytes(ctypes.byref(args), int(flat), ctypes.byref(b), ctypes.byref(mb))
+    ab = ctypes.c_size_t(0)
+    rc = lib().hisa_workspace_bytes(ctypes.byref(args), int(flat), ctypes.byref(b), ctypes.byref(mb),
+                                    ctypes.byref(ab))
     _check(rc, "hisa_workspace_bytes")
+    if all_queries:
+        return int(b.value), int(mb.value), int(ab.value)
     return int(b.value), int(mb.value)
 
 

@@ -83,8 +83,8 @@ def test_flat_ignores_block_arguments(lib):
 def test_workspace_checks(lib):
     a = _args()
     assert _rc(lib.hisa_index, a) == hisa.HISA_ERR_WORKSPACE          # none given
-    want, least = hisa.hisa_workspace_bytes(a)
-    assert 0 < least <= want
+    want, least, whole = hisa.hisa_workspace_bytes(a, all_queries=True)
+    assert 0 < least <= want <= whole
     a = _args(workspace=FAKE, workspace_bytes=least - 1)
     assert _rc(lib.hisa_index, a) == hisa.HISA_ERR_WORKSPACE
     fw, fl = hisa.hisa_workspace_bytes(_args(), flat=True)

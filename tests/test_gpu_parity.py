@@ -408,3 +408,30 @@ def test_tie_bin_taken_whole():
     for flat in (False, True):                  # m = 32 keeps all 32 blocks: HISA sees every key
         idx, _, _ = _check_phase(w, cache, ph, k, 32, flat, label="tiebin")
         assert np.array_equal(np.sort(idx[0]), np.sort(order[:1000]))
+
+
+@pytest.mark.parametrize("force_fallback", [False, True])
+def test_many_queries_packed_sequences(force_fallback):
+    """Hundreds of queries spread over packed sequences of different
+    lengths: the block-major token stage groups (sequence, block) pairs.
+    With a declared max_len large enough that (sequences x blocks) passes
+    2^20 bins, the one-workgroup-per-query stage runs instead."""
+    print("many packed queries fallback=%s" % force_fallback, flush=True)
+    dv = _dev()
+    nseq = 70 if force_fallback else 6
+    B = 16 if force_fallback else 64
+    m, k = 8, 64
+    g = np.random.default_rng(32)
+    lens = g.integers(40, 400, nseq).astype(np.int64)
+    w = synth.decode_batch(nseq=nseq, L=int(lens.max()), seed=32, B=B, m=m, k=k)
+    cache = dv.DeviceCache(w, B=B)
+    cache.set_lengths(lens)
+    cache.pool()
+    nq = 700
+    q_seq = g.integers(0, nseq, nq).astype(np.int32)
+    q_pos = (g.random(nq) * lens[q_seq]).astype(np.int64)
+    queries = synth.to_bf16(g.standard_normal((nq, synth.D)).astype(np.float32))
+    ph = synth.Phase("p", queries, q_pos, q_seq)
+    max_len = 262144 if force_fallback else None
+    for flat in (False, True):
+        _check_phase(w, cache, ph, k, m, flat, label="manypacked", props=False, max_len=max_len)
