@@ -39,8 +39,6 @@ WORKLOADS = ("decode_32k_x16", "chunked_prefill_32k", "long_context_128k", "long
              "tiny_prefill_4k")
 
 STAGES_HISA = ("block_stage", "token_scores", "token_topk")
-STAGES_HISA_FUSED = ("block_stage", "token_fused")
-HISA_SPLIT_BELOW = 512          # the library splits the token stage below this many queries
 STAGES_FLAT = ("flat_scores", "flat_topk")
 
 
@@ -65,8 +63,9 @@ def hisa_stage_bytes(q_pos, B, m, k):
         # few queries: scores go to a workspace row, then the top-k reads it
         "token_scores": float((128 + m * 4 + cand * 128 + m * B * 4).sum()),
         "token_topk": float(len(q_pos) * (m * B * 4 + m * 4 + k * 8)),
-        # one workgroup per query: both in one kernel
-        "token_fused": float((128 + m * 4 + cand * 128 + k * 8).sum()),
+        # the token stage without the workspace round trip: query, kept
+        # list and candidate keys in, indices and scores out
+        "token_ideal": float((128 + m * 4 + cand * 128 + k * 8).sum()),
     }
 
 
@@ -84,9 +83,10 @@ def flat_stage_bytes(q_pos, k):
 # ---- measured HBM traffic ----------------------------------------------------------
 
 # kernel symbol that carries each stage
-STAGE_KERNEL = {"block_stage": "stage1_select_kernel", "token_scores": "stage2_score_kernel",
-                "token_topk": "topk_rows_kernel", "token_fused": "stage2_fused_kernel",
-                "flat_scores": "flat_score_kernel"}
+STAGE_KERNEL = {"block_stage": ("stage1_select_kernel",),
+                "token_scores": ("stage2_score_kernel", "stage2_tile_kernel"),
+                "token_topk": ("topk_rows_kernel",),
+                "flat_scores": ("flat_score_kernel", "flat_score_mfma_kernel")}
 
 
 def kernel_source_hash(root):
@@ -113,7 +113,7 @@ def measured_traffic(root, workload, stage):
             continue
         for l in lines:
             f = l.split("\t")
-            if len(f) == 4 and f[0] == "traffic" and f[1] == workload and sym in f[2]:
+            if len(f) == 4 and f[0] == "traffic" and f[1] == workload and any(x in f[2] for x in sym):
                 return float(f[3])
     return None
 
@@ -274,12 +274,7 @@ def stage_times(S, flat, nsteps, torch):
     torch.cuda.synchronize()
     out = {}
     for p in range(nph):
-        if flat:
-            names = STAGES_FLAT
-        elif len(S.phases[p].q_pos) < HISA_SPLIT_BELOW:
-            names = STAGES_HISA            # scored across workgroups, then selected
-        else:
-            names = STAGES_HISA_FUSED      # one workgroup per query scores and selects
+        names = STAGES_FLAT if flat else STAGES_HISA
         for s_, nm in enumerate(names):
             vals = [evs[i][p].stage_ms(s_) for i in range(nsteps)]
             out["%s/%s" % (S.phases[p].name, nm)] = float(np.mean(vals))
@@ -410,7 +405,7 @@ def main():
     # (no workspace round trips) plus the append (new rows written, touched
     # blocks re-read, representatives written)
     append_rows = 0 if S.append_src is None else S.append_src.shape[0] * S.append_src.shape[1]
-    h_step_bytes = sum(b for n, b in stage_bytes.items() if n.split("/")[-1] in STAGES_HISA_FUSED)
+    h_step_bytes = sum(b for n, b in stage_bytes.items() if n.split("/")[-1] in ("block_stage", "token_ideal"))
     f_step_bytes = sum(b for n, b in stage_bytes.items() if n.split("/")[-1] in STAGES_FLAT)
     h_step_bytes += append_rows * 128 * 2
     f_step_bytes += append_rows * 128 * 2

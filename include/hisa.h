@@ -155,9 +155,7 @@ typedef struct hisa_index_args {
                                     when the first kernel of stage s starts and its last kernel
                                     ends, for the call's last query chunk, from the dispatch
                                     itself.  HISA stages: 0 block scores and top-m; 1 token
-                                    scores; 2 token top-k.  (Stage 1 also selects, and stage 2
-                                    is not recorded, only on the fallback that handles one
-                                    query per workgroup.)  Flat stages: 0 scores, 1 top-k
+                                    scores; 2 token top-k.  Flat stages: 0 scores, 1 top-k
                                     (2 not recorded). */
 } hisa_index_args;
 

@@ -72,8 +72,8 @@ int log2_of(int B)
 FlatPlan flat_plan_of(const hisa_index_args* a) { return flat_plan(a->nq, a->max_len, a->k); }
 
 // Flat scores on the matrix cores once a call has enough queries to fill
-// 16-row tiles (the radix top-k needs the masked entries zeroed instead).
-bool flat_mfma(const hisa_index_args* a) { return a->nq >= 32 && !flat_plan_of(a).radix; }
+// 16-row tiles.
+bool flat_mfma(const hisa_index_args* a) { return a->nq >= 32; }
 
 Layout layout_for(const hisa_index_args* a, int flat, int64_t chunk)
 {
@@ -87,10 +87,8 @@ Layout layout_for(const hisa_index_args* a, int flat, int64_t chunk)
             L.sigma = off;
             off += align_up((size_t)chunk * Mmax * sizeof(float));
         }
-        if (hisa_split(a)) {
-            L.ukeys = off;
-            off += align_up((size_t)chunk * a->m * a->B * sizeof(uint32_t));
-        }
+        L.ukeys = off;                          // candidate ranking keys [chunk, m*B]
+        off += align_up((size_t)chunk * a->m * a->B * sizeof(uint32_t));
     } else {
         L.ukeys = off;
         off += align_up((size_t)chunk * a->max_len * sizeof(uint32_t));
@@ -244,23 +242,23 @@ int hisa_index(const hisa_index_args* a, void* stream_)
     const bool split = hisa_split(a);
     float* sigma = Mmax > kStage1FusedMax ? at<float>(a->workspace, L.sigma) : nullptr;
     int32_t* sel = at<int32_t>(a->workspace, L.sel);
-    uint32_t* ukeys = split ? at<uint32_t>(a->workspace, L.ukeys) : nullptr;
+    uint32_t* ukeys = at<uint32_t>(a->workspace, L.ukeys);
     for (int64_t q0 = 0; q0 < a->nq; q0 += chunk) {
         const int64_t nc = std::min(chunk, a->nq - q0);
         const bool last = q0 + nc >= a->nq;
         hipError_t err = launch_stage1(qm, a->reps, q0, nc, lb, a->m, Mmax, sigma, sel, a->out_blocks, stream,
                                        stage_timing(a, last, 0));
-        if (err == hipSuccess && split) {
-            err = launch_stage2_split_scores(qm, a->keys, q0, nc, lb, a->m, sel, ukeys, stream,
-                                             stage_timing(a, last, 1));
-            if (err == hipSuccess)
-                err = launch_topk_small(ukeys, nc, a->m << lb, a->k, sel, a->m, lb, a->out_idx + q0 * a->k,
-                                        a->out_scores ? a->out_scores + q0 * a->k : nullptr, stream,
-                                        stage_timing(a, last, 2));
-        } else if (err == hipSuccess) {
-            err = launch_stage2_fused(qm, a->keys, q0, nc, lb, a->m, a->k, sel, a->out_idx, a->out_scores, stream,
-                                      stage_timing(a, last, 1));
-        }
+        // token scores into ukeys: few queries split each row over several
+        // workgroups, many queries share key loads 16 at a time on the MFMA
+        if (err == hipSuccess)
+            err = split ? launch_stage2_split_scores(qm, a->keys, q0, nc, lb, a->m, sel, ukeys, stream,
+                                                     stage_timing(a, last, 1))
+                        : launch_stage2_tile_scores(qm, a->keys, q0, nc, lb, a->m, Mmax, sel, ukeys, stream,
+                                                    stage_timing(a, last, 1));
+        if (err == hipSuccess)
+            err = launch_topk_small(ukeys, nc, a->m << lb, a->k, sel, a->m, lb, a->out_idx + q0 * a->k,
+                                    a->out_scores ? a->out_scores + q0 * a->k : nullptr, stream,
+                                    stage_timing(a, last, 2));
         if (err != hipSuccess) return HISA_ERR_HIP;
     }
     return HISA_OK;
@@ -283,8 +281,9 @@ int hisa_flat_index(const hisa_index_args* a, void* stream_)
         const bool last = q0 + nc >= a->nq;
         int32_t* oi = a->out_idx + q0 * a->k;
         float* os = a->out_scores ? a->out_scores + q0 * a->k : nullptr;
-        hipError_t err = launch_flat_scores(qm, a->keys, q0, nc, a->max_len, ukeys, flat_mfma(a), stream,
-                                            stage_timing(a, last, 0));
+        // the radix top-k reads whole rows, so it needs the masked keys zeroed
+        hipError_t err = launch_flat_scores(qm, a->keys, q0, nc, a->max_len, ukeys, flat_mfma(a),
+                                            flat_plan_of(a).radix, stream, stage_timing(a, last, 0));
         if (err == hipSuccess) {
             if (!flat_plan_of(a).radix) {
                 uint32_t* ck[2] = {at<uint32_t>(a->workspace, L.cand_key[0]), at<uint32_t>(a->workspace, L.cand_key[1])};

@@ -55,11 +55,12 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
                          int64_t Mmax, float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream,
                          Timing t = {});
 
-// HISA stage 2, one workgroup per query: token scores in the kept blocks
-// and the top-k, written at query offset q0 of out_idx / out_scores.
-hipError_t launch_stage2_fused(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m, int k,
-                               const int32_t* sel, int32_t* out_idx, float* out_scores, hipStream_t stream,
-                               Timing t = {});
+// HISA stage 2 for many queries: 16 query rows per wave scored on the
+// MFMA against the union of their kept blocks, into ukeys [nq, m*B] (only
+// the kept blocks' slots are written); launch_topk_small then selects.
+hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m,
+                                     int64_t Mmax, const int32_t* sel, uint32_t* ukeys, hipStream_t stream,
+                                     Timing t = {});
 
 // HISA stage 2 for few queries: kStage2SlotsPerWg candidate slots per
 // workgroup scored into ukeys [nq, m*B]; launch_topk_small then selects.
@@ -68,11 +69,13 @@ hipError_t launch_stage2_split_scores(const QueryMeta& qm, const uint16_t* keys,
                                       int m, const int32_t* sel, uint32_t* ukeys, hipStream_t stream, Timing t = {});
 
 // Flat: ranking keys of the visible keys into ukeys [nq, Lmax].  mfma: 16
-// query rows per tile on the matrix cores, only visible keys written (the
-// levelled top-k reads rows up to t); otherwise one thread per (query,
-// key) and masked keys written as 0 (what the radix top-k needs).
+// query rows per tile on the matrix cores, otherwise one thread per
+// (query, key).  zero_masked: keys after the query get key 0 (what the
+// radix top-k needs; the levelled top-k reads rows only up to t).  The
+// one-thread path always zeroes them.
 hipError_t launch_flat_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq,
-                              int64_t Lmax, uint32_t* ukeys, bool mfma, hipStream_t stream, Timing t = {});
+                              int64_t Lmax, uint32_t* ukeys, bool mfma, bool zero_masked, hipStream_t stream,
+                              Timing t = {});
 
 // Flat top-k in levels: slices of SL keys keep their top K1 = min(k, SL),
 // then groups of G = kFlatMergeWidth / K1 slices are merged until one is
@@ -87,6 +90,9 @@ FlatPlan flat_plan(int64_t nq, int64_t Lmax, int k);
 hipError_t launch_flat_topk(const FlatPlan& p, const QueryMeta& qm, int64_t q0, int64_t nq, const uint32_t* ukeys,
                             int64_t Lmax, int k, uint32_t* cand_key[2], int32_t* cand_tok[2], int32_t* out_idx,
                             float* out_scores, hipStream_t stream, Timing t = {});
+
+// Rows per launch from which a select is sized for throughput, not latency.
+constexpr int64_t kManyRows = 256;
 
 // Top-k of rows of N ranking keys held by one workgroup (N <= 16384).
 // sel == NULL: slot s is token s; otherwise slot s is token

@@ -37,6 +37,15 @@ static hipError_t launch_k(void (*kernel)(P...), dim3 grid, dim3 block, hipStrea
     return hipGetLastError();
 }
 
+// The same with `lds` bytes of dynamic shared memory.
+template <typename... P>
+static hipError_t launch_kl(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                            hipEvent_t ev0, hipEvent_t ev1, typename exact<P>::type... args)
+{
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ev0, ev1, 0, args...);
+    return hipGetLastError();
+}
+
 __global__ __launch_bounds__(kThreads) void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
 {
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -277,36 +286,6 @@ HISA_INLINE void select_and_write(const uint32_t (&key)[ITEMS], int k, int lb, c
     }
 }
 
-// One workgroup per query: gather, score and select without leaving the
-// workgroup (many queries in flight).
-template <int NT, int ITEMS>
-__global__ __launch_bounds__(NT) void stage2_fused_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0, int lb,
-                                                          int m, int k, const int32_t* sel, int32_t* out_idx,
-                                                          float* out_scores)
-{
-    __shared__ BucketSmem<NT> sm;
-    const int64_t row = blockIdx.x;
-    const int64_t i = q0 + row;
-    const QueryInfo qi =
-        query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
-    const int N = m << lb;
-    const int32_t* srow = sel + row * m;
-    uint32_t key[ITEMS];
-    if (qi.valid) {
-        uint32_t q[32];
-        load_query(qm.queries + i * kDim, q);
-#pragma unroll
-        for (int it = 0; it < ITEMS; ++it) {
-            const int s = slot_of<ITEMS>(it);
-            key[it] = s < N ? token_key(q, keys, qi, srow, lb, s) : 0u;
-        }
-    } else {
-#pragma unroll
-        for (int it = 0; it < ITEMS; ++it) key[it] = 0u;
-    }
-    select_and_write<NT, ITEMS>(key, k, lb, srow, out_idx + i * k, out_scores ? out_scores + i * k : nullptr, sm);
-}
-
 // Several workgroups per query, each scoring `per_wg` slots into ukeys;
 // few queries still fill the chip.  The top-k follows in topk_rows_kernel.
 __global__ __launch_bounds__(kThreads) void stage2_score_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0,
@@ -331,6 +310,160 @@ __global__ __launch_bounds__(kThreads) void stage2_score_kernel(QueryMeta qm, co
     }
 }
 
+// Many queries: tiles of 16 consecutive query rows on the bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16, two per 16 keys since d = 64).  Workgroup
+// (tile, g) has four waves; wave w takes the blocks [b0, b0 + range) with
+// b0 = (4g + w) * range and walks the union of the 16 rows' kept blocks
+// inside them in ascending order: lane r (r < 16) holds a cursor into row
+// r's list, and the next block is the smallest one under the 16 cursors.
+// Each union block is scored for all 16 rows at once, so a key row is read
+// once per 16 queries rather than once per query.  A row that kept the
+// block at list position p writes the scores to its slots [p*B, (p+1)*B),
+// key 0 for tokens after the query; slots of -1 entries are never written
+// (the top-k stops at the kept blocks).  Rows of a tile in different
+// sequences are walked one sequence at a time.  MFMA lanes: lane l feeds
+// query row l%16 and key l%16 with dims 8*(l/16)..+8 of each half of d, and
+// receives the scores of key l%16 for query rows 4*(l/16)..+4.
+
+constexpr int kTileQueries = 16;
+constexpr int kTileWaves = 4;
+constexpr int kTileEnd = 0x7fffffff;     // cursor past the end of a list
+constexpr int64_t kTileTargetWaves = 16384;
+
+template <int LB>
+__global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0,
+                                                                      int64_t nq, int m, int range, const int32_t* sel,
+                                                                      uint32_t* ukeys)
+{
+    extern __shared__ int32_t s_sel[];            // [16][m] kept-block lists of the tile's rows
+    constexpr int B = 1 << LB;
+    constexpr int KT = B / 16;
+    const int lane = lane_id();
+    const int64_t row0 = (int64_t)blockIdx.x * kTileQueries;
+    const int nrows = (int)min<int64_t>(kTileQueries, nq - row0);
+    const int N = m << LB;
+    for (int e = threadIdx.x; e < kTileQueries * m; e += 64 * kTileWaves)
+        s_sel[e] = e < nrows * m ? sel[row0 * m + e] : -1;
+    __syncthreads();
+    const int blo = ((int)blockIdx.y * kTileWaves + wave_id()) * range;
+    const int bhi = blo + range;
+    // lanes 0..15: one row each
+    const int r = lane & 15;
+    const int32_t* lst = s_sel + r * m;
+    QueryInfo qi;
+    qi.valid = false;
+    qi.seq = -1;
+    qi.t = -1;
+    qi.key_off = 0;
+    if (lane < kTileQueries && r < nrows)
+        qi = query_info(q0 + row0 + r, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq,
+                        qm.max_len);
+    // this row's first list entry at or after blo (the list ascends, then -1s)
+    int first = m;
+    if (qi.valid) {
+        int lo = 0, hi = m;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            const int v = lst[mid];
+            if (v >= 0 && v < blo)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        first = lo;
+    }
+    const bool active = qi.valid && first < m && lst[first] >= 0 && lst[first] < bhi;
+    const int seq = active ? qi.seq : -1;
+    const int t32 = qi.valid ? (int)qi.t : -1;
+    uint64_t pending = __ballot(lane < kTileQueries && seq >= 0);
+    if (!pending) return;
+    // A operand: the 16 queries
+    const int col = lane & 15, kg = lane >> 4;
+    bf16x8_t a0 = {}, a1 = {};
+    if (col < nrows) {
+        const uint16_t* qrow = qm.queries + (q0 + row0 + col) * kDim + 8 * kg;
+        a0 = *reinterpret_cast<const bf16x8_t*>(qrow);
+        a1 = *reinterpret_cast<const bf16x8_t*>(qrow + 32);
+    }
+    while (pending) {
+        const int lead = (int)__builtin_ctzll(pending);
+        const int s = __builtin_amdgcn_readlane(seq, lead);
+        const bool mine = lane < kTileQueries && seq == s && seq >= 0;
+        pending &= ~__ballot(mine);
+        const int64_t koff = ((int64_t)__builtin_amdgcn_readlane((int)(qi.key_off >> 32), lead) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)qi.key_off, lead);
+        const int tmax = (int)wave_max_u32(mine ? (uint32_t)t32 : 0u);
+        // the query position of each output row of this lane, -1 when not walked now
+        const int tm = mine ? t32 : -1;
+        int te[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) te[e] = __shfl(tm, 4 * kg + e);
+        int cur = first;
+        int nxt = mine ? lst[first] : kTileEnd;
+        int b = (int)wave_min_u32((uint32_t)nxt);
+        while (b != kTileEnd) {
+            const bool hit = nxt == b;
+            const int pos = hit ? cur : -1;
+            if (hit) {
+                ++cur;
+                const int v = cur < m ? lst[cur] : -1;
+                nxt = v >= 0 && v < bhi ? v : kTileEnd;
+            }
+            int pe[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pe[e] = __shfl(pos, 4 * kg + e);    // -1 unless that row kept b
+            const uint16_t* kb = keys + (koff + ((int64_t)b << LB)) * kDim + 8 * kg;
+            bf16x8_t k0[KT], k1[KT];
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                const int jj = kt * 16 + col;
+                k0[kt] = bf16x8_t{};
+                k1[kt] = bf16x8_t{};
+                if ((b << LB) + jj <= tmax) {
+                    k0[kt] = *reinterpret_cast<const bf16x8_t*>(kb + jj * kDim);
+                    k1[kt] = *reinterpret_cast<const bf16x8_t*>(kb + jj * kDim + 32);
+                }
+            }
+            const int bn = (int)wave_min_u32((uint32_t)nxt);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                const int jj = kt * 16 + col;
+                const int j = (b << LB) + jj;
+                f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, k0[kt], c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, k1[kt], c, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (pe[e] >= 0)
+                        ukeys[(row0 + 4 * kg + e) * N + (pe[e] << LB) + jj] = j <= te[e] ? score_key(c[e]) : 0u;
+            }
+            b = bn;
+        }
+    }
+}
+
+hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m,
+                                     int64_t Mmax, const int32_t* sel, uint32_t* ukeys, hipStream_t stream, Timing t)
+{
+    // enough waves to fill the chip: split each tile's blocks into ranges
+    const int64_t ntiles = (nq + kTileQueries - 1) / kTileQueries;
+    const int64_t want = std::max<int64_t>(1, (kTileTargetWaves + ntiles - 1) / ntiles);
+    const int64_t range = std::max<int64_t>(1, (Mmax + want - 1) / want);
+    const int64_t nranges = (Mmax + range - 1) / range;
+    const dim3 grid((unsigned)ntiles, (unsigned)((nranges + kTileWaves - 1) / kTileWaves));
+    const dim3 block(64 * kTileWaves);
+    const size_t lds = (size_t)kTileQueries * m * sizeof(int32_t);
+#define HISA_T2(LB_) \
+    if (lb == LB_) return launch_kl(stage2_tile_kernel<LB_>, grid, block, lds, stream, t.start, t.stop, qm, keys, q0, nq, m, (int)range, sel, ukeys)
+    HISA_T2(4);
+    HISA_T2(5);
+    HISA_T2(6);
+    HISA_T2(7);
+    HISA_T2(8);
+#undef HISA_T2
+    return hipErrorInvalidValue;
+}
+
 // Top-k of rows of N ranking keys, one workgroup per row; out rows start at
 // out_idx / out_scores (the caller offsets them).  sel: slot -> token map.
 template <int NT, int ITEMS>
@@ -340,11 +473,18 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(const uint32_t* ukeys, in
     __shared__ BucketSmem<NT> sm;
     const int64_t row = blockIdx.x;
     const uint32_t* src = ukeys + row * N;
+    // slots of -1 list entries (a suffix of the list) hold no candidate
+    int n = N;
+    if (sel) {
+        int cnt = 0;
+        for (int i = lane_id(); i < m; i += 64) cnt += sel[row * m + i] >= 0;
+        n = min(N, wave_sum(cnt) << lb);
+    }
     uint32_t key[ITEMS];
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
         const int s = slot_of<ITEMS>(it);
-        key[it] = s < N ? src[s] : 0u;
+        key[it] = s < n ? src[s] : 0u;
     }
     select_and_write<NT, ITEMS>(key, k, lb, sel ? sel + row * m : nullptr, out_idx + row * k,
                                 out_scores ? out_scores + row * k : nullptr, sm);
@@ -362,7 +502,10 @@ static hipError_t launch_topk_rows_items(const uint32_t* ukeys, int64_t nrows, i
 hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel, int m, int lb,
                              int32_t* out_idx, float* out_scores, hipStream_t stream, Timing t)
 {
-    if (N <= 2048) {
+    // rows up to 4096 keys: 256 threads.  Longer rows: 1024 threads when
+    // there are few of them (one row's latency is the cost), 512 threads
+    // otherwise (two workgroups per CU hide each other's barriers).
+    if (N <= 4096) {
         const int per = (N + 255) / 256;
 #define HISA_TK(N_) \
     if (per <= N_) return launch_topk_rows_items<256, N_>(ukeys, nrows, N, k, sel, m, lb, out_idx, out_scores, stream, t)
@@ -370,26 +513,25 @@ hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k,
         HISA_TK(2);
         HISA_TK(4);
         HISA_TK(8);
+        HISA_TK(16);
 #undef HISA_TK
+    }
+    if (nrows >= kManyRows) {
+        const int per = (N + 511) / 512;
+#define HISA_TK(N_) \
+    if (per <= N_) return launch_topk_rows_items<512, N_>(ukeys, nrows, N, k, sel, m, lb, out_idx, out_scores, stream, t)
+        HISA_TK(16);
+        HISA_TK(32);
+#undef HISA_TK
+        return hipErrorInvalidValue;
     }
     const int per = (N + 1023) / 1024;
 #define HISA_TK(N_) \
     if (per <= N_) return launch_topk_rows_items<1024, N_>(ukeys, nrows, N, k, sel, m, lb, out_idx, out_scores, stream, t)
-    HISA_TK(2);
-    HISA_TK(4);
     HISA_TK(8);
     HISA_TK(16);
 #undef HISA_TK
     return hipErrorInvalidValue;
-}
-
-template <int NT, int ITEMS>
-static hipError_t launch_stage2_fused_items(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq,
-                                            int lb, int m, int k, const int32_t* sel, int32_t* out_idx,
-                                            float* out_scores, hipStream_t stream, Timing t)
-{
-    return launch_k(stage2_fused_kernel<NT, ITEMS>, dim3((unsigned)nq), dim3(NT), stream, t.start, t.stop, qm, keys,
-                    q0, lb, m, k, sel, out_idx, out_scores);
 }
 
 hipError_t launch_stage2_split_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb,
@@ -400,36 +542,6 @@ hipError_t launch_stage2_split_scores(const QueryMeta& qm, const uint16_t* keys,
     dim3 grid((unsigned)nq, (unsigned)((N + per_wg - 1) / per_wg));
     return launch_k(stage2_score_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm, keys, q0, lb, m, per_wg,
                     sel, ukeys);
-}
-
-hipError_t launch_stage2_fused(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m, int k,
-                               const int32_t* sel, int32_t* out_idx, float* out_scores, hipStream_t stream, Timing t)
-{
-    const int N = m << lb;
-    if (N <= 2048) {
-        const int per = (N + 255) / 256;
-#define HISA_S2(N_) \
-    if (per <= N_) return launch_stage2_fused_items<256, N_>(qm, keys, q0, nq, lb, m, k, sel, out_idx, out_scores, stream, t)
-        HISA_S2(1);
-        HISA_S2(2);
-        HISA_S2(4);
-        HISA_S2(8);
-#undef HISA_S2
-    }
-    if (N <= 8192) {
-        const int per = (N + 511) / 512;
-#define HISA_S2(N_) \
-    if (per <= N_) return launch_stage2_fused_items<512, N_>(qm, keys, q0, nq, lb, m, k, sel, out_idx, out_scores, stream, t)
-        HISA_S2(8);
-        HISA_S2(16);
-#undef HISA_S2
-    }
-    const int per = (N + 1023) / 1024;
-#define HISA_S2(N_) \
-    if (per <= N_) return launch_stage2_fused_items<1024, N_>(qm, keys, q0, nq, lb, m, k, sel, out_idx, out_scores, stream, t)
-    HISA_S2(16);
-#undef HISA_S2
-    return hipErrorInvalidValue;
 }
 
 // ---- flat indexer: every key ------------------------------------------------
@@ -459,15 +571,17 @@ __global__ __launch_bounds__(kThreads) void flat_score_kernel(QueryMeta qm, cons
 // (v_mfma_f32_16x16x32_bf16, two per 16x16 tile since d = 64), so every
 // key row is loaded once per 16 queries.  Lane l feeds query row l%16 and
 // key l%16 with dims 8*(l/16)..+8 of each half of d, and receives the
-// scores of key l%16 for query rows 4*(l/16)..+4.  Only visible keys
-// (j <= t) are written; rows are read back up to t.  A tile whose queries
-// sit in different sequences falls back to one thread per key.
+// scores of key l%16 for query rows 4*(l/16)..+4.  Visible keys (j <= t)
+// get their score; the rest of the row is left alone (rows are read back
+// up to t) or, with zero_masked, gets key 0.  A tile whose queries sit in
+// different sequences falls back to one thread per key.
 
 constexpr int kTileRows = 16;
 constexpr int kTileKeys = 256;
 
 __global__ __launch_bounds__(kThreads) void flat_score_mfma_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0,
-                                                                   int64_t nq, int64_t Lmax, uint32_t* ukeys)
+                                                                   int64_t nq, int64_t Lmax, bool zero_masked,
+                                                                   uint32_t* ukeys)
 {
     __shared__ int64_t s_t[kTileRows];
     __shared__ int64_t s_koff[kTileRows];
@@ -500,7 +614,14 @@ __global__ __launch_bounds__(kThreads) void flat_score_mfma_kernel(QueryMeta qm,
         }
         tmax = max(tmax, s_t[r]);
     }
-    if (kt0 > tmax) return;                    // no row sees any key of this tile
+    if (kt0 > tmax) {                          // no row sees any key of this tile
+        if (zero_masked)
+            for (int r = 0; r < kTileRows; ++r) {
+                const int64_t j = kt0 + threadIdx.x;
+                if (row0 + r < nq && j < Lmax) ukeys[(row0 + r) * Lmax + j] = 0u;
+            }
+        return;
+    }
     const int lane = lane_id();
     if (uniform) {
         const int col = lane & 15, kg = lane >> 4;
@@ -525,13 +646,19 @@ __global__ __launch_bounds__(kThreads) void flat_score_mfma_kernel(QueryMeta qm,
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * kg + e;
-                if (j <= s_t[r]) ukeys[(row0 + r) * Lmax + j] = score_key(c[e]);
+                if (j <= s_t[r])
+                    ukeys[(row0 + r) * Lmax + j] = score_key(c[e]);
+                else if (zero_masked && row0 + r < nq && j < Lmax)
+                    ukeys[(row0 + r) * Lmax + j] = 0u;
             }
         }
     } else {
         const int64_t j = kt0 + threadIdx.x;
         for (int r = 0; r < kTileRows; ++r) {
-            if (j > s_t[r]) continue;
+            if (j > s_t[r]) {
+                if (zero_masked && row0 + r < nq && j < Lmax) ukeys[(row0 + r) * Lmax + j] = 0u;
+                continue;
+            }
             uint32_t q[32];
             load_query(qm.queries + (q0 + row0 + r) * kDim, q);
             ukeys[(row0 + r) * Lmax + j] =
@@ -541,12 +668,12 @@ __global__ __launch_bounds__(kThreads) void flat_score_mfma_kernel(QueryMeta qm,
 }
 
 hipError_t launch_flat_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int64_t Lmax,
-                              uint32_t* ukeys, bool mfma, hipStream_t stream, Timing t)
+                              uint32_t* ukeys, bool mfma, bool zero_masked, hipStream_t stream, Timing t)
 {
     if (mfma) {
         dim3 grid((unsigned)((Lmax + kTileKeys - 1) / kTileKeys), (unsigned)((nq + kTileRows - 1) / kTileRows));
         return launch_k(flat_score_mfma_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm, keys, q0, nq, Lmax,
-                        ukeys);
+                        zero_masked, ukeys);
     }
     dim3 grid((unsigned)((Lmax + kThreads - 1) / kThreads), (unsigned)nq);
     return launch_k(flat_score_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm, keys, q0, Lmax, ukeys);
@@ -697,6 +824,9 @@ FlatPlan flat_plan(int64_t nq, int64_t Lmax, int k)
             S = (S + p.G - 1) / p.G;
             ++p.levels;
         }
+        // few long rows: each level is one latency-bound launch, and the
+        // multi-workgroup radix select needs fewer steps than three levels
+        if (nq < 256 && p.levels >= 3) p.radix = true;
     }
     return p;
 }
@@ -707,18 +837,24 @@ hipError_t launch_flat_topk(const FlatPlan& p, const QueryMeta& qm, int64_t q0, 
 {
     hipEvent_t first_stop = p.S > 1 ? nullptr : t.stop;
     hipError_t err;
+    // few rows: 1024 threads (latency); many rows: 512 threads, two
+    // workgroups per CU (throughput)
     if (p.SL == 8192)
         err = launch_flat_level<1024, 8>(qm, q0, nq, ukeys, Lmax, p.SL, p.S, k, p.K1, cand_key[0], cand_tok[0],
                                          out_idx, out_scores, stream, t.start, first_stop);
     else
-        err = launch_flat_level<1024, 16>(qm, q0, nq, ukeys, Lmax, p.SL, p.S, k, p.K1, cand_key[0], cand_tok[0],
-                                          out_idx, out_scores, stream, t.start, first_stop);
+        err = launch_flat_level<512, 32>(qm, q0, nq, ukeys, Lmax, p.SL, p.S, k, p.K1, cand_key[0], cand_tok[0],
+                                         out_idx, out_scores, stream, t.start, first_stop);
     int S = p.S, cur = 0;
     while (err == hipSuccess && S > 1) {
         const int S_out = (S + p.G - 1) / p.G;
-        err = launch_cand_level<1024, 16>(q0, nq, cand_key[cur], cand_tok[cur], S, p.G, S_out, k, p.K1,
-                                          cand_key[cur ^ 1], cand_tok[cur ^ 1], out_idx, out_scores, stream,
-                                          S_out > 1 ? nullptr : t.stop);
+        hipEvent_t stop = S_out > 1 ? nullptr : t.stop;
+        if (p.SL == 8192)
+            err = launch_cand_level<1024, 16>(q0, nq, cand_key[cur], cand_tok[cur], S, p.G, S_out, k, p.K1,
+                                              cand_key[cur ^ 1], cand_tok[cur ^ 1], out_idx, out_scores, stream, stop);
+        else
+            err = launch_cand_level<512, 32>(q0, nq, cand_key[cur], cand_tok[cur], S, p.G, S_out, k, p.K1,
+                                             cand_key[cur ^ 1], cand_tok[cur ^ 1], out_idx, out_scores, stream, stop);
         S = S_out;
         cur ^= 1;
     }
