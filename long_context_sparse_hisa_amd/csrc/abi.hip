@@ -19,7 +19,8 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-inline bool valid_B(int B) { return B >= 16 && B <= 256 && (B & (B - 1)) == 0; }
+static_assert(kMaxKept * kMinB == HISA_MAX_CANDIDATES, "kept-block bound of the kernels");
+inline bool valid_B(int B) { return B >= kMinB && B <= kMaxB && (B & (B - 1)) == 0; }
 
 int status_of(hipError_t e) { return e == hipSuccess ? HISA_OK : HISA_ERR_HIP; }
 
@@ -48,7 +49,7 @@ int validate_index(const hisa_index_args* a, int flat)
 // Workspace regions of one chunk of `chunk` queries.
 struct Layout {
     // HISA
-    size_t sigma = 0, sel = 0, ukeys = 0;
+    size_t sigma = 0, sel = 0, rinfo = 0, ukeys = 0;
     // flat
     size_t hist = 0, state = 0, counts = 0, cand_key[2] = {0, 0}, cand_tok[2] = {0, 0};
     size_t total = 0;
@@ -83,6 +84,8 @@ Layout layout_for(const hisa_index_args* a, int flat, int64_t chunk)
         const int64_t Mmax = hisa_Mmax(a);
         L.sel = off;
         off += align_up((size_t)chunk * a->m * sizeof(int32_t));
+        L.rinfo = off;
+        off += align_up((size_t)chunk * sizeof(RowInfo));
         if (Mmax > kStage1FusedMax) {
             L.sigma = off;
             off += align_up((size_t)chunk * Mmax * sizeof(float));
@@ -242,18 +245,19 @@ int hisa_index(const hisa_index_args* a, void* stream_)
     const bool split = hisa_split(a);
     float* sigma = Mmax > kStage1FusedMax ? at<float>(a->workspace, L.sigma) : nullptr;
     int32_t* sel = at<int32_t>(a->workspace, L.sel);
+    RowInfo* rinfo = at<RowInfo>(a->workspace, L.rinfo);
     uint32_t* ukeys = at<uint32_t>(a->workspace, L.ukeys);
     for (int64_t q0 = 0; q0 < a->nq; q0 += chunk) {
         const int64_t nc = std::min(chunk, a->nq - q0);
         const bool last = q0 + nc >= a->nq;
-        hipError_t err = launch_stage1(qm, a->reps, q0, nc, lb, a->m, Mmax, sigma, sel, a->out_blocks, stream,
+        hipError_t err = launch_stage1(qm, a->reps, q0, nc, lb, a->m, Mmax, sigma, sel, rinfo, a->out_blocks, stream,
                                        stage_timing(a, last, 0));
         // token scores into ukeys: few queries split each row over several
         // workgroups, many queries share key loads 16 at a time on the MFMA
         if (err == hipSuccess)
-            err = split ? launch_stage2_split_scores(qm, a->keys, q0, nc, lb, a->m, sel, ukeys, stream,
+            err = split ? launch_stage2_split_scores(qm, a->keys, q0, nc, lb, a->m, rinfo, sel, ukeys, stream,
                                                      stage_timing(a, last, 1))
-                        : launch_stage2_tile_scores(qm, a->keys, q0, nc, lb, a->m, Mmax, sel, ukeys, stream,
+                        : launch_stage2_tile_scores(qm, a->keys, q0, nc, lb, a->m, Mmax, rinfo, sel, ukeys, stream,
                                                     stage_timing(a, last, 1));
         if (err == hipSuccess)
             err = launch_topk_small(ukeys, nc, a->m << lb, a->k, sel, a->m, lb, a->out_idx + q0 * a->k,

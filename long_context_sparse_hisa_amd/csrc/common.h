@@ -21,21 +21,30 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
 
-// fp32 dot of two 64-element bf16 rows held as 32 packed words each.  Each
-// v_dot2 step adds two exact bf16 products; four independent partial sums
-// keep the rounding error of the 64-term sum small.
-__device__ __forceinline__ float dot64_packed(const uint32_t (&q)[32], const uint4* row)
+// fp32 dot of two 64-element bf16 rows: the query as 32 packed words, the
+// key row as eight 16-byte parts.  Each v_dot2 step adds two exact bf16
+// products; four independent partial sums keep the rounding error of the
+// 64-term sum small.
+__device__ __forceinline__ float dot64_regs(const uint32_t (&q)[32], const uint4 (&v)[8])
 {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-        uint4 v = row[c];
-        acc[c & 3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[4 * c + 0]), as_bf16x2(v.x), acc[c & 3], false);
-        acc[c & 3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[4 * c + 1]), as_bf16x2(v.y), acc[c & 3], false);
-        acc[c & 3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[4 * c + 2]), as_bf16x2(v.z), acc[c & 3], false);
-        acc[c & 3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[4 * c + 3]), as_bf16x2(v.w), acc[c & 3], false);
+        acc[c & 3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[4 * c + 0]), as_bf16x2(v[c].x), acc[c & 3], false);
+        acc[c & 3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[4 * c + 1]), as_bf16x2(v[c].y), acc[c & 3], false);
+        acc[c & 3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[4 * c + 2]), as_bf16x2(v[c].z), acc[c & 3], false);
+        acc[c & 3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[4 * c + 3]), as_bf16x2(v[c].w), acc[c & 3], false);
     }
     return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// The same dot, loading the key row from memory.
+__device__ __forceinline__ float dot64_packed(const uint32_t (&q)[32], const uint4* row)
+{
+    uint4 v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) v[c] = row[c];
+    return dot64_regs(q, v);
 }
 
 __device__ __forceinline__ void load_query(const uint16_t* q, uint32_t (&out)[32])

@@ -17,6 +17,13 @@ struct Timing {
     hipEvent_t stop = nullptr;
 };
 
+// What stage 1 learns about a query row, kept for the stage-2 kernels so
+// they start with one round trip instead of the query -> sequence chain.
+struct RowInfo {
+    int64_t key_off;  // first key row of its sequence
+    int64_t t;        // position in its sequence, -1 for an invalid query
+};
+
 // One sequence's part of a pool / append launch.
 struct PoolJob {
     int64_t key_off;    // first key row of the sequence
@@ -46,27 +53,28 @@ struct QueryMeta {
 };
 
 // HISA stage 1: block scores, causal + forced top-m.  sel [nq, m] (the
-// chunk's rows); out_blocks (nullable) gets the same rows at query offset
+// chunk's rows) and rinfo [nq]; out_blocks (nullable) gets the same rows at query offset
 // q0.  Queries with at most kStage1FusedMax blocks are scored by the
 // selecting workgroup; longer ones go through sigma [nq, Mmax].
 // lb = log2(B).
 constexpr int64_t kStage1FusedMax = 2048;
 hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
-                         int64_t Mmax, float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream,
-                         Timing t = {});
+                         int64_t Mmax, float* sigma, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
+                         hipStream_t stream, Timing t = {});
 
 // HISA stage 2 for many queries: 16 query rows per wave scored on the
 // MFMA against the union of their kept blocks, into ukeys [nq, m*B] (only
 // the kept blocks' slots are written); launch_topk_small then selects.
 hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m,
-                                     int64_t Mmax, const int32_t* sel, uint32_t* ukeys, hipStream_t stream,
-                                     Timing t = {});
+                                     int64_t Mmax, const RowInfo* rinfo, const int32_t* sel, uint32_t* ukeys,
+                                     hipStream_t stream, Timing t = {});
 
 // HISA stage 2 for few queries: kStage2SlotsPerWg candidate slots per
 // workgroup scored into ukeys [nq, m*B]; launch_topk_small then selects.
 constexpr int kStage2SlotsPerWg = 512;
 hipError_t launch_stage2_split_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb,
-                                      int m, const int32_t* sel, uint32_t* ukeys, hipStream_t stream, Timing t = {});
+                                      int m, const RowInfo* rinfo, const int32_t* sel, uint32_t* ukeys,
+                                      hipStream_t stream, Timing t = {});
 
 // Flat: ranking keys of the visible keys into ukeys [nq, Lmax].  mfma: 16
 // query rows per tile on the matrix cores, otherwise one thread per
@@ -90,6 +98,12 @@ FlatPlan flat_plan(int64_t nq, int64_t Lmax, int k);
 hipError_t launch_flat_topk(const FlatPlan& p, const QueryMeta& qm, int64_t q0, int64_t nq, const uint32_t* ukeys,
                             int64_t Lmax, int k, uint32_t* cand_key[2], int32_t* cand_tok[2], int32_t* out_idx,
                             float* out_scores, hipStream_t stream, Timing t = {});
+
+// Block sizes are powers of two in [kMinB, kMaxB]; m*B is at most 16384
+// candidates, so a query keeps at most kMaxKept blocks.
+constexpr int kMinB = 16;
+constexpr int kMaxB = 256;
+constexpr int kMaxKept = 16384 / kMinB;
 
 // Rows per launch from which a select is sized for throughput, not latency.
 constexpr int64_t kManyRows = 256;

@@ -74,19 +74,32 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(uint16_t* keys, uint16_t
     const int col = threadIdx.x & 7;
     const int grp = threadIdx.x >> 3;
 
+    // every row of the block is loaded before any is used, so one block
+    // costs one memory round trip; new rows are then written to the cache
+    constexpr int kPasses = kMaxB / (kThreads / 8);
+    uint4 v[kPasses];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const int r = grp + p * (kThreads / 8);
+        const int64_t j = start + r;
+        v[p] = make_uint4(0u, 0u, 0u, 0u);
+        if (r < count)
+            v[p] = j < job.len_old
+                       ? reinterpret_cast<const uint4*>(keys + (job.key_off + j) * kDim)[col]
+                       : reinterpret_cast<const uint4*>(new_keys + (job.new_row + (j - job.len_old)) * kDim)[col];
+    }
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const int r = grp + p * (kThreads / 8);
+        const int64_t j = start + r;
+        if (r < count && j >= job.len_old) reinterpret_cast<uint4*>(keys + (job.key_off + j) * kDim)[col] = v[p];
+    }
     double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-    for (int r = grp; r < count; r += 32) {
-        const int64_t j = start + r;
-        uint4 v;
-        if (j < job.len_old) {
-            v = reinterpret_cast<const uint4*>(keys + (job.key_off + j) * kDim)[col];
-        } else {
-            v = reinterpret_cast<const uint4*>(new_keys + (job.new_row + (j - job.len_old)) * kDim)[col];
-            reinterpret_cast<uint4*>(keys + (job.key_off + j) * kDim)[col] = v;
-        }
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+        const uint32_t w[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             acc[2 * e + 0] += (double)bf16_lo(w[e]);
@@ -155,13 +168,14 @@ __global__ __launch_bounds__(kThreads) void block_score_kernel(QueryMeta qm, con
 template <int NT, int ITEMS, bool FUSED>
 __global__ __launch_bounds__(NT) void stage1_select_kernel(QueryMeta qm, const uint16_t* reps, int64_t q0, int lb,
                                                            int m, int64_t Mmax, const float* sigma, int32_t* sel,
-                                                           int32_t* out_blocks)
+                                                           RowInfo* rinfo, int32_t* out_blocks)
 {
     __shared__ BucketSmem<NT> sm;
     const int64_t row = blockIdx.x;
     const int64_t i = q0 + row;
     const QueryInfo qi =
         query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
+    if (threadIdx.x == 0) rinfo[row] = RowInfo{qi.key_off, qi.valid ? qi.t : -1};
     int32_t* srow = sel + row * m;
     int32_t* orow = out_blocks ? out_blocks + i * m : nullptr;
     if (!qi.valid) {
@@ -218,21 +232,22 @@ __global__ __launch_bounds__(NT) void stage1_select_kernel(QueryMeta qm, const u
 
 template <int NT, int ITEMS, bool FUSED>
 static hipError_t launch_stage1_items(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb,
-                                      int m, int64_t Mmax, const float* sigma, int32_t* sel, int32_t* out_blocks,
-                                      hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1)
+                                      int m, int64_t Mmax, const float* sigma, int32_t* sel, RowInfo* rinfo,
+                                      int32_t* out_blocks, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1)
 {
     return launch_k(stage1_select_kernel<NT, ITEMS, FUSED>, dim3((unsigned)nq), dim3(NT), stream, ev0, ev1, qm, reps,
-                    q0, lb, m, Mmax, sigma, sel, out_blocks);
+                    q0, lb, m, Mmax, sigma, sel, rinfo, out_blocks);
 }
 
 hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
-                         int64_t Mmax, float* sigma, int32_t* sel, int32_t* out_blocks, hipStream_t stream, Timing t)
+                         int64_t Mmax, float* sigma, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
+                         hipStream_t stream, Timing t)
 {
     if (Mmax <= kStage1FusedMax) {
         // 256 threads score up to 2048 representatives, 8 per thread
         const int64_t per = (Mmax + 255) / 256;
 #define HISA_S1F(N) \
-    if (per <= N) return launch_stage1_items<256, N, true>(qm, reps, q0, nq, lb, m, Mmax, nullptr, sel, out_blocks, stream, t.start, t.stop)
+    if (per <= N) return launch_stage1_items<256, N, true>(qm, reps, q0, nq, lb, m, Mmax, nullptr, sel, rinfo, out_blocks, stream, t.start, t.stop)
         HISA_S1F(1);
         HISA_S1F(2);
         HISA_S1F(4);
@@ -247,7 +262,7 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
     // 1024 threads select among up to 16384 scores, 16 per thread
     const int64_t per = (Mmax + 1023) / 1024;
 #define HISA_S1S(N) \
-    if (per <= N) return launch_stage1_items<1024, N, false>(qm, reps, q0, nq, lb, m, Mmax, sigma, sel, out_blocks, stream, nullptr, t.stop)
+    if (per <= N) return launch_stage1_items<1024, N, false>(qm, reps, q0, nq, lb, m, Mmax, sigma, sel, rinfo, out_blocks, stream, nullptr, t.stop)
     HISA_S1S(2);
     HISA_S1S(4);
     HISA_S1S(8);
@@ -260,53 +275,33 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
 // Candidate slot s of a query is row s % B of kept block s / B; slots of
 // padding blocks and keys after the query get key 0.
 
-HISA_INLINE uint32_t token_key(const uint32_t (&q)[32], const uint16_t* keys, const QueryInfo& qi,
-                               const int32_t* srow, int lb, int s)
-{
-    const int32_t blk = srow[s >> lb];
-    const int64_t j = ((int64_t)blk << lb) + (s & ((1 << lb) - 1));
-    if (blk < 0 || j > qi.t) return 0u;
-    return score_key(dot64_packed(q, reinterpret_cast<const uint4*>(keys + (qi.key_off + j) * kDim)));
-}
-
-// Select the k best slots of one row and write them (ascending token index)
-// with their scores, then the -1 padding.  srow == NULL: slot s is token s.
-template <int NT, int ITEMS>
-HISA_INLINE void select_and_write(const uint32_t (&key)[ITEMS], int k, int lb, const int32_t* srow, int32_t* orow,
-                                  float* scrow, BucketSmem<NT>& sm)
-{
-    const Threshold th = wg_bucket_select<NT, ITEMS>(key, k, sm);
-    const int total = wg_emit_selected<NT, ITEMS>(key, th, sm, k, [&](int slot, uint32_t kk, int rank) {
-        orow[rank] = srow ? (srow[slot >> lb] << lb) + (slot & ((1 << lb) - 1)) : slot;
-        if (scrow) scrow[rank] = key_score(kk);
-    });
-    for (int r = total + threadIdx.x; r < k; r += NT) {
-        orow[r] = -1;
-        if (scrow) scrow[r] = __builtin_nanf("");
-    }
-}
-
-// Several workgroups per query, each scoring `per_wg` slots into ukeys;
-// few queries still fill the chip.  The top-k follows in topk_rows_kernel.
-__global__ __launch_bounds__(kThreads) void stage2_score_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0,
-                                                                int lb, int m, int per_wg, const int32_t* sel,
-                                                                uint32_t* ukeys)
+// Few queries: kStage2SlotsPerWg slots of one query per workgroup, scored
+// into ukeys so that few queries still fill the chip.  Slot s is row s % B
+// of kept block s / B; slots of -1 blocks and keys after the query get
+// key 0.  The top-k follows in topk_rows_kernel.
+__global__ __launch_bounds__(kThreads) void stage2_score_kernel(const uint16_t* queries, const uint16_t* keys,
+                                                                int64_t q0, int lb, int m, const RowInfo* rinfo,
+                                                                const int32_t* sel, uint32_t* ukeys)
 {
     const int64_t row = blockIdx.x;
-    const int64_t i = q0 + row;
-    const QueryInfo qi =
-        query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
     const int N = m << lb;
     const int32_t* srow = sel + row * m;
     uint32_t* urow = ukeys + row * N;
-    const int beg = blockIdx.y * per_wg;
-    const int end = min(N, beg + per_wg);
-    if (qi.valid) {
-        uint32_t q[32];
-        load_query(qm.queries + i * kDim, q);
-        for (int s = beg + threadIdx.x; s < end; s += kThreads) urow[s] = token_key(q, keys, qi, srow, lb, s);
-    } else {
+    const int beg = blockIdx.y * kStage2SlotsPerWg;
+    const int end = min(N, beg + kStage2SlotsPerWg);
+    const RowInfo ri = rinfo[row];
+    if (ri.t < 0) {
         for (int s = beg + threadIdx.x; s < end; s += kThreads) urow[s] = 0u;
+        return;
+    }
+    uint32_t q[32];
+    load_query(queries + (q0 + row) * kDim, q);
+    for (int s = beg + threadIdx.x; s < end; s += kThreads) {
+        const int32_t blk = srow[s >> lb];
+        const int64_t j = ((int64_t)blk << lb) + (s & ((1 << lb) - 1));
+        urow[s] = (blk >= 0 && j <= ri.t)
+                      ? score_key(dot64_packed(q, reinterpret_cast<const uint4*>(keys + (ri.key_off + j) * kDim)))
+                      : 0u;
     }
 }
 
@@ -331,8 +326,9 @@ constexpr int kTileEnd = 0x7fffffff;     // cursor past the end of a list
 constexpr int64_t kTileTargetWaves = 16384;
 
 template <int LB>
-__global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0,
-                                                                      int64_t nq, int m, int range, const int32_t* sel,
+__global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint16_t* queries, const uint16_t* keys,
+                                                                      int64_t q0, int64_t nq, int m, int range,
+                                                                      const RowInfo* rinfo, const int32_t* sel,
                                                                       uint32_t* ukeys)
 {
     extern __shared__ int32_t s_sel[];            // [16][m] kept-block lists of the tile's rows
@@ -347,20 +343,16 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(QueryMeta 
     __syncthreads();
     const int blo = ((int)blockIdx.y * kTileWaves + wave_id()) * range;
     const int bhi = blo + range;
-    // lanes 0..15: one row each
+    // lanes 0..15: one row each; rows whose keys start at the same row of
+    // the cache are walked together
     const int r = lane & 15;
     const int32_t* lst = s_sel + r * m;
-    QueryInfo qi;
-    qi.valid = false;
-    qi.seq = -1;
-    qi.t = -1;
-    qi.key_off = 0;
-    if (lane < kTileQueries && r < nrows)
-        qi = query_info(q0 + row0 + r, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq,
-                        qm.max_len);
+    RowInfo ri{0, -1};
+    if (lane < kTileQueries && r < nrows) ri = rinfo[row0 + r];
+    const bool valid = ri.t >= 0;
     // this row's first list entry at or after blo (the list ascends, then -1s)
     int first = m;
-    if (qi.valid) {
+    if (valid) {
         int lo = 0, hi = m;
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
@@ -372,26 +364,24 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(QueryMeta 
         }
         first = lo;
     }
-    const bool active = qi.valid && first < m && lst[first] >= 0 && lst[first] < bhi;
-    const int seq = active ? qi.seq : -1;
-    const int t32 = qi.valid ? (int)qi.t : -1;
-    uint64_t pending = __ballot(lane < kTileQueries && seq >= 0);
+    const bool active = valid && first < m && lst[first] >= 0 && lst[first] < bhi;
+    const int t32 = valid ? (int)ri.t : -1;
+    uint64_t pending = __ballot(active);
     if (!pending) return;
     // A operand: the 16 queries
     const int col = lane & 15, kg = lane >> 4;
     bf16x8_t a0 = {}, a1 = {};
     if (col < nrows) {
-        const uint16_t* qrow = qm.queries + (q0 + row0 + col) * kDim + 8 * kg;
+        const uint16_t* qrow = queries + (q0 + row0 + col) * kDim + 8 * kg;
         a0 = *reinterpret_cast<const bf16x8_t*>(qrow);
         a1 = *reinterpret_cast<const bf16x8_t*>(qrow + 32);
     }
     while (pending) {
         const int lead = (int)__builtin_ctzll(pending);
-        const int s = __builtin_amdgcn_readlane(seq, lead);
-        const bool mine = lane < kTileQueries && seq == s && seq >= 0;
+        const int64_t koff = ((int64_t)__builtin_amdgcn_readlane((int)(ri.key_off >> 32), lead) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)ri.key_off, lead);
+        const bool mine = active && ri.key_off == koff;
         pending &= ~__ballot(mine);
-        const int64_t koff = ((int64_t)__builtin_amdgcn_readlane((int)(qi.key_off >> 32), lead) << 32) |
-                             (uint32_t)__builtin_amdgcn_readlane((int)qi.key_off, lead);
         const int tmax = (int)wave_max_u32(mine ? (uint32_t)t32 : 0u);
         // the query position of each output row of this lane, -1 when not walked now
         const int tm = mine ? t32 : -1;
@@ -443,7 +433,8 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(QueryMeta 
 }
 
 hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m,
-                                     int64_t Mmax, const int32_t* sel, uint32_t* ukeys, hipStream_t stream, Timing t)
+                                     int64_t Mmax, const RowInfo* rinfo, const int32_t* sel, uint32_t* ukeys,
+                                     hipStream_t stream, Timing t)
 {
     // enough waves to fill the chip: split each tile's blocks into ranges
     const int64_t ntiles = (nq + kTileQueries - 1) / kTileQueries;
@@ -454,7 +445,7 @@ hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, 
     const dim3 block(64 * kTileWaves);
     const size_t lds = (size_t)kTileQueries * m * sizeof(int32_t);
 #define HISA_T2(LB_) \
-    if (lb == LB_) return launch_kl(stage2_tile_kernel<LB_>, grid, block, lds, stream, t.start, t.stop, qm, keys, q0, nq, m, (int)range, sel, ukeys)
+    if (lb == LB_) return launch_kl(stage2_tile_kernel<LB_>, grid, block, lds, stream, t.start, t.stop, qm.queries, keys, q0, nq, m, (int)range, rinfo, sel, ukeys)
     HISA_T2(4);
     HISA_T2(5);
     HISA_T2(6);
@@ -471,23 +462,41 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(const uint32_t* ukeys, in
                                                        int lb, int32_t* out_idx, float* out_scores)
 {
     __shared__ BucketSmem<NT> sm;
+    __shared__ int32_t s_list[kMaxKept];                   // the row's kept blocks
     const int64_t row = blockIdx.x;
     const uint32_t* src = ukeys + row * N;
-    // slots of -1 list entries (a suffix of the list) hold no candidate
-    int n = N;
-    if (sel) {
-        int cnt = 0;
-        for (int i = lane_id(); i < m; i += 64) cnt += sel[row * m + i] >= 0;
-        n = min(N, wave_sum(cnt) << lb);
-    }
+    // the keys and the kept-block list load together; slots of -1 list
+    // entries (a suffix of the list) hold no candidate and are masked after
     uint32_t key[ITEMS];
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
         const int s = slot_of<ITEMS>(it);
-        key[it] = s < n ? src[s] : 0u;
+        key[it] = s < N ? src[s] : 0u;
     }
-    select_and_write<NT, ITEMS>(key, k, lb, sel ? sel + row * m : nullptr, out_idx + row * k,
-                                out_scores ? out_scores + row * k : nullptr, sm);
+    if (sel) {
+        int cnt = 0;
+        for (int i = lane_id(); i < m; i += 64) {
+            const int32_t v = sel[row * m + i];
+            cnt += v >= 0;
+            if (wave_id() == 0) s_list[i] = v;
+        }
+        const int n = min(N, wave_sum(cnt) << lb);
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it)
+            if (slot_of<ITEMS>(it) >= n) key[it] = 0u;
+    }
+    // the select's barriers publish s_list before anything is emitted
+    int32_t* orow = out_idx + row * k;
+    float* scrow = out_scores ? out_scores + row * k : nullptr;
+    const Threshold th = wg_bucket_select<NT, ITEMS>(key, k, sm);
+    const int total = wg_emit_selected<NT, ITEMS>(key, th, sm, k, [&](int slot, uint32_t kk, int rank) {
+        orow[rank] = sel ? (s_list[slot >> lb] << lb) + (slot & ((1 << lb) - 1)) : slot;
+        if (scrow) scrow[rank] = key_score(kk);
+    });
+    for (int r = total + threadIdx.x; r < k; r += NT) {
+        orow[r] = -1;
+        if (scrow) scrow[r] = __builtin_nanf("");
+    }
 }
 
 template <int NT, int ITEMS>
@@ -535,13 +544,13 @@ hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k,
 }
 
 hipError_t launch_stage2_split_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb,
-                                      int m, const int32_t* sel, uint32_t* ukeys, hipStream_t stream, Timing t)
+                                      int m, const RowInfo* rinfo, const int32_t* sel, uint32_t* ukeys,
+                                      hipStream_t stream, Timing t)
 {
     const int N = m << lb;
-    const int per_wg = kStage2SlotsPerWg;
-    dim3 grid((unsigned)nq, (unsigned)((N + per_wg - 1) / per_wg));
-    return launch_k(stage2_score_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm, keys, q0, lb, m, per_wg,
-                    sel, ukeys);
+    dim3 grid((unsigned)nq, (unsigned)((N + kStage2SlotsPerWg - 1) / kStage2SlotsPerWg));
+    return launch_k(stage2_score_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm.queries, keys, q0, lb, m,
+                    rinfo, sel, ukeys);
 }
 
 // ---- flat indexer: every key ------------------------------------------------
