@@ -99,8 +99,10 @@ __device__ __forceinline__ uint32_t score_key(float f)
 
 __device__ __forceinline__ float key_score(uint32_t key)
 {
-    uint32_t u = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
-    return __uint_as_float(u);
+    // top bit set: a non-negative score, clear that bit; otherwise a
+    // negative score, invert every bit
+    const uint32_t t = (uint32_t)((int32_t)key >> 31);
+    return __uint_as_float(key ^ 0x80000000u ^ (~t & 0x7fffffffu));
 }
 
 // ---- workgroup scans (256 threads) ------------------------------------------

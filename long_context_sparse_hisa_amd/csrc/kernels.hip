@@ -239,10 +239,178 @@ static hipError_t launch_stage1_items(const QueryMeta& qm, const uint16_t* reps,
                     q0, lb, m, Mmax, sigma, sel, rinfo, out_blocks);
 }
 
+// Many queries (prefill): 16 consecutive query rows form a tile, scored
+// against the representatives on the bf16 MFMA (16 blocks x 16 rows per
+// pair of v_mfma_f32_16x16x32_bf16).  WT waves share a tile: each computes
+// the tile's scores (cheap) but keeps only its own rows r = wt (mod WT) in
+// its LDS, kS1RowsPerPass at a time, and selects their top-m with the
+// barrier-free wave select.  WT grows when there are few tiles, so the
+// selects still fill the chip.  Rows of a tile in different sequences are
+// handled one sequence at a time.  ITEMS = 64-slot groups per row: block b
+// is slot b.
+
+constexpr int kS1TileWaves = 2;               // waves per workgroup
+constexpr int kS1TileMaxBlocks = 1024;
+constexpr int64_t kS1TargetWaves = 4096;
+
+__host__ __device__ constexpr int s1_rows_per_pass(int items) { return items <= 4 ? 16 : 64 / items; }
+__host__ __device__ constexpr int s1_row_stride(int items) { return 64 * items + 16; }   // floats; +16 spreads banks
+__host__ __device__ constexpr size_t s1_wave_lds(int items)
+{
+    return (size_t)s1_rows_per_pass(items) * s1_row_stride(items) * sizeof(float) + sizeof(WaveSmem);
+}
+
+template <int ITEMS>
+__global__ __launch_bounds__(64 * kS1TileWaves) void stage1_tile_kernel(QueryMeta qm, const uint16_t* reps, int64_t q0,
+                                                                        int64_t nq, int lb, int m, int WT, int32_t* sel,
+                                                                        RowInfo* rinfo, int32_t* out_blocks)
+{
+    extern __shared__ __align__(16) float s_dyn[];
+    constexpr int R = s1_rows_per_pass(ITEMS);
+    constexpr int RS = s1_row_stride(ITEMS);
+    const int w = wave_id(), lane = lane_id();
+    float* sc = s_dyn + w * (s1_wave_lds(ITEMS) / sizeof(float));
+    WaveSmem& ws = *reinterpret_cast<WaveSmem*>(sc + R * RS);
+    const int64_t gw = (int64_t)blockIdx.x * kS1TileWaves + w;
+    const int wt = (int)(gw % WT);
+    const int64_t row0 = (gw / WT) * 16;
+    if (row0 >= nq) return;
+    const int nrows = (int)min<int64_t>(16, nq - row0);
+    const int r = lane & 15;
+    QueryInfo qi;
+    qi.valid = false;
+    qi.seq = -1;
+    qi.t = -1;
+    qi.key_off = 0;
+    qi.rep_off = 0;
+    if (lane < 16 && r < nrows) {
+        qi = query_info(q0 + row0 + r, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq,
+                        qm.max_len);
+        if (wt == 0) rinfo[row0 + r] = RowInfo{qi.key_off, qi.valid ? qi.t : -1};
+    }
+    const bool own = lane < 16 && r < nrows && r % WT == wt;
+    // invalid rows keep no block
+    for (uint64_t iv = __ballot(own && !qi.valid); iv; iv &= iv - 1) {
+        const int rr = (int)__builtin_ctzll(iv);
+        for (int i = lane; i < m; i += 64) {
+            sel[(row0 + rr) * m + i] = -1;
+            if (out_blocks) out_blocks[(q0 + row0 + rr) * m + i] = -1;
+        }
+    }
+    const int col = lane & 15, kg = lane >> 4;
+    bf16x8_t a0 = {}, a1 = {};
+    if (col < nrows) {
+        const uint16_t* qrow = qm.queries + (q0 + row0 + col) * kDim + 8 * kg;
+        a0 = *reinterpret_cast<const bf16x8_t*>(qrow);
+        a1 = *reinterpret_cast<const bf16x8_t*>(qrow + 32);
+    }
+    const int c_own = qi.valid ? (int)(qi.t >> lb) : -1;
+    uint64_t pending = __ballot(own && qi.valid);
+    while (pending) {
+        const int lead = (int)__builtin_ctzll(pending);
+        const int s = __builtin_amdgcn_readlane(qi.seq, lead);
+        const bool mine = own && qi.valid && qi.seq == s;
+        const uint64_t mine_rows = __ballot(mine);
+        pending &= ~mine_rows;
+        const int64_t rep_off = ((int64_t)__builtin_amdgcn_readlane((int)(qi.rep_off >> 32), lead) << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane((int)qi.rep_off, lead);
+        const int cmax = (int)wave_max_u32(mine ? (uint32_t)c_own : 0u);
+        // own rows are wt, wt+WT, ...: own index i = row / WT
+        const int nown = (16 - wt + WT - 1) / WT;
+        for (int i0 = 0; i0 < nown; i0 += R) {
+            bool any = false;
+            for (int i = i0; i < i0 + R && i < nown; ++i) any |= (mine_rows >> (wt + i * WT)) & 1ull;
+            if (!any) continue;
+            // scores of blocks 0 .. cmax for own rows i0 .. i0+R-1: the
+            // representatives are the A operand, so lane l receives blocks
+            // 4*(l/16)..+4 of the tile for query row l%16 and stores them as
+            // one 16-byte vector
+            const int iq = col / WT - i0;
+            const bool keep = col % WT == wt && iq >= 0 && iq < R;
+            for (int bt = 0; bt * 16 <= cmax; ++bt) {
+                const int b = bt * 16 + col;
+                bf16x8_t b0 = {}, b1 = {};
+                if (b <= cmax) {
+                    const uint16_t* rp = reps + (rep_off + b) * kDim + 8 * kg;
+                    b0 = *reinterpret_cast<const bf16x8_t*>(rp);
+                    b1 = *reinterpret_cast<const bf16x8_t*>(rp + 32);
+                }
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, a0, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, a1, acc, 0, 0, 0);
+                if (keep) *reinterpret_cast<f32x4_t*>(sc + iq * RS + bt * 16 + 4 * kg) = acc;
+            }
+            wave_lds_fence();
+            for (int i = i0; i < i0 + R && i < nown; ++i) {
+                const int rr = wt + i * WT;
+                if (!((mine_rows >> rr) & 1ull)) continue;
+                const int cr = __builtin_amdgcn_readlane(c_own, rr);
+                int32_t* srow = sel + (row0 + rr) * m;
+                int32_t* orow = out_blocks ? out_blocks + (q0 + row0 + rr) * m : nullptr;
+                if (cr + 1 <= m) {
+                    for (int j = lane; j < m; j += 64) {
+                        const int32_t v = j <= cr ? j : -1;
+                        srow[j] = v;
+                        if (orow) orow[j] = v;
+                    }
+                    continue;
+                }
+                uint32_t key[ITEMS];
+#pragma unroll
+                for (int it = 0; it < ITEMS; ++it) {
+                    const int b = it * 64 + lane;
+                    key[it] = (b >= 1 && b <= cr - 2) ? score_key(sc[(i - i0) * RS + b]) : 0u;
+                }
+                wave_select<ITEMS>(key, m - 3, ws, [&](int slot, uint32_t, int rank) {
+                    srow[1 + rank] = slot;
+                    if (orow) orow[1 + rank] = slot;
+                });
+                if (lane == 0) {
+                    srow[0] = 0;
+                    srow[m - 2] = cr - 1;
+                    srow[m - 1] = cr;
+                    if (orow) {
+                        orow[0] = 0;
+                        orow[m - 2] = cr - 1;
+                        orow[m - 1] = cr;
+                    }
+                }
+            }
+            wave_lds_fence();
+        }
+    }
+}
+
+template <int ITEMS>
+static hipError_t launch_stage1_tile_items(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb,
+                                           int m, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
+                                           hipStream_t stream, Timing t)
+{
+    const int64_t tiles = (nq + 15) / 16;
+    int WT = 1;
+    while (WT < 16 && tiles * WT < kS1TargetWaves) WT *= 2;
+    const int64_t waves = tiles * WT;
+    const dim3 grid((unsigned)((waves + kS1TileWaves - 1) / kS1TileWaves));
+    return launch_kl(stage1_tile_kernel<ITEMS>, grid, dim3(64 * kS1TileWaves), kS1TileWaves * s1_wave_lds(ITEMS),
+                     stream, t.start, t.stop, qm, reps, q0, nq, lb, m, WT, sel, rinfo, out_blocks);
+}
+
 hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
                          int64_t Mmax, float* sigma, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
                          hipStream_t stream, Timing t)
 {
+    if (nq >= kManyRows && Mmax <= kS1TileMaxBlocks) {
+        // many queries: MFMA block scores, wave-level top-m
+        const int64_t per = (Mmax + 63) / 64;
+#define HISA_S1T(N) \
+    if (per <= N) return launch_stage1_tile_items<N>(qm, reps, q0, nq, lb, m, sel, rinfo, out_blocks, stream, t)
+        HISA_S1T(1);
+        HISA_S1T(2);
+        HISA_S1T(4);
+        HISA_S1T(8);
+        HISA_S1T(16);
+#undef HISA_S1T
+    }
     if (Mmax <= kStage1FusedMax) {
         // 256 threads score up to 2048 representatives, 8 per thread
         const int64_t per = (Mmax + 255) / 256;
@@ -317,8 +485,9 @@ __global__ __launch_bounds__(kThreads) void stage2_score_kernel(const uint16_t* 
 // key 0 for tokens after the query; slots of -1 entries are never written
 // (the top-k stops at the kept blocks).  Rows of a tile in different
 // sequences are walked one sequence at a time.  MFMA lanes: lane l feeds
-// query row l%16 and key l%16 with dims 8*(l/16)..+8 of each half of d, and
-// receives the scores of key l%16 for query rows 4*(l/16)..+4.
+// key l%16 (A operand) and query row l%16 (B operand) with dims
+// 8*(l/16)..+8 of each half of d, and receives the scores of keys
+// 4*(l/16)..+4 for query row l%16, which it stores as one 16-byte vector.
 
 constexpr int kTileQueries = 16;
 constexpr int kTileWaves = 4;
@@ -383,14 +552,13 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
         const bool mine = active && ri.key_off == koff;
         pending &= ~__ballot(mine);
         const int tmax = (int)wave_max_u32(mine ? (uint32_t)t32 : 0u);
-        // the query position of each output row of this lane, -1 when not walked now
         const int tm = mine ? t32 : -1;
-        int te[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) te[e] = __shfl(tm, 4 * kg + e);
         int cur = first;
         int nxt = mine ? lst[first] : kTileEnd;
         int b = (int)wave_min_u32((uint32_t)nxt);
+        // this lane's output row is row `col` of the tile (position -1 when
+        // that row is not walked now)
+        const int tq = __shfl(tm, col);
         while (b != kTileEnd) {
             const bool hit = nxt == b;
             const int pos = hit ? cur : -1;
@@ -399,9 +567,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
                 const int v = cur < m ? lst[cur] : -1;
                 nxt = v >= 0 && v < bhi ? v : kTileEnd;
             }
-            int pe[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pe[e] = __shfl(pos, 4 * kg + e);    // -1 unless that row kept b
+            const int pq = __shfl(pos, col);           // -1 unless row `col` kept b
             const uint16_t* kb = keys + (koff + ((int64_t)b << LB)) * kDim + 8 * kg;
             bf16x8_t k0[KT], k1[KT];
 #pragma unroll
@@ -415,17 +581,24 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
                 }
             }
             const int bn = (int)wave_min_u32((uint32_t)nxt);
+            uint32_t* urow = ukeys + (row0 + col) * N + ((int64_t)(pq < 0 ? 0 : pq) << LB);
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-                const int jj = kt * 16 + col;
-                const int j = (b << LB) + jj;
+                // keys as the A operand: lane l receives keys 4*(l/16)..+4 of
+                // the 16-key tile for query row l%16
                 f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, k0[kt], c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, k1[kt], c, 0, 0, 0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (pe[e] >= 0)
-                        ukeys[(row0 + 4 * kg + e) * N + (pe[e] << LB) + jj] = j <= te[e] ? score_key(c[e]) : 0u;
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[kt], a0, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[kt], a1, c, 0, 0, 0);
+                const int jj = kt * 16 + 4 * kg;
+                const int j = (b << LB) + jj;
+                if (pq >= 0) {
+                    uint4 o;
+                    o.x = j + 0 <= tq ? score_key(c[0]) : 0u;
+                    o.y = j + 1 <= tq ? score_key(c[1]) : 0u;
+                    o.z = j + 2 <= tq ? score_key(c[2]) : 0u;
+                    o.w = j + 3 <= tq ? score_key(c[3]) : 0u;
+                    *reinterpret_cast<uint4*>(urow + jj) = o;
+                }
             }
             b = bn;
         }
@@ -512,8 +685,9 @@ hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k,
                              int32_t* out_idx, float* out_scores, hipStream_t stream, Timing t)
 {
     // rows up to 4096 keys: 256 threads.  Longer rows: 1024 threads when
-    // there are few of them (one row's latency is the cost), 512 threads
-    // otherwise (two workgroups per CU hide each other's barriers).
+    // there are few of them (one row's latency is the cost), otherwise 32
+    // keys per thread in 256- or 512-thread workgroups, several per CU
+    // hiding each other's barriers.
     if (N <= 4096) {
         const int per = (N + 255) / 256;
 #define HISA_TK(N_) \
@@ -526,13 +700,8 @@ hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k,
 #undef HISA_TK
     }
     if (nrows >= kManyRows) {
-        const int per = (N + 511) / 512;
-#define HISA_TK(N_) \
-    if (per <= N_) return launch_topk_rows_items<512, N_>(ukeys, nrows, N, k, sel, m, lb, out_idx, out_scores, stream, t)
-        HISA_TK(16);
-        HISA_TK(32);
-#undef HISA_TK
-        return hipErrorInvalidValue;
+        if (N <= 8192) return launch_topk_rows_items<256, 32>(ukeys, nrows, N, k, sel, m, lb, out_idx, out_scores, stream, t);
+        return launch_topk_rows_items<512, 32>(ukeys, nrows, N, k, sel, m, lb, out_idx, out_scores, stream, t);
     }
     const int per = (N + 1023) / 1024;
 #define HISA_TK(N_) \
@@ -578,9 +747,10 @@ __global__ __launch_bounds__(kThreads) void flat_score_kernel(QueryMeta qm, cons
 
 // Many queries: 16 query rows x 256 keys per workgroup on the bf16 MFMA
 // (v_mfma_f32_16x16x32_bf16, two per 16x16 tile since d = 64), so every
-// key row is loaded once per 16 queries.  Lane l feeds query row l%16 and
-// key l%16 with dims 8*(l/16)..+8 of each half of d, and receives the
-// scores of key l%16 for query rows 4*(l/16)..+4.  Visible keys (j <= t)
+// key row is loaded once per 16 queries.  Lane l feeds key l%16 (A
+// operand) and query row l%16 (B operand) with dims 8*(l/16)..+8 of each
+// half of d, and receives the scores of keys 4*(l/16)..+4 for query row
+// l%16, written as one 16-byte vector.  Visible keys (j <= t)
 // get their score; the rest of the row is left alone (rows are read back
 // up to t) or, with zero_masked, gets key 0.  A tile whose queries sit in
 // different sequences falls back to one thread per key.
@@ -632,6 +802,7 @@ __global__ __launch_bounds__(kThreads) void flat_score_mfma_kernel(QueryMeta qm,
         return;
     }
     const int lane = lane_id();
+    const bool vec_rows = (Lmax & 3) == 0;         // rows start 16-byte aligned
     if (uniform) {
         const int col = lane & 15, kg = lane >> 4;
         bf16x8_t a0 = {}, a1 = {};
@@ -649,16 +820,25 @@ __global__ __launch_bounds__(kThreads) void flat_score_mfma_kernel(QueryMeta qm,
                 b0 = *reinterpret_cast<const bf16x8_t*>(krow);
                 b1 = *reinterpret_cast<const bf16x8_t*>(krow + 32);
             }
+            // keys as the A operand: lane l receives keys j0..j0+3 for
+            // query row l%16
             f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, a0, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, a1, c, 0, 0, 0);
+            const int64_t j0 = kt0 + 64 * wave_id() + 16 * st + 4 * kg;
+            const int64_t t = s_t[col];
+            if (row0 + col < nq && j0 <= (zero_masked ? Lmax - 1 : t)) {
+                uint32_t o[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * kg + e;
-                if (j <= s_t[r])
-                    ukeys[(row0 + r) * Lmax + j] = score_key(c[e]);
-                else if (zero_masked && row0 + r < nq && j < Lmax)
-                    ukeys[(row0 + r) * Lmax + j] = 0u;
+                for (int e = 0; e < 4; ++e) o[e] = j0 + e <= t ? score_key(c[e]) : 0u;
+                uint32_t* dst = ukeys + (row0 + col) * Lmax + j0;
+                if (vec_rows && j0 + 3 < Lmax) {
+                    *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (j0 + e < Lmax) dst[e] = o[e];
+                }
             }
         }
     } else {

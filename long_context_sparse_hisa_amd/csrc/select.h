@@ -142,15 +142,74 @@ struct BucketSmem {
     RadixSmem<NT> radix;
 };
 
+// Inclusive prefix sum within each row of 16 lanes.
+HISA_INLINE int row_incl_scan(int v)
+{
+    uint32_t x = (uint32_t)v;
+    x += dpp_u32<0x111>(x);
+    x += dpp_u32<0x112>(x);
+    x += dpp_u32<0x114>(x);
+    x += dpp_u32<0x118>(x);
+    return (int)x;
+}
+
+// Orders one wave's LDS accesses around it (a compiler fence: the LDS
+// operations of one wave complete in order).
+HISA_INLINE void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The bin of a key in [kmin, kmax]: x = score * scale + off, clamped to
+// [0, kBins-1] and truncated.  Monotone in the key (equal keys share a
+// bin); keys below kmin (the empty key 0) fall in bin 0.
 struct Binning {
-    float lo;
+    uint32_t kmin;
     float scale;
+    float off;
     HISA_INLINE int operator()(uint32_t key) const
     {
-        const float x = (key_score(key) - lo) * scale;
-        return x >= (float)(kBins - 1) ? kBins - 1 : (int)x;
+        const float x = fmaf(key_score(max(key, kmin)), scale, off);
+        return (int)__builtin_amdgcn_fmed3f(x, 0.f, (float)(kBins - 1));
     }
 };
+
+// Smallest key in [lo, hi] whose bin is >= b, given that hi's is.  One
+// wave: first a window of 64 keys around the bin edge computed from the
+// scale, then, if the edge is not in it, rounds that each test 64 evenly
+// spaced keys (six rounds cover 32 bits).  Uniform over the wave.
+HISA_INLINE uint32_t first_key_of_bin(uint32_t lo, uint32_t hi, int b, const Binning& bin)
+{
+    const int lane = lane_id();
+    {
+        const float edge = (b - bin.off) / bin.scale;
+        const uint32_t g = score_key(edge);
+        const uint32_t g0 = min(g < lo + 32u ? lo : g - 32u, hi);
+        const uint32_t k = min(g0 + (uint32_t)lane, hi);
+        const uint64_t bal = __ballot(bin(k) >= b);
+        // the edge lies in the window when the window starts below it and
+        // reaches it
+        if (bal != 0 && (g0 == lo || !(bal & 1ull))) return (uint32_t)__builtin_amdgcn_readlane((int)k, (int)__builtin_ctzll(bal));
+        if (bal == 0) lo = (uint32_t)__builtin_amdgcn_readlane((int)k, 63) + 1u;
+        else hi = g0;
+    }
+    while (lo < hi) {
+        const uint32_t w = hi - lo;
+        const uint32_t k = lo + min((w / 64u + 1u) * (uint32_t)lane, w);
+        const uint64_t bal = __ballot(bin(k) >= b);
+        if (bal == 0) {
+            lo = (uint32_t)__builtin_amdgcn_readlane((int)k, 63) + 1u;
+        } else {
+            const int f = (int)__builtin_ctzll(bal);
+            if (f == 0) return lo;
+            hi = (uint32_t)__builtin_amdgcn_readlane((int)k, f);
+            lo = (uint32_t)__builtin_amdgcn_readlane((int)k, f - 1) + 1u;
+        }
+    }
+    return lo;
+}
 
 template <int NT, int ITEMS>
 HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, BucketSmem<NT>& sm)
@@ -164,34 +223,35 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
         return th;
     }
     // count, smallest and largest candidate key; clear the histogram
-    uint32_t cnt = 0, kmin = 0xffffffffu, kmax = 0u;
+    int nz = 0;
+    uint32_t kmax = 0u, kmin1 = 0xffffffffu;
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
-        const uint32_t kk = key[it];
-        cnt += kk != 0u;
-        kmin = kk ? min(kmin, kk) : kmin;
-        kmax = max(kmax, kk);
+        kmax = max(kmax, key[it]);
+        kmin1 = min(kmin1, key[it] - 1u);     // an empty slot wraps to the top
+        nz += key[it] != 0u;
     }
-    cnt = (uint32_t)wave_sum((int)cnt);
-    kmin = wave_min_u32(kmin);
+    nz = wave_sum(nz);
     kmax = wave_max_u32(kmax);
+    kmin1 = wave_min_u32(kmin1);
     if (lane_id() == 0) {
-        sm.red[0][wave_id()] = cnt;
-        sm.red[1][wave_id()] = kmin;
+        sm.red[0][wave_id()] = (uint32_t)nz;
+        sm.red[1][wave_id()] = kmin1;
         sm.red[2][wave_id()] = kmax;
     }
-    for (int b = threadIdx.x; b <= kBins; b += NT) sm.hist[b] = 0;
+    for (int b = threadIdx.x; b < kBins; b += NT) sm.hist[b] = 0;
     if (threadIdx.x == 0) sm.misc[2] = 0;
     __syncthreads();
     int nvalid = 0;
-    kmin = 0xffffffffu;
+    kmin1 = 0xffffffffu;
     kmax = 0u;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         nvalid += (int)sm.red[0][w];
-        kmin = min(kmin, sm.red[1][w]);
+        kmin1 = min(kmin1, sm.red[1][w]);
         kmax = max(kmax, sm.red[2][w]);
     }
+    const uint32_t kmin = kmin1 + 1u;
     if (nvalid <= n) {
         th.T = 0u;
         th.need_eq = 0;
@@ -206,46 +266,72 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
     }
     const float smin = key_score(kmin), smax = key_score(kmax);
     const float range = smax - smin;
-    if (!(range > 0.f) || !__builtin_isfinite(range))
-        return wg_radix_select<NT, ITEMS>(key, n, sm.radix, true);   // non-finite scores: exact radix path
-    const Binning bin{smin, (float)kBins / range};
+    const float scale = (float)kBins / range;
+    const float off = -smin * scale;
+    if (!(range > 0.f) || !__builtin_isfinite(range) || !__builtin_isfinite(scale) || !__builtin_isfinite(off))
+        return wg_radix_select<NT, ITEMS>(key, n, sm.radix, true);   // non-finite or unbinnable scores
+    const Binning bin{kmin, scale, off};
+    // empty slots land in bin 0 and are taken off it below
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) atomicAdd(&sm.hist[key[it] ? bin(key[it]) : kBins], 1);   // no branch
+    for (int it = 0; it < ITEMS; ++it) atomicAdd(&sm.hist[bin(key[it])], 1);
     __syncthreads();
-    // one wave finds the bin of the n-th largest key: lane l owns the 16
-    // bins counted down from kBins-1-16l
+    // one wave finds the bin of the n-th largest key (lane l owns the 16
+    // bins counted down from kBins-1-16l) and the range of keys in it
     if (wave_id() == 0) {
         constexpr int kPer = kBins / 64;
+        const int nzero = NT * ITEMS - nvalid;
+        if (threadIdx.x == 0) sm.hist[0] -= nzero;
+        wave_lds_fence();
         int own = 0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) own += sm.hist[kBins - 1 - kPer * lane_id() - j];
         const int cum = wave_incl_scan(own);
-        if (cum >= n && cum - own < n) {
-            int above = cum - own;
-            int b = kBins - 1 - kPer * lane_id();
-            for (int j = 0; j < kPer; ++j, --b) {
-                const int h = sm.hist[b];
-                if (above + h >= n) break;
-                above += h;
-            }
-            sm.misc[0] = b;
+        const int L = (int)__builtin_ctzll(__ballot(cum >= n && cum - own < n));
+        // lanes 0..15 take the 16 bins of lane L, a row scan finds the bin
+        const int h = lane_id() < kPer ? sm.hist[kBins - 1 - kPer * L - lane_id()] : 0;
+        const int rc = row_incl_scan(h);
+        const int aboveL = __builtin_amdgcn_readlane(cum - own, L);
+        const int J = (int)__builtin_ctzll(__ballot(lane_id() < kPer && aboveL + rc >= n));
+        const int bstar = kBins - 1 - kPer * L - J;
+        const int c = __builtin_amdgcn_readlane(h, J);
+        const int above = aboveL + __builtin_amdgcn_readlane(rc, J) - c;
+        uint32_t klo = kmin, khi1 = kmax + 1u;
+        if (n - above < c) {                  // the bin is split: its key range
+            if (bstar > 0) klo = first_key_of_bin(kmin, kmax, bstar, bin);
+            if (bstar < kBins - 1) khi1 = first_key_of_bin(klo, kmax, bstar + 1, bin);
+        } else if (bstar > 0) {
+            klo = first_key_of_bin(kmin, kmax, bstar, bin);
+        }
+        if (lane_id() == 0) {
+            sm.misc[0] = bstar;
             sm.misc[1] = above;
+            sm.misc[3] = c;
+            sm.misc[4] = (int)klo;
+            sm.misc[5] = (int)khi1;
         }
     }
     __syncthreads();
-    const int bstar = sm.misc[0];
-    const int need = n - sm.misc[1];          // >= 1 keys still to take from bin bstar
-    const int c = sm.hist[bstar];
+    const int need = n - sm.misc[1];          // 1 <= need <= c keys still to take from the bin
+    const int c = sm.misc[3];
+    const uint32_t klo = (uint32_t)sm.misc[4], khi1 = (uint32_t)sm.misc[5];
+    if (need == c) {
+        // the whole bin is taken: everything from its smallest key up
+        th.T = klo;
+        th.need_eq = c;
+        th.all = false;
+        return th;
+    }
+    const uint32_t span = khi1 - klo;
     if (c > kListCap) {
-        // heavy ties: exact radix select on the members of bin bstar
+        // heavy ties: exact radix select on the members of the bin
         uint32_t sub[ITEMS];
 #pragma unroll
-        for (int it = 0; it < ITEMS; ++it) sub[it] = (key[it] && bin(key[it]) == bstar) ? key[it] : 0u;
+        for (int it = 0; it < ITEMS; ++it) sub[it] = key[it] - klo < span ? key[it] : 0u;
         return wg_radix_select<NT, ITEMS>(sub, need, sm.radix, false);
     }
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
-        if (key[it] && bin(key[it]) == bstar) {
+        if (key[it] - klo < span) {
             const int p = atomicAdd(&sm.misc[2], 1);
             sm.list_key[p] = key[it];
             sm.list_slot[p] = slot_of<ITEMS>(it);
@@ -266,13 +352,13 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
             eq_before += before;
         }
         if (r == need - 1) {
-            sm.misc[3] = (int)kj;
-            sm.misc[4] = eq_before + 1;
+            sm.misc[6] = (int)kj;
+            sm.misc[7] = eq_before + 1;
         }
     }
     __syncthreads();
-    th.T = (uint32_t)sm.misc[3];
-    th.need_eq = sm.misc[4];
+    th.T = (uint32_t)sm.misc[6];
+    th.need_eq = sm.misc[7];
     th.all = false;
     return th;
 }
@@ -340,6 +426,190 @@ HISA_INLINE int wg_emit_selected(const uint32_t (&key)[ITEMS], const Threshold& 
         re += __popcll(be);
     }
     return min(limit, tg + min(te, th.need_eq));
+}
+
+// ---- wave-level select -------------------------------------------------------------
+// One wave selects alone, with no workgroup barrier: key[it] of lane l is
+// slot it*64 + l.  The same bucket idea on kWaveBins bins: count, range,
+// histogram in the wave's own LDS, the threshold bin found by a wave scan,
+// its members ranked exactly; more than 64 members (heavy ties) or
+// non-finite scores go to an 8-bit radix select.  LDS traffic of one wave
+// is ordered, so only compiler ordering fences separate the phases.
+
+constexpr int kWaveBins = 256;
+
+struct WaveSmem {
+    int hist[kWaveBins];
+    uint32_t list_key[64];
+    int list_slot[64];
+};
+
+// Exact n-th largest nonzero key by four 8-bit passes (n <= count of
+// nonzero keys), and how many of its copies to take.
+template <int ITEMS>
+HISA_INLINE Threshold wave_radix_select(const uint32_t (&key)[ITEMS], int n, WaveSmem& ws)
+{
+    const int lane = lane_id();
+    uint32_t prefix = 0u, mask = 0u;
+    int rem = n;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+#pragma unroll
+        for (int j = 0; j < kWaveBins / 64; ++j) ws.hist[lane + 64 * j] = 0;
+        wave_lds_fence();
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const uint32_t kk = key[it];
+            if (kk != 0u && (kk & mask) == prefix) atomicAdd(&ws.hist[(kk >> shift) & 255u], 1);
+        }
+        wave_lds_fence();
+        // lane l owns digits 255-4l .. 252-4l (descending)
+        int h[4], own = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            h[j] = ws.hist[255 - 4 * lane - j];
+            own += h[j];
+        }
+        const int cum = wave_incl_scan(own);
+        const int L = (int)__builtin_ctzll(__ballot(cum >= rem && cum - own < rem));
+        int above = __builtin_amdgcn_readlane(cum - own, L);
+        int digit = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int hj = __builtin_amdgcn_readlane(h[j], L);
+            if (digit == 0 && above + hj >= rem) digit = 255 - 4 * L - j + 1;   // +1: 0 means not found yet
+            else if (digit == 0) above += hj;
+        }
+        prefix |= (uint32_t)(digit - 1) << shift;
+        mask |= 0xffu << shift;
+        rem -= above;
+        wave_lds_fence();
+    }
+    Threshold th;
+    th.T = prefix;
+    th.need_eq = rem;
+    th.all = false;
+    return th;
+}
+
+// Select the n largest nonzero keys of the wave (equal keys: lower slot
+// first) and hand each to emit(slot, key, rank), rank in ascending slot
+// order.  Returns the number selected, min(n, number of nonzero keys).
+template <int ITEMS, class Emit>
+HISA_INLINE int wave_select(const uint32_t (&key)[ITEMS], int n, WaveSmem& ws, Emit emit)
+{
+    const int lane = lane_id();
+    const uint64_t lt = lanemask_lt();
+    if (n <= 0) return 0;
+    int nvalid = 0;
+    uint32_t kmax = 0u, kmin1 = 0xffffffffu;
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        nvalid += __popcll(__ballot(key[it] != 0u));
+        kmax = max(kmax, key[it]);
+        kmin1 = min(kmin1, key[it] - 1u);     // an empty slot wraps to the top
+    }
+    kmax = wave_max_u32(kmax);
+    const uint32_t kmin = wave_min_u32(kmin1) + 1u;
+    Threshold th;
+    th.all = false;
+    if (nvalid <= n || kmin == kmax) {
+        // every nonzero key, or the first n of all-equal keys
+        th.T = nvalid <= n ? 0u : kmin;
+        th.need_eq = nvalid <= n ? 0 : n;
+        th.all = nvalid <= n;
+    } else {
+        const float smin = key_score(kmin), smax = key_score(kmax);
+        const float range = smax - smin;
+        const float scale = (float)kWaveBins / range;
+        if (!(range > 0.f) || !__builtin_isfinite(range) || !__builtin_isfinite(scale)) {
+            th = wave_radix_select<ITEMS>(key, n, ws);
+        } else {
+            auto bin = [&](uint32_t kk) {
+                const float x = (key_score(max(kk, kmin)) - smin) * scale;   // >= 0, finite
+                return (int)min((uint32_t)x, (uint32_t)(kWaveBins - 1));
+            };
+#pragma unroll
+            for (int j = 0; j < kWaveBins / 64; ++j) ws.hist[lane + 64 * j] = 0;
+            wave_lds_fence();
+#pragma unroll
+            for (int it = 0; it < ITEMS; ++it)
+                if (key[it]) atomicAdd(&ws.hist[bin(key[it])], 1);
+            wave_lds_fence();
+            int h[4], own = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h[j] = ws.hist[kWaveBins - 1 - 4 * lane - j];
+                own += h[j];
+            }
+            const int cum = wave_incl_scan(own);
+            const int L = (int)__builtin_ctzll(__ballot(cum >= n && cum - own < n));
+            int above = __builtin_amdgcn_readlane(cum - own, L);
+            int bstar = -1, c = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int hj = __builtin_amdgcn_readlane(h[j], L);
+                if (bstar < 0 && above + hj >= n) {
+                    bstar = kWaveBins - 1 - 4 * L - j;
+                    c = hj;
+                } else if (bstar < 0) {
+                    above += hj;
+                }
+            }
+            const int need = n - above;        // 1 <= need <= c
+            if (c > 64) {
+                uint32_t sub[ITEMS];
+#pragma unroll
+                for (int it = 0; it < ITEMS; ++it) sub[it] = (key[it] && bin(key[it]) == bstar) ? key[it] : 0u;
+                th = wave_radix_select<ITEMS>(sub, need, ws);
+            } else {
+                // list the bin's members, then rank them in (key desc, slot asc) order
+                int base = 0;
+#pragma unroll
+                for (int it = 0; it < ITEMS; ++it) {
+                    const bool mem = key[it] && bin(key[it]) == bstar;
+                    const uint64_t b = __ballot(mem);
+                    if (mem) {
+                        const int p = base + __popcll(b & lt);
+                        ws.list_key[p] = key[it];
+                        ws.list_slot[p] = it * 64 + lane;
+                    }
+                    base += __popcll(b);
+                }
+                wave_lds_fence();
+                const uint32_t kj = lane < c ? ws.list_key[lane] : 0u;
+                const int sj = lane < c ? ws.list_slot[lane] : 0;
+                int r = 0, eq_before = 0;
+                for (int i = 0; i < c; ++i) {
+                    const uint32_t ki = ws.list_key[i];
+                    const bool before = ki == kj && ws.list_slot[i] < sj;
+                    r += (ki > kj) || before;
+                    eq_before += before;
+                }
+                const int J = (int)__builtin_ctzll(__ballot(lane < c && r == need - 1));
+                th.T = (uint32_t)__builtin_amdgcn_readlane((int)kj, J);
+                th.need_eq = __builtin_amdgcn_readlane(eq_before, J) + 1;
+                wave_lds_fence();
+            }
+        }
+    }
+    // emit in slot order: keys above T, then the first need_eq copies of T
+    const uint32_t lo = th.all ? 1u : th.T;
+    int rank = 0, eq = 0;
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const bool gt = th.all ? key[it] >= lo : key[it] > th.T;
+        const bool is_eq = !th.all && key[it] == th.T;
+        const uint64_t bg = __ballot(gt), be = __ballot(is_eq);
+        const int pe = eq + __popcll(be & lt);
+        const bool take = gt || (is_eq && pe < th.need_eq);
+        const uint64_t bt = __ballot(take);
+        if (take) emit(it * 64 + lane, key[it], rank + __popcll(bt & lt));
+        rank += __popcll(bt);
+        eq += __popcll(be);
+        (void)bg;
+    }
+    return rank;
 }
 
 }  // namespace hisa

@@ -412,10 +412,11 @@ def test_tie_bin_taken_whole():
 
 @pytest.mark.parametrize("force_fallback", [False, True])
 def test_many_queries_packed_sequences(force_fallback):
-    """Hundreds of queries spread over packed sequences of different
-    lengths: the block-major token stage groups (sequence, block) pairs.
-    With a declared max_len large enough that (sequences x blocks) passes
-    2^20 bins, the one-workgroup-per-query stage runs instead."""
+    """Hundreds of queries in random order over packed sequences of
+    different lengths: 16-query tiles span several sequences, so the MFMA
+    tile kernels walk one sequence at a time.  With a declared max_len of
+    more blocks than the stage-1 tile kernel holds, stage 1 scores into a
+    row per query and selects with one workgroup per query instead."""
     print("many packed queries fallback=%s" % force_fallback, flush=True)
     dv = _dev()
     nseq = 70 if force_fallback else 6
