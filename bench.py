@@ -34,6 +34,11 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak of one MI355X
+# where the library switches to its MFMA kernels (queries per call)
+TOKEN_TILES_FROM = 512          # token scores in 16-query MFMA tiles
+BLOCK_TILES_FROM = 256          # block scores in 16-query MFMA tiles
+FLAT_MFMA_FROM = 32             # flat scores in 16-query MFMA tiles
 
 WORKLOADS = ("decode_32k_x16", "chunked_prefill_32k", "long_context_128k", "long_decode_1m",
              "tiny_prefill_4k")
@@ -52,8 +57,7 @@ def hisa_stage_bytes(q_pos, B, m, k):
     """Algorithmic HBM bytes of the two HISA stages for queries at q_pos
     (d = 64: a key or representative row is 128 bytes).  Block stage: the
     query, its causal representatives, the kept-block list out.  Token
-    stage: the query, the kept list, the candidate keys, indices and scores
-    out."""
+    stage: the query, the kept list, the candidate keys, int32 indices out."""
     q_pos = np.asarray(q_pos, np.int64)
     nb = q_pos // B + 1                                  # causal blocks
     kept = np.minimum(nb, m)
@@ -62,21 +66,43 @@ def hisa_stage_bytes(q_pos, B, m, k):
         "block_stage": float((128 + nb * 128 + 2 * m * 4).sum()),
         # few queries: scores go to a workspace row, then the top-k reads it
         "token_scores": float((128 + m * 4 + cand * 128 + m * B * 4).sum()),
-        "token_topk": float(len(q_pos) * (m * B * 4 + m * 4 + k * 8)),
+        "token_topk": float(len(q_pos) * (m * B * 4 + m * 4 + k * 4)),
         # the token stage without the workspace round trip: query, kept
-        # list and candidate keys in, indices and scores out
-        "token_ideal": float((128 + m * 4 + cand * 128 + k * 8).sum()),
+        # list and candidate keys in, indices out
+        "token_ideal": float((128 + m * 4 + cand * 128 + k * 4).sum()),
     }
+
+
+def stage_flops(q_pos, B, m):
+    """Algorithmic flops of the contractions: 2*64 per (query, row) pair
+    over the causal representatives (block stage), the kept candidates
+    (token stage) and every visible key (flat scores)."""
+    q_pos = np.asarray(q_pos, np.int64)
+    nb = q_pos // B + 1
+    cand = np.minimum(np.minimum(nb, m) * B, q_pos + 1)
+    return {"block_stage": float(128 * nb.sum()), "token_scores": float(128 * cand.sum()),
+            "flat_scores": float(128 * (q_pos + 1).sum())}
+
+
+def stage_roofline(name, ms, nq, flops, nbytes):
+    """(bound, achieved, peak, unit, work per launch) of one stage: the
+    MFMA-tiled stages against the bf16 matrix peak, the rest against HBM."""
+    st = name.split("/")[-1]
+    mfma = ((st == "token_scores" and nq >= TOKEN_TILES_FROM) or (st == "block_stage" and nq >= BLOCK_TILES_FROM)
+            or (st == "flat_scores" and nq >= FLAT_MFMA_FROM))
+    if mfma:
+        return "mfma", flops / (ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", flops
+    return "hbm", nbytes / (ms * 1e-3) / 1e9, HBM_PEAK_GBPS, "GB/s", nbytes
 
 
 def flat_stage_bytes(q_pos, k):
     """Flat: the scores stage reads every visible key and writes its score;
-    the top-k stage reads the scores and writes indices and scores."""
+    the top-k stage reads the scores and writes int32 indices."""
     q_pos = np.asarray(q_pos, np.int64)
     n = q_pos + 1
     return {
         "flat_scores": float((n * 128 + 128 + n * 4).sum()),
-        "flat_topk": float((n * 4).sum() + len(n) * k * 8),
+        "flat_topk": float((n * 4).sum() + len(n) * k * 4),
     }
 
 
@@ -177,7 +203,7 @@ class Setup:
             calls = []
             for ph in self.phases:
                 ic = device_mod.IndexCall(c, ph.queries, ph.q_pos, ph.q_seq, k=self.k, m=self.m,
-                                          flat=flat, scores=True, blocks=not flat,
+                                          flat=flat, scores=False, blocks=False,
                                           one_chunk_limit=16 << 30)
                 per_rep = []
                 for r in range(replicas):
@@ -397,10 +423,17 @@ def main():
             stage_bytes["%s/%s" % (ph.name, nm)] = b
         for nm, b in flat_stage_bytes(ph.q_pos, S.k).items():
             stage_bytes["%s/%s" % (ph.name, nm)] = b
+    stage_fl, stage_nq = {}, {}
+    for ph in S.phases:
+        for nm, f in stage_flops(ph.q_pos, S.B, S.m).items():
+            stage_fl["%s/%s" % (ph.name, nm)] = f
+            stage_nq["%s/%s" % (ph.name, nm)] = len(ph.q_pos)
     kern = max((n for n in h_stage if n in stage_bytes), key=lambda n: h_stage[n])
-    achieved = stage_bytes[kern] / (h_stage[kern] * 1e-3) / 1e9
+    bound, achieved, peak, unit, work = stage_roofline(kern, h_stage[kern], stage_nq.get(kern, 0),
+                                                       stage_fl.get(kern, 0.0), stage_bytes[kern])
     fkern = max((n for n in f_stage if n in stage_bytes), key=lambda n: f_stage[n])
-    f_achieved = stage_bytes[fkern] / (f_stage[fkern] * 1e-3) / 1e9
+    fbound, f_achieved, fpeak, funit, _ = stage_roofline(fkern, f_stage[fkern], stage_nq.get(fkern, 0),
+                                                         stage_fl.get(fkern, 0.0), stage_bytes[fkern])
     # algorithmic bytes of a whole step: every stage's per-query traffic
     # (no workspace round trips) plus the append (new rows written, touched
     # blocks re-read, representatives written)
@@ -435,11 +468,12 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "description": S.desc, "queries_per_step": S.q_per_step,
+                   "outputs": "int32 top-k indices (the optional scores and kept-block lists are not requested)",
                    "replicas": R, "B": S.B, "m": S.m, "k": S.k},
-        "roofline": {"bound": "hbm", "kernel": kern, "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+        "roofline": {"bound": bound, "kernel": kern, "achieved": achieved, "peak": peak,
+                     "unit": unit, "frac": achieved / peak,
                      "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)), args.workload, kern),
-                     "algorithmic_bytes_per_launch": stage_bytes[kern],
+                     ("algorithmic_flops_per_launch" if bound == "mfma" else "algorithmic_bytes_per_launch"): work,
                      "avg_launch_ms": h_stage[kern]},
         "cpu_baseline": cpu,
         "step_bytes": h_step_bytes,
@@ -448,8 +482,8 @@ def main():
         "flat": {"value": fqps, "unit": "queries/s", "ms_per_step": f_ms, "kernels": per_kernel(f_stage),
                  "step_bytes": f_step_bytes,
                  "hbm_gbps_step": f_step_bytes / (f_ms * 1e-3) / 1e9,
-                 "dominant": {"kernel": fkern, "achieved_gbps": f_achieved,
-                              "frac": f_achieved / HBM_PEAK_GBPS}},
+                 "dominant": {"kernel": fkern, "bound": fbound, "achieved": f_achieved, "unit": funit,
+                              "frac": f_achieved / fpeak}},
         "speedup_vs_flat": f_ms / h_ms,
     }
     print(json.dumps(out), flush=True)

@@ -8,14 +8,25 @@ def test_stage_bytes_decode_32k():
     # one decode query at 32767: 256 representatives, 64 kept blocks of 128 keys
     b = bench.hisa_stage_bytes(np.array([32767]), 128, 64, 2048)
     assert b["block_stage"] == 128 + 256 * 128 + 2 * 64 * 4
-    assert b["token_ideal"] == 128 + 64 * 4 + 8192 * 128 + 2048 * 8
-    assert b["token_topk"] == 8192 * 4 + 64 * 4 + 2048 * 8
+    assert b["token_ideal"] == 128 + 64 * 4 + 8192 * 128 + 2048 * 4
+    assert b["token_topk"] == 8192 * 4 + 64 * 4 + 2048 * 4
     f = bench.flat_stage_bytes(np.array([32767, 32767]), 2048)
     assert f["flat_scores"] == 2 * (32768 * 132 + 128)
-    assert f["flat_topk"] == 2 * (32768 * 4 + 2048 * 8)
+    assert f["flat_topk"] == 2 * (32768 * 4 + 2048 * 4)
 
 
 def test_stage_bytes_early_queries_are_causal():
     b = bench.hisa_stage_bytes(np.array([0, 200]), 128, 64, 16)
     # query 0 sees one block and one key, query 200 two blocks and 201 keys
-    assert b["token_ideal"] == 2 * (128 + 64 * 4 + 16 * 8) + (1 + 201) * 128
+    assert b["token_ideal"] == 2 * (128 + 64 * 4 + 16 * 4) + (1 + 201) * 128
+
+
+def test_stage_flops_and_bound():
+    f = bench.stage_flops(np.array([32767, 200]), 128, 64)
+    assert f["block_stage"] == 128 * (256 + 2)
+    assert f["token_scores"] == 128 * (8192 + 201)
+    assert f["flat_scores"] == 128 * (32768 + 201)
+    # few queries: HBM; many: the MFMA tiles
+    assert bench.stage_roofline("d/token_scores", 1.0, 16, 1e9, 1e6)[0] == "hbm"
+    b, a, p, u, w = bench.stage_roofline("p/token_scores", 1.0, 4096, 1e12, 1e6)
+    assert (b, u, w) == ("mfma", "TFLOP/s", 1e12) and abs(a - 1000.0) < 1e-9
