@@ -92,9 +92,11 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double v)
 
 __device__ __forceinline__ uint32_t score_key(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return key == 0u ? 1u : key;
+    // negative: invert every bit; otherwise set the top bit.  Key 0 stays
+    // free for "no candidate" (only the all-ones NaN would map to it).
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+    return max(key, 1u);
 }
 
 __device__ __forceinline__ float key_score(uint32_t key)

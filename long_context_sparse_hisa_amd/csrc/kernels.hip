@@ -552,6 +552,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
         const bool mine = active && ri.key_off == koff;
         pending &= ~__ballot(mine);
         const int tmax = (int)wave_max_u32(mine ? (uint32_t)t32 : 0u);
+        const int tmin = (int)wave_min_u32(mine ? (uint32_t)t32 : 0xffffffffu);
         const int tm = mine ? t32 : -1;
         int cur = first;
         int nxt = mine ? lst[first] : kTileEnd;
@@ -569,35 +570,52 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
             }
             const int pq = __shfl(pos, col);           // -1 unless row `col` kept b
             const uint16_t* kb = keys + (koff + ((int64_t)b << LB)) * kDim + 8 * kg;
+            const int bend = ((b + 1) << LB) - 1;     // last token of block b
             bf16x8_t k0[KT], k1[KT];
+            if (bend <= tmax) {                       // every key of the block exists
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                const int jj = kt * 16 + col;
-                k0[kt] = bf16x8_t{};
-                k1[kt] = bf16x8_t{};
-                if ((b << LB) + jj <= tmax) {
+                for (int kt = 0; kt < KT; ++kt) {
+                    const int jj = kt * 16 + col;
                     k0[kt] = *reinterpret_cast<const bf16x8_t*>(kb + jj * kDim);
                     k1[kt] = *reinterpret_cast<const bf16x8_t*>(kb + jj * kDim + 32);
                 }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) {
+                    const int jj = kt * 16 + col;
+                    k0[kt] = bf16x8_t{};
+                    k1[kt] = bf16x8_t{};
+                    if ((b << LB) + jj <= tmax) {
+                        k0[kt] = *reinterpret_cast<const bf16x8_t*>(kb + jj * kDim);
+                        k1[kt] = *reinterpret_cast<const bf16x8_t*>(kb + jj * kDim + 32);
+                    }
+                }
             }
             const int bn = (int)wave_min_u32((uint32_t)nxt);
-            uint32_t* urow = ukeys + (row0 + col) * N + ((int64_t)(pq < 0 ? 0 : pq) << LB);
+            const bool seen = bend <= tmin;           // no walked row masks a token of b
+            // keys as the A operand: lane l receives keys 4*(l/16)..+4 of
+            // each 16-key tile for query row l%16.  The KT tiles are
+            // independent accumulations, issued back to back.
+            f32x4_t c[KT];
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                // keys as the A operand: lane l receives keys 4*(l/16)..+4 of
-                // the 16-key tile for query row l%16
-                f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[kt], a0, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[kt], a1, c, 0, 0, 0);
-                const int jj = kt * 16 + 4 * kg;
-                const int j = (b << LB) + jj;
-                if (pq >= 0) {
-                    uint4 o;
-                    o.x = j + 0 <= tq ? score_key(c[0]) : 0u;
-                    o.y = j + 1 <= tq ? score_key(c[1]) : 0u;
-                    o.z = j + 2 <= tq ? score_key(c[2]) : 0u;
-                    o.w = j + 3 <= tq ? score_key(c[3]) : 0u;
-                    *reinterpret_cast<uint4*>(urow + jj) = o;
+            for (int kt = 0; kt < KT; ++kt)
+                c[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[kt], a0, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) c[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[kt], a1, c[kt], 0, 0, 0);
+            if (pq >= 0) {
+                uint32_t* urow = ukeys + (row0 + col) * N + ((int64_t)pq << LB) + 4 * kg;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) {
+                    uint4 o = make_uint4(score_key(c[kt][0]), score_key(c[kt][1]), score_key(c[kt][2]),
+                                         score_key(c[kt][3]));
+                    if (!seen) {
+                        const int j = (b << LB) + kt * 16 + 4 * kg;
+                        o.x = j + 0 <= tq ? o.x : 0u;
+                        o.y = j + 1 <= tq ? o.y : 0u;
+                        o.z = j + 2 <= tq ? o.z : 0u;
+                        o.w = j + 3 <= tq ? o.w : 0u;
+                    }
+                    *reinterpret_cast<uint4*>(urow + kt * 16) = o;
                 }
             }
             b = bn;
