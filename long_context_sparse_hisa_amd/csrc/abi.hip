@@ -184,7 +184,7 @@ int hisa_pool_blocks(const uint16_t* keys, int64_t L, int d, int B, uint16_t* re
     if (d != 64 || !valid_B(B)) return HISA_ERR_UNSUPPORTED;
     if (L == 0) return HISA_OK;
     if (!keys || !reps) return HISA_ERR_INVALID_ARG;
-    PoolJob job{0, 0, L, L, 0, 0, (L + B - 1) / B};
+    PoolJob job{0, 0, (int32_t)L, (int32_t)L, 0, 0, (int32_t)((L + B - 1) / B), 0};
     return status_of(launch_pool(const_cast<uint16_t*>(keys), reps, nullptr, B, &job, 1,
                                  static_cast<hipStream_t>(stream)));
 }
@@ -196,6 +196,7 @@ int hisa_append_keys(uint16_t* keys, uint16_t* reps, const hisa_seq* seqs, int n
     if (d != 64 || !valid_B(B)) return HISA_ERR_UNSUPPORTED;
     if (nseq == 0 || n_new == 0) return HISA_OK;
     if (!keys || !reps || !seqs || !new_keys) return HISA_ERR_INVALID_ARG;
+    if (n_new > HISA_MAX_LEN || (int64_t)nseq * n_new > INT32_MAX) return HISA_ERR_INVALID_ARG;
     for (int s = 0; s < nseq; ++s) {
         const hisa_seq& q = seqs[s];
         if (q.key_off < 0 || q.rep_off < 0 || q.len < 0 || q.capacity > HISA_MAX_LEN) return HISA_ERR_INVALID_ARG;
@@ -208,8 +209,8 @@ int hisa_append_keys(uint16_t* keys, uint16_t* reps, const hisa_seq* seqs, int n
             const hisa_seq& q = seqs[base + i];
             const int64_t first = q.len / B;
             const int64_t last = (q.len + n_new - 1) / B;
-            jobs[i] = PoolJob{q.key_off, q.rep_off, q.len, q.len + n_new, (int64_t)(base + i) * n_new, first,
-                              last - first + 1};
+            jobs[i] = PoolJob{q.key_off, q.rep_off, (int32_t)q.len, (int32_t)(q.len + n_new),
+                              (int32_t)((int64_t)(base + i) * n_new), (int32_t)first, (int32_t)(last - first + 1), 0};
         }
         const hipError_t err = launch_pool(keys, reps, new_keys, B, jobs, n, static_cast<hipStream_t>(stream));
         if (err != hipSuccess) return HISA_ERR_HIP;

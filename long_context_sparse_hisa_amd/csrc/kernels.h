@@ -28,14 +28,17 @@ struct RowInfo {
 struct PoolJob {
     int64_t key_off;    // first key row of the sequence
     int64_t rep_off;    // first representative row
-    int64_t len_old;    // keys already in the cache
-    int64_t len_new;    // keys after the append (== len_old for plain pooling)
-    int64_t new_row;    // row of this sequence's first key in new_keys
-    int64_t blk_first;  // first block to (re)compute
-    int64_t nblk;       // blocks to (re)compute
+    int32_t len_old;    // keys already in the cache
+    int32_t len_new;    // keys after the append (== len_old for plain pooling)
+    int32_t new_row;    // row of this sequence's first key in new_keys
+    int32_t blk_first;  // first block to (re)compute
+    int32_t nblk;       // blocks to (re)compute
+    int32_t pad;
 };
 
-constexpr int kPoolJobsPerLaunch = 16;
+// Jobs travel in the kernel arguments (96 x 40 bytes, inside the 4 KiB
+// argument limit), so a decode step of up to 96 sequences is one launch.
+constexpr int kPoolJobsPerLaunch = 96;
 
 hipError_t launch_pool(uint16_t* keys, uint16_t* reps, const uint16_t* new_keys, int B, const PoolJob* jobs,
                        int njobs, hipStream_t stream);

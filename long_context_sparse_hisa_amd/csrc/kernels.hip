@@ -126,8 +126,8 @@ hipError_t launch_pool(uint16_t* keys, uint16_t* reps, const uint16_t* new_keys,
         PoolJobs pj;
         int64_t maxblk = 0;
         for (int i = 0; i < kPoolJobsPerLaunch; ++i) {
-            pj.j[i] = i < n ? jobs[base + i] : PoolJob{0, 0, 0, 0, 0, 0, 0};
-            if (i < n) maxblk = std::max(maxblk, pj.j[i].nblk);
+            pj.j[i] = i < n ? jobs[base + i] : PoolJob{0, 0, 0, 0, 0, 0, 0, 0};
+            if (i < n) maxblk = std::max<int64_t>(maxblk, pj.j[i].nblk);
         }
         if (maxblk == 0) continue;
         const hipError_t err = launch_k(pool_kernel, dim3((unsigned)maxblk, (unsigned)n), dim3(kThreads), stream,

@@ -282,6 +282,19 @@ def test_decode_32k_x16_full():
         _check_phase(w, cache, w.phases[0], w.k, w.m, flat, label="cfg2")
 
 
+def test_decode_32k_x256_batch():
+    """The decode step at 256 sequences (the batch sweep's largest point):
+    the stage-1 MFMA tiles, the split token stage and the many-row top-k
+    shapes, every query checked."""
+    print("decode 32K x256", flush=True)
+    dv = _dev()
+    w = synth.decode_batch(nseq=256)
+    cache = dv.DeviceCache(w)
+    cache.pool()
+    for flat in (False, True):
+        _check_phase(w, cache, w.phases[0], w.k, w.m, flat, label="dec256")
+
+
 def test_chunked_prefill_32k_sampled():
     print("chunked prefill 32K", flush=True)
     dv = _dev()
