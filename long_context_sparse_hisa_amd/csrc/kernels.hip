@@ -446,7 +446,13 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
 // Few queries: kStage2SlotsPerWg slots of one query per workgroup, scored
 // into ukeys so that few queries still fill the chip.  Slot s is row s % B
 // of kept block s / B; slots of -1 blocks and keys after the query get
-// key 0.  The top-k follows in topk_rows_kernel.
+// key 0.  Eight lanes share a candidate row, each reading 16 of its 128
+// bytes, so every wave load is 1 KiB of whole rows; the eight partial dots
+// are summed across the lanes with DPP.  The top-k follows in
+// topk_rows_kernel.
+constexpr int kScoreRowsPerPass = kThreads / 8;
+constexpr int kScorePasses = kStage2SlotsPerWg / kScoreRowsPerPass;
+
 __global__ __launch_bounds__(kThreads) void stage2_score_kernel(const uint16_t* queries, const uint16_t* keys,
                                                                 int64_t q0, int lb, int m, const RowInfo* rinfo,
                                                                 const int32_t* sel, uint32_t* ukeys)
@@ -455,21 +461,39 @@ __global__ __launch_bounds__(kThreads) void stage2_score_kernel(const uint16_t* 
     const int N = m << lb;
     const int32_t* srow = sel + row * m;
     uint32_t* urow = ukeys + row * N;
-    const int beg = blockIdx.y * kStage2SlotsPerWg;
-    const int end = min(N, beg + kStage2SlotsPerWg);
+    const int sub = threadIdx.x & 7;              // which 16 bytes of a row
+    const int grp = threadIdx.x >> 3;             // which row of a pass
+    const int beg = blockIdx.y * kStage2SlotsPerWg + grp;
     const RowInfo ri = rinfo[row];
-    if (ri.t < 0) {
-        for (int s = beg + threadIdx.x; s < end; s += kThreads) urow[s] = 0u;
-        return;
+    const uint4 qv = reinterpret_cast<const uint4*>(queries + (q0 + row) * kDim)[sub];
+    // two round trips, no branches: every pass's list entry, then every
+    // pass's key part (row 0 of the sequence stands in for a masked slot)
+    int32_t blk[kScorePasses];
+#pragma unroll
+    for (int p = 0; p < kScorePasses; ++p) blk[p] = srow[min(beg + p * kScoreRowsPerPass, N - 1) >> lb];
+    uint4 v[kScorePasses];
+    bool ok[kScorePasses];
+#pragma unroll
+    for (int p = 0; p < kScorePasses; ++p) {
+        const int s = beg + p * kScoreRowsPerPass;
+        const int64_t j = ((int64_t)blk[p] << lb) + (s & ((1 << lb) - 1));
+        ok[p] = s < N && blk[p] >= 0 && j <= ri.t;
+        v[p] = reinterpret_cast<const uint4*>(keys + (ri.key_off + (ok[p] ? j : 0)) * kDim)[sub];
     }
-    uint32_t q[32];
-    load_query(queries + (q0 + row) * kDim, q);
-    for (int s = beg + threadIdx.x; s < end; s += kThreads) {
-        const int32_t blk = srow[s >> lb];
-        const int64_t j = ((int64_t)blk << lb) + (s & ((1 << lb) - 1));
-        urow[s] = (blk >= 0 && j <= ri.t)
-                      ? score_key(dot64_packed(q, reinterpret_cast<const uint4*>(keys + (ri.key_off + j) * kDim)))
-                      : 0u;
+#pragma unroll
+    for (int p = 0; p < kScorePasses; ++p) {
+        if (!ok[p]) v[p] = make_uint4(0u, 0u, 0u, 0u);
+        float acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv.x), as_bf16x2(v[p].x), 0.f, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv.y), as_bf16x2(v[p].y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv.z), as_bf16x2(v[p].z), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv.w), as_bf16x2(v[p].w), acc, false);
+        // sum over the 8 lanes of the row: xor 1 and 2 inside quads, then the
+        // other quad (row_ror:4); lanes 8r hold the total
+        acc += __uint_as_float(dpp_u32<0xb1>(__float_as_uint(acc)));
+        acc += __uint_as_float(dpp_u32<0x4e>(__float_as_uint(acc)));
+        acc += __uint_as_float(dpp_u32<0x124>(__float_as_uint(acc)));
+        const int s = beg + p * kScoreRowsPerPass;
+        if (sub == 0 && s < N) urow[s] = ok[p] ? score_key(acc) : 0u;
     }
 }
 
