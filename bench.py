@@ -48,6 +48,15 @@ DECODE_BATCH = {"decode_32k_x16": 16, "decode_32k_x64": 64, "decode_32k_x256": 2
 
 STAGES_HISA = ("block_stage", "token_scores", "token_topk")
 STAGES_FLAT = ("flat_scores", "flat_topk")
+SPLIT_BELOW = 512               # fewer queries: the token stage splits each query over workgroups
+FUSED_MAX_BLOCKS = 2048         # ... and with at most this many blocks stage 1 joins it in one kernel
+
+
+def hisa_stage_names(nq, max_len, B):
+    """Stage index -> name for one HISA call (the library's stage events)."""
+    if nq < SPLIT_BELOW and (max_len + B - 1) // B <= FUSED_MAX_BLOCKS:
+        return {1: "select_and_scores", 2: "token_topk"}
+    return dict(enumerate(STAGES_HISA))
 
 
 def log(*a):
@@ -70,6 +79,8 @@ def hisa_stage_bytes(q_pos, B, m, k):
         # few queries: scores go to a workspace row, then the top-k reads it
         "token_scores": float((128 + m * 4 + cand * 128 + m * B * 4).sum()),
         "token_topk": float(len(q_pos) * (m * B * 4 + m * 4 + k * 4)),
+        # stage 1 and the token scores as one kernel (few queries)
+        "select_and_scores": float((128 + nb * 128 + 2 * m * 4).sum() + (128 + m * 4 + cand * 128 + m * B * 4).sum()),
         # the token stage without the workspace round trip: query, kept
         # list and candidate keys in, indices out
         "token_ideal": float((128 + m * 4 + cand * 128 + k * 4).sum()),
@@ -115,6 +126,7 @@ def flat_stage_bytes(q_pos, k):
 STAGE_KERNEL = {"block_stage": ("stage1_select_kernel",),
                 "token_scores": ("stage2_score_kernel", "stage2_tile_kernel"),
                 "token_topk": ("topk_rows_kernel",),
+                "select_and_scores": ("decode_fused_kernel",),
                 "flat_scores": ("flat_score_kernel", "flat_score_mfma_kernel")}
 
 
@@ -199,6 +211,7 @@ class Setup:
         torch.cuda.synchronize()
         self.phases = w.phases if name != "long_decode_1m" else w.phases[:1]
         self.B, self.m, self.k = w.B, w.m, w.k
+        self.max_len = int(c.seq_cap.max())
         # replicas (cold-cache rotation)
         self.keys = [c.keys] + [c.keys.clone() for _ in range(replicas - 1)]
         self.reps = [c.reps] + [c.reps.clone() for _ in range(replicas - 1)]
@@ -304,8 +317,9 @@ def stage_times(S, flat, nsteps, torch):
     torch.cuda.synchronize()
     out = {}
     for p in range(nph):
-        names = STAGES_FLAT if flat else STAGES_HISA
-        for s_, nm in enumerate(names):
+        ph = S.phases[p]
+        names = dict(enumerate(STAGES_FLAT)) if flat else hisa_stage_names(len(ph.q_pos), S.max_len, S.B)
+        for s_, nm in names.items():
             vals = [evs[i][p].stage_ms(s_) for i in range(nsteps)]
             out["%s/%s" % (S.phases[p].name, nm)] = float(np.mean(vals))
     if app:

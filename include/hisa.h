@@ -155,8 +155,10 @@ typedef struct hisa_index_args {
                                     when the first kernel of stage s starts and its last kernel
                                     ends, for the call's last query chunk, from the dispatch
                                     itself.  HISA stages: 0 block scores and top-m; 1 token
-                                    scores; 2 token top-k.  Flat stages: 0 scores, 1 top-k
-                                    (2 not recorded). */
+                                    scores; 2 token top-k.  With fewer than 512 queries and
+                                    at most 2048 blocks, stages 0 and 1 are one kernel,
+                                    recorded as stage 1 (0 not recorded).  Flat stages:
+                                    0 scores, 1 top-k (2 not recorded). */
 } hisa_index_args;
 
 #define HISA_STAGES 3

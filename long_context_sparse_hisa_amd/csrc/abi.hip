@@ -251,15 +251,23 @@ int hisa_index(const hisa_index_args* a, void* stream_)
     for (int64_t q0 = 0; q0 < a->nq; q0 += chunk) {
         const int64_t nc = std::min(chunk, a->nq - q0);
         const bool last = q0 + nc >= a->nq;
-        hipError_t err = launch_stage1(qm, a->reps, q0, nc, lb, a->m, Mmax, sigma, sel, rinfo, a->out_blocks, stream,
-                                       stage_timing(a, last, 0));
-        // token scores into ukeys: few queries split each row over several
-        // workgroups, many queries share key loads 16 at a time on the MFMA
-        if (err == hipSuccess)
-            err = split ? launch_stage2_split_scores(qm, a->keys, q0, nc, lb, a->m, rinfo, sel, ukeys, stream,
-                                                     stage_timing(a, last, 1))
-                        : launch_stage2_tile_scores(qm, a->keys, q0, nc, lb, a->m, Mmax, rinfo, sel, ukeys, stream,
-                                                    stage_timing(a, last, 1));
+        hipError_t err;
+        if (split && Mmax <= kStage1FusedMax) {
+            // few queries, few blocks: stage 1 and the token scores in one
+            // launch (recorded as stage 1)
+            err = launch_decode_fused(qm, a->reps, a->keys, q0, nc, lb, a->m, Mmax, sel, rinfo, a->out_blocks, ukeys,
+                                      stream, stage_timing(a, last, 1));
+        } else {
+            err = launch_stage1(qm, a->reps, q0, nc, lb, a->m, Mmax, sigma, sel, rinfo, a->out_blocks, stream,
+                                stage_timing(a, last, 0));
+            // token scores into ukeys: few queries split each row over several
+            // workgroups, many queries share key loads 16 at a time on the MFMA
+            if (err == hipSuccess)
+                err = split ? launch_stage2_split_scores(qm, a->keys, q0, nc, lb, a->m, rinfo, sel, ukeys, stream,
+                                                         stage_timing(a, last, 1))
+                            : launch_stage2_tile_scores(qm, a->keys, q0, nc, lb, a->m, Mmax, rinfo, sel, ukeys,
+                                                        stream, stage_timing(a, last, 1));
+        }
         if (err == hipSuccess)
             err = launch_topk_small(ukeys, nc, a->m << lb, a->k, sel, a->m, lb, a->out_idx + q0 * a->k,
                                     a->out_scores ? a->out_scores + q0 * a->k : nullptr, stream,

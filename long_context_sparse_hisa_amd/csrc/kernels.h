@@ -72,6 +72,13 @@ hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, 
                                      int64_t Mmax, const RowInfo* rinfo, const int32_t* sel, uint32_t* ukeys,
                                      hipStream_t stream, Timing t = {});
 
+// Few queries with at most kStage1FusedMax blocks: stage 1 and the token
+// scores of stage 2 in one launch (every workgroup of a query selects the
+// kept blocks itself); writes sel, rinfo, out_blocks and ukeys.
+hipError_t launch_decode_fused(const QueryMeta& qm, const uint16_t* reps, const uint16_t* keys, int64_t q0,
+                               int64_t nq, int lb, int m, int64_t Mmax, int32_t* sel, RowInfo* rinfo,
+                               int32_t* out_blocks, uint32_t* ukeys, hipStream_t stream, Timing t = {});
+
 // HISA stage 2 for few queries: kStage2SlotsPerWg candidate slots per
 // workgroup scored into ukeys [nq, m*B]; launch_topk_small then selects.
 constexpr int kStage2SlotsPerWg = 512;

@@ -453,32 +453,29 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
 constexpr int kScoreRowsPerPass = kThreads / 8;
 constexpr int kScorePasses = kStage2SlotsPerWg / kScoreRowsPerPass;
 
-__global__ __launch_bounds__(kThreads) void stage2_score_kernel(const uint16_t* queries, const uint16_t* keys,
-                                                                int64_t q0, int lb, int m, const RowInfo* rinfo,
-                                                                const int32_t* sel, uint32_t* ukeys)
+// The slots of this workgroup: kept(i) gives entry i of the row's kept list.
+// Two round trips when the list is in memory, no branches: every pass's
+// list entry, then every pass's key part (row 0 of the sequence stands in
+// for a masked slot).
+template <class Kept>
+HISA_INLINE void score_slots(const uint16_t* qrow, const uint16_t* keys, int64_t key_off, int64_t t, int lb, int N,
+                             Kept kept, uint32_t* urow)
 {
-    const int64_t row = blockIdx.x;
-    const int N = m << lb;
-    const int32_t* srow = sel + row * m;
-    uint32_t* urow = ukeys + row * N;
     const int sub = threadIdx.x & 7;              // which 16 bytes of a row
     const int grp = threadIdx.x >> 3;             // which row of a pass
     const int beg = blockIdx.y * kStage2SlotsPerWg + grp;
-    const RowInfo ri = rinfo[row];
-    const uint4 qv = reinterpret_cast<const uint4*>(queries + (q0 + row) * kDim)[sub];
-    // two round trips, no branches: every pass's list entry, then every
-    // pass's key part (row 0 of the sequence stands in for a masked slot)
+    const uint4 qv = reinterpret_cast<const uint4*>(qrow)[sub];
     int32_t blk[kScorePasses];
 #pragma unroll
-    for (int p = 0; p < kScorePasses; ++p) blk[p] = srow[min(beg + p * kScoreRowsPerPass, N - 1) >> lb];
+    for (int p = 0; p < kScorePasses; ++p) blk[p] = kept(min(beg + p * kScoreRowsPerPass, N - 1) >> lb);
     uint4 v[kScorePasses];
     bool ok[kScorePasses];
 #pragma unroll
     for (int p = 0; p < kScorePasses; ++p) {
         const int s = beg + p * kScoreRowsPerPass;
         const int64_t j = ((int64_t)blk[p] << lb) + (s & ((1 << lb) - 1));
-        ok[p] = s < N && blk[p] >= 0 && j <= ri.t;
-        v[p] = reinterpret_cast<const uint4*>(keys + (ri.key_off + (ok[p] ? j : 0)) * kDim)[sub];
+        ok[p] = s < N && blk[p] >= 0 && j <= t;
+        v[p] = reinterpret_cast<const uint4*>(keys + (key_off + (ok[p] ? j : 0)) * kDim)[sub];
     }
 #pragma unroll
     for (int p = 0; p < kScorePasses; ++p) {
@@ -487,14 +484,105 @@ __global__ __launch_bounds__(kThreads) void stage2_score_kernel(const uint16_t* 
         acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv.y), as_bf16x2(v[p].y), acc, false);
         acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv.z), as_bf16x2(v[p].z), acc, false);
         acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv.w), as_bf16x2(v[p].w), acc, false);
-        // sum over the 8 lanes of the row: xor 1 and 2 inside quads, then the
-        // other quad (row_ror:4); lanes 8r hold the total
+        // sum over the 8 lanes of the row: xor 1 and 2 inside quads (DPP
+        // quad_perm), then xor 4; every lane of the row holds the total
         acc += __uint_as_float(dpp_u32<0xb1>(__float_as_uint(acc)));
         acc += __uint_as_float(dpp_u32<0x4e>(__float_as_uint(acc)));
-        acc += __uint_as_float(dpp_u32<0x124>(__float_as_uint(acc)));
+        acc += __shfl_xor(acc, 4);
         const int s = beg + p * kScoreRowsPerPass;
         if (sub == 0 && s < N) urow[s] = ok[p] ? score_key(acc) : 0u;
     }
+}
+
+__global__ __launch_bounds__(kThreads) void stage2_score_kernel(const uint16_t* queries, const uint16_t* keys,
+                                                                int64_t q0, int lb, int m, const RowInfo* rinfo,
+                                                                const int32_t* sel, uint32_t* ukeys)
+{
+    const int64_t row = blockIdx.x;
+    const int N = m << lb;
+    const int32_t* srow = sel + row * m;
+    const RowInfo ri = rinfo[row];
+    score_slots(queries + (q0 + row) * kDim, keys, ri.key_off, ri.t, lb, N, [&](int i) { return srow[i]; },
+                ukeys + row * N);
+}
+
+// Few queries with at most kStage1FusedMax blocks: stage 1 and the token
+// scores in one launch.  Every workgroup of a query scores the causal
+// representatives (v_dot2 GEMV) and selects the kept blocks itself - the
+// same selection in each, a few KiB of L2 reads - then scores its own
+// slots from the list in LDS.  Workgroup 0 of the query also writes the
+// kept list, the row info and out_blocks.
+template <int ITEMS>
+__global__ __launch_bounds__(kThreads) void decode_fused_kernel(QueryMeta qm, const uint16_t* reps,
+                                                                const uint16_t* keys, int64_t q0, int lb, int m,
+                                                                int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
+                                                                uint32_t* ukeys)
+{
+    __shared__ BucketSmem<kThreads> sm;
+    __shared__ int32_t s_kept[kMaxKept];
+    const int64_t row = blockIdx.x;
+    const int64_t i = q0 + row;
+    const QueryInfo qi =
+        query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
+    const int64_t c = qi.valid ? qi.t >> lb : -1;
+    if (!qi.valid || c + 1 <= m) {
+        for (int r = threadIdx.x; r < m; r += kThreads) s_kept[r] = r <= c ? r : -1;
+    } else {
+        uint32_t q[32];
+        load_query(qm.queries + i * kDim, q);
+        uint32_t key[ITEMS];
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int64_t b = slot_of<ITEMS>(it);
+            key[it] = (b >= 1 && b <= c - 2)
+                          ? score_key(dot64_packed(q, reinterpret_cast<const uint4*>(reps + (qi.rep_off + b) * kDim)))
+                          : 0u;
+        }
+        const Threshold th = wg_bucket_select<kThreads, ITEMS>(key, m - 3, sm);
+        wg_emit_selected<kThreads, ITEMS>(key, th, sm, m - 3, [&](int slot, uint32_t, int rank) { s_kept[1 + rank] = slot; });
+        if (threadIdx.x == 0) {
+            s_kept[0] = 0;
+            s_kept[m - 2] = (int32_t)(c - 1);
+            s_kept[m - 1] = (int32_t)c;
+        }
+    }
+    __syncthreads();
+    if (blockIdx.y == 0) {
+        if (threadIdx.x == 0) rinfo[row] = RowInfo{qi.key_off, qi.valid ? qi.t : -1};
+        for (int r = threadIdx.x; r < m; r += kThreads) {
+            sel[row * m + r] = s_kept[r];
+            if (out_blocks) out_blocks[i * m + r] = s_kept[r];
+        }
+    }
+    const int N = m << lb;
+    score_slots(qm.queries + i * kDim, keys, qi.key_off, qi.valid ? qi.t : -1, lb, N,
+                [&](int e) { return s_kept[e]; }, ukeys + row * N);
+}
+
+template <int ITEMS>
+static hipError_t launch_decode_fused_items(const QueryMeta& qm, const uint16_t* reps, const uint16_t* keys,
+                                            int64_t q0, int64_t nq, int lb, int m, int32_t* sel, RowInfo* rinfo,
+                                            int32_t* out_blocks, uint32_t* ukeys, hipStream_t stream, Timing t)
+{
+    const int N = m << lb;
+    const dim3 grid((unsigned)nq, (unsigned)((N + kStage2SlotsPerWg - 1) / kStage2SlotsPerWg));
+    return launch_k(decode_fused_kernel<ITEMS>, grid, dim3(kThreads), stream, t.start, t.stop, qm, reps, keys, q0, lb,
+                    m, sel, rinfo, out_blocks, ukeys);
+}
+
+hipError_t launch_decode_fused(const QueryMeta& qm, const uint16_t* reps, const uint16_t* keys, int64_t q0,
+                               int64_t nq, int lb, int m, int64_t Mmax, int32_t* sel, RowInfo* rinfo,
+                               int32_t* out_blocks, uint32_t* ukeys, hipStream_t stream, Timing t)
+{
+    const int64_t per = (Mmax + kThreads - 1) / kThreads;
+#define HISA_DF(N_) \
+    if (per <= N_) return launch_decode_fused_items<N_>(qm, reps, keys, q0, nq, lb, m, sel, rinfo, out_blocks, ukeys, stream, t)
+    HISA_DF(1);
+    HISA_DF(2);
+    HISA_DF(4);
+    HISA_DF(8);
+#undef HISA_DF
+    return hipErrorInvalidValue;
 }
 
 // Many queries: tiles of 16 consecutive query rows on the bf16 MFMA
