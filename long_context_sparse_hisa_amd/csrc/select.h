@@ -340,20 +340,42 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
     __syncthreads();
     // rank of member j in (key desc, slot asc) order; the member of rank
     // need-1 is the threshold key, and the equal keys before it plus itself
-    // are the copies of it to take
-    for (int j = threadIdx.x; j < c; j += NT) {
-        const uint32_t kj = sm.list_key[j];
-        const int sj = sm.list_slot[j];
-        int r = 0, eq_before = 0;
-        for (int i = 0; i < c; ++i) {
-            const uint32_t ki = sm.list_key[i];
-            const bool before = ki == kj && sm.list_slot[i] < sj;
-            r += (ki > kj) || before;
-            eq_before += before;
+    // are the copies of it to take.  Up to 64 members: wave 0 holds one per
+    // lane and compares against the others by readlane, without LDS round
+    // trips; more: every thread ranks its members from LDS.
+    if (c <= 64) {
+        if (wave_id() == 0) {
+            const int l = lane_id();
+            const uint32_t kj = l < c ? sm.list_key[l] : 0u;
+            const int sj = l < c ? sm.list_slot[l] : 0;
+            int r = 0, eq_before = 0;
+            for (int i = 0; i < c; ++i) {
+                const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)kj, i);
+                const int si = __builtin_amdgcn_readlane(sj, i);
+                const bool before = ki == kj && si < sj;
+                r += (ki > kj) || before;
+                eq_before += before;
+            }
+            if (l < c && r == need - 1) {
+                sm.misc[6] = (int)kj;
+                sm.misc[7] = eq_before + 1;
+            }
         }
-        if (r == need - 1) {
-            sm.misc[6] = (int)kj;
-            sm.misc[7] = eq_before + 1;
+    } else {
+        for (int j = threadIdx.x; j < c; j += NT) {
+            const uint32_t kj = sm.list_key[j];
+            const int sj = sm.list_slot[j];
+            int r = 0, eq_before = 0;
+            for (int i = 0; i < c; ++i) {
+                const uint32_t ki = sm.list_key[i];
+                const bool before = ki == kj && sm.list_slot[i] < sj;
+                r += (ki > kj) || before;
+                eq_before += before;
+            }
+            if (r == need - 1) {
+                sm.misc[6] = (int)kj;
+                sm.misc[7] = eq_before + 1;
+            }
         }
     }
     __syncthreads();
