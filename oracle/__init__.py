@@ -57,6 +57,10 @@ def _load():
             lib.oracle_hisa_query.argtypes = [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32,
                                               _P, _P, _P, _P]
             lib.oracle_flat_query.argtypes = [_P, _P, _I64, _I64, _I32, _I32, _P, _P, _P]
+            lib.oracle_attention_row.argtypes = [_P, _P, _P, _I64, _I32, _P, _I32, ctypes.c_double, _P]
+            lib.oracle_attention_row.restype = _I32
+            lib.oracle_attention_batch.argtypes = [_P, _P, _P, _I64, _I32, _P, _P, _P, _I32,
+                                                   ctypes.c_double, _P]
             lib.oracle_index_batch.argtypes = [_I32, _P, _P, _P, _I64, _P, _P, _P, _P, _P,
                                                _I32, _I32, _I32, _I32, _I32, _P, _P, _P]
             lib.oracle_bf16_round.argtypes = [ctypes.c_double]
@@ -210,3 +214,29 @@ def index_batch(flat: bool, queries, q_pos, keys, k: int, *, reps=None, q_seq=No
     if rc != 0:
         raise ValueError("oracle_index_batch: bad arguments")
     return idx, sc, blk
+
+
+def attention_row(qa, ka, v, idx, scale: float) -> np.ndarray:
+    """Sparse attention of one row (fp64): softmax over the valid indices of
+    idx of scale * qa . ka_j, applied to the v rows.  ka, v: [len, dh]."""
+    qa, ka, v = _u16(qa), _u16(ka), _u16(v)
+    idx = np.ascontiguousarray(idx, np.int32)
+    dh = qa.shape[-1]
+    out = np.zeros(dh, np.float64)
+    _load().oracle_attention_row(_ptr(qa), _ptr(ka), _ptr(v), ka.shape[0], dh, _ptr(idx), len(idx), scale,
+                                 _ptr(out))
+    return out
+
+
+def attention_batch(qa, ka, v, key_off, lens, idx, scale: float) -> np.ndarray:
+    """Rows i of qa [nq, dh] over the sequence at key_off[i] of length
+    lens[i] (negative: zero output) in ka / v [rows, dh]; idx [nq, kk]."""
+    qa, ka, v = _u16(qa), _u16(ka), _u16(v)
+    idx = np.ascontiguousarray(idx, np.int32)
+    key_off = np.ascontiguousarray(key_off, np.int64)
+    lens = np.ascontiguousarray(lens, np.int64)
+    nq, dh = qa.shape
+    out = np.zeros((nq, dh), np.float64)
+    _load().oracle_attention_batch(_ptr(qa), _ptr(ka), _ptr(v), nq, dh, _ptr(key_off), _ptr(lens), _ptr(idx),
+                                   idx.shape[1], scale, _ptr(out))
+    return out

@@ -45,6 +45,15 @@
  *   - output: the selected token indices in ascending order followed by -1
  *     padding up to k; the selected blocks likewise, padded to m.
  *
+ * Sparse attention over the selected tokens (the consumer of the indices):
+ *   [HISA] stage-2 paragraph: the top-k token indices go to the sparse
+ *   attention operator; [VID] "HISA" section: only the selected keys and
+ *   values are gathered into smaller tensors and attention is computed on
+ *   that set.  Readings: softmax attention of one head, weights
+ *   softmax_j(scale * qa . ka_j) over the valid indices j of the row, output
+ *   sum_j w_j v_j; an empty row (every index -1) gives a zero output; an
+ *   index at or past its sequence's length counts as absent.
+ *
  * Exactness precondition for pooling: every addition of the fp64 block sum
  * must be exact.  That holds when no nonzero |key| is below 2^-34 and the
  * block sums stay below 2^10 in magnitude; the synthetic generators flush
@@ -365,6 +374,61 @@ int oracle_index_batch(int flat, const uint16_t* queries, const int64_t* q_pos,
 }
 
 /* Threads an OpenMP parallel region will use. */
+/* Sparse attention of one query row: qa [dh], ka / v [len, dh] (the
+ * row's sequence), idx [kk].  fp64 throughout: s_j = scale * sum qa ka_j,
+ * w_j = exp(s_j - max s), out = sum w_j v_j / sum w_j.  Returns the number
+ * of indices used. */
+int oracle_attention_row(const uint16_t* qa, const uint16_t* ka, const uint16_t* v, int64_t len, int dh,
+                         const int32_t* idx, int kk, double scale, double* out)
+{
+    double smax = -INFINITY;
+    int used = 0;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(kk > 0 ? kk : 1));
+    for (int r = 0; r < kk; ++r) {
+        const int64_t j = idx[r];
+        s[r] = NAN;
+        if (j < 0 || j >= len) continue;
+        double dot = 0.0;
+        for (int c = 0; c < dh; ++c) dot += bf16_value(qa[c]) * bf16_value(ka[j * dh + c]);
+        s[r] = scale * dot;
+        if (s[r] > smax) smax = s[r];
+        ++used;
+    }
+    for (int c = 0; c < dh; ++c) out[c] = 0.0;
+    if (used == 0) {
+        free(s);
+        return 0;
+    }
+    double wsum = 0.0;
+    for (int r = 0; r < kk; ++r) {
+        const int64_t j = idx[r];
+        if (j < 0 || j >= len) continue;
+        const double w = exp(s[r] - smax);
+        wsum += w;
+        for (int c = 0; c < dh; ++c) out[c] += w * bf16_value(v[j * dh + c]);
+    }
+    for (int c = 0; c < dh; ++c) out[c] /= wsum;
+    free(s);
+    return used;
+}
+
+/* A batch of rows: query i reads its sequence at key_off[i] with length
+ * len[i] (len < 0: an invalid query, zero output). */
+void oracle_attention_batch(const uint16_t* qa, const uint16_t* ka, const uint16_t* v, int64_t nq, int dh,
+                            const int64_t* key_off, const int64_t* len, const int32_t* idx, int kk,
+                            double scale, double* out)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < nq; ++i) {
+        if (len[i] < 0) {
+            for (int c = 0; c < dh; ++c) out[i * dh + c] = 0.0;
+            continue;
+        }
+        oracle_attention_row(qa + i * dh, ka + key_off[i] * dh, v + key_off[i] * dh, len[i], dh, idx + i * kk,
+                             kk, scale, out + i * dh);
+    }
+}
+
 int oracle_threads(void)
 {
 #ifdef _OPENMP
