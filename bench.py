@@ -15,6 +15,11 @@ last-level cache from serving repeated steps, the step rotates over
 `--replicas` copies of the key cache and representatives (cold-cache
 numbers); `--replicas 1` gives the warm-cache figure.
 
+On the 32K decode batch the JSON line also carries an "attention" object:
+the sparse attention that consumes the indices (one head of dimension 128,
+bf16 queries, keys and values drawn i.i.d. N(0, 1)), timed alone and as
+index + attention steps over HISA's and over the flat indexer's output.
+
 The timed region replays one captured HIP graph per step (per replica):
 the step's kernels without host work in between.  Per-kernel durations come
 from HIP start / stop events attached to the kernel dispatches of a
@@ -45,6 +50,9 @@ WORKLOADS = ("decode_32k_x16", "chunked_prefill_32k", "long_context_128k", "long
 # decode batches of more sequences: the same step at larger batch, to show
 # where the decode path reaches its steady-state HBM fraction
 DECODE_BATCH = {"decode_32k_x16": 16, "decode_32k_x64": 64, "decode_32k_x256": 256}
+
+ATTN_WORKLOADS = ("decode_32k_x16",)
+ATTN_SEED = 56
 
 STAGES_HISA = ("block_stage", "token_scores", "token_topk")
 STAGES_FLAT = ("flat_scores", "flat_topk")
@@ -256,29 +264,89 @@ class Setup:
             (h.hisa_flat_index if flat else h.hisa_index)(a)
 
 
-def capture_graphs(S, flat, torch):
+class AttentionLeg:
+    """The sparse attention over one decode step's indices: per replica of
+    the attention keys and values, one call reading the index call's
+    output buffer (HISA's or the flat indexer's)."""
+
+    def __init__(self, S, replicas, device_mod, synth, torch):
+        w = S.w
+        ph = S.phases[0]
+        qa, ka, va = synth.attention_inputs(w.keys.shape[0], len(ph.q_pos), seed=ATTN_SEED)
+        c = S.cache
+        dev = "cuda:0"
+        self.scale = 1.0 / np.sqrt(synth.DA)
+        q = device_mod.to_dev(qa, dev)
+        kr = [device_mod.to_dev(ka, dev)]
+        vr = [device_mod.to_dev(va, dev)]
+        for _ in range(replicas - 1):
+            kr.append(kr[0].clone())
+            vr.append(vr[0].clone())
+        self.replicas = replicas
+        self.kk = S.k
+        self.calls = {}
+        for flat in (False, True):
+            ic = S.calls[flat][0][0]
+            self.calls[flat] = [device_mod.AttentionCall(q, kr[r], vr[r], ic.out_idx, self.scale, q_seq=ic.q_seq,
+                                                         seq_key_off=c.d_key_off, seq_len=c.d_len)
+                                for r in range(replicas)]
+        self.nq = len(ph.q_pos)
+        self.desc = ("one head, d=128, bf16 q/k/v ~ N(0,1) beside every index key; k=%d indices per query; "
+                     "%d replicas of k and v (%.0f MiB each)" % (S.k, replicas, kr[0].numel() * 4 / 2 ** 20))
+        torch.cuda.synchronize()
+
+    def algorithmic_bytes(self, n_valid):
+        """q row, the index row, the selected key and value rows, the output row."""
+        return self.nq * (256 + 4 * self.kk + 512) + int(n_valid) * 512
+
+    def run(self, r, flat):
+        self.calls[flat][r % self.replicas].run()
+
+
+def attention_kernel_ms(S, A, nsteps, torch):
+    """Average duration of the attention call (both of its kernels), from
+    torch events on the stream it runs on, queued behind a sleep kernel so
+    the calls run back to back; inputs are one HISA step's indices."""
+    S.step(0, False, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nsteps)]
+    torch.cuda._sleep(int(2.0e7))
+    for i in range(nsteps):
+        ev[i][0].record()
+        A.run(i, False)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def capture_graphs(S, flat, torch, attn=None):
     """One HIP graph per replica holding one whole step (kernels only: no
-    events, no allocation, no memset nodes)."""
+    events, no allocation, no memset nodes), followed by the sparse
+    attention over its output when attn is given."""
     graphs = []
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):                   # warm the path once outside capture
         S.step(0, flat, side.cuda_stream)
+        if attn is not None:
+            attn.run(0, flat)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     for r in range(S.replicas):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             S.step(r, flat, torch.cuda.current_stream().cuda_stream)
+            if attn is not None:
+                attn.run(r, flat)
         graphs.append(g)
     torch.cuda.synchronize()
     return graphs
 
 
-def time_method(S, flat, steps, warmup, torch):
+def time_method(S, flat, steps, warmup, torch, attn=None):
     """Wall time of `steps` graph replays (one step each, rotating over the
     replicas), bracketed by device synchronisation."""
-    graphs = capture_graphs(S, flat, torch)
+    graphs = capture_graphs(S, flat, torch, attn)
     for i in range(warmup):
         graphs[i % S.replicas].replay()
     torch.cuda.synchronize()
@@ -390,6 +458,9 @@ def main():
     ap.add_argument("--stage-steps", type=int, default=32,
                     help="eager steps whose stages are timed with HIP events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attention", action="store_true", help="skip the sparse-attention leg")
+    ap.add_argument("--attn-replicas", type=int, default=8,
+                    help="copies of the attention keys and values rotated over")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -468,6 +539,23 @@ def main():
                     "gbps": (stage_bytes[n] / (v * 1e-3) / 1e9) if n in stage_bytes and v > 0 else None}
                 for n, v in stage.items()}
 
+    attention = None
+    if args.workload in ATTN_WORKLOADS and not args.no_attention:
+        log("attention leg: inputs and %d replicas" % args.attn_replicas)
+        A = AttentionLeg(S, args.attn_replicas, device, synth, torch)
+        a_ms = attention_kernel_ms(S, A, max(8, nst), torch)
+        n_valid = int((A.calls[False][0].idx >= 0).sum().item())
+        a_bytes = A.algorithmic_bytes(n_valid)
+        log("timing index + attention steps (HISA, flat)")
+        ha_ms = time_method(S, False, args.steps, args.warmup, torch, A) / args.steps * 1e3
+        fa_ms = time_method(S, True, args.steps, args.warmup, torch, A) / args.steps * 1e3
+        a_gbps = a_bytes / (a_ms * 1e-3) / 1e9
+        attention = {"description": A.desc, "kernel": "attn_partial_kernel + attn_combine_kernel",
+                     "avg_call_ms": a_ms, "algorithmic_bytes": a_bytes, "gbps": a_gbps,
+                     "frac_of_hbm_peak": a_gbps / HBM_PEAK_GBPS,
+                     "ms_per_step_hisa_plus_attention": ha_ms, "ms_per_step_flat_plus_attention": fa_ms,
+                     "speedup_vs_flat": fa_ms / ha_ms}
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -505,6 +593,7 @@ def main():
                  "dominant": {"kernel": fkern, "bound": fbound, "achieved": f_achieved, "unit": funit,
                               "frac": f_achieved / fpeak}},
         "speedup_vs_flat": f_ms / h_ms,
+        "attention": attention,
     }
     print(json.dumps(out), flush=True)
 

@@ -194,6 +194,54 @@ int hisa_index(const hisa_index_args* a, void* stream);
  */
 int hisa_flat_index(const hisa_index_args* a, void* stream);
 
+/*
+ * Sparse attention over an index call's output -- the operator the indices
+ * are for: [HISA] stage-2 paragraph (the top-k indices go to the sparse
+ * attention operator) and the video summary's "HISA" section (gather only
+ * the selected keys and values, attend over that small set).
+ * Per query i with valid indices J (entries of idx row i that are >= 0 and
+ * below its sequence's length):
+ *     w_j = softmax over J of  scale * (q_i . ka_j),   out_i = sum_j w_j v_j,
+ * one head, fp32 arithmetic on bf16 inputs; a row with no valid index (or a
+ * query whose sequence id is outside [0, nseq)) gets a zero output.
+ */
+#define HISA_ATTN_DIM 128
+
+typedef struct hisa_attn_args {
+    const uint16_t* q;           /* [nq, 128] bf16 attention queries */
+    const uint16_t* k;           /* [rows, 128] bf16 attention keys, packed per sequence like the index keys */
+    const uint16_t* v;           /* [rows, 128] bf16 values, the same rows */
+    const int32_t* idx;          /* [nq, kk] token indices relative to the sequence start, -1 = none
+                                    (out_idx of hisa_index / hisa_flat_index) */
+    const int32_t* q_seq;        /* [nq] sequence of each query, or NULL: sequence 0 */
+    const int64_t* seq_key_off;  /* [nseq] first row of each sequence, or NULL if nseq == 1: 0 */
+    const int64_t* seq_len;      /* [nseq] rows of each sequence (required) */
+    int32_t nseq;
+    int64_t nq;
+    int32_t kk;                  /* indices per query, 1 <= kk <= HISA_MAX_K */
+    int32_t dh;                  /* head dimension, must be HISA_ATTN_DIM */
+    float scale;                 /* softmax scale, e.g. 1/sqrt(128) */
+    float* out;                  /* [nq, 128] fp32 */
+    void* workspace;             /* device scratch owned by the caller */
+    size_t workspace_bytes;      /* at least hisa_attention_workspace_bytes */
+} hisa_attn_args;
+
+/* Workspace hisa_sparse_attention needs for these sizes (nq, kk): the
+ * per-chunk partial softmax states. */
+int hisa_attention_workspace_bytes(const hisa_attn_args* a, size_t* bytes);
+
+/*
+ * hisa_sparse_attention -- gather the keys and values at each query's
+ * indices, softmax attention over them.  Every query's indices are split
+ * into chunks of 128 handled by separate workgroups (partial max, sum and
+ * weighted value sum), then merged.
+ * Errors: INVALID_ARG (null q, k, v, idx, seq_len or out with nq > 0;
+ *         nq < 0; nseq < 1; nseq > 1 without seq_key_off; kk < 1;
+ *         non-finite scale), UNSUPPORTED
+ *         (dh != 128, kk > HISA_MAX_K), WORKSPACE.
+ */
+int hisa_sparse_attention(const hisa_attn_args* a, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* hisa_status_str(int status);
 

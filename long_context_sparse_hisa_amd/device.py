@@ -119,3 +119,42 @@ class IndexCall:
         sc = None if self.out_scores is None else self.out_scores.cpu().numpy()
         blk = None if self.out_blocks is None else self.out_blocks.cpu().numpy()
         return idx, sc, blk
+
+
+class AttentionCall:
+    """Buffers and arguments of one sparse-attention call over index rows
+    idx [nq, kk] (a torch tensor, e.g. an IndexCall's out_idx, or numpy)."""
+
+    def __init__(self, qa, ka, va, idx, scale: float, *, q_seq=None, seq_key_off=None, seq_len=None,
+                 device: str = "cuda:0", stream=None):
+        dev = torch.device(device)
+        self.stream = stream
+        def t(a, dtype=None):
+            if a is None or isinstance(a, torch.Tensor):
+                return a
+            return to_dev(np.asarray(a, dtype) if dtype else a, dev)
+        self.qa, self.ka, self.va = t(qa), t(ka), t(va)
+        self.idx = t(idx, np.int32)
+        if seq_len is None:
+            seq_len = np.array([self.ka.shape[0]], np.int64)
+        self.q_seq = t(q_seq, np.int32)
+        self.seq_key_off = t(seq_key_off, np.int64)
+        self.seq_len = t(seq_len, np.int64)
+        nq = self.qa.shape[0]
+        self.out = torch.empty((nq, self.qa.shape[1]), dtype=torch.float32, device=dev)
+        args = self._args(None, scale)
+        nbytes = hisa.hisa_attention_workspace_bytes(args)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.args = self._args(self.workspace, scale)
+
+    def _args(self, ws, scale):
+        return hisa.make_attn_args(self.qa, self.ka, self.va, self.idx, scale, q_seq=self.q_seq,
+                                   seq_key_off=self.seq_key_off, seq_len=self.seq_len, out=self.out,
+                                   workspace=ws)
+
+    def run(self, stream=None):
+        hisa.hisa_sparse_attention(self.args, stream or self.stream)
+
+    def result(self) -> np.ndarray:
+        torch.cuda.synchronize()
+        return self.out.cpu().numpy()

@@ -49,6 +49,15 @@ class hisa_index_args(ctypes.Structure):
 
 
 HISA_STAGES = 3
+HISA_ATTN_DIM = 128
+
+
+class hisa_attn_args(ctypes.Structure):
+    _fields_ = [
+        ("q", _P), ("k", _P), ("v", _P), ("idx", _P), ("q_seq", _P), ("seq_key_off", _P), ("seq_len", _P),
+        ("nseq", ctypes.c_int32), ("nq", ctypes.c_int64), ("kk", ctypes.c_int32), ("dh", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("out", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+    ]
 
 
 def lib():
@@ -68,6 +77,9 @@ def lib():
                                            ctypes.POINTER(ctypes.c_size_t)]
         L.hisa_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
         L.hisa_flat_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
+        L.hisa_attention_workspace_bytes.argtypes = [ctypes.POINTER(hisa_attn_args),
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+        L.hisa_sparse_attention.argtypes = [ctypes.POINTER(hisa_attn_args), _P]
         L.hisa_status_str.restype = ctypes.c_char_p
         L.hisa_status_str.argtypes = [ctypes.c_int]
         L.hisa_abi_version.restype = ctypes.c_int
@@ -177,6 +189,44 @@ def hisa_index(args: hisa_index_args, stream=None):
 
 def hisa_flat_index(args: hisa_index_args, stream=None):
     _check(lib().hisa_flat_index(ctypes.byref(args), _stream(stream)), "hisa_flat_index")
+
+
+def make_attn_args(q, k, v, idx, scale: float, *, q_seq=None, seq_key_off=None, seq_len=None,
+                   out=None, workspace=None) -> hisa_attn_args:
+    """Arguments of hisa_sparse_attention: q [nq, 128], k and v [L, 128]
+    (bf16 bits), idx [nq, kk] int32, seq_len [nseq] int64 (required),
+    out [nq, 128] float32."""
+    if seq_len is None:
+        raise ValueError("seq_len is required")
+    a = hisa_attn_args()
+    a.q = _dev(q, "q", 2)
+    a.k = _dev(k, "k", 2)
+    a.v = _dev(v, "v", 2)
+    a.idx = _dev(idx, "idx", 4)
+    a.q_seq = _dev(q_seq, "q_seq", 4)
+    a.seq_key_off = _dev(seq_key_off, "seq_key_off", 8)
+    a.seq_len = _dev(seq_len, "seq_len", 8)
+    a.nseq = seq_len.shape[0]
+    a.nq = q.shape[0]
+    a.kk = idx.shape[1]
+    a.dh = q.shape[1]
+    a.scale = float(scale)
+    a.out = _dev(out, "out", 4)
+    if workspace is not None:
+        a.workspace = _dev(workspace, "workspace")
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def hisa_attention_workspace_bytes(args: hisa_attn_args) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().hisa_attention_workspace_bytes(ctypes.byref(args), ctypes.byref(b)),
+           "hisa_attention_workspace_bytes")
+    return int(b.value)
+
+
+def hisa_sparse_attention(args: hisa_attn_args, stream=None):
+    _check(lib().hisa_sparse_attention(ctypes.byref(args), _stream(stream)), "hisa_sparse_attention")
 
 
 # ---- HIP events (stage timing) -------------------------------------------------

@@ -16,7 +16,10 @@ Key distributions:
     blocks 0 .. t // 128, plus 0.5 * N(0, I_64).
 
 Random streams per workload seed: 0 centroids and keys, 1 queries, 2 needle
-positions, 3 appended keys.
+positions, 3 appended keys; 4, 5, 6 the attention queries, keys and values.
+
+Attention inputs (the consumer of the indices) are i.i.d. N(0, 1) rows of
+DA = 128 coordinates, one key and one value row beside each index key.
 """
 from __future__ import annotations
 
@@ -26,6 +29,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 D = 64                 # index-key dimension of every workload
+DA = 128               # attention head dimension
 CENTROID_RUN = 128     # keys sharing one mixture centroid
 
 
@@ -201,6 +205,15 @@ def long_decode_append(L0: int = 1_047_552, steps: int = 8, n_new: int = 128, se
         q = to_bf16(_mog_queries(gq, cent, pos))
         w.phases.append(Phase("step%d" % s, q, pos, np.zeros(1, np.int32), append=new))
     return w
+
+
+def attention_inputs(rows: int, nq: int, seed: int):
+    """(queries [nq, DA], keys [rows, DA], values [rows, DA]) as bf16 bits,
+    i.i.d. N(0, 1), from streams 4, 5 and 6 of the seed."""
+    qa = to_bf16(rng(seed, 4).standard_normal((nq, DA), dtype=np.float32))
+    ka = to_bf16(rng(seed, 5).standard_normal((rows, DA), dtype=np.float32))
+    va = to_bf16(rng(seed, 6).standard_normal((rows, DA), dtype=np.float32))
+    return qa, ka, va
 
 
 # The five workloads at full size, by short name.

@@ -21,7 +21,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = hisa.header_functions()
     assert {"hisa_pool_blocks", "hisa_append_keys", "hisa_index", "hisa_flat_index",
-            "hisa_workspace_bytes", "hisa_status_str", "hisa_abi_version"} <= set(names)
+            "hisa_workspace_bytes", "hisa_status_str", "hisa_abi_version", "hisa_sparse_attention",
+            "hisa_attention_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -115,3 +116,41 @@ def test_pool_and_append_validation(lib):
         hisa.HISA_ERR_UNSUPPORTED
     assert lib.hisa_append_keys(P(FAKE), P(FAKE), seqs, -1, P(FAKE), 8, 64, 128, None) == \
         hisa.HISA_ERR_INVALID_ARG
+
+
+def _attn(**kw):
+    a = hisa.hisa_attn_args()
+    a.q = a.k = a.v = a.idx = a.seq_len = a.out = FAKE
+    a.nq, a.nseq, a.kk, a.dh, a.scale = 16, 1, 2048, 128, 0.088
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("dh", 64, hisa.HISA_ERR_UNSUPPORTED),
+    ("kk", 0, hisa.HISA_ERR_INVALID_ARG),
+    ("kk", 16385, hisa.HISA_ERR_UNSUPPORTED),
+    ("nq", -1, hisa.HISA_ERR_INVALID_ARG),
+    ("nseq", 0, hisa.HISA_ERR_INVALID_ARG),
+    ("nseq", 2, hisa.HISA_ERR_INVALID_ARG),        # several sequences need offsets
+    ("scale", float("nan"), hisa.HISA_ERR_INVALID_ARG),
+    ("scale", float("inf"), hisa.HISA_ERR_INVALID_ARG),
+    ("v", None, hisa.HISA_ERR_INVALID_ARG),
+    ("seq_len", None, hisa.HISA_ERR_INVALID_ARG),
+    ("out", None, hisa.HISA_ERR_INVALID_ARG),
+])
+def test_attention_validation(lib, field, value, code):
+    a = _attn(**{field: value})
+    assert lib.hisa_sparse_attention(ctypes.byref(a), None) == code
+
+
+def test_attention_workspace(lib):
+    a = _attn()
+    assert lib.hisa_sparse_attention(ctypes.byref(a), None) == hisa.HISA_ERR_WORKSPACE
+    # 16 queries x 16 chunks of 128 indices x (max, sum, 128 weighted values)
+    assert hisa.hisa_attention_workspace_bytes(a) == 16 * 16 * 130 * 4
+    a = _attn(workspace=FAKE, workspace_bytes=16 * 16 * 130 * 4 - 1)
+    assert lib.hisa_sparse_attention(ctypes.byref(a), None) == hisa.HISA_ERR_WORKSPACE
+    a = _attn(nq=0, q=None, out=None)
+    assert lib.hisa_sparse_attention(ctypes.byref(a), None) == hisa.HISA_OK
