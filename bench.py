@@ -550,7 +550,7 @@ def main():
         ha_ms = time_method(S, False, args.steps, args.warmup, torch, A) / args.steps * 1e3
         fa_ms = time_method(S, True, args.steps, args.warmup, torch, A) / args.steps * 1e3
         a_gbps = a_bytes / (a_ms * 1e-3) / 1e9
-        attention = {"description": A.desc, "kernel": "attn_partial_kernel + attn_combine_kernel",
+        attention = {"description": A.desc, "kernels": "attn_partial_kernel + attn_combine_kernel",
                      "avg_call_ms": a_ms, "algorithmic_bytes": a_bytes, "gbps": a_gbps,
                      "frac_of_hbm_peak": a_gbps / HBM_PEAK_GBPS,
                      "ms_per_step_hisa_plus_attention": ha_ms, "ms_per_step_flat_plus_attention": fa_ms,

@@ -227,14 +227,17 @@ typedef struct hisa_attn_args {
 } hisa_attn_args;
 
 /* Workspace hisa_sparse_attention needs for these sizes (nq, kk): the
- * per-chunk partial softmax states. */
+ * per-chunk partial softmax states (nq * ceil(kk / 128) * 130 floats).  No
+ * initial contents are required; calls that share a workspace must not
+ * overlap. */
 int hisa_attention_workspace_bytes(const hisa_attn_args* a, size_t* bytes);
 
 /*
  * hisa_sparse_attention -- gather the keys and values at each query's
  * indices, softmax attention over them.  Every query's indices are split
  * into chunks of 128 handled by separate workgroups (partial max, sum and
- * weighted value sum), then merged.
+ * weighted value sum), then a second kernel merges each query's chunks
+ * (one launch when kk <= 128).  Both on `stream`.
  * Errors: INVALID_ARG (null q, k, v, idx, seq_len or out with nq > 0;
  *         nq < 0; nseq < 1; nseq > 1 without seq_key_off; kk < 1;
  *         non-finite scale), UNSUPPORTED

@@ -8,9 +8,9 @@
 // Each query's indices are cut into chunks of kAttnChunk; a workgroup takes
 // one chunk and leaves its partial softmax state (chunk maximum m, sum of
 // exp(s - m), and the exp-weighted value sum), so even a few queries spread
-// over the chip.  A second kernel merges the chunks of a query.  Sixteen
-// lanes share a key or value row (16 bytes each), so every wave load is
-// four whole 256-byte rows.
+// over the chip; a second kernel merges the states of each query.
+// Sixteen lanes share a key or value row (16 bytes each), so every wave
+// load is four whole 256-byte rows.
 #include "../../include/hisa.h"
 
 #include <hip/hip_runtime.h>
@@ -31,6 +31,7 @@ constexpr int kAttnLanesPerRow = 16;                  // 16 x 16 bytes = one row
 constexpr int kAttnRowsPerPass = kAttnThreads / kAttnLanesPerRow;
 constexpr int kAttnPasses = kAttnChunk / kAttnRowsPerPass;
 constexpr int kAttnState = kAttnDim + 2;              // m, l, weighted value sum
+constexpr int kAttnMaxChunks = (HISA_MAX_K + kAttnChunk - 1) / kAttnChunk;
 
 static_assert(HISA_ATTN_DIM == kAttnDim, "head dimension");
 
@@ -74,16 +75,68 @@ __device__ __forceinline__ float wave_max_f32(float x)
     return key_score(wave_max_u32(score_key(x)));
 }
 
+// Merge the chunk states of one query: with M the largest chunk maximum,
+// out = sum_g exp(m_g - M) acc_g / sum_g exp(m_g - M) l_g (zero when no
+// chunk saw a valid index).  One round trip for everything: thread g loads
+// (m_g, l_g), and every thread loads its column of the first chunks of its
+// half of the workgroup (even or odd g) before the maximum is known.
+__device__ void attn_merge(const float* st, int G, float* out_row, float* s_f, float* s_half)
+{
+    constexpr int kPre = 8;
+    const int t = threadIdx.x;
+    const int c = t & (kAttnDim - 1);
+    const int h = t / kAttnDim;
+    const float m = t < G ? st[(int64_t)t * kAttnState] : -INFINITY;
+    const float lg = t < G ? st[(int64_t)t * kAttnState + 1] : 0.f;
+    float av[kPre];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+        const int g = h + 2 * i;
+        av[i] = g < G ? st[(int64_t)g * kAttnState + 2 + c] : 0.f;
+    }
+    float M = wave_max_f32(m);
+    __shared__ float s_m[kAttnThreads / 64];
+    if (lane_id() == 0) s_m[wave_id()] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kAttnThreads / 64; ++w) M = fmaxf(M, s_m[w]);
+    if (t < G) {
+        const float f = m > -INFINITY ? expf(m - M) : 0.f;
+        s_f[t] = f;
+        s_f[kAttnMaxChunks + t] = f * lg;
+    }
+    __syncthreads();
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+        const int g = h + 2 * i;
+        if (g < G) a += s_f[g] * av[i];
+    }
+    for (int g = h + 2 * kPre; g < G; g += 2) a += s_f[g] * st[(int64_t)g * kAttnState + 2 + c];
+    if (h == 1) s_half[c] = a;
+    __syncthreads();
+    if (h == 0) {
+        float l = 0.f;
+        for (int g = 0; g < G; ++g) l += s_f[kAttnMaxChunks + g];
+        a += s_half[c];
+        out_row[c] = l > 0.f ? a / l : 0.f;
+    }
+}
+
+// One chunk of kAttnChunk indices of one query (grid: queries x chunks).
+// With a single chunk the workgroup writes the output itself; otherwise it
+// stores its partial state for attn_combine_kernel.
 __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(const uint16_t* q, const uint16_t* k,
                                                                     const uint16_t* v, const int32_t* idx,
                                                                     const int32_t* q_seq, const int64_t* seq_key_off,
                                                                     const int64_t* seq_len, int nseq, int kk,
-                                                                    float scale, float* state)
+                                                                    float scale, float* state, float* out)
 {
     __shared__ float s_red[2][kAttnThreads / 64];
     __shared__ float s_acc[kAttnRowsPerPass][kAttnDim];
     const int64_t row = blockIdx.x;
     const int g = blockIdx.y;
+    const int G = gridDim.y;
     const int sub = threadIdx.x & (kAttnLanesPerRow - 1);     // which 16 bytes (8 dims) of a row
     const int grp = threadIdx.x / kAttnLanesPerRow;           // which row of a pass
     const int s = q_seq ? q_seq[row] : 0;
@@ -145,43 +198,39 @@ __global__ __launch_bounds__(kAttnThreads) void attn_partial_kernel(const uint16
 #pragma unroll
     for (int e = 0; e < 8; ++e) s_acc[grp][sub * 8 + e] = acc[e];
     __syncthreads();
-    float* st = state + ((int64_t)row * gridDim.y + g) * kAttnState;
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnThreads / 64; ++w) l += s_red[1][w];
+    float a = 0.f;
     if (threadIdx.x < kAttnDim) {
-        float a = 0.f;
 #pragma unroll
         for (int r = 0; r < kAttnRowsPerPass; ++r) a += s_acc[r][threadIdx.x];
-        st[2 + threadIdx.x] = a;
     }
+    if (G == 1) {
+        if (threadIdx.x < kAttnDim) out[row * kAttnDim + threadIdx.x] = l > 0.f ? a / l : 0.f;
+        return;
+    }
+    float* st = state + (row * G + g) * kAttnState;
+    if (threadIdx.x < kAttnDim) st[2 + threadIdx.x] = a;
     if (threadIdx.x == 0) {
-        float l = 0.f;
-#pragma unroll
-        for (int w = 0; w < kAttnThreads / 64; ++w) l += s_red[1][w];
         st[0] = mx;
         st[1] = l;
     }
 }
 
-// Merge the chunks of one query: with M the largest chunk maximum,
-// out = sum_g exp(m_g - M) acc_g / sum_g exp(m_g - M) l_g.
-__global__ __launch_bounds__(kAttnDim) void attn_combine_kernel(const float* state, int G, float* out)
+// The chunk states of one query merged (grid: queries).  A separate launch:
+// the kernel boundary makes every chunk's stores visible, which a counter
+// in the partial kernel could only do with a device-scope fence per chunk
+// (a write-back of its die's L2), measured slower than the second launch.
+__global__ __launch_bounds__(kAttnThreads) void attn_combine_kernel(const float* state, int G, float* out)
 {
-    const int64_t row = blockIdx.x;
-    const float* st = state + row * G * kAttnState;
-    float M = -INFINITY;
-    for (int g = 0; g < G; ++g) M = fmaxf(M, st[g * kAttnState]);
-    float l = 0.f, a = 0.f;
-    if (M > -INFINITY) {
-        for (int g = 0; g < G; ++g) {
-            const float m = st[g * kAttnState];
-            if (!(m > -INFINITY)) continue;
-            const float f = expf(m - M);
-            l += f * st[g * kAttnState + 1];
-            a += f * st[g * kAttnState + 2 + threadIdx.x];
-        }
-    }
-    out[row * kAttnDim + threadIdx.x] = l > 0.f ? a / l : 0.f;
+    __shared__ float s_f[2 * kAttnMaxChunks];
+    __shared__ float s_half[kAttnDim];
+    static_assert(kAttnMaxChunks <= kAttnThreads, "one merging thread per chunk");
+    attn_merge(state + (int64_t)blockIdx.x * G * kAttnState, G, out + (int64_t)blockIdx.x * kAttnDim, s_f, s_half);
 }
 
+// Workspace: the chunk states, G = ceil(kk / kAttnChunk) per query.
 size_t state_bytes(int64_t nq, int kk)
 {
     const int64_t G = (kk + kAttnChunk - 1) / kAttnChunk;
@@ -226,11 +275,13 @@ int hisa_sparse_attention(const hisa_attn_args* a, void* stream_)
     float* state = static_cast<float*>(a->workspace);
     hipLaunchKernelGGL(attn_partial_kernel, dim3((unsigned)a->nq, (unsigned)G), dim3(kAttnThreads), 0, stream, a->q,
                        a->k, a->v, a->idx, a->q_seq, a->seq_key_off, a->seq_len, (int)a->nseq, (int)a->kk, a->scale,
-                       state);
+                       state, a->out);
     if (hipGetLastError() != hipSuccess) return HISA_ERR_HIP;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)a->nq), dim3(kAttnDim), 0, stream,
-                       static_cast<const float*>(state), G, a->out);
-    if (hipGetLastError() != hipSuccess) return HISA_ERR_HIP;
+    if (G > 1) {
+        hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)a->nq), dim3(kAttnThreads), 0, stream,
+                           static_cast<const float*>(state), G, a->out);
+        if (hipGetLastError() != hipSuccess) return HISA_ERR_HIP;
+    }
     return HISA_OK;
 }
 
