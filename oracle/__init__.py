@@ -57,6 +57,7 @@ def _load():
             lib.oracle_hisa_query.argtypes = [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32,
                                               _P, _P, _P, _P]
             lib.oracle_flat_query.argtypes = [_P, _P, _I64, _I64, _I32, _I32, _P, _P, _P]
+            lib.oracle_block_only_query.argtypes = [_P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P]
             lib.oracle_attention_row.argtypes = [_P, _P, _P, _I64, _I32, _P, _I32, ctypes.c_double, _P]
             lib.oracle_attention_row.restype = _I32
             lib.oracle_attention_batch.argtypes = [_P, _P, _P, _I64, _I32, _P, _P, _P, _I32,
@@ -185,11 +186,25 @@ def flat_query(q, keys, t: int, k: int):
     return idx, sc, (int(counts[0]), int(counts[1]))
 
 
+def block_only_query(q, reps, L: int, t: int, B: int, m: int):
+    """Block-only selection of one query: (idx[m*B], blocks[m])."""
+    q = _u16(q)
+    reps = _u16(reps)
+    idx = np.zeros(m * B, np.int32)
+    blk = np.zeros(m, np.int32)
+    rc = _load().oracle_block_only_query(_ptr(q), _ptr(reps), L, t, q.shape[-1], B, m, _ptr(idx), _ptr(blk))
+    if rc != 0:
+        raise ValueError("oracle_block_only_query: bad arguments")
+    return idx, blk
+
+
 def index_batch(flat: bool, queries, q_pos, keys, k: int, *, reps=None, q_seq=None,
-                seq_key_off=None, seq_rep_off=None, seq_len=None, B: int = 128, m: int = 3):
-    """Batched HISA (flat=False) or flat (flat=True) over packed sequences.
-    Returns (idx[nq,k] int32, scores[nq,k] fp64, blocks[nq,m] int32 or
-    None)."""
+                seq_key_off=None, seq_rep_off=None, seq_len=None, B: int = 128, m: int = 3,
+                block_only: bool = False):
+    """Batched HISA (flat=False) or flat (flat=True) over packed sequences,
+    or with block_only the block-only selection (k = m*B, no scores).
+    Returns (idx[nq,k] int32, scores[nq,k] fp64 or None, blocks[nq,m]
+    int32 or None)."""
     queries = _u16(queries)
     keys = _u16(keys)
     nq, d = queries.shape
@@ -205,9 +220,10 @@ def index_batch(flat: bool, queries, q_pos, keys, k: int, *, reps=None, q_seq=No
     if reps is not None:
         reps = _u16(reps)
     idx = np.zeros((nq, k), np.int32)
-    sc = np.zeros((nq, k), np.float64)
+    sc = None if block_only else np.zeros((nq, k), np.float64)
     blk = None if flat else np.zeros((nq, m), np.int32)
-    rc = _load().oracle_index_batch(int(flat), _ptr(queries), _ptr(q_pos), _ptr(q_seq), nq,
+    mode = 2 if block_only else int(bool(flat))
+    rc = _load().oracle_index_batch(mode, _ptr(queries), _ptr(q_pos), _ptr(q_seq), nq,
                                     _ptr(keys), _ptr(reps), _ptr(seq_key_off), _ptr(seq_rep_off),
                                     _ptr(seq_len), len(seq_len), d, B, m, k, _ptr(idx), _ptr(sc),
                                     _ptr(blk))

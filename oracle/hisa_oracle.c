@@ -323,6 +323,35 @@ int oracle_flat_query(const uint16_t* q, const uint16_t* keys, int64_t L,
     return rc;
 }
 
+/* ---- block-only selection ---------------------------------------------- */
+
+/* The variant HISA is contrasted with ([HISA] results paragraph: choosing
+ * whole blocks without the token-level refinement loses accuracy at long
+ * context).  Reading: stage 1 unchanged, then every visible token (j <= t)
+ * of the kept blocks, ascending, followed by -1 up to m*B entries; no token
+ * is scored. */
+int oracle_block_only_query(const uint16_t* q, const uint16_t* reps, int64_t L, int64_t t, int d, int B, int m,
+                            int32_t* out_idx, int32_t* out_blocks)
+{
+    if (t < 0 || t >= L || m < 3 || B <= 0) return -1;
+    int64_t* sel = (int64_t*)malloc((size_t)m * sizeof(int64_t));
+    if (!sel) return -1;
+    const int ns = oracle_select_blocks(q, reps, t, d, B, m, sel, NULL);
+    if (ns < 0) {
+        free(sel);
+        return -1;
+    }
+    int64_t n = 0;
+    for (int i = 0; i < ns; ++i)
+        for (int64_t j = sel[i] * B; j < (sel[i] + 1) * B; ++j)
+            if (j <= t) out_idx[n++] = (int32_t)j;
+    for (; n < (int64_t)m * B; ++n) out_idx[n] = -1;
+    if (out_blocks)
+        for (int i = 0; i < m; ++i) out_blocks[i] = i < ns ? (int32_t)sel[i] : -1;
+    free(sel);
+    return 0;
+}
+
 /* ---- batches over packed sequences -------------------------------------- */
 
 static void fill_invalid(int32_t* idx, double* sc, int32_t* blk, int k, int m)
@@ -338,8 +367,9 @@ static void fill_invalid(int32_t* idx, double* sc, int32_t* blk, int k, int m)
  * [seq_key_off[s], seq_key_off[s] + seq_len[s]) and block-representative
  * rows starting at seq_rep_off[s]; q_seq == NULL puts every query in
  * sequence 0.  A query whose sequence id or position is out of range gets a
- * row of -1.  flat != 0 runs the flat indexer (reps, B, m unused). */
-int oracle_index_batch(int flat, const uint16_t* queries, const int64_t* q_pos,
+ * row of -1.  mode 0 runs HISA, 1 the flat indexer (reps, B, m unused), 2
+ * the block-only selection (k must be m*B; out_scores unused). */
+int oracle_index_batch(int mode, const uint16_t* queries, const int64_t* q_pos,
                        const int32_t* q_seq, int64_t nq, const uint16_t* keys,
                        const uint16_t* reps, const int64_t* seq_key_off,
                        const int64_t* seq_rep_off, const int64_t* seq_len,
@@ -348,13 +378,16 @@ int oracle_index_batch(int flat, const uint16_t* queries, const int64_t* q_pos,
 {
     if (!queries || !q_pos || !keys || !seq_key_off || !seq_len || !out_idx)
         return -1;
+    const int flat = mode == 1;
+    if (mode < 0 || mode > 2) return -1;
     if (!flat && (!reps || !seq_rep_off)) return -1;
+    if (mode == 2 && (int64_t)k != (int64_t)m * B) return -1;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 8) reduction(| : bad)
     for (int64_t i = 0; i < nq; ++i) {
         int32_t s = q_seq ? q_seq[i] : 0;
         int32_t* idx = out_idx + i * k;
-        double* sc = out_scores ? out_scores + i * k : NULL;
+        double* sc = (out_scores && mode != 2) ? out_scores + i * k : NULL;
         int32_t* blk = (out_blocks && !flat) ? out_blocks + i * m : NULL;
         if (s < 0 || s >= nseq || q_pos[i] < 0 || q_pos[i] >= seq_len[s]) {
             fill_invalid(idx, sc, blk, k, m);
@@ -365,6 +398,8 @@ int oracle_index_batch(int flat, const uint16_t* queries, const int64_t* q_pos,
         int rc;
         if (flat)
             rc = oracle_flat_query(q, K, seq_len[s], q_pos[i], d, k, idx, sc, NULL);
+        else if (mode == 2)
+            rc = oracle_block_only_query(q, reps + seq_rep_off[s] * d, seq_len[s], q_pos[i], d, B, m, idx, blk);
         else
             rc = oracle_hisa_query(q, K, reps + seq_rep_off[s] * d, seq_len[s],
                                    q_pos[i], d, B, m, k, idx, sc, blk, NULL);
@@ -373,7 +408,6 @@ int oracle_index_batch(int flat, const uint16_t* queries, const int64_t* q_pos,
     return bad ? -1 : 0;
 }
 
-/* Threads an OpenMP parallel region will use. */
 /* Sparse attention of one query row: qa [dh], ka / v [len, dh] (the
  * row's sequence), idx [kk].  fp64 throughout: s_j = scale * sum qa ka_j,
  * w_j = exp(s_j - max s), out = sum w_j v_j / sum w_j.  Returns the number
@@ -429,6 +463,7 @@ void oracle_attention_batch(const uint16_t* qa, const uint16_t* ka, const uint16
     }
 }
 
+/* Threads an OpenMP parallel region will use. */
 int oracle_threads(void)
 {
 #ifdef _OPENMP
