@@ -223,27 +223,30 @@ class Setup:
         # replicas (cold-cache rotation)
         self.keys = [c.keys] + [c.keys.clone() for _ in range(replicas - 1)]
         self.reps = [c.reps] + [c.reps.clone() for _ in range(replicas - 1)]
-        self.calls = {}
-        for flat in (False, True):
-            calls = []
-            for ph in self.phases:
-                ic = device_mod.IndexCall(c, ph.queries, ph.q_pos, ph.q_seq, k=self.k, m=self.m,
-                                          flat=flat, scores=False, blocks=False,
-                                          one_chunk_limit=16 << 30)
-                per_rep = []
-                for r in range(replicas):
-                    a = hisa_mod.make_args(ic.queries, ic.q_pos, self.keys[r], self.k, reps=self.reps[r],
-                                           q_seq=ic.q_seq, seq_key_off=c.d_key_off,
-                                           seq_rep_off=c.d_rep_off, seq_len=c.d_len,
-                                           max_len=ic.max_len, B=self.B, m=self.m,
-                                           out_idx=ic.out_idx, out_scores=ic.out_scores,
-                                           out_blocks=ic.out_blocks, workspace=ic.workspace)
-                    a.workspace_bytes = ic.args.workspace_bytes
-                    per_rep.append(a)
-                calls.append((ic, per_rep))
-            self.calls[flat] = calls
+        self.dev_mod = device_mod
         self.replicas = replicas
+        self.block_only = False
+        self.calls = {flat: self.build_calls(flat, self.m, self.k) for flat in (False, True)}
         self.q_per_step = sum(len(ph.q_pos) for ph in self.phases)
+
+    def build_calls(self, flat, m, k, block_only=False):
+        """Per phase: an IndexCall (buffers) and one argument block per
+        replica of the keys and representatives."""
+        c = self.cache
+        calls = []
+        for ph in self.phases:
+            ic = self.dev_mod.IndexCall(c, ph.queries, ph.q_pos, ph.q_seq, k=k, m=m, flat=flat, scores=False,
+                                        blocks=False, one_chunk_limit=16 << 30, block_only=block_only)
+            per_rep = []
+            for r in range(self.replicas):
+                a = self.h.make_args(ic.queries, ic.q_pos, self.keys[r], k, reps=self.reps[r], q_seq=ic.q_seq,
+                                     seq_key_off=c.d_key_off, seq_rep_off=c.d_rep_off, seq_len=c.d_len,
+                                     max_len=ic.max_len, B=self.B, m=m, out_idx=ic.out_idx,
+                                     out_scores=ic.out_scores, out_blocks=ic.out_blocks, workspace=ic.workspace)
+                a.workspace_bytes = ic.args.workspace_bytes
+                per_rep.append(a)
+            calls.append((ic, per_rep))
+        return calls
 
     def step(self, r, flat, stream, events=None, append_events=None):
         """One step on replica r; events: one StageEvents per phase."""
@@ -261,7 +264,7 @@ class Setup:
                 events[p].attach(a)
             else:
                 a.stage_events = None
-            (h.hisa_flat_index if flat else h.hisa_index)(a)
+            (h.hisa_flat_index if flat else h.hisa_block_index if self.block_only else h.hisa_index)(a)
 
 
 class AttentionLeg:
@@ -402,6 +405,58 @@ def stage_times(S, flat, nsteps, torch):
     return out
 
 
+def row_overlap(a, b):
+    """Mean over rows of |A & F| / |A | F| and of |A & F| / |F| for index
+    rows a (a method) and b (the flat indexer), -1 entries ignored."""
+    iou, rec = [], []
+    for x, y in zip(a, b):
+        x = x[x >= 0]
+        y = y[y >= 0]
+        inter = len(np.intersect1d(x, y, assume_unique=True))
+        union = len(x) + len(y) - inter
+        iou.append(inter / union if union else 1.0)
+        rec.append(inter / len(y) if len(y) else 1.0)
+    return float(np.mean(iou)), float(np.mean(rec))
+
+
+def sweep_m(S, ms, steps, warmup, torch):
+    """HISA at each m (k fixed) and block-only selection at the same token
+    budget (m = k/B) and at HISA's candidate set (the workload's m): time
+    per step (graph replays) and overlap with the flat indexer's rows."""
+    sp = torch.cuda.current_stream().cuda_stream
+    nrow = 1024                                      # rows compared (evenly spaced)
+
+    def rows_of(calls):
+        out = []
+        for ic, _ in calls:
+            n = ic.out_idx.shape[0]
+            pick = np.unique(np.linspace(0, n - 1, min(n, nrow)).astype(np.int64))
+            out.append(ic.out_idx[torch.from_numpy(pick).to(ic.out_idx.device)].cpu().numpy())
+        return np.concatenate(out)
+
+    f_ms = time_method(S, True, steps, warmup, torch) / steps * 1e3
+    S.step(0, True, sp)
+    torch.cuda.synchronize()
+    flat_rows = rows_of(S.calls[True])
+    base = S.calls[False]
+    points = []
+    variants = [(False, m, S.k) for m in ms if m * S.B >= S.k and m * S.B <= 16384]
+    variants += [(True, mb, mb * S.B) for mb in sorted({S.k // S.B, S.m}) if mb >= 3]
+    for block_only, m, k in variants:
+        log("sweep: %s m=%d k=%d" % ("block-only" if block_only else "hisa", m, k))
+        S.calls[False] = S.build_calls(False, m, k, block_only=block_only)
+        S.block_only = block_only
+        ms_step = time_method(S, False, steps, warmup, torch) / steps * 1e3
+        S.step(0, False, sp)
+        torch.cuda.synchronize()
+        iou, rec = row_overlap(rows_of(S.calls[False]), flat_rows)
+        points.append({"method": "block_only" if block_only else "hisa", "m": m, "k": k, "ms_per_step": ms_step,
+                       "speedup_vs_flat": f_ms / ms_step, "iou_vs_flat": iou, "recall_of_flat_topk": rec})
+    S.calls[False] = base
+    S.block_only = False
+    return f_ms, points
+
+
 def cpu_baseline(S, seconds, oracle):
     """The oracle on the same step, repeated for about `seconds`."""
     w = S.w
@@ -459,6 +514,9 @@ def main():
                     help="eager steps whose stages are timed with HIP events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attention", action="store_true", help="skip the sparse-attention leg")
+    ap.add_argument("--sweep-m", default=None, metavar="M1,M2,...",
+                    help="instead of the default line: HISA at each m and block-only selection, time per "
+                         "step and overlap with the flat indexer's rows")
     ap.add_argument("--attn-replicas", type=int, default=8,
                     help="copies of the attention keys and values rotated over")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -494,6 +552,16 @@ def main():
     R = args.replicas or default_rep[args.workload]
     log("setting up %s with %d replicas" % (args.workload, R))
     S = Setup(args.workload, R, hisa, synth, device, torch)
+    if args.sweep_m:
+        ms = [int(x) for x in args.sweep_m.split(",")]
+        f_ms, points = sweep_m(S, ms, args.steps, args.warmup, torch)
+        print(json.dumps({"metric": "HISA m-sweep: ms per step and overlap with the flat indexer's top-k rows",
+                          "workload": args.workload, "description": S.desc, "n_gpus": 1, "steps": args.steps,
+                          "replicas": R, "B": S.B, "k": S.k, "flat_ms_per_step": f_ms,
+                          "overlap": "iou = mean |A & F| / |A | F|, recall = mean |A & F| / |F| over up to "
+                                     "1024 evenly spaced rows per phase, F the flat indexer's row",
+                          "points": points}), flush=True)
+        return
     log("timing HISA: %d warmup + %d graph-replayed steps" % (args.warmup, args.steps))
     h_el = time_method(S, False, args.steps, args.warmup, torch)
     log("timing flat: %d warmup + %d graph-replayed steps" % (args.warmup, args.steps))

@@ -195,6 +195,21 @@ int hisa_index(const hisa_index_args* a, void* stream);
 int hisa_flat_index(const hisa_index_args* a, void* stream);
 
 /*
+ * hisa_block_index -- block-only selection, the variant the HISA summary's
+ * results paragraph contrasts with HISA (whole blocks chosen without the
+ * token-level refinement): stage 1 exactly as in hisa_index, then each
+ * out_idx row holds every visible token (j <= t) of the kept blocks in
+ * ascending order, followed by -1.  No token is scored.  The row width
+ * must be the whole candidate set: k == m*B.  out_blocks as in hisa_index;
+ * out_scores must be NULL.  Workspace: what hisa_workspace_bytes reports
+ * for hisa_index (flat = 0).  Stage events 0 (stage 1) and 1 (the
+ * expansion).
+ * Errors: those of hisa_index, and INVALID_ARG for k != m*B or a non-NULL
+ *         out_scores.
+ */
+int hisa_block_index(const hisa_index_args* a, void* stream);
+
+/*
  * Sparse attention over an index call's output -- the operator the indices
  * are for: [HISA] stage-2 paragraph (the top-k indices go to the sparse
  * attention operator) and the video summary's "HISA" section (gather only

@@ -277,6 +277,36 @@ int hisa_index(const hisa_index_args* a, void* stream_)
     return HISA_OK;
 }
 
+int hisa_block_index(const hisa_index_args* a, void* stream_)
+{
+    const int rc = validate_index(a, 0);
+    if (rc != HISA_OK) return rc;
+    if ((int64_t)a->k != (int64_t)a->m * a->B || a->out_scores) return HISA_ERR_INVALID_ARG;
+    if (a->nq == 0) return HISA_OK;
+    if (!a->workspace) return HISA_ERR_WORKSPACE;
+    const int64_t chunk = chunk_for(a, 0, a->workspace_bytes);
+    if (chunk < 1) return HISA_ERR_WORKSPACE;
+    const Layout L = layout_for(a, 0, chunk);
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const QueryMeta qm = meta_of(a);
+    const int64_t Mmax = hisa_Mmax(a);
+    const int lb = log2_of(a->B);
+    float* sigma = Mmax > kStage1FusedMax ? at<float>(a->workspace, L.sigma) : nullptr;
+    int32_t* sel = at<int32_t>(a->workspace, L.sel);
+    RowInfo* rinfo = at<RowInfo>(a->workspace, L.rinfo);
+    for (int64_t q0 = 0; q0 < a->nq; q0 += chunk) {
+        const int64_t nc = std::min(chunk, a->nq - q0);
+        const bool last = q0 + nc >= a->nq;
+        hipError_t err = launch_stage1(qm, a->reps, q0, nc, lb, a->m, Mmax, sigma, sel, rinfo, a->out_blocks, stream,
+                                       stage_timing(a, last, 0));
+        if (err == hipSuccess)
+            err = launch_expand_blocks(sel, rinfo, nc, a->m, lb, a->out_idx + q0 * a->k, stream,
+                                       stage_timing(a, last, 1));
+        if (err != hipSuccess) return HISA_ERR_HIP;
+    }
+    return HISA_OK;
+}
+
 int hisa_flat_index(const hisa_index_args* a, void* stream_)
 {
     const int rc = validate_index(a, 1);

@@ -125,6 +125,11 @@ constexpr int64_t kManyRows = 256;
 hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel, int m,
                              int lb, int32_t* out_idx, float* out_scores, hipStream_t stream, Timing t = {});
 
+// Block-only rows [nq, m*B]: every visible token of each query's kept
+// blocks (sel, ascending with -1 padding), ascending, then -1.
+hipError_t launch_expand_blocks(const int32_t* sel, const RowInfo* rinfo, int64_t nq, int m, int lb,
+                                int32_t* out_idx, hipStream_t stream, Timing t = {});
+
 // Top-k of long rows (slot s is token s) with several workgroups per row.
 struct RadixWorkspace {
     int* hist;        // [nrows, 256]

@@ -811,6 +811,58 @@ static hipError_t launch_topk_rows_items(const uint32_t* ukeys, int64_t nrows, i
                     sel, m, lb, out_idx, out_scores);
 }
 
+// ---- block-only selection: the kept blocks expanded -------------------------
+// Entry e of a row is row e % B of kept block e / B.  The kept list is
+// ascending and only its last block (the query's own) can hold keys past
+// t, so the visible entries form a prefix of the row and the rest is -1.
+// Each workgroup writes kExpandPerWg entries of one row, VEC per store.
+constexpr int kExpandPerWg = 2048;
+
+template <int VEC>
+__global__ __launch_bounds__(kThreads) void expand_blocks_kernel(const int32_t* sel, const RowInfo* rinfo, int m,
+                                                                 int lb, int32_t* out_idx)
+{
+    __shared__ int32_t s_blk[kMaxKept];
+    const int64_t row = blockIdx.x;
+    const int N = m << lb;
+    const int e0 = blockIdx.y * kExpandPerWg;
+    const int r0 = e0 >> lb;
+    const int nr = min(kExpandPerWg >> lb, m - r0) + 1;
+    for (int r = threadIdx.x; r < nr; r += kThreads) s_blk[r] = r0 + r < m ? sel[row * m + r0 + r] : -1;
+    const int64_t t = rinfo[row].t;
+    __syncthreads();
+    int32_t* o = out_idx + row * (int64_t)N;
+    const int e1 = min(N, e0 + kExpandPerWg);
+    const int mask = (1 << lb) - 1;
+    for (int e = e0 + threadIdx.x * VEC; e < e1; e += kThreads * VEC) {
+        int v[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            const int32_t b = s_blk[((e + i) >> lb) - r0];
+            const int64_t tok = ((int64_t)b << lb) + ((e + i) & mask);
+            v[i] = (b >= 0 && tok <= t) ? (int32_t)tok : -1;
+        }
+        if constexpr (VEC == 4)
+            *reinterpret_cast<int4*>(o + e) = make_int4(v[0], v[1], v[2], v[3]);
+        else
+            o[e] = v[0];
+    }
+}
+
+hipError_t launch_expand_blocks(const int32_t* sel, const RowInfo* rinfo, int64_t nq, int m, int lb,
+                                int32_t* out_idx, hipStream_t stream, Timing t)
+{
+    const int N = m << lb;
+    dim3 grid((unsigned)nq, (unsigned)((N + kExpandPerWg - 1) / kExpandPerWg));
+    // rows of m*B >= 48 entries (a multiple of 16): 16-byte stores when the
+    // output is 16-byte aligned
+    if ((reinterpret_cast<uintptr_t>(out_idx) & 15) == 0)
+        return launch_k(expand_blocks_kernel<4>, grid, dim3(kThreads), stream, t.start, t.stop, sel, rinfo, m, lb,
+                        out_idx);
+    return launch_k(expand_blocks_kernel<1>, grid, dim3(kThreads), stream, t.start, t.stop, sel, rinfo, m, lb,
+                    out_idx);
+}
+
 hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k, const int32_t* sel, int m, int lb,
                              int32_t* out_idx, float* out_scores, hipStream_t stream, Timing t)
 {

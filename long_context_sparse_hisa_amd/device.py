@@ -75,10 +75,14 @@ class IndexCall:
     def __init__(self, cache: DeviceCache, queries, q_pos, q_seq, k: int, m: int | None = None,
                  flat: bool = False, scores: bool = True, blocks: bool = True,
                  max_len: int | None = None, workspace_bytes: int | None = None,
-                 one_chunk_limit: int = 0):
+                 one_chunk_limit: int = 0, block_only: bool = False):
+        """block_only: the block-only selection (k must be m*B; no scores)."""
         dev = cache.device
         self.cache = cache
         self.flat = flat
+        self.block_only = block_only
+        if block_only:
+            scores = False
         self.queries = queries if isinstance(queries, torch.Tensor) else to_dev(queries, dev)
         self.q_pos = q_pos if isinstance(q_pos, torch.Tensor) else to_dev(np.asarray(q_pos, np.int64), dev)
         self.q_seq = q_seq if isinstance(q_seq, torch.Tensor) else to_dev(np.asarray(q_seq, np.int32), dev)
@@ -109,6 +113,8 @@ class IndexCall:
     def run(self, stream=None):
         if self.flat:
             hisa.hisa_flat_index(self.args, stream or self.cache.stream)
+        elif self.block_only:
+            hisa.hisa_block_index(self.args, stream or self.cache.stream)
         else:
             hisa.hisa_index(self.args, stream or self.cache.stream)
 

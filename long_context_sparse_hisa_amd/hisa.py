@@ -77,6 +77,7 @@ def lib():
                                            ctypes.POINTER(ctypes.c_size_t)]
         L.hisa_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
         L.hisa_flat_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
+        L.hisa_block_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
         L.hisa_attention_workspace_bytes.argtypes = [ctypes.POINTER(hisa_attn_args),
                                                      ctypes.POINTER(ctypes.c_size_t)]
         L.hisa_sparse_attention.argtypes = [ctypes.POINTER(hisa_attn_args), _P]
@@ -189,6 +190,10 @@ def hisa_index(args: hisa_index_args, stream=None):
 
 def hisa_flat_index(args: hisa_index_args, stream=None):
     _check(lib().hisa_flat_index(ctypes.byref(args), _stream(stream)), "hisa_flat_index")
+
+
+def hisa_block_index(args: hisa_index_args, stream=None):
+    _check(lib().hisa_block_index(ctypes.byref(args), _stream(stream)), "hisa_block_index")
 
 
 def make_attn_args(q, k, v, idx, scale: float, *, q_seq=None, seq_key_off=None, seq_len=None,

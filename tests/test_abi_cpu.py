@@ -22,7 +22,7 @@ def test_exports_every_declared_function(lib):
     names = hisa.header_functions()
     assert {"hisa_pool_blocks", "hisa_append_keys", "hisa_index", "hisa_flat_index",
             "hisa_workspace_bytes", "hisa_status_str", "hisa_abi_version", "hisa_sparse_attention",
-            "hisa_attention_workspace_bytes"} <= set(names)
+            "hisa_attention_workspace_bytes", "hisa_block_index"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -154,3 +154,12 @@ def test_attention_workspace(lib):
     assert lib.hisa_sparse_attention(ctypes.byref(a), None) == hisa.HISA_ERR_WORKSPACE
     a = _attn(nq=0, q=None, out=None)
     assert lib.hisa_sparse_attention(ctypes.byref(a), None) == hisa.HISA_OK
+
+
+def test_block_index_validation(lib):
+    a = _args(k=64 * 128)                       # the whole candidate set
+    assert _rc(lib.hisa_block_index, a) == hisa.HISA_ERR_WORKSPACE
+    assert _rc(lib.hisa_block_index, _args(k=2048)) == hisa.HISA_ERR_INVALID_ARG       # k != m*B
+    assert _rc(lib.hisa_block_index, _args(k=64 * 128, out_scores=FAKE)) == hisa.HISA_ERR_INVALID_ARG
+    assert _rc(lib.hisa_block_index, _args(k=64 * 128, B=100)) == hisa.HISA_ERR_UNSUPPORTED
+    assert _rc(lib.hisa_block_index, _args(k=64 * 128, nq=0, queries=None)) == hisa.HISA_OK

@@ -30,3 +30,12 @@ def test_stage_flops_and_bound():
     assert bench.stage_roofline("d/token_scores", 1.0, 16, 1e9, 1e6)[0] == "hbm"
     b, a, p, u, w = bench.stage_roofline("p/token_scores", 1.0, 4096, 1e12, 1e6)
     assert (b, u, w) == ("mfma", "TFLOP/s", 1e12) and abs(a - 1000.0) < 1e-9
+
+
+def test_row_overlap():
+    a = np.array([[0, 1, 2, 3], [5, 6, -1, -1], [-1, -1, -1, -1]])
+    f = np.array([[2, 3, 4, 5], [5, 6, -1, -1], [-1, -1, -1, -1]])
+    iou, rec = bench.row_overlap(a, f)
+    # row 0: 2 shared of 6 distinct, 2 of 4 flat; row 1 identical; row 2 empty on both sides
+    assert abs(iou - (2 / 6 + 1 + 1) / 3) < 1e-12
+    assert abs(rec - (0.5 + 1 + 1) / 3) < 1e-12
