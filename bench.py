@@ -46,7 +46,7 @@ BLOCK_TILES_FROM = 256          # block scores in 16-query MFMA tiles
 FLAT_MFMA_FROM = 32             # flat scores in 16-query MFMA tiles
 
 WORKLOADS = ("decode_32k_x16", "chunked_prefill_32k", "long_context_128k", "long_decode_1m",
-             "tiny_prefill_4k", "decode_32k_x64", "decode_32k_x256")
+             "tiny_prefill_4k", "decode_32k_x64", "decode_32k_x256", "decode_varlen_x64")
 # decode batches of more sequences: the same step at larger batch, to show
 # where the decode path reaches its steady-state HBM fraction
 DECODE_BATCH = {"decode_32k_x16": 16, "decode_32k_x64": 64, "decode_32k_x256": 256}
@@ -183,6 +183,11 @@ class Setup:
             w = synth.decode_batch(nseq=ns)
             self.desc = ("%d sequences x 32768 keys, d=64 bf16 MoG; B=128 m=64 k=2048; per step: append "
                          "the key at 32767 of every sequence (rep update) + index its query at 32767" % ns)
+        elif name == "decode_varlen_x64":
+            w = synth.decode_varlen()
+            self.desc = ("64 sequences of mixed length (log-uniform in [4096, 131072], %d keys in all), d=64 bf16 "
+                         "MoG; B=128 m=64 k=2048; per step: append every sequence's last key (rep update) + index "
+                         "its query there, one launch for the batch" % int(w.seq_len.sum()))
         elif name == "chunked_prefill_32k":
             w = synth.chunked_prefill()
             self.desc = "32768 keys, all 32768 causal queries (MoG), d=64 bf16; B=128 m=64 k=2048"
@@ -204,7 +209,7 @@ class Setup:
         c = self.cache
         # decode workloads: the cache holds L-n_new keys, the step appends n_new
         self.append_src = None
-        if name in DECODE_BATCH:
+        if name in DECODE_BATCH or name == "decode_varlen_x64":
             c.set_lengths(w.seq_len - 1)
             last = np.stack([w.keys[int(o) + int(L) - 1] for o, L in zip(w.seq_key_off, w.seq_len)])
             self.append_src = device_mod.to_dev(last[:, None, :], dev)
@@ -548,6 +553,7 @@ def main():
     # replicas rotate about 4 GiB of keys so the 256 MB MALL cannot serve
     # repeated decode steps
     default_rep = {"decode_32k_x16": 64, "decode_32k_x64": 16, "decode_32k_x256": 4, "long_decode_1m": 256,
+                   "decode_varlen_x64": 16,
                    "chunked_prefill_32k": 1, "long_context_128k": 1, "tiny_prefill_4k": 1}
     R = args.replicas or default_rep[args.workload]
     log("setting up %s with %d replicas" % (args.workload, R))

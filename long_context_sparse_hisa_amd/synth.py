@@ -16,7 +16,8 @@ Key distributions:
     blocks 0 .. t // 128, plus 0.5 * N(0, I_64).
 
 Random streams per workload seed: 0 centroids and keys, 1 queries, 2 needle
-positions, 3 appended keys; 4, 5, 6 the attention queries, keys and values.
+positions, 3 appended keys; 4, 5, 6 the attention queries, keys and values;
+7 the sequence lengths of a mixed-length batch.
 
 Attention inputs (the consumer of the indices) are i.i.d. N(0, 1) rows of
 DA = 128 coordinates, one key and one value row beside each index key.
@@ -143,6 +144,28 @@ def decode_batch(nseq: int = 16, L: int = 32768, seed: int = 2, B: int = 128, m:
     w = Workload("decode_batch", keys, np.arange(nseq, dtype=np.int64) * cap,
                  np.full(nseq, L, np.int64), np.full(nseq, cap, np.int64), B, m, k)
     w.phases.append(Phase("decode", queries, pos, np.arange(nseq, dtype=np.int32)))
+    return w
+
+
+def decode_varlen(nseq: int = 64, lo: int = 4096, hi: int = 131072, seed: int = 7, B: int = 128, m: int = 64,
+                  k: int = 2048) -> Workload:
+    """nseq MoG sequences whose lengths are drawn log-uniformly from
+    [lo, hi] (stream 7), packed back to back, one query per sequence at its
+    last position: a decode batch of mixed lengths in one launch."""
+    gl, gk, gq = rng(seed, 7), rng(seed, 0), rng(seed, 1)
+    lens = np.exp(gl.uniform(np.log(lo), np.log(hi), nseq)).astype(np.int64)
+    lens = np.clip(lens, lo, hi)
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    keys = np.zeros((int(lens.sum()), D), np.uint16)
+    queries = np.zeros((nseq, D), np.uint16)
+    pos = lens - 1
+    for s in range(nseq):
+        L = int(lens[s])
+        cent = gk.standard_normal(((L + CENTROID_RUN - 1) // CENTROID_RUN, D), dtype=np.float32)
+        keys[offs[s]: offs[s] + L] = to_bf16(_mog_keys(gk, cent, 0, L))
+        queries[s] = to_bf16(_mog_queries(gq, cent, pos[s:s + 1]))[0]
+    w = Workload("decode_varlen", keys, offs, lens.copy(), lens.copy(), B, m, k)
+    w.phases.append(Phase("decode", queries, pos.astype(np.int64), np.arange(nseq, dtype=np.int32)))
     return w
 
 

@@ -295,6 +295,19 @@ def test_decode_32k_x256_batch():
         _check_phase(w, cache, w.phases[0], w.k, w.m, flat, label="dec256")
 
 
+def test_decode_varlen_x64_full():
+    """64 sequences of mixed length (4K to 128K keys, log-uniform) in one
+    decode launch, every query checked: per-sequence causal bounds and
+    forced blocks inside one call."""
+    print("decode varlen x64", flush=True)
+    dv = _dev()
+    w = synth.decode_varlen()
+    cache = dv.DeviceCache(w)
+    cache.pool()
+    for flat in (False, True):
+        _check_phase(w, cache, w.phases[0], w.k, w.m, flat, label="varlen")
+
+
 def test_chunked_prefill_32k_sampled():
     print("chunked prefill 32K", flush=True)
     dv = _dev()
