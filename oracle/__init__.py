@@ -4,10 +4,11 @@ TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the bench's
 CPU-baseline leg are the only callers.  The product path never imports this
 package, and this package imports nothing from the product package.
 
-The arithmetic lives in ``hisa_oracle.c`` (plain C, fp64, OpenMP over
-queries); this module compiles it with gcc on first use and marshals numpy
-arrays.  See the header of ``hisa_oracle.c`` for the passages of the pages
-each step follows and for the readings taken where the pages are silent.
+The arithmetic lives in ``hisa_oracle.c`` and ``lsa_oracle.c`` (LSA-Flat)
+(plain C, fp64, OpenMP over queries); this module compiles them with gcc on
+first use and marshals numpy arrays.  See the headers of the C files for the
+passages of the pages each step follows and for the readings taken where
+the pages are silent.
 """
 from __future__ import annotations
 
@@ -19,7 +20,7 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "hisa_oracle.c")
+_SRCS = [os.path.join(_HERE, "hisa_oracle.c"), os.path.join(_HERE, "lsa_oracle.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -32,11 +33,11 @@ _I32 = ctypes.c_int
 def build(force: bool = True) -> str:
     """Compile the oracle into ``oracle/liboracle.so`` (IEEE semantics kept:
     no fast-math, no FMA contraction)."""
-    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+    if not force and os.path.exists(_LIB) and all(os.path.getmtime(_LIB) >= os.path.getmtime(s) for s in _SRCS):
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
-           "-fno-fast-math", "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+           "-fno-fast-math", "-ffp-contract=off", "-o", tmp] + _SRCS + ["-lm"]
     subprocess.check_call(cmd)
     os.replace(tmp, _LIB)
     return _LIB
@@ -64,6 +65,13 @@ def _load():
                                                    ctypes.c_double, _P]
             lib.oracle_index_batch.argtypes = [_I32, _P, _P, _P, _I64, _P, _P, _P, _P, _P,
                                                _I32, _I32, _I32, _I32, _I32, _P, _P, _P]
+            lib.oracle_lsa_ward.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P]
+            lib.oracle_lsa_ward.restype = _I32
+            lib.oracle_lsa_block.argtypes = [_P, _I32, _P, _P, _P, _P]
+            lib.oracle_lsa_build.argtypes = [_P, _I64, _I32, _P, _P, _P, _P]
+            lib.oracle_lsa_query.argtypes = [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P]
+            lib.oracle_lsa_batch.argtypes = [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                             _P, _P]
             lib.oracle_bf16_round.argtypes = [ctypes.c_double]
             lib.oracle_bf16_round.restype = ctypes.c_uint16
             lib.oracle_threads.restype = ctypes.c_int
@@ -256,3 +264,78 @@ def attention_batch(qa, ka, v, key_off, lens, idx, scale: float) -> np.ndarray:
     _load().oracle_attention_batch(_ptr(qa), _ptr(ka), _ptr(v), nq, dh, _ptr(key_off), _ptr(lens), _ptr(idx),
                                    idx.shape[1], scale, _ptr(out))
     return out
+
+
+# ---- LSA-Flat (lsa_oracle.c) ----------------------------------------------------
+
+LSA_BLOCK = 512
+LSA_POINTS = 128
+LSA_BUCKETS = 64
+
+
+def lsa_ward(points, target: int, cap: int):
+    """Agglomerate the rows of points (fp64) by rounds of mutual cheapest
+    pairs down to `target` buckets of at most `cap` points.  Returns
+    (labels [n] -- each point's bucket root, the bucket's smallest point --,
+    merges [(kept, absorbed), ...] in merge order, margin, buckets left)."""
+    P = np.ascontiguousarray(points, np.float64)
+    n, d = P.shape
+    label = np.zeros(n, np.int32)
+    margin = np.zeros(1, np.float64)
+    merges = np.zeros(2 * n, np.int32)
+    nm = np.zeros(1, np.int32)
+    left = _load().oracle_lsa_ward(_ptr(P), n, d, target, cap, _ptr(label), _ptr(margin), _ptr(merges), _ptr(nm))
+    return label, merges[: 2 * int(nm[0])].reshape(-1, 2), float(margin[0]), int(left)
+
+
+def lsa_build(keys):
+    """Buckets of every complete 512-key block of one sequence: (centroids
+    [nblk*64, d] bf16 bits, members [nblk, 128] uint8, offs [nblk, 65]
+    uint8, margins [nblk])."""
+    keys = _u16(keys)
+    L, d = keys.shape
+    nblk = L // LSA_BLOCK
+    cen = np.zeros((max(nblk, 1) * LSA_BUCKETS, d), np.uint16)
+    mem = np.zeros((max(nblk, 1), LSA_POINTS), np.uint8)
+    off = np.zeros((max(nblk, 1), LSA_BUCKETS + 1), np.uint8)
+    mg = np.zeros(max(nblk, 1), np.float64)
+    rc = _load().oracle_lsa_build(_ptr(keys), L, d, _ptr(cen), _ptr(mem), _ptr(off), _ptr(mg))
+    if rc < 0:
+        raise ValueError("oracle_lsa_build failed")
+    return cen[: nblk * LSA_BUCKETS], mem[:nblk], off[:nblk], mg[:nblk]
+
+
+def lsa_query(q, cen, mem, off, t: int, p: int, k: int):
+    """One flat-search query: (idx [k], buckets [p], scores [p])."""
+    q = _u16(q)
+    cen = _u16(cen)
+    mem = np.ascontiguousarray(mem, np.uint8)
+    off = np.ascontiguousarray(off, np.uint8)
+    idx = np.zeros(k, np.int32)
+    bk = np.zeros(p, np.int32)
+    sc = np.zeros(p, np.float64)
+    rc = _load().oracle_lsa_query(_ptr(q), _ptr(cen), _ptr(mem), _ptr(off), mem.shape[0], t, q.shape[-1], p, k,
+                                  _ptr(idx), _ptr(bk), _ptr(sc))
+    if rc < 0:
+        raise ValueError("oracle_lsa_query: bad arguments")
+    return idx, bk, sc
+
+
+def lsa_batch(queries, q_pos, q_seq, cen, mem, off, seq_blk_off, seq_nblk, seq_len, p: int, k: int):
+    """Batched flat search over packed sequences: (idx [nq, k], buckets
+    [nq, p], ids relative to each query's sequence)."""
+    queries = _u16(queries)
+    nq, d = queries.shape
+    idx = np.zeros((nq, k), np.int32)
+    bk = np.zeros((nq, p), np.int32)
+    seq_len = np.ascontiguousarray(seq_len, np.int64)
+    rc = _load().oracle_lsa_batch(_ptr(queries), _ptr(np.ascontiguousarray(q_pos, np.int64)),
+                                  _ptr(None if q_seq is None else np.ascontiguousarray(q_seq, np.int32)), nq,
+                                  _ptr(_u16(cen)), _ptr(np.ascontiguousarray(mem, np.uint8)),
+                                  _ptr(np.ascontiguousarray(off, np.uint8)),
+                                  _ptr(np.ascontiguousarray(seq_blk_off, np.int64)),
+                                  _ptr(np.ascontiguousarray(seq_nblk, np.int64)), _ptr(seq_len), len(seq_len), d, p,
+                                  k, _ptr(idx), _ptr(bk))
+    if rc != 0:
+        raise ValueError("oracle_lsa_batch: bad arguments")
+    return idx, bk
