@@ -52,6 +52,8 @@ WORKLOADS = ("decode_32k_x16", "chunked_prefill_32k", "long_context_128k", "long
 DECODE_BATCH = {"decode_32k_x16": 16, "decode_32k_x64": 64, "decode_32k_x256": 256}
 
 ATTN_WORKLOADS = ("decode_32k_x16",)
+# LSA-Flat leg: workload -> (p buckets searched, k keys); p = k / 8 (8 keys per bucket on average)
+LSA_WORKLOADS = {"decode_32k_x16": (256, 2048), "decode_32k_x64": (256, 2048), "decode_varlen_x64": (256, 2048)}
 ATTN_SEED = 56
 
 STAGES_HISA = ("block_stage", "token_scores", "token_topk")
@@ -311,6 +313,74 @@ class AttentionLeg:
         self.calls[flat][r % self.replicas].run()
 
 
+class LsaLeg:
+    """LSA-Flat on the workload's keys: the bucket cache of every complete
+    512-key block (built once, timed), replicated like the key cache, and
+    one flat-search call per replica over the step's queries."""
+
+    def __init__(self, S, replicas, p, k, device_mod, torch):
+        self.S, self.p, self.k = S, p, k
+        self.torch = torch
+        self.lsa = device_mod.LsaCache(S.cache)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        self.lsa.build()
+        e1.record()
+        torch.cuda.synchronize()
+        self.build_ms = e0.elapsed_time(e1)
+        self.nblk = int(self.lsa.nblk.sum())
+        ph = S.phases[0]
+        base = device_mod.LsaCall(self.lsa, ph.queries, ph.q_pos, ph.q_seq, p, k, buckets=False)
+        self.out_idx = base.out_idx
+        self.calls = []
+        L = self.lsa
+        for r in range(replicas):
+            cen = L.centroids if r == 0 else L.centroids.clone()
+            mem = L.members if r == 0 else L.members.clone()
+            off = L.offs if r == 0 else L.offs.clone()
+            a = S.h.make_lsa_args(base.queries, base.q_pos, cen, mem, off, L.d_blk_off, L.d_nblk, S.cache.d_len,
+                                  base.max_len, p, k, q_seq=base.q_seq, out_idx=base.out_idx,
+                                  workspace=base.workspace)
+            self.calls.append((a, cen, mem, off))
+        self.base = base
+        self.replicas = replicas
+
+    def run(self, r):
+        """One decode step: the same key append as the other methods' steps
+        (the search does not read the new key until its block completes),
+        then the search."""
+        S = self.S
+        if S.append_src is not None:
+            rr = r % S.replicas
+            S.h.hisa_append_keys(S.keys[rr], S.reps[rr], S.seqs, S.append_src, S.B)
+        S.h.hisa_lsa_index(self.calls[r % self.replicas][0])
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        n = max(self.replicas, self.S.replicas)
+        for r in range(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.run(r)
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % n].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[(warmup + i) % n].replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3
+
+
 def attention_kernel_ms(S, A, nsteps, torch):
     """Average duration of the attention call (both of its kernels), from
     torch events on the stream it runs on, queued behind a sleep kernel so
@@ -519,6 +589,8 @@ def main():
                     help="eager steps whose stages are timed with HIP events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attention", action="store_true", help="skip the sparse-attention leg")
+    ap.add_argument("--no-lsa", action="store_true", help="skip the LSA-Flat leg")
+    ap.add_argument("--lsa-replicas", type=int, default=8, help="copies of the LSA bucket cache rotated over")
     ap.add_argument("--sweep-m", default=None, metavar="M1,M2,...",
                     help="instead of the default line: HISA at each m and block-only selection, time per "
                          "step and overlap with the flat indexer's rows")
@@ -630,6 +702,35 @@ def main():
                      "ms_per_step_hisa_plus_attention": ha_ms, "ms_per_step_flat_plus_attention": fa_ms,
                      "speedup_vs_flat": fa_ms / ha_ms}
 
+    lsa = None
+    if args.workload in LSA_WORKLOADS and not args.no_lsa:
+        p_l, k_l = LSA_WORKLOADS[args.workload]
+        log("LSA-Flat leg: build and %d replicas (p=%d, k=%d)" % (args.lsa_replicas, p_l, k_l))
+        Lg = LsaLeg(S, args.lsa_replicas, p_l, k_l, device, torch)
+        l_ms = Lg.time_steps(args.steps, args.warmup)
+        Lg.run(0)
+        S.step(0, True, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        f_rows = S.calls[True][0][0].out_idx.cpu().numpy()
+        l_rows = Lg.out_idx.cpu().numpy()
+        S.step(0, False, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        h_rows = S.calls[False][0][0].out_idx.cpu().numpy()
+        l_iou, l_rec = row_overlap(l_rows, f_rows)
+        h_iou, h_rec = row_overlap(h_rows, f_rows)
+        per_block_us = Lg.build_ms * 1e3 / max(Lg.nblk, 1)
+        lsa = {"description": "LSA-Flat on the same keys and queries: 64 buckets per complete 512-key block "
+                              "(Ward, fp64), p=%d buckets searched, k=%d keys; %d replicas of the bucket cache"
+                              % (p_l, k_l, args.lsa_replicas),
+               "ms_per_step": l_ms, "speedup_vs_flat": f_ms / l_ms, "vs_hisa": h_ms / l_ms,
+               "build_ms": Lg.build_ms, "blocks_built": Lg.nblk, "build_us_per_block": per_block_us,
+               "build_us_per_decode_step_amortized": per_block_us * S.cache.nseq / 512.0,
+               "iou_vs_flat": l_iou, "recall_of_flat_topk": l_rec,
+               "hisa_iou_vs_flat": h_iou, "hisa_recall_of_flat_topk": h_rec,
+               "note": "a step is the same key append as HISA's and flat's steps, then the search; a sequence "
+                       "completes a block every 512 decode steps, so the build adds "
+                       "build_us_per_decode_step_amortized per step"}
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -668,6 +769,7 @@ def main():
                               "frac": f_achieved / fpeak}},
         "speedup_vs_flat": f_ms / h_ms,
         "attention": attention,
+        "lsa_flat": lsa,
     }
     print(json.dumps(out), flush=True)
 

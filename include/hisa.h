@@ -260,6 +260,87 @@ int hisa_attention_workspace_bytes(const hisa_attn_args* a, size_t* bytes);
  */
 int hisa_sparse_attention(const hisa_attn_args* a, void* stream);
 
+/*
+ * LSA-Flat: semantic buckets instead of positional blocks, the indexer of
+ * the latent sparse attention digest (section on how LSA works, steps 1-4
+ * and Fig. 2, Flat search; footnote 3 for the fill to exactly k), on the
+ * same d = 64 bf16 index keys.
+ *
+ * Cache of one sequence, per complete block of HISA_LSA_BLOCK keys
+ * (block b covers keys 512 b .. 512 b + 511):
+ *   centroids [nblk * 64, 64] bf16   unit centroid of each bucket
+ *   members   [nblk, 128] uint8      the block's pool keys (pool key i =
+ *                                    keys 4i .. 4i+3) grouped by bucket,
+ *                                    ascending inside a bucket
+ *   offs      [nblk, 65] uint8       bucket j holds members[offs[j] ..
+ *                                    offs[j+1]); 1 to 4 pool keys each
+ * Buckets are numbered by their smallest pool key.  Several sequences pack
+ * their block rows back to back (seq_blk_off below).
+ */
+#define HISA_LSA_BLOCK 512
+#define HISA_LSA_BUCKETS 64
+#define HISA_LSA_POOL_KEYS 128
+#define HISA_LSA_MAX_P 4096
+#define HISA_LSA_MAX_LEN (1LL << 20)
+
+/*
+ * hisa_lsa_build -- buckets of blocks first_block .. len/512 - 1 of one
+ * sequence: keys [len, 64] bf16 (16-byte aligned) are L2-normalised, summed
+ * four at a time into 128 pool keys per block, and merged by rounds of
+ * mutually cheapest pairs under Ward's criterion (fp64), at most 16 keys
+ * per bucket, down to 64 buckets; the cheapest pairs merge first when a
+ * round offers more than are needed.  centroids, members and offs point at
+ * the sequence's block row 0.  A block whose keys hold non-finite values
+ * gets 64 empty buckets.  One workgroup per block.
+ * Errors: INVALID_ARG (null pointer with blocks to build, len < 0,
+ *         first_block < 0), UNSUPPORTED (d != 64, len > HISA_LSA_MAX_LEN,
+ *         misaligned keys).
+ */
+int hisa_lsa_build(const uint16_t* keys, int64_t len, int64_t first_block, int d, uint16_t* centroids,
+                   uint8_t* members, uint8_t* offs, void* stream);
+
+typedef struct hisa_lsa_args {
+    const uint16_t* queries;     /* [nq, 64] bf16 index queries */
+    const int64_t* q_pos;        /* [nq] position of each query in its sequence */
+    const int32_t* q_seq;        /* [nq] sequence of each query, or NULL: sequence 0 */
+    int64_t nq;
+    const uint16_t* centroids;   /* the cache above, all sequences' block rows */
+    const uint8_t* members;
+    const uint8_t* offs;
+    const int64_t* seq_blk_off;  /* [nseq] first block row of each sequence */
+    const int64_t* seq_nblk;     /* [nseq] built blocks of each sequence */
+    const int64_t* seq_len;      /* [nseq] keys of each sequence */
+    int32_t nseq;
+    int64_t max_len;             /* HOST bound: every seq_len <= max_len <= HISA_LSA_MAX_LEN */
+    int32_t d;                   /* must be 64 */
+    int32_t p;                   /* buckets searched, 1 .. HISA_LSA_MAX_P */
+    int32_t k;                   /* keys out, 1 .. HISA_MAX_K */
+    int32_t* out_idx;            /* [nq, k] positions ascending, then -1 */
+    int32_t* out_buckets;        /* [nq, p] or NULL: the buckets keys came from, in rank order
+                                    (ids relative to the sequence: block * 64 + bucket), then -1 */
+    void* workspace;
+    size_t workspace_bytes;      /* at least hisa_lsa_workspace_bytes */
+} hisa_lsa_args;
+
+/* Workspace for hisa_lsa_index with these sizes. */
+int hisa_lsa_workspace_bytes(const hisa_lsa_args* a, size_t* bytes);
+
+/*
+ * hisa_lsa_index -- LSA flat search.  A query at t sees the built blocks
+ * that end at or before t (min(floor((t+1)/512), seq_nblk) of them); every
+ * visible centroid is scored by its dot product with the query (fp32; the
+ * query's normalisation would not change the order), the p best buckets
+ * are ranked (score descending, lower id first), and their keys are taken
+ * bucket by bucket, each in ascending position, until k: the row is those
+ * positions ascending, then -1.  A query with no visible block, or whose
+ * position or sequence is out of range, gets a row of -1.  Three kernels
+ * and the flat indexer's selection on `stream`.
+ * Errors: INVALID_ARG (null required pointer with nq > 0, nq < 0, nseq < 1,
+ *         p < 1, k < 1, max_len < 1), UNSUPPORTED (d, p, k, max_len beyond
+ *         the limits), WORKSPACE.
+ */
+int hisa_lsa_index(const hisa_lsa_args* a, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* hisa_status_str(int status);
 

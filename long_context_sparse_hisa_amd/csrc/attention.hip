@@ -80,7 +80,7 @@ __device__ __forceinline__ float wave_max_f32(float x)
 // chunk saw a valid index).  One round trip for everything: thread g loads
 // (m_g, l_g), and every thread loads its column of the first chunks of its
 // half of the workgroup (even or odd g) before the maximum is known.
-__device__ void attn_merge(const float* st, int G, float* out_row, float* s_f, float* s_half)
+__device__ __forceinline__ void attn_merge(const float* st, int G, float* out_row, float* s_f, float* s_half)
 {
     constexpr int kPre = 8;
     const int t = threadIdx.x;

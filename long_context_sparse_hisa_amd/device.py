@@ -164,3 +164,76 @@ class AttentionCall:
     def result(self) -> np.ndarray:
         torch.cuda.synchronize()
         return self.out.cpu().numpy()
+
+
+class LsaCache:
+    """Bucket cache (centroids, members, offsets) of a DeviceCache's
+    sequences, built by hisa_lsa_build over each sequence's complete
+    512-key blocks."""
+
+    def __init__(self, cache: DeviceCache):
+        self.cache = cache
+        dev = cache.device
+        cap_blocks = cache.seq_cap // hisa.HISA_LSA_BLOCK
+        self.seq_blk_off = np.concatenate([[0], np.cumsum(cap_blocks)[:-1]]).astype(np.int64)
+        nb = max(int(cap_blocks.sum()), 1)
+        self.centroids = torch.zeros((nb * hisa.HISA_LSA_BUCKETS, D), dtype=torch.int16, device=dev)
+        self.members = torch.zeros((nb, hisa.HISA_LSA_POOL_KEYS), dtype=torch.uint8, device=dev)
+        self.offs = torch.zeros((nb, hisa.HISA_LSA_BUCKETS + 1), dtype=torch.uint8, device=dev)
+        self.nblk = np.zeros(cache.nseq, np.int64)
+        self.d_blk_off = to_dev(self.seq_blk_off, dev)
+        self.d_nblk = to_dev(self.nblk, dev)
+
+    def build(self, stream=None):
+        """Build every complete block not built yet."""
+        c = self.cache
+        for s in range(c.nseq):
+            o, n, b = int(c.seq_key_off[s]), int(c.seq_len[s]), int(self.seq_blk_off[s])
+            full = n // hisa.HISA_LSA_BLOCK
+            if full > self.nblk[s]:
+                hisa.hisa_lsa_build(c.keys[o:o + n], int(self.nblk[s]), self.centroids[b * hisa.HISA_LSA_BUCKETS:],
+                                    self.members[b:], self.offs[b:], stream)
+                self.nblk[s] = full
+        self.d_nblk.copy_(torch.from_numpy(self.nblk))
+
+    def host(self, s: int):
+        """(centroids, members, offs) of sequence s as numpy arrays."""
+        b, n = int(self.seq_blk_off[s]), int(self.nblk[s])
+        torch.cuda.synchronize()
+        return (self.centroids[b * hisa.HISA_LSA_BUCKETS:(b + n) * hisa.HISA_LSA_BUCKETS].cpu().numpy().view(np.uint16),
+                self.members[b:b + n].cpu().numpy(), self.offs[b:b + n].cpu().numpy())
+
+
+class LsaCall:
+    """Buffers and arguments of one LSA flat-search call."""
+
+    def __init__(self, lsa: LsaCache, queries, q_pos, q_seq, p: int, k: int, max_len: int | None = None,
+                 buckets: bool = True):
+        c = lsa.cache
+        dev = c.device
+        self.lsa = lsa
+        self.queries = queries if isinstance(queries, torch.Tensor) else to_dev(queries, dev)
+        self.q_pos = q_pos if isinstance(q_pos, torch.Tensor) else to_dev(np.asarray(q_pos, np.int64), dev)
+        self.q_seq = q_seq if isinstance(q_seq, torch.Tensor) else to_dev(np.asarray(q_seq, np.int32), dev)
+        nq = self.queries.shape[0]
+        self.p, self.k = p, k
+        self.out_idx = torch.empty((nq, k), dtype=torch.int32, device=dev)
+        self.out_buckets = torch.empty((nq, p), dtype=torch.int32, device=dev) if buckets else None
+        self.max_len = int(max_len if max_len is not None else c.seq_cap.max())
+        nbytes = hisa.hisa_lsa_workspace_bytes(self._args(None))
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.args = self._args(self.workspace)
+
+    def _args(self, ws):
+        lsa, c = self.lsa, self.lsa.cache
+        return hisa.make_lsa_args(self.queries, self.q_pos, lsa.centroids, lsa.members, lsa.offs, lsa.d_blk_off,
+                                  lsa.d_nblk, c.d_len, self.max_len, self.p, self.k, q_seq=self.q_seq,
+                                  out_idx=self.out_idx, out_buckets=self.out_buckets, workspace=ws)
+
+    def run(self, stream=None):
+        hisa.hisa_lsa_index(self.args, stream or self.lsa.cache.stream)
+
+    def results(self):
+        torch.cuda.synchronize()
+        return (self.out_idx.cpu().numpy(),
+                None if self.out_buckets is None else self.out_buckets.cpu().numpy())

@@ -50,6 +50,19 @@ class hisa_index_args(ctypes.Structure):
 
 HISA_STAGES = 3
 HISA_ATTN_DIM = 128
+HISA_LSA_BLOCK = 512
+HISA_LSA_BUCKETS = 64
+HISA_LSA_POOL_KEYS = 128
+
+
+class hisa_lsa_args(ctypes.Structure):
+    _fields_ = [
+        ("queries", _P), ("q_pos", _P), ("q_seq", _P), ("nq", ctypes.c_int64),
+        ("centroids", _P), ("members", _P), ("offs", _P),
+        ("seq_blk_off", _P), ("seq_nblk", _P), ("seq_len", _P), ("nseq", ctypes.c_int32),
+        ("max_len", ctypes.c_int64), ("d", ctypes.c_int32), ("p", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("out_idx", _P), ("out_buckets", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+    ]
 
 
 class hisa_attn_args(ctypes.Structure):
@@ -81,6 +94,9 @@ def lib():
         L.hisa_attention_workspace_bytes.argtypes = [ctypes.POINTER(hisa_attn_args),
                                                      ctypes.POINTER(ctypes.c_size_t)]
         L.hisa_sparse_attention.argtypes = [ctypes.POINTER(hisa_attn_args), _P]
+        L.hisa_lsa_build.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _P, _P, _P, _P]
+        L.hisa_lsa_workspace_bytes.argtypes = [ctypes.POINTER(hisa_lsa_args), ctypes.POINTER(ctypes.c_size_t)]
+        L.hisa_lsa_index.argtypes = [ctypes.POINTER(hisa_lsa_args), _P]
         L.hisa_status_str.restype = ctypes.c_char_p
         L.hisa_status_str.argtypes = [ctypes.c_int]
         L.hisa_abi_version.restype = ctypes.c_int
@@ -232,6 +248,50 @@ def hisa_attention_workspace_bytes(args: hisa_attn_args) -> int:
 
 def hisa_sparse_attention(args: hisa_attn_args, stream=None):
     _check(lib().hisa_sparse_attention(ctypes.byref(args), _stream(stream)), "hisa_sparse_attention")
+
+
+def hisa_lsa_build(keys, first_block: int, centroids, members, offs, stream=None):
+    """Buckets of blocks first_block .. len(keys)//512 - 1 of one sequence
+    (keys [L, 64] bf16 bits; cache arrays start at the sequence's block 0)."""
+    rc = lib().hisa_lsa_build(_dev(keys, "keys", 2), keys.shape[0], int(first_block), keys.shape[1],
+                              _dev(centroids, "centroids", 2), _dev(members, "members", 1),
+                              _dev(offs, "offs", 1), _stream(stream))
+    _check(rc, "hisa_lsa_build")
+
+
+def make_lsa_args(queries, q_pos, centroids, members, offs, seq_blk_off, seq_nblk, seq_len, max_len: int, p: int,
+                  k: int, *, q_seq=None, out_idx=None, out_buckets=None, workspace=None) -> hisa_lsa_args:
+    a = hisa_lsa_args()
+    a.queries = _dev(queries, "queries", 2)
+    a.q_pos = _dev(q_pos, "q_pos", 8)
+    a.q_seq = _dev(q_seq, "q_seq", 4)
+    a.nq = queries.shape[0]
+    a.centroids = _dev(centroids, "centroids", 2)
+    a.members = _dev(members, "members", 1)
+    a.offs = _dev(offs, "offs", 1)
+    a.seq_blk_off = _dev(seq_blk_off, "seq_blk_off", 8)
+    a.seq_nblk = _dev(seq_nblk, "seq_nblk", 8)
+    a.seq_len = _dev(seq_len, "seq_len", 8)
+    a.nseq = seq_len.shape[0]
+    a.max_len = int(max_len)
+    a.d = queries.shape[1]
+    a.p, a.k = p, k
+    a.out_idx = _dev(out_idx, "out_idx", 4)
+    a.out_buckets = _dev(out_buckets, "out_buckets", 4)
+    if workspace is not None:
+        a.workspace = _dev(workspace, "workspace")
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def hisa_lsa_workspace_bytes(args: hisa_lsa_args) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().hisa_lsa_workspace_bytes(ctypes.byref(args), ctypes.byref(b)), "hisa_lsa_workspace_bytes")
+    return int(b.value)
+
+
+def hisa_lsa_index(args: hisa_lsa_args, stream=None):
+    _check(lib().hisa_lsa_index(ctypes.byref(args), _stream(stream)), "hisa_lsa_index")
 
 
 # ---- HIP events (stage timing) -------------------------------------------------

@@ -163,3 +163,46 @@ def test_block_index_validation(lib):
     assert _rc(lib.hisa_block_index, _args(k=64 * 128, out_scores=FAKE)) == hisa.HISA_ERR_INVALID_ARG
     assert _rc(lib.hisa_block_index, _args(k=64 * 128, B=100)) == hisa.HISA_ERR_UNSUPPORTED
     assert _rc(lib.hisa_block_index, _args(k=64 * 128, nq=0, queries=None)) == hisa.HISA_OK
+
+
+def _lsa(**kw):
+    a = hisa.hisa_lsa_args()
+    a.queries = a.q_pos = a.centroids = a.members = a.offs = FAKE
+    a.seq_blk_off = a.seq_nblk = a.seq_len = a.out_idx = FAKE
+    a.nq, a.nseq, a.max_len, a.d, a.p, a.k = 16, 1, 32768, 64, 256, 2048
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("d", 32, hisa.HISA_ERR_UNSUPPORTED),
+    ("p", 0, hisa.HISA_ERR_INVALID_ARG),
+    ("p", 4097, hisa.HISA_ERR_UNSUPPORTED),
+    ("k", 0, hisa.HISA_ERR_INVALID_ARG),
+    ("k", 16385, hisa.HISA_ERR_UNSUPPORTED),
+    ("max_len", (1 << 20) + 1, hisa.HISA_ERR_UNSUPPORTED),
+    ("nseq", 0, hisa.HISA_ERR_INVALID_ARG),
+    ("centroids", None, hisa.HISA_ERR_INVALID_ARG),
+    ("seq_nblk", None, hisa.HISA_ERR_INVALID_ARG),
+])
+def test_lsa_index_validation(lib, field, value, code):
+    a = _lsa(**{field: value})
+    assert lib.hisa_lsa_index(ctypes.byref(a), None) == code
+
+
+def test_lsa_workspace_and_build_validation(lib):
+    a = _lsa()
+    assert lib.hisa_lsa_index(ctypes.byref(a), None) == hisa.HISA_ERR_WORKSPACE
+    n = hisa.hisa_lsa_workspace_bytes(a)
+    # the ranked bucket lists (ids and scores) of every query come first
+    assert n > 16 * 256 * 8
+    a = _lsa(nq=0, queries=None)
+    assert lib.hisa_lsa_index(ctypes.byref(a), None) == hisa.HISA_OK
+    P = ctypes.c_void_p
+    assert lib.hisa_lsa_build(P(FAKE), 4096, 0, 32, P(FAKE), P(FAKE), P(FAKE), None) == hisa.HISA_ERR_UNSUPPORTED
+    assert lib.hisa_lsa_build(P(FAKE), -1, 0, 64, P(FAKE), P(FAKE), P(FAKE), None) == hisa.HISA_ERR_INVALID_ARG
+    assert lib.hisa_lsa_build(P(FAKE + 2), 4096, 0, 64, P(FAKE), P(FAKE), P(FAKE), None) == hisa.HISA_ERR_UNSUPPORTED
+    assert lib.hisa_lsa_build(P(FAKE), 511, 0, 64, P(FAKE), P(FAKE), P(FAKE), None) == hisa.HISA_OK
+    assert lib.hisa_lsa_build(P(FAKE), 4096, 8, 64, P(FAKE), P(FAKE), P(FAKE), None) == hisa.HISA_OK
+    assert lib.hisa_lsa_build(None, 4096, 0, 64, P(FAKE), P(FAKE), P(FAKE), None) == hisa.HISA_ERR_INVALID_ARG
