@@ -280,7 +280,7 @@ int hisa_sparse_attention(const hisa_attn_args* a, void* stream);
 #define HISA_LSA_BLOCK 512
 #define HISA_LSA_BUCKETS 64
 #define HISA_LSA_POOL_KEYS 128
-#define HISA_LSA_MAX_P 4096
+#define HISA_LSA_MAX_P 2048
 #define HISA_LSA_MAX_LEN (1LL << 20)
 
 /*

@@ -301,13 +301,14 @@ constexpr int kLsaMaxWords = (int)(HISA_LSA_MAX_LEN / kLsaBlock * kLsaPoints / 3
 // in the form the flat indexer takes (keys -> centroids).
 __global__ void lsa_meta_kernel(const int64_t* q_pos, const int32_t* q_seq, int64_t nq, const int64_t* seq_blk_off,
                                 const int64_t* seq_nblk, const int64_t* seq_len, int nseq, int64_t max_blocks,
-                                int64_t* q_bucket, int64_t* seq_boff, int64_t* seq_blen)
+                                int64_t* q_bucket, int64_t* q_blk_off, int64_t* seq_boff, int64_t* seq_blen)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < nq) {
         const int s = q_seq ? q_seq[i] : 0;
-        int64_t last = -1;
+        int64_t last = -1, bo = 0;
         if (s >= 0 && s < nseq) {
+            bo = seq_blk_off[s];
             const int64_t t = q_pos[i];
             if (t >= 0 && t < seq_len[s]) {
                 // never more blocks than the host bound the fill kernel's
@@ -317,6 +318,7 @@ __global__ void lsa_meta_kernel(const int64_t* q_pos, const int32_t* q_seq, int6
             }
         }
         q_bucket[i] = last;
+        q_blk_off[i] = bo;
     }
     if (i < nseq) {
         seq_boff[i] = seq_blk_off[i] * kLsaBuckets;
@@ -324,110 +326,182 @@ __global__ void lsa_meta_kernel(const int64_t* q_pos, const int32_t* q_seq, int6
     }
 }
 
-// One workgroup per query: rank the selected buckets (score descending,
-// lower id first) with a bitonic sort of 64-bit keys, scan their sizes in
-// rank order, mark the pool keys of the buckets that fit (the last one cut
-// to the keys left) in a bitmap, then write the positions in ascending
-// order.
+// One workgroup per query.  Every selected bucket's id, score, offsets and
+// members are loaded up front (three dependent round trips, all entries at
+// once) into a 64-bit payload; the buckets are ranked (score descending,
+// lower id first: the selection lists them by ascending id, so the entry
+// index breaks ties) by counting for up to kLsaCountRank entries, by a
+// bitonic sort beyond; their sizes are scanned in rank order, the pool keys
+// of the buckets that fit (the last one cut to the keys left) are marked
+// in a bitmap, and the positions are written in ascending order.
+constexpr int kLsaCountRank = 512;
+
+__host__ __device__ constexpr size_t lsa_rank_bytes(int P2)
+{
+    return (size_t)P2 * 16 > (size_t)kLsaFillThreads * 4 ? (size_t)P2 * 16 : (size_t)kLsaFillThreads * 4;
+}
+
+// payload: bucket id (bits 0-31), pool-key count (32-34), up to four
+// member pool keys (7 bits each from bit 35)
+__device__ __forceinline__ uint64_t lsa_payload(uint32_t id, int n, const int (&m)[kLsaCap])
+{
+    uint64_t v = (uint64_t)id | ((uint64_t)n << 32);
+#pragma unroll
+    for (int j = 0; j < kLsaCap; ++j) v |= (uint64_t)(m[j] & 127) << (35 + 7 * j);
+    return v;
+}
+
 __global__ __launch_bounds__(kLsaFillThreads) void lsa_fill_kernel(const int32_t* sel, const float* score, int p,
                                                                    int P2, const int64_t* q_bucket,
-                                                                   const int32_t* q_seq, const int64_t* seq_blk_off,
-                                                                   const uint8_t* members, const uint8_t* offs, int k,
-                                                                   int32_t* out_idx, int32_t* out_buckets)
+                                                                   const int64_t* q_blk_off, const uint8_t* members,
+                                                                   const uint8_t* offs, int k, int32_t* out_idx,
+                                                                   int32_t* out_buckets)
 {
     extern __shared__ uint64_t s_dyn[];
-    uint64_t* skey = s_dyn;                                     // [P2]
-    uint32_t* bits = reinterpret_cast<uint32_t*>(skey + P2);    // [visible words]
+    uint64_t* skey = s_dyn;                                     // [P2] rank keys, then sorted
+    uint64_t* pay = skey + P2;                                  // [P2] payload by entry
+    // [visible words], after the rank arrays (at least one int per thread:
+    // they hold the owners' first slots at the end)
+    uint32_t* bits = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(s_dyn) + lsa_rank_bytes(P2));
     __shared__ int s_scan[kLsaFillThreads / 64];
     __shared__ int s_part_g, s_part_n;
+    constexpr int kPer = kLsaMaxP / kLsaFillThreads;            // entries per thread
     const int t = threadIdx.x;
     const int64_t row = blockIdx.x;
     int32_t* orow = out_idx + row * (int64_t)k;
     int32_t* brow = out_buckets ? out_buckets + row * (int64_t)p : nullptr;
+    // one round trip for the query's meta data and its selected buckets
+    // (rows of an invalid query hold -1 entries), then the offsets, then
+    // the members
     const int64_t last = q_bucket[row];
+    const int64_t boff = q_blk_off[row];
+    int32_t id[kPer];
+    uint32_t sk[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = t + j * kLsaFillThreads;
+        id[j] = i < p ? sel[row * p + i] : -1;
+        sk[j] = i < p ? score_key(score[row * p + i]) : 0u;
+    }
     if (last < 0) {
         for (int e = t; e < k; e += kLsaFillThreads) orow[e] = -1;
         if (brow)
             for (int e = t; e < p; e += kLsaFillThreads) brow[e] = -1;
         return;
     }
-    const int64_t boff = seq_blk_off[q_seq ? q_seq[row] : 0];
     const int words = (int)((last + 1) / kLsaBuckets) * (kLsaPoints / 32);
-    for (int i = t; i < P2; i += kLsaFillThreads) {
-        uint64_t key = 0;
-        if (i < p) {
-            const int32_t id = sel[row * p + i];
-            if (id >= 0)
-                key = ((uint64_t)score_key(score[row * p + i]) << 32) | (uint32_t)~(uint32_t)id;
+    int o0[kPer], o1[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        o0[j] = o1[j] = 0;
+        if (id[j] >= 0) {
+            const int64_t base = (boff + id[j] / kLsaBuckets) * (kLsaBuckets + 1) + id[j] % kLsaBuckets;
+            // offsets clamped to the block row: a damaged cache cannot send
+            // the reads past it
+            o1[j] = min((int)offs[base + 1], kLsaPoints);
+            o0[j] = min((int)offs[base], o1[j]);
+            o1[j] = min(o1[j], o0[j] + kLsaCap);
         }
-        skey[i] = key;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = t + j * kLsaFillThreads;
+        if (i >= P2) continue;
+        int m[kLsaCap];
+        const uint8_t* mrow = members + (boff + max(id[j], 0) / kLsaBuckets) * kLsaPoints;
+#pragma unroll
+        for (int c = 0; c < kLsaCap; ++c) m[c] = o0[j] + c < o1[j] ? mrow[o0[j] + c] : 0;
+        pay[i] = lsa_payload((uint32_t)id[j], o1[j] - o0[j], m);
+        skey[i] = id[j] >= 0 ? ((uint64_t)sk[j] << 32) | (uint32_t)~(uint32_t)i : 0ull;
     }
     for (int i = t; i < words; i += kLsaFillThreads) bits[i] = 0u;
     if (t == 0) {
         s_part_g = -1;
         s_part_n = 0;
     }
-    // bitonic sort, descending
-    for (int size = 2; size <= P2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            __syncthreads();
-            for (int i = t; i < (P2 >> 1); i += kLsaFillThreads) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const uint64_t x = skey[lo], y = skey[hi];
-                if ((x < y) == desc) {
-                    skey[lo] = y;
-                    skey[hi] = x;
+    __syncthreads();
+    if (P2 <= kLsaCountRank) {
+        // rank = number of larger keys (keys are distinct); then place
+        uint64_t mine[kLsaCountRank / kLsaFillThreads];
+        int rank[kLsaCountRank / kLsaFillThreads];
+#pragma unroll
+        for (int j = 0; j < kLsaCountRank / kLsaFillThreads; ++j) {
+            const int i = t + j * kLsaFillThreads;
+            mine[j] = i < P2 ? skey[i] : 0ull;
+            int r = 0;
+            for (int x = 0; x < P2; ++x) r += skey[x] > mine[j] ? 1 : 0;
+            rank[j] = r;
+        }
+        __syncthreads();
+        // clear, then place the keys of real buckets (the empty ones rank
+        // last and stay zero)
+#pragma unroll
+        for (int j = 0; j < kLsaCountRank / kLsaFillThreads; ++j) {
+            const int i = t + j * kLsaFillThreads;
+            if (i < P2) skey[i] = 0ull;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kLsaCountRank / kLsaFillThreads; ++j) {
+            const int i = t + j * kLsaFillThreads;
+            if (i < P2 && mine[j] != 0ull) skey[rank[j]] = mine[j];
+        }
+    } else {
+        for (int size = 2; size <= P2; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int i = t; i < (P2 >> 1); i += kLsaFillThreads) {
+                    const int lo = 2 * i - (i & (stride - 1));
+                    const int hi = lo + stride;
+                    const bool desc = (lo & size) == 0;
+                    const uint64_t x = skey[lo], y = skey[hi];
+                    if ((x < y) == desc) {
+                        skey[lo] = y;
+                        skey[hi] = x;
+                    }
                 }
+                __syncthreads();
             }
         }
     }
     __syncthreads();
     // sizes in rank order: thread t owns ranks [t * per, (t + 1) * per)
     const int per = (P2 + kLsaFillThreads - 1) / kLsaFillThreads;
-    int mine = 0;
+    int mine_keys = 0;
     for (int j = 0; j < per; ++j) {
         const int r = t * per + j;
-        if (r < p && skey[r] != 0) {
-            const uint32_t id = ~(uint32_t)skey[r];
-            const int64_t blk = boff + id / kLsaBuckets;
-            const int lb = id % kLsaBuckets;
-            const int o1 = min((int)offs[blk * (kLsaBuckets + 1) + lb + 1], kLsaPoints);
-            mine += kLsaPool * max(o1 - (int)offs[blk * (kLsaBuckets + 1) + lb], 0);
-        }
+        if (r < p && skey[r] != 0ull)
+            mine_keys += kLsaPool * (int)((pay[~(uint32_t)skey[r]] >> 32) & 7u);
     }
-    int excl = wg_incl_scan<kLsaFillThreads>(mine, s_scan) - mine;
+    int excl = wg_incl_scan<kLsaFillThreads>(mine_keys, s_scan) - mine_keys;
     for (int j = 0; j < per; ++j) {
         const int r = t * per + j;
         if (r >= p) break;
         int32_t used = -1;
-        if (skey[r] != 0 && excl < k) {
-            const uint32_t id = ~(uint32_t)skey[r];
-            const int64_t blk = boff + id / kLsaBuckets;
-            const int lb = id % kLsaBuckets;
-            // offsets clamped to the block row: a damaged cache cannot send
-            // the reads past it
-            const int o1 = min((int)offs[blk * (kLsaBuckets + 1) + lb + 1], kLsaPoints);
-            const int o0 = min((int)offs[blk * (kLsaBuckets + 1) + lb], o1);
-            const int take = min(kLsaPool * (o1 - o0), k - excl);
-            for (int m = o0; m < o1; ++m) {
-                const int got = take - kLsaPool * (m - o0);
+        if (skey[r] != 0ull && excl < k) {
+            const uint64_t v = pay[~(uint32_t)skey[r]];
+            const uint32_t bid = (uint32_t)v;
+            const int n = (int)((v >> 32) & 7u);
+            const int take = min(kLsaPool * n, k - excl);
+            for (int c = 0; c < n; ++c) {
+                const int got = take - kLsaPool * c;
                 if (got <= 0) break;
-                const int g = (int)(id / kLsaBuckets) * kLsaPoints + members[blk * kLsaPoints + m];
+                const int g = (int)(bid / kLsaBuckets) * kLsaPoints + (int)((v >> (35 + 7 * c)) & 127u);
                 atomicOr(&bits[g >> 5], 1u << (g & 31));
                 if (got < kLsaPool) {
                     s_part_g = g;
                     s_part_n = got;
                 }
             }
-            excl += kLsaPool * (o1 - o0);
-            used = (int32_t)id;
+            excl += kLsaPool * n;
+            used = (int32_t)bid;
         }
         if (brow) brow[r] = used;
     }
     __syncthreads();
-    // emit: thread t owns words [t * wper, (t + 1) * wper)
+    // emit: thread t owns words [t * wper, (t + 1) * wper) and counts their
+    // keys; then every output slot e (strided over the threads, so the
+    // stores coalesce) finds its owner by binary search over the owners'
+    // first slots and its pool key by counting set bits
     const int wper = (words + kLsaFillThreads - 1) / kLsaFillThreads;
     const int pg = s_part_g, pn = s_part_n;
     int cnt = 0;
@@ -437,22 +511,47 @@ __global__ __launch_bounds__(kLsaFillThreads) void lsa_fill_kernel(const int32_t
     }
     if (pg >= 0 && (pg >> 5) >= t * wper && (pg >> 5) < (t + 1) * wper) cnt -= kLsaPool - pn;
     const int incl = wg_incl_scan<kLsaFillThreads>(cnt, s_scan);
-    int o = incl - cnt;
-    for (int j = 0; j < wper; ++j) {
-        const int wi = t * wper + j;
-        if (wi >= words) break;
-        uint32_t b = bits[wi];
-        while (b) {
-            const int g = wi * 32 + __builtin_ctz(b);
-            b &= b - 1;
-            const int n = g == pg ? pn : kLsaPool;
-            for (int r = 0; r < n; ++r) orow[o++] = kLsaPool * g + r;
-        }
-    }
-    // the total is the last thread's inclusive count
+    int* first = reinterpret_cast<int*>(skey);            // [threads] first slot of each owner
+    first[t] = incl - cnt;
     if (t == kLsaFillThreads - 1) s_scan[0] = incl;
     __syncthreads();
-    for (int e = s_scan[0] + t; e < k; e += kLsaFillThreads) orow[e] = -1;
+    const int total = s_scan[0];
+    for (int e = t; e < total; e += kLsaFillThreads) {
+        int lo = 0, hi = kLsaFillThreads - 1;             // last owner whose first slot is <= e
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (first[mid] <= e) lo = mid;
+            else hi = mid - 1;
+        }
+        int rem = e - first[lo];
+        int pos = -1;
+        for (int j = 0; j < wper && pos < 0; ++j) {
+            const int wi = lo * wper + j;
+            const uint32_t b = bits[wi];
+            const bool part = pg >= 0 && (pg >> 5) == wi;
+            const int c = kLsaPool * __popc(b) - (part ? kLsaPool - pn : 0);
+            if (rem >= c) {
+                rem -= c;
+                continue;
+            }
+            // set bit number i of the word holds slot rem; the partial pool
+            // key (if it is in this word and before, or is that bit and rem
+            // runs past its keys) shifts the count by the keys it lacks
+            int i = rem / kLsaPool;
+            if (part) {
+                const int ip = __popc(b & ((1u << (pg & 31)) - 1u));       // its ordinal
+                if (ip < i || (ip == i && rem - kLsaPool * ip >= pn)) {
+                    rem += kLsaPool - pn;
+                    i = rem / kLsaPool;
+                }
+            }
+            uint32_t x = b;
+            for (int q = 0; q < i; ++q) x &= x - 1;
+            pos = kLsaPool * (wi * 32 + __builtin_ctz(x)) + rem % kLsaPool;
+        }
+        orow[e] = pos;
+    }
+    for (int e = total + t; e < k; e += kLsaFillThreads) orow[e] = -1;
 }
 
 }  // namespace
@@ -515,7 +614,7 @@ hisa_index_args bucket_args(const hisa_lsa_args* a, int64_t* q_bucket, int64_t* 
 }
 
 struct LsaLayout {
-    size_t q_bucket, seq_boff, seq_blen, sel, score, flat, total;
+    size_t q_bucket, q_blk_off, seq_boff, seq_blen, sel, score, flat, total;
 };
 
 LsaLayout lsa_layout(const hisa_lsa_args* a, size_t flat_bytes)
@@ -523,6 +622,8 @@ LsaLayout lsa_layout(const hisa_lsa_args* a, size_t flat_bytes)
     LsaLayout L;
     size_t off = 0;
     L.q_bucket = off;
+    off += align_256((size_t)std::max<int64_t>(a->nq, 1) * 8);
+    L.q_blk_off = off;
     off += align_256((size_t)std::max<int64_t>(a->nq, 1) * 8);
     L.seq_boff = off;
     off += align_256((size_t)a->nseq * 8);
@@ -597,6 +698,7 @@ int hisa_lsa_index(const hisa_lsa_args* a, void* stream_)
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     char* ws = static_cast<char*>(a->workspace);
     int64_t* q_bucket = reinterpret_cast<int64_t*>(ws + L.q_bucket);
+    int64_t* q_blk_off = reinterpret_cast<int64_t*>(ws + L.q_blk_off);
     int64_t* seq_boff = reinterpret_cast<int64_t*>(ws + L.seq_boff);
     int64_t* seq_blen = reinterpret_cast<int64_t*>(ws + L.seq_blen);
     int32_t* sel = reinterpret_cast<int32_t*>(ws + L.sel);
@@ -604,7 +706,7 @@ int hisa_lsa_index(const hisa_lsa_args* a, void* stream_)
     const int64_t nthreads = std::max<int64_t>(a->nq, a->nseq);
     hipLaunchKernelGGL(lsa_meta_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, stream, a->q_pos,
                        a->q_seq, a->nq, a->seq_blk_off, a->seq_nblk, a->seq_len, (int)a->nseq,
-                       (int64_t)(a->max_len / kLsaBlock), q_bucket, seq_boff, seq_blen);
+                       (int64_t)(a->max_len / kLsaBlock), q_bucket, q_blk_off, seq_boff, seq_blen);
     if (hipGetLastError() != hipSuccess) return HISA_ERR_HIP;
     hisa_index_args b = bucket_args(a, q_bucket, seq_boff, seq_blen, sel, score, ws + L.flat,
                                     a->workspace_bytes - L.flat);
@@ -612,11 +714,11 @@ int hisa_lsa_index(const hisa_lsa_args* a, void* stream_)
     if (frc != HISA_OK) return frc;
     const int P2 = next_pow2(a->p);
     const int words = (int)(a->max_len / kLsaBlock * kLsaPoints / 32);
-    const size_t lds = (size_t)P2 * 8 + (size_t)std::max(words, 1) * 4;
+    const size_t lds = lsa_rank_bytes(P2) + (size_t)std::max(words, 1) * 4;
     hipLaunchKernelGGL(lsa_fill_kernel, dim3((unsigned)a->nq), dim3(kLsaFillThreads), lds, stream,
                        static_cast<const int32_t*>(sel), static_cast<const float*>(score), (int)a->p, P2,
-                       static_cast<const int64_t*>(q_bucket), a->q_seq, a->seq_blk_off, a->members, a->offs,
-                       (int)a->k, a->out_idx, a->out_buckets);
+                       static_cast<const int64_t*>(q_bucket), static_cast<const int64_t*>(q_blk_off), a->members,
+                       a->offs, (int)a->k, a->out_idx, a->out_buckets);
     if (hipGetLastError() != hipSuccess) return HISA_ERR_HIP;
     return HISA_OK;
 }

@@ -178,7 +178,7 @@ def _lsa(**kw):
 @pytest.mark.parametrize("field,value,code", [
     ("d", 32, hisa.HISA_ERR_UNSUPPORTED),
     ("p", 0, hisa.HISA_ERR_INVALID_ARG),
-    ("p", 4097, hisa.HISA_ERR_UNSUPPORTED),
+    ("p", 2049, hisa.HISA_ERR_UNSUPPORTED),
     ("k", 0, hisa.HISA_ERR_INVALID_ARG),
     ("k", 16385, hisa.HISA_ERR_UNSUPPORTED),
     ("max_len", (1 << 20) + 1, hisa.HISA_ERR_UNSUPPORTED),
