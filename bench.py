@@ -136,7 +136,7 @@ def flat_stage_bytes(q_pos, k):
 STAGE_KERNEL = {"block_stage": ("stage1_select_kernel",),
                 "token_scores": ("stage2_score_kernel", "stage2_tile_kernel"),
                 "token_topk": ("topk_rows_kernel",),
-                "select_and_scores": ("decode_fused_kernel",),
+                "select_and_scores": ("decode_fused_kernel", "decode_step_kernel"),
                 "flat_scores": ("flat_score_kernel", "flat_score_mfma_kernel")}
 
 
@@ -233,6 +233,9 @@ class Setup:
         self.dev_mod = device_mod
         self.replicas = replicas
         self.block_only = False
+        # HISA decode steps: append and index in one hisa_decode_step call
+        # (False: the two calls, the form the flat indexer's step takes)
+        self.fused_step = self.append_src is not None
         self.calls = {flat: self.build_calls(flat, self.m, self.k) for flat in (False, True)}
         self.q_per_step = sum(len(ph.q_pos) for ph in self.phases)
 
@@ -258,6 +261,15 @@ class Setup:
     def step(self, r, flat, stream, events=None, append_events=None):
         """One step on replica r; events: one StageEvents per phase."""
         h = self.h
+        if self.append_src is not None and not flat and not self.block_only and self.fused_step:
+            (ic, per_rep), = self.calls[False]
+            a = per_rep[r]
+            if events is not None:
+                events[0].attach(a)
+            else:
+                a.stage_events = None
+            h.hisa_decode_step(a, self.seqs, self.append_src)
+            return
         if self.append_src is not None:
             if append_events is not None:
                 h._hiprt().hipEventRecord(append_events[0], stream)
@@ -397,10 +409,14 @@ def attention_kernel_ms(S, A, nsteps, torch):
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
+STEPS_PER_GRAPH = 1
+
+
 def capture_graphs(S, flat, torch, attn=None):
     """One HIP graph per replica holding one whole step (kernels only: no
     events, no allocation, no memset nodes), followed by the sparse
-    attention over its output when attn is given."""
+    attention over its output when attn is given.  With STEPS_PER_GRAPH > 1
+    a graph holds that many consecutive steps (on consecutive replicas)."""
     graphs = []
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -413,9 +429,11 @@ def capture_graphs(S, flat, torch, attn=None):
     for r in range(S.replicas):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            S.step(r, flat, torch.cuda.current_stream().cuda_stream)
-            if attn is not None:
-                attn.run(r, flat)
+            for j in range(STEPS_PER_GRAPH):
+                rr = (r + j) % S.replicas
+                S.step(rr, flat, torch.cuda.current_stream().cuda_stream)
+                if attn is not None:
+                    attn.run(rr, flat)
         graphs.append(g)
     torch.cuda.synchronize()
     return graphs
@@ -425,14 +443,16 @@ def time_method(S, flat, steps, warmup, torch, attn=None):
     """Wall time of `steps` graph replays (one step each, rotating over the
     replicas), bracketed by device synchronisation."""
     graphs = capture_graphs(S, flat, torch, attn)
-    for i in range(warmup):
-        graphs[i % S.replicas].replay()
+    spg = STEPS_PER_GRAPH
+    n = max(1, steps // spg)                # replays of spg steps each, consecutive replays on fresh replicas
+    for i in range(max(1, warmup // spg)):
+        graphs[(i * spg) % S.replicas].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[(warmup + i) % S.replicas].replay()
+    for i in range(n):
+        graphs[((warmup + i) * spg) % S.replicas].replay()
     torch.cuda.synchronize()
-    return time.perf_counter() - t0
+    return (time.perf_counter() - t0) * steps / (n * spg)
 
 
 def stage_times(S, flat, nsteps, torch):
@@ -448,7 +468,7 @@ def stage_times(S, flat, nsteps, torch):
     evs = [[h.StageEvents() for _ in range(nph)] for _ in range(nsteps)]
     hr = h._hiprt()
     app = []
-    if S.append_src is not None:
+    if S.append_src is not None and (flat or not S.fused_step):
         for _ in range(nsteps):
             pair = []
             for _ in range(2):
@@ -590,6 +610,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attention", action="store_true", help="skip the sparse-attention leg")
     ap.add_argument("--no-lsa", action="store_true", help="skip the LSA-Flat leg")
+    ap.add_argument("--steps-per-graph", type=int, default=1,
+                    help="consecutive steps captured in one graph (1: one replay per step, the serving form)")
     ap.add_argument("--lsa-replicas", type=int, default=8, help="copies of the LSA bucket cache rotated over")
     ap.add_argument("--sweep-m", default=None, metavar="M1,M2,...",
                     help="instead of the default line: HISA at each m and block-only selection, time per "
@@ -599,6 +621,8 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (a known-size reference for HBM counters)")
     args = ap.parse_args()
+    global STEPS_PER_GRAPH
+    STEPS_PER_GRAPH = max(1, args.steps_per_graph)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the indexer here runs on a single MI355X and has no "
@@ -642,6 +666,12 @@ def main():
         return
     log("timing HISA: %d warmup + %d graph-replayed steps" % (args.warmup, args.steps))
     h_el = time_method(S, False, args.steps, args.warmup, torch)
+    two_ms = None
+    if S.fused_step:
+        log("timing HISA as two calls (append, then index)")
+        S.fused_step = False
+        two_ms = time_method(S, False, args.steps, args.warmup, torch) / args.steps * 1e3
+        S.fused_step = True
     log("timing flat: %d warmup + %d graph-replayed steps" % (args.warmup, args.steps))
     f_el = time_method(S, True, args.steps, args.warmup, torch)
     nst = max(4, min(args.stage_steps, S.replicas * 4))
@@ -665,6 +695,15 @@ def main():
         for nm, f in stage_flops(ph.q_pos, S.B, S.m).items():
             stage_fl["%s/%s" % (ph.name, nm)] = f
             stage_nq["%s/%s" % (ph.name, nm)] = len(ph.q_pos)
+    if S.fused_step:
+        # the decode step's launch also appends: new rows written, touched
+        # blocks read, their representatives written
+        n_new = S.append_src.shape[1]
+        blocks = sum((int(sq[2]) + n_new - 1) // S.B - int(sq[2]) // S.B + 1 for sq in S.seqs)
+        app_bytes = len(S.seqs) * n_new * 128 + blocks * (S.B * 128 + 128)
+        for n in list(stage_bytes):
+            if n.endswith("/select_and_scores"):
+                stage_bytes[n] += app_bytes
     kern = max((n for n in h_stage if n in stage_bytes), key=lambda n: h_stage[n])
     bound, achieved, peak, unit, work = stage_roofline(kern, h_stage[kern], stage_nq.get(kern, 0),
                                                        stage_fl.get(kern, 0.0), stage_bytes[kern])
@@ -768,6 +807,10 @@ def main():
                  "dominant": {"kernel": fkern, "bound": fbound, "achieved": f_achieved, "unit": funit,
                               "frac": f_achieved / fpeak}},
         "speedup_vs_flat": f_ms / h_ms,
+        "hisa_two_calls_ms_per_step": two_ms,
+        "step_note": ("HISA decode steps are one hisa_decode_step call (the append in the same launch as the block "
+                      "selection and token scores); hisa_two_calls_ms_per_step is the same step as append + index, "
+                      "the form the flat indexer's step takes" if two_ms is not None else None),
         "attention": attention,
         "lsa_flat": lsa,
     }

@@ -195,6 +195,26 @@ int hisa_index(const hisa_index_args* a, void* stream);
 int hisa_flat_index(const hisa_index_args* a, void* stream);
 
 /*
+ * hisa_decode_step -- hisa_append_keys(keys, reps, seqs, nseq, new_keys,
+ * n_new, d, B) followed by hisa_index(a): the same outputs, keys and
+ * representatives, in fewer launches.  The append writes a->keys and
+ * a->reps (the const of hisa_index_args does not hold for this call).
+ * seqs[s] describes sequence s of `a` (the same key and representative
+ * offsets) with its length BEFORE the append; a->seq_len holds the lengths
+ * AFTER it.  With fewer than 512 queries, at most 2048 blocks, n_new <= B,
+ * at most 64 sequences and a workspace that holds every query, the append
+ * runs in the same launch as the block selection and
+ * token scores (the index reads the new keys from new_keys, and the blocks
+ * the append re-pools are the queries' forced last two, whose
+ * representatives stage 1 never scores; stage event 1 then covers that
+ * launch, 2 the top-k); otherwise the two calls run one after the other.
+ * Errors: those of hisa_index and hisa_append_keys; INVALID_ARG also when
+ *         an appended length exceeds max_len.
+ */
+int hisa_decode_step(const hisa_index_args* a, const hisa_seq* seqs, const uint16_t* new_keys, int64_t n_new,
+                     void* stream);
+
+/*
  * hisa_block_index -- block-only selection, the variant the HISA summary's
  * results paragraph contrasts with HISA (whole blocks chosen without the
  * token-level refinement): stage 1 exactly as in hisa_index, then each

@@ -277,6 +277,58 @@ int hisa_index(const hisa_index_args* a, void* stream_)
     return HISA_OK;
 }
 
+int hisa_decode_step(const hisa_index_args* a, const hisa_seq* seqs, const uint16_t* new_keys, int64_t n_new,
+                     void* stream_)
+{
+    const int rc = validate_index(a, 0);
+    if (rc != HISA_OK) return rc;
+    if (n_new < 0) return HISA_ERR_INVALID_ARG;
+    if (n_new > 0 && (!seqs || !new_keys)) return HISA_ERR_INVALID_ARG;
+    for (int s = 0; s < a->nseq && n_new > 0; ++s) {
+        const hisa_seq& q = seqs[s];
+        if (q.key_off < 0 || q.rep_off < 0 || q.len < 0 || q.capacity > HISA_MAX_LEN || q.len + n_new > q.capacity)
+            return HISA_ERR_INVALID_ARG;
+        if (q.len + n_new > a->max_len) return HISA_ERR_INVALID_ARG;
+    }
+    if (n_new > 0 && (int64_t)a->nseq * n_new > INT32_MAX) return HISA_ERR_INVALID_ARG;
+    if (a->nq > 0 && !a->workspace) return HISA_ERR_WORKSPACE;
+    const int64_t chunk = a->nq > 0 ? chunk_for(a, 0, a->workspace_bytes) : 1;
+    if (chunk < 1) return HISA_ERR_WORKSPACE;
+    const int64_t Mmax = hisa_Mmax(a);
+    const bool fuse = n_new > 0 && a->nq > 0 && hisa_split(a) && Mmax <= kStage1FusedMax && n_new <= a->B &&
+                      a->nseq <= kDecodeJobs && chunk >= a->nq;
+    if (!fuse) {
+        // the same results as the two calls in order
+        const int arc = hisa_append_keys(const_cast<uint16_t*>(a->keys), const_cast<uint16_t*>(a->reps), seqs,
+                                         a->nseq, new_keys, n_new, a->d, a->B, stream_);
+        if (arc != HISA_OK) return arc;
+        return hisa_index(a, stream_);
+    }
+    const Layout L = layout_for(a, 0, chunk);
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const int lb = log2_of(a->B);
+    PoolJob jobs[kDecodeJobs];
+    for (int s = 0; s < a->nseq; ++s) {
+        const hisa_seq& q = seqs[s];
+        const int64_t first = q.len / a->B;
+        const int64_t last = (q.len + n_new - 1) / a->B;
+        jobs[s] = PoolJob{q.key_off, q.rep_off, (int32_t)q.len, (int32_t)(q.len + n_new), (int32_t)(s * n_new),
+                          (int32_t)first, (int32_t)(last - first + 1), 0};
+    }
+    int32_t* sel = at<int32_t>(a->workspace, L.sel);
+    RowInfo* rinfo = at<RowInfo>(a->workspace, L.rinfo);
+    uint32_t* ukeys = at<uint32_t>(a->workspace, L.ukeys);
+    // stage events as in hisa_index's fused case: stage 1 is the launch
+    // (append included), stage 2 the top-k
+    hipError_t err = launch_decode_step(meta_of(a), const_cast<uint16_t*>(a->reps), const_cast<uint16_t*>(a->keys),
+                                        new_keys, a->B, jobs, a->nseq, a->nq, lb, a->m, Mmax, sel, rinfo,
+                                        a->out_blocks, ukeys, stream, stage_timing(a, true, 1));
+    if (err == hipSuccess)
+        err = launch_topk_small(ukeys, a->nq, a->m << lb, a->k, sel, a->m, lb, a->out_idx, a->out_scores, stream,
+                                stage_timing(a, true, 2));
+    return err == hipSuccess ? HISA_OK : HISA_ERR_HIP;
+}
+
 int hisa_block_index(const hisa_index_args* a, void* stream_)
 {
     const int rc = validate_index(a, 0);

@@ -79,6 +79,14 @@ hipError_t launch_decode_fused(const QueryMeta& qm, const uint16_t* reps, const 
                                int64_t nq, int lb, int m, int64_t Mmax, int32_t* sel, RowInfo* rinfo,
                                int32_t* out_blocks, uint32_t* ukeys, hipStream_t stream, Timing t = {});
 
+// The same launch with the decode step's append folded in: one job per
+// sequence (at most kDecodeJobs, new keys spanning at most two blocks);
+// jobs travel in the kernel arguments.
+constexpr int kDecodeJobs = 64;
+hipError_t launch_decode_step(const QueryMeta& qm, uint16_t* reps, uint16_t* keys, const uint16_t* new_keys, int B,
+                              const PoolJob* jobs, int njobs, int64_t nq, int lb, int m, int64_t Mmax, int32_t* sel,
+                              RowInfo* rinfo, int32_t* out_blocks, uint32_t* ukeys, hipStream_t stream, Timing t = {});
+
 // HISA stage 2 for few queries: kStage2SlotsPerWg candidate slots per
 // workgroup scored into ukeys [nq, m*B]; launch_topk_small then selects.
 constexpr int kStage2SlotsPerWg = 512;

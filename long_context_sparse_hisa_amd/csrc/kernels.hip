@@ -63,12 +63,17 @@ struct PoolJobs {
     PoolJob j[kPoolJobsPerLaunch];
 };
 
-__global__ __launch_bounds__(kThreads) void pool_kernel(uint16_t* keys, uint16_t* reps, const uint16_t* new_keys,
-                                                        int B, PoolJobs jobs)
+struct DecodeJobs {
+    PoolJob j[kDecodeJobs];
+};
+
+// Block `bx` of one job: load every row of the block (old rows from the
+// cache, new rows from new_keys), write the new rows, write the block's
+// representative.
+HISA_INLINE void pool_block(uint16_t* keys, uint16_t* reps, const uint16_t* new_keys, int B, const PoolJob& job,
+                            int64_t bx)
 {
-    const PoolJob& job = jobs.j[blockIdx.y];
-    if ((int64_t)blockIdx.x >= job.nblk) return;
-    const int64_t blk = job.blk_first + blockIdx.x;
+    const int64_t blk = job.blk_first + bx;
     const int64_t start = blk * B;
     const int count = (int)min((int64_t)B, job.len_new - start);
     const int col = threadIdx.x & 7;
@@ -116,6 +121,14 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(uint16_t* keys, uint16_t
         const double mean = s / (double)count;
         reps[(job.rep_off + blk) * kDim + threadIdx.x] = f64_to_bf16_rne(mean);
     }
+}
+
+__global__ __launch_bounds__(kThreads) void pool_kernel(uint16_t* keys, uint16_t* reps, const uint16_t* new_keys,
+                                                        int B, PoolJobs jobs)
+{
+    const PoolJob& job = jobs.j[blockIdx.y];
+    if ((int64_t)blockIdx.x >= job.nblk) return;
+    pool_block(keys, reps, new_keys, B, job, blockIdx.x);
 }
 
 hipError_t launch_pool(uint16_t* keys, uint16_t* reps, const uint16_t* new_keys, int B, const PoolJob* jobs,
@@ -457,9 +470,8 @@ constexpr int kScorePasses = kStage2SlotsPerWg / kScoreRowsPerPass;
 // Two round trips when the list is in memory, no branches: every pass's
 // list entry, then every pass's key part (row 0 of the sequence stands in
 // for a masked slot).
-template <class Kept>
-HISA_INLINE void score_slots(const uint16_t* qrow, const uint16_t* keys, int64_t key_off, int64_t t, int lb, int N,
-                             Kept kept, uint32_t* urow)
+template <class Kept, class Row>
+HISA_INLINE void score_slots(const uint16_t* qrow, Row row_of, int64_t t, int lb, int N, Kept kept, uint32_t* urow)
 {
     const int sub = threadIdx.x & 7;              // which 16 bytes of a row
     const int grp = threadIdx.x >> 3;             // which row of a pass
@@ -475,7 +487,7 @@ HISA_INLINE void score_slots(const uint16_t* qrow, const uint16_t* keys, int64_t
         const int s = beg + p * kScoreRowsPerPass;
         const int64_t j = ((int64_t)blk[p] << lb) + (s & ((1 << lb) - 1));
         ok[p] = s < N && blk[p] >= 0 && j <= t;
-        v[p] = reinterpret_cast<const uint4*>(keys + (key_off + (ok[p] ? j : 0)) * kDim)[sub];
+        v[p] = reinterpret_cast<const uint4*>(row_of(ok[p] ? j : 0))[sub];
     }
 #pragma unroll
     for (int p = 0; p < kScorePasses; ++p) {
@@ -502,8 +514,8 @@ __global__ __launch_bounds__(kThreads) void stage2_score_kernel(const uint16_t* 
     const int N = m << lb;
     const int32_t* srow = sel + row * m;
     const RowInfo ri = rinfo[row];
-    score_slots(queries + (q0 + row) * kDim, keys, ri.key_off, ri.t, lb, N, [&](int i) { return srow[i]; },
-                ukeys + row * N);
+    score_slots(queries + (q0 + row) * kDim, [&](int64_t j) { return keys + (ri.key_off + j) * kDim; }, ri.t, lb, N,
+                [&](int i) { return srow[i]; }, ukeys + row * N);
 }
 
 // Few queries with at most kStage1FusedMax blocks: stage 1 and the token
@@ -512,15 +524,14 @@ __global__ __launch_bounds__(kThreads) void stage2_score_kernel(const uint16_t* 
 // same selection in each, a few KiB of L2 reads - then scores its own
 // slots from the list in LDS.  Workgroup 0 of the query also writes the
 // kept list, the row info and out_blocks.
-template <int ITEMS>
-__global__ __launch_bounds__(kThreads) void decode_fused_kernel(QueryMeta qm, const uint16_t* reps,
-                                                                const uint16_t* keys, int64_t q0, int lb, int m,
-                                                                int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
-                                                                uint32_t* ukeys)
+// The body of a fused workgroup; source(qi) gives the key-row functor of
+// the query's sequence.
+template <int ITEMS, class Source>
+HISA_INLINE void decode_fused_body(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t row, int lb, int m,
+                                   int32_t* sel, RowInfo* rinfo, int32_t* out_blocks, uint32_t* ukeys, Source source)
 {
     __shared__ BucketSmem<kThreads> sm;
     __shared__ int32_t s_kept[kMaxKept];
-    const int64_t row = blockIdx.x;
     const int64_t i = q0 + row;
     const QueryInfo qi =
         query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
@@ -555,8 +566,52 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(QueryMeta qm, co
         }
     }
     const int N = m << lb;
-    score_slots(qm.queries + i * kDim, keys, qi.key_off, qi.valid ? qi.t : -1, lb, N,
-                [&](int e) { return s_kept[e]; }, ukeys + row * N);
+    score_slots(qm.queries + i * kDim, source(qi), qi.valid ? qi.t : -1, lb, N, [&](int e) { return s_kept[e]; },
+                ukeys + row * N);
+}
+
+template <int ITEMS>
+__global__ __launch_bounds__(kThreads) void decode_fused_kernel(QueryMeta qm, const uint16_t* reps,
+                                                                const uint16_t* keys, int64_t q0, int lb, int m,
+                                                                int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
+                                                                uint32_t* ukeys)
+{
+    decode_fused_body<ITEMS>(qm, reps, q0, blockIdx.x, lb, m, sel, rinfo, out_blocks, ukeys, [&](const QueryInfo& qi) {
+        return [=](int64_t j) { return keys + (qi.key_off + j) * kDim; };
+    });
+}
+
+// A decode step in one launch: workgroups x < nq index the queries as
+// decode_fused_kernel does, workgroups x >= nq run the append jobs (job
+// x - nq, block y).  An index workgroup reads a key at or past its
+// sequence's old length from new_keys, not from the cache the append
+// workgroups are writing.  The blocks the append re-pools are the query's
+// own block and the one before (the new keys span at most two blocks and
+// no query lies past them), which are forced and never scored, so no
+// index workgroup reads a representative being rewritten.
+template <int ITEMS>
+__global__ __launch_bounds__(kThreads) void decode_step_kernel(QueryMeta qm, uint16_t* reps, uint16_t* keys,
+                                                               const uint16_t* new_keys, int B, DecodeJobs jobs,
+                                                               int64_t nq, int splits, int lb, int m, int32_t* sel,
+                                                               RowInfo* rinfo, int32_t* out_blocks, uint32_t* ukeys)
+{
+    if ((int64_t)blockIdx.x >= nq) {
+        const PoolJob& job = jobs.j[blockIdx.x - nq];
+        if ((int64_t)blockIdx.y < job.nblk) pool_block(keys, reps, new_keys, B, job, blockIdx.y);
+        return;
+    }
+    if ((int)blockIdx.y >= splits) return;       // rows of the grid kept for two-block appends
+    decode_fused_body<ITEMS>(qm, reps, 0, blockIdx.x, lb, m, sel, rinfo, out_blocks, ukeys, [&](const QueryInfo& qi) {
+        // an invalid query reads no key; job 0 (or a zero padding job)
+        // keeps its row functor in bounds
+        const PoolJob& job = jobs.j[(qi.seq >= 0 && qi.seq < kDecodeJobs) ? qi.seq : 0];
+        const int64_t len_old = job.len_old, len_new = job.len_new;
+        const uint16_t* nk = new_keys + (int64_t)job.new_row * kDim;
+        const uint16_t* ck = keys + qi.key_off * kDim;
+        // rows past the appended ones (only for lengths inconsistent with
+        // the append) stay in the cache, inside the sequence's capacity
+        return [=](int64_t j) { return (j >= len_old && j < len_new) ? nk + (j - len_old) * kDim : ck + j * kDim; };
+    });
 }
 
 template <int ITEMS>
@@ -568,6 +623,30 @@ static hipError_t launch_decode_fused_items(const QueryMeta& qm, const uint16_t*
     const dim3 grid((unsigned)nq, (unsigned)((N + kStage2SlotsPerWg - 1) / kStage2SlotsPerWg));
     return launch_k(decode_fused_kernel<ITEMS>, grid, dim3(kThreads), stream, t.start, t.stop, qm, reps, keys, q0, lb,
                     m, sel, rinfo, out_blocks, ukeys);
+}
+
+hipError_t launch_decode_step(const QueryMeta& qm, uint16_t* reps, uint16_t* keys, const uint16_t* new_keys, int B,
+                              const PoolJob* jobs, int njobs, int64_t nq, int lb, int m, int64_t Mmax, int32_t* sel,
+                              RowInfo* rinfo, int32_t* out_blocks, uint32_t* ukeys, hipStream_t stream, Timing t)
+{
+    DecodeJobs dj;
+    for (int i = 0; i < kDecodeJobs; ++i) dj.j[i] = i < njobs ? jobs[i] : PoolJob{0, 0, 0, 0, 0, 0, 0, 0};
+    const int N = m << lb;
+    const int splits = (N + kStage2SlotsPerWg - 1) / kStage2SlotsPerWg;
+    int rows = splits;                                // an append touches at most two blocks
+    for (int i = 0; i < njobs; ++i) rows = std::max<int>(rows, jobs[i].nblk);
+    const dim3 grid((unsigned)(nq + njobs), (unsigned)rows);
+    const int64_t per = (Mmax + kThreads - 1) / kThreads;
+#define HISA_DS(N_)                                                                                             \
+    if (per <= N_)                                                                                              \
+    return launch_k(decode_step_kernel<N_>, grid, dim3(kThreads), stream, t.start, t.stop, qm, reps, keys, new_keys, \
+                    B, dj, nq, splits, lb, m, sel, rinfo, out_blocks, ukeys)
+    HISA_DS(1);
+    HISA_DS(2);
+    HISA_DS(4);
+    HISA_DS(8);
+#undef HISA_DS
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_fused(const QueryMeta& qm, const uint16_t* reps, const uint16_t* keys, int64_t q0,

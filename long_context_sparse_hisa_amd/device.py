@@ -57,6 +57,17 @@ class DeviceCache:
             self.seq_len += nk.shape[1]
             self.d_len.copy_(torch.from_numpy(self.seq_len))
 
+    def decode_step(self, call: "IndexCall", new_keys: np.ndarray | torch.Tensor, stream=None):
+        """Append new_keys [nseq, n_new, D] to every sequence and run the
+        index call in one hisa_decode_step (the call's queries should sit at
+        positions valid after the append)."""
+        nk = new_keys if isinstance(new_keys, torch.Tensor) else to_dev(new_keys, self.device)
+        seqs = [(self.seq_key_off[s], self.seq_rep_off[s], self.seq_len[s], self.seq_cap[s])
+                for s in range(self.nseq)]
+        self.seq_len += nk.shape[1]
+        self.d_len.copy_(torch.from_numpy(self.seq_len))
+        hisa.hisa_decode_step(call.args, seqs, nk, stream or self.stream)
+
     def set_lengths(self, lengths):
         self.seq_len = np.asarray(lengths, np.int64).copy()
         self.d_len.copy_(torch.from_numpy(self.seq_len))

@@ -91,6 +91,8 @@ def lib():
         L.hisa_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
         L.hisa_flat_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
         L.hisa_block_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
+        L.hisa_decode_step.argtypes = [ctypes.POINTER(hisa_index_args), ctypes.POINTER(hisa_seq), _P,
+                                       ctypes.c_int64, _P]
         L.hisa_attention_workspace_bytes.argtypes = [ctypes.POINTER(hisa_attn_args),
                                                      ctypes.POINTER(ctypes.c_size_t)]
         L.hisa_sparse_attention.argtypes = [ctypes.POINTER(hisa_attn_args), _P]
@@ -206,6 +208,15 @@ def hisa_index(args: hisa_index_args, stream=None):
 
 def hisa_flat_index(args: hisa_index_args, stream=None):
     _check(lib().hisa_flat_index(ctypes.byref(args), _stream(stream)), "hisa_flat_index")
+
+
+def hisa_decode_step(args: hisa_index_args, seqs, new_keys, stream=None):
+    """Append new_keys [nseq, n_new, 64] to every sequence (seqs: host
+    (key_off, rep_off, len before, capacity) per sequence) and index."""
+    arr = (hisa_seq * max(1, len(seqs)))(*[hisa_seq(*map(int, s)) for s in seqs])
+    n_new = 0 if new_keys is None else (new_keys.shape[1] if new_keys.dim() == 3 else new_keys.shape[0])
+    rc = lib().hisa_decode_step(ctypes.byref(args), arr, _dev(new_keys, "new_keys", 2), n_new, _stream(stream))
+    _check(rc, "hisa_decode_step")
 
 
 def hisa_block_index(args: hisa_index_args, stream=None):

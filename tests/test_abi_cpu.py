@@ -206,3 +206,17 @@ def test_lsa_workspace_and_build_validation(lib):
     assert lib.hisa_lsa_build(P(FAKE), 511, 0, 64, P(FAKE), P(FAKE), P(FAKE), None) == hisa.HISA_OK
     assert lib.hisa_lsa_build(P(FAKE), 4096, 8, 64, P(FAKE), P(FAKE), P(FAKE), None) == hisa.HISA_OK
     assert lib.hisa_lsa_build(None, 4096, 0, 64, P(FAKE), P(FAKE), P(FAKE), None) == hisa.HISA_ERR_INVALID_ARG
+
+
+def test_decode_step_validation(lib):
+    seqs = (hisa.hisa_seq * 1)(hisa.hisa_seq(0, 0, 100, 200))
+    P = ctypes.c_void_p
+    a = _args(max_len=200)
+    assert lib.hisa_decode_step(ctypes.byref(a), seqs, P(FAKE), -1, None) == hisa.HISA_ERR_INVALID_ARG
+    assert lib.hisa_decode_step(ctypes.byref(a), seqs, P(FAKE), 101, None) == hisa.HISA_ERR_INVALID_ARG   # capacity
+    a = _args(max_len=150)
+    assert lib.hisa_decode_step(ctypes.byref(a), seqs, P(FAKE), 60, None) == hisa.HISA_ERR_INVALID_ARG    # max_len
+    a = _args(max_len=200)
+    assert lib.hisa_decode_step(ctypes.byref(a), seqs, None, 5, None) == hisa.HISA_ERR_INVALID_ARG
+    assert lib.hisa_decode_step(ctypes.byref(a), seqs, P(FAKE), 5, None) == hisa.HISA_ERR_WORKSPACE
+    assert lib.hisa_decode_step(ctypes.byref(_args(d=32)), seqs, P(FAKE), 5, None) == hisa.HISA_ERR_UNSUPPORTED

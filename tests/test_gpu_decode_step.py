@@ -1,0 +1,105 @@
+"""hisa_decode_step (append + index in one call) against the two calls it
+replaces, bit for bit (indices, scores, kept blocks, keys and
+representatives), on the fused path and on the fallback, and against the
+oracle on the 32K decode batch."""
+import numpy as np
+import pytest
+
+import oracle
+from long_context_sparse_hisa_amd import synth
+from parity import check_all_rows_properties, check_rows
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_context_sparse_hisa_amd import hisa
+    hisa.lib()                                  # raises if the library is missing
+
+
+def _pair(w, B, lens_before, new, ph, k, m, **kw):
+    """(two-call results, one-call results) as numpy arrays."""
+    from long_context_sparse_hisa_amd import device
+    out = []
+    for fused in (False, True):
+        cache = device.DeviceCache(w, B=B)
+        cache.set_lengths(lens_before)
+        cache.pool()
+        call = device.IndexCall(cache, ph.queries, ph.q_pos, ph.q_seq, k=k, m=m, one_chunk_limit=16 << 30, **kw)
+        if fused:
+            cache.decode_step(call, new)
+        else:
+            cache.append(new)
+            call.run()
+        idx, sc, blk = call.results()
+        out.append((idx, sc, blk, cache.keys.cpu().numpy(), cache.reps.cpu().numpy(), cache))
+    return out
+
+
+def _same(a, b, label):
+    for x, y, what in zip(a[:5], b[:5], ("idx", "scores", "blocks", "keys", "reps")):
+        if x is None:
+            assert y is None
+            continue
+        assert np.array_equal(x, y, equal_nan=True), "%s: %s differ" % (label, what)
+
+
+@pytest.mark.parametrize("B,n_new", [(64, 1), (64, 7), (64, 64), (128, 2), (128, 200), (16, 16)])
+def test_packed_batch_equals_two_calls(B, n_new):
+    """Five sequences of mixed length with room to grow; queries at each new
+    last position, one earlier position, one past the end and one of an
+    invalid sequence.  n_new = 200 > B takes the two-call path."""
+    print("decode step B=%d n_new=%d" % (B, n_new), flush=True)
+    g = np.random.default_rng(70 + n_new)
+    cap = 3000 + n_new
+    w = synth.decode_batch(nseq=5, L=3000, seed=71, B=B, m=6, k=200, spare=n_new)
+    before = np.array([3000, 1, 127, 2000, 0], np.int64)
+    new = synth.to_bf16(g.standard_normal((5, n_new, synth.D)).astype(np.float32))
+    after = before + n_new
+    assert np.all(after <= cap)
+    q_seq = np.array([0, 1, 2, 3, 4, 0, 3, -1], np.int32)
+    q_pos = np.concatenate([after - 1, [1500, after[3], 5]]).astype(np.int64)
+    queries = synth.to_bf16(g.standard_normal((8, synth.D)).astype(np.float32))
+    ph = synth.Phase("p", queries, q_pos, q_seq)
+    k = min(200, 6 * B)
+    a, b = _pair(w, B, before, new, ph, k, 6)
+    _same(a, b, "B=%d n_new=%d" % (B, n_new))
+    assert np.all(a[0][6] == -1) and np.all(a[0][7] == -1)
+
+
+def test_many_sequences_take_the_two_call_path():
+    print("decode step 70 sequences", flush=True)
+    w = synth.decode_batch(nseq=70, L=600, seed=72, B=64, m=4, k=100, spare=1)
+    before = np.full(70, 600, np.int64)
+    new = np.stack([synth.to_bf16(np.full((1, synth.D), 0.5 + s / 100, np.float32)) for s in range(70)])
+    ph = synth.Phase("p", w.phases[0].queries, np.full(70, 600, np.int64), np.arange(70, dtype=np.int32))
+    a, b = _pair(w, 64, before, new, ph, 100, 4)
+    _same(a, b, "70 sequences")
+
+
+def test_decode_32k_x16_matches_two_calls_and_oracle():
+    print("decode step 32K x16", flush=True)
+    w = synth.decode_batch()
+    before = w.seq_len - 1
+    new = np.stack([w.keys[int(o) + int(L) - 1][None] for o, L in zip(w.seq_key_off, w.seq_len)])
+    ph = w.phases[0]
+    a, b = _pair(w, 128, before, new, ph, w.k, w.m)
+    _same(a, b, "32K x16")
+    idx, sc, blk = b[0], b[1], b[2]
+    check_all_rows_properties(idx, blk, ph.q_pos, 128, w.m, w.k, False)
+    reps = [oracle.pool(w.keys[int(o):int(o) + int(L)], 128) for o, L in zip(w.seq_key_off, w.seq_len)]
+    counts = check_rows(range(16), ph.queries, ph.q_pos,
+                        lambda i: w.keys[int(w.seq_key_off[i]):int(w.seq_key_off[i]) + int(w.seq_len[i])],
+                        lambda i: reps[i], 128, w.m, w.k, idx, sc, blk, False, "step")
+    print("decode step vs oracle", counts, flush=True)
+    # the representatives the step re-pooled equal the oracle's pooling
+    cache = b[5]
+    for s in range(16):
+        r = int(cache.seq_rep_off[s])
+        got = b[4][r:r + 256].view(np.uint16)
+        assert np.array_equal(got, reps[s])
