@@ -581,9 +581,9 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(QueryMeta qm, co
     });
 }
 
-// A decode step in one launch: workgroups x < nq index the queries as
-// decode_fused_kernel does, workgroups x >= nq run the append jobs (job
-// x - nq, block y).  An index workgroup reads a key at or past its
+// A decode step in one launch: workgroups x < njobs run the append jobs
+// (job x, block y; first in the grid so they are dispatched early),
+// workgroups x >= njobs index query x - njobs as decode_fused_kernel does.  An index workgroup reads a key at or past its
 // sequence's old length from new_keys, not from the cache the append
 // workgroups are writing.  The blocks the append re-pools are the query's
 // own block and the one before (the new keys span at most two blocks and
@@ -592,16 +592,17 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(QueryMeta qm, co
 template <int ITEMS>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(QueryMeta qm, uint16_t* reps, uint16_t* keys,
                                                                const uint16_t* new_keys, int B, DecodeJobs jobs,
-                                                               int64_t nq, int splits, int lb, int m, int32_t* sel,
+                                                               int njobs, int splits, int lb, int m, int32_t* sel,
                                                                RowInfo* rinfo, int32_t* out_blocks, uint32_t* ukeys)
 {
-    if ((int64_t)blockIdx.x >= nq) {
-        const PoolJob& job = jobs.j[blockIdx.x - nq];
+    if ((int)blockIdx.x < njobs) {
+        const PoolJob& job = jobs.j[blockIdx.x];
         if ((int64_t)blockIdx.y < job.nblk) pool_block(keys, reps, new_keys, B, job, blockIdx.y);
         return;
     }
     if ((int)blockIdx.y >= splits) return;       // rows of the grid kept for two-block appends
-    decode_fused_body<ITEMS>(qm, reps, 0, blockIdx.x, lb, m, sel, rinfo, out_blocks, ukeys, [&](const QueryInfo& qi) {
+    decode_fused_body<ITEMS>(qm, reps, 0, blockIdx.x - njobs, lb, m, sel, rinfo, out_blocks, ukeys,
+                             [&](const QueryInfo& qi) {
         // an invalid query reads no key; job 0 (or a zero padding job)
         // keeps its row functor in bounds
         const PoolJob& job = jobs.j[(qi.seq >= 0 && qi.seq < kDecodeJobs) ? qi.seq : 0];
@@ -640,7 +641,7 @@ hipError_t launch_decode_step(const QueryMeta& qm, uint16_t* reps, uint16_t* key
 #define HISA_DS(N_)                                                                                             \
     if (per <= N_)                                                                                              \
     return launch_k(decode_step_kernel<N_>, grid, dim3(kThreads), stream, t.start, t.stop, qm, reps, keys, new_keys, \
-                    B, dj, nq, splits, lb, m, sel, rinfo, out_blocks, ukeys)
+                    B, dj, njobs, splits, lb, m, sel, rinfo, out_blocks, ukeys)
     HISA_DS(1);
     HISA_DS(2);
     HISA_DS(4);
