@@ -201,13 +201,15 @@ int hisa_flat_index(const hisa_index_args* a, void* stream);
  * a->reps (the const of hisa_index_args does not hold for this call).
  * seqs[s] describes sequence s of `a` (the same key and representative
  * offsets) with its length BEFORE the append; a->seq_len holds the lengths
- * AFTER it.  With fewer than 512 queries, at most 2048 blocks, n_new <= B,
- * at most 64 sequences and a workspace that holds every query, the append
- * runs in the same launch as the block selection and
- * token scores (the index reads the new keys from new_keys, and the blocks
- * the append re-pools are the queries' forced last two, whose
- * representatives stage 1 never scores; stage event 1 then covers that
- * launch, 2 the top-k); otherwise the two calls run one after the other.
+ * AFTER it.  With fewer than 512 queries, n_new <= B, at most 64
+ * sequences and a workspace that holds every query, the append runs inside
+ * the index's first launch: with at most 2048 blocks the launch that
+ * selects the blocks and scores the tokens (which reads the new keys from
+ * new_keys; stage event 1 covers it, 2 the top-k), with more the
+ * block-score launch (stage events 0, 1, 2 as in hisa_index).  Either way
+ * the blocks the append re-pools are the queries' forced last two, whose
+ * representatives stage 1 never scores.  Otherwise the two calls run one
+ * after the other.
  * Errors: those of hisa_index and hisa_append_keys; INVALID_ARG also when
  *         an appended length exceeds max_len.
  */

@@ -295,8 +295,39 @@ int hisa_decode_step(const hisa_index_args* a, const hisa_seq* seqs, const uint1
     const int64_t chunk = a->nq > 0 ? chunk_for(a, 0, a->workspace_bytes) : 1;
     if (chunk < 1) return HISA_ERR_WORKSPACE;
     const int64_t Mmax = hisa_Mmax(a);
-    const bool fuse = n_new > 0 && a->nq > 0 && hisa_split(a) && Mmax <= kStage1FusedMax && n_new <= a->B &&
-                      a->nseq <= kDecodeJobs && chunk >= a->nq;
+    const bool foldable = n_new > 0 && a->nq > 0 && hisa_split(a) && n_new <= a->B && a->nseq <= kDecodeJobs &&
+                          chunk >= a->nq;
+    const bool fuse = foldable && Mmax <= kStage1FusedMax;
+    if (foldable && !fuse) {
+        // more than 2048 blocks: the append joins the block-score launch,
+        // then the selection, the token scores and the top-k as in hisa_index
+        const Layout L = layout_for(a, 0, chunk);
+        hipStream_t stream = static_cast<hipStream_t>(stream_);
+        const int lb = log2_of(a->B);
+        PoolJob jobs[kDecodeJobs];
+        for (int s = 0; s < a->nseq; ++s) {
+            const hisa_seq& q = seqs[s];
+            const int64_t first = q.len / a->B;
+            const int64_t last = (q.len + n_new - 1) / a->B;
+            jobs[s] = PoolJob{q.key_off, q.rep_off, (int32_t)q.len, (int32_t)(q.len + n_new), (int32_t)(s * n_new),
+                              (int32_t)first, (int32_t)(last - first + 1), 0};
+        }
+        const StepAppend app{const_cast<uint16_t*>(a->keys), new_keys, a->B, jobs, a->nseq};
+        const QueryMeta qm = meta_of(a);
+        float* sigma = at<float>(a->workspace, L.sigma);
+        int32_t* sel = at<int32_t>(a->workspace, L.sel);
+        RowInfo* rinfo = at<RowInfo>(a->workspace, L.rinfo);
+        uint32_t* ukeys = at<uint32_t>(a->workspace, L.ukeys);
+        hipError_t err = launch_stage1(qm, a->reps, 0, a->nq, lb, a->m, Mmax, sigma, sel, rinfo, a->out_blocks, stream,
+                                       stage_timing(a, true, 0), &app);
+        if (err == hipSuccess)
+            err = launch_stage2_split_scores(qm, a->keys, 0, a->nq, lb, a->m, rinfo, sel, ukeys, stream,
+                                             stage_timing(a, true, 1));
+        if (err == hipSuccess)
+            err = launch_topk_small(ukeys, a->nq, a->m << lb, a->k, sel, a->m, lb, a->out_idx, a->out_scores, stream,
+                                    stage_timing(a, true, 2));
+        return err == hipSuccess ? HISA_OK : HISA_ERR_HIP;
+    }
     if (!fuse) {
         // the same results as the two calls in order
         const int arc = hisa_append_keys(const_cast<uint16_t*>(a->keys), const_cast<uint16_t*>(a->reps), seqs,

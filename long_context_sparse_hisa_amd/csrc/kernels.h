@@ -61,9 +61,21 @@ struct QueryMeta {
 // selecting workgroup; longer ones go through sigma [nq, Mmax].
 // lb = log2(B).
 constexpr int64_t kStage1FusedMax = 2048;
+// A decode step's append, folded into the first launch of the path for
+// more than 2048 blocks (launch_stage1's block scores): one job per
+// sequence, at most kDecodeJobs.
+struct StepAppend {
+    uint16_t* keys;
+    const uint16_t* new_keys;
+    int B;
+    const PoolJob* jobs;
+    int njobs;
+};
+
 hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
                          int64_t Mmax, float* sigma, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
-                         hipStream_t stream, Timing t = {});
+                         hipStream_t stream, Timing t = {},
+                         const struct StepAppend* app = nullptr);
 
 // HISA stage 2 for many queries: 16 query rows per wave scored on the
 // MFMA against the union of their kept blocks, into ukeys [nq, m*B] (only

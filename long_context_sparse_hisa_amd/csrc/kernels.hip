@@ -165,7 +165,35 @@ __global__ __launch_bounds__(kThreads) void block_score_kernel(QueryMeta qm, con
     if (!qi.valid) return;
     const int64_t c = qi.t >> lb;
     const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (b > c) return;
+    if (b < 1 || b > c - 2) return;               // the selection reads only the free candidates
+    uint32_t q[32];
+    load_query(qm.queries + i * kDim, q);
+    const uint4* rp = reinterpret_cast<const uint4*>(reps + (qi.rep_off + b) * kDim);
+    sigma[row * Mmax + b] = dot64_packed(q, rp);
+}
+
+// The same with a decode step's append folded in: rows y < njobs run the
+// append jobs (job y, block x), rows y >= njobs score query y - njobs.  The
+// blocks the append re-pools are the queries' forced last two, which are
+// not scored; the token stage runs after this launch.
+__global__ __launch_bounds__(kThreads) void block_score_append_kernel(QueryMeta qm, uint16_t* reps, uint16_t* keys,
+                                                                      const uint16_t* new_keys, int B,
+                                                                      DecodeJobs jobs, int njobs, int64_t q0, int lb,
+                                                                      int64_t Mmax, float* sigma)
+{
+    if ((int)blockIdx.y < njobs) {
+        const PoolJob& job = jobs.j[blockIdx.y];
+        if ((int64_t)blockIdx.x < job.nblk) pool_block(keys, reps, new_keys, B, job, blockIdx.x);
+        return;
+    }
+    const int64_t row = blockIdx.y - njobs;
+    const int64_t i = q0 + row;
+    const QueryInfo qi =
+        query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
+    if (!qi.valid) return;
+    const int64_t c = qi.t >> lb;
+    const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (b < 1 || b > c - 2) return;
     uint32_t q[32];
     load_query(qm.queries + i * kDim, q);
     const uint4* rp = reinterpret_cast<const uint4*>(reps + (qi.rep_off + b) * kDim);
@@ -410,7 +438,7 @@ static hipError_t launch_stage1_tile_items(const QueryMeta& qm, const uint16_t* 
 
 hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
                          int64_t Mmax, float* sigma, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
-                         hipStream_t stream, Timing t)
+                         hipStream_t stream, Timing t, const StepAppend* app)
 {
     if (nq >= kManyRows && Mmax <= kS1TileMaxBlocks) {
         // many queries: MFMA block scores, wave-level top-m
@@ -436,9 +464,23 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
 #undef HISA_S1F
         return hipErrorInvalidValue;
     }
-    dim3 grid((unsigned)((Mmax + kThreads - 1) / kThreads), (unsigned)nq);
-    const hipError_t err =
-        launch_k(block_score_kernel, grid, dim3(kThreads), stream, t.start, nullptr, qm, reps, q0, lb, Mmax, sigma);
+    hipError_t err;
+    if (app) {
+        DecodeJobs dj;
+        int rows = 1;
+        for (int i = 0; i < kDecodeJobs; ++i) {
+            dj.j[i] = i < app->njobs ? app->jobs[i] : PoolJob{0, 0, 0, 0, 0, 0, 0, 0};
+            if (i < app->njobs) rows = std::max<int>(rows, app->jobs[i].nblk);
+        }
+        dim3 grid((unsigned)std::max<int64_t>((Mmax + kThreads - 1) / kThreads, rows), (unsigned)(nq + app->njobs));
+        err = launch_k(block_score_append_kernel, grid, dim3(kThreads), stream, t.start, nullptr, qm,
+                       const_cast<uint16_t*>(reps), app->keys, app->new_keys, app->B, dj, app->njobs, q0, lb, Mmax,
+                       sigma);
+    } else {
+        dim3 grid((unsigned)((Mmax + kThreads - 1) / kThreads), (unsigned)nq);
+        err = launch_k(block_score_kernel, grid, dim3(kThreads), stream, t.start, nullptr, qm, reps, q0, lb, Mmax,
+                       sigma);
+    }
     if (err != hipSuccess) return err;
     // 1024 threads select among up to 16384 scores, 16 per thread
     const int64_t per = (Mmax + 1023) / 1024;

@@ -103,3 +103,19 @@ def test_decode_32k_x16_matches_two_calls_and_oracle():
         r = int(cache.seq_rep_off[s])
         got = b[4][r:r + 256].view(np.uint16)
         assert np.array_equal(got, reps[s])
+
+
+@pytest.mark.parametrize("n_new", [1, 128])
+def test_long_rows_fold_the_append_into_the_block_scores(n_new):
+    """More than 2048 blocks (300,000 keys, B = 128): the append joins the
+    block-score launch; 128 new keys after 300,000 cross a block edge."""
+    print("decode step 300K n_new=%d" % n_new, flush=True)
+    g = np.random.default_rng(73 + n_new)
+    w = synth.decode_batch(nseq=2, L=300_000, seed=74, B=128, m=16, k=2048, spare=n_new)
+    before = np.array([300_000, 299_000], np.int64)
+    new = synth.to_bf16(g.standard_normal((2, n_new, synth.D)).astype(np.float32))
+    after = before + n_new
+    ph = synth.Phase("p", synth.to_bf16(g.standard_normal((3, synth.D)).astype(np.float32)),
+                     np.array([after[0] - 1, after[1] - 1, 150_000], np.int64), np.array([0, 1, 1], np.int32))
+    a, b = _pair(w, 128, before, new, ph, 2048, 16)
+    _same(a, b, "300K n_new=%d" % n_new)
