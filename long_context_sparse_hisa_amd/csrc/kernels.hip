@@ -727,31 +727,38 @@ constexpr int kTileQueries = 16;
 constexpr int kTileWaves = 4;
 constexpr int kTileEnd = 0x7fffffff;     // cursor past the end of a list
 constexpr int64_t kTileTargetWaves = 16384;
+// LDS budget of one tile's kept-block lists: two workgroups per CU (the
+// kernel's occupancy) fit in the 160 KB of LDS
+constexpr size_t kTileListBytes = 80 * 1024;
 
-template <int LB>
+template <int LB, int SUB>
 __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint16_t* queries, const uint16_t* keys,
                                                                       int64_t q0, int64_t nq, int m, int range,
                                                                       const RowInfo* rinfo, const int32_t* sel,
                                                                       uint32_t* ukeys)
 {
-    extern __shared__ int32_t s_sel[];            // [16][m] kept-block lists of the tile's rows
+    // SUB sub-tiles of 16 query rows per wave: every key block loaded from
+    // L2 feeds SUB MFMA tiles, so the union walk reads each block once per
+    // 16 * SUB queries
+    constexpr int TQ = kTileQueries * SUB;
+    extern __shared__ int32_t s_sel[];            // [TQ][m] kept-block lists of the tile's rows
     constexpr int B = 1 << LB;
     constexpr int KT = B / 16;
     const int lane = lane_id();
-    const int64_t row0 = (int64_t)blockIdx.x * kTileQueries;
-    const int nrows = (int)min<int64_t>(kTileQueries, nq - row0);
+    const int64_t row0 = (int64_t)blockIdx.x * TQ;
+    const int nrows = (int)min<int64_t>(TQ, nq - row0);
     const int N = m << LB;
-    for (int e = threadIdx.x; e < kTileQueries * m; e += 64 * kTileWaves)
+    for (int e = threadIdx.x; e < TQ * m; e += 64 * kTileWaves)
         s_sel[e] = e < nrows * m ? sel[row0 * m + e] : -1;
     __syncthreads();
     const int blo = ((int)blockIdx.y * kTileWaves + wave_id()) * range;
     const int bhi = blo + range;
-    // lanes 0..15: one row each; rows whose keys start at the same row of
+    // lanes 0..TQ-1: one row each; rows whose keys start at the same row of
     // the cache are walked together
-    const int r = lane & 15;
+    const int r = lane % TQ;
     const int32_t* lst = s_sel + r * m;
     RowInfo ri{0, -1};
-    if (lane < kTileQueries && r < nrows) ri = rinfo[row0 + r];
+    if (lane < TQ && r < nrows) ri = rinfo[row0 + r];
     const bool valid = ri.t >= 0;
     // this row's first list entry at or after blo (the list ascends, then -1s)
     int first = m;
@@ -771,13 +778,18 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
     const int t32 = valid ? (int)ri.t : -1;
     uint64_t pending = __ballot(active);
     if (!pending) return;
-    // A operand: the 16 queries
+    // A operands: the queries of each sub-tile
     const int col = lane & 15, kg = lane >> 4;
-    bf16x8_t a0 = {}, a1 = {};
-    if (col < nrows) {
-        const uint16_t* qrow = queries + (q0 + row0 + col) * kDim + 8 * kg;
-        a0 = *reinterpret_cast<const bf16x8_t*>(qrow);
-        a1 = *reinterpret_cast<const bf16x8_t*>(qrow + 32);
+    bf16x8_t a0[SUB], a1[SUB];
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+        a0[sb] = bf16x8_t{};
+        a1[sb] = bf16x8_t{};
+        if (16 * sb + col < nrows) {
+            const uint16_t* qrow = queries + (q0 + row0 + 16 * sb + col) * kDim + 8 * kg;
+            a0[sb] = *reinterpret_cast<const bf16x8_t*>(qrow);
+            a1[sb] = *reinterpret_cast<const bf16x8_t*>(qrow + 32);
+        }
     }
     while (pending) {
         const int lead = (int)__builtin_ctzll(pending);
@@ -791,9 +803,11 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
         int cur = first;
         int nxt = mine ? lst[first] : kTileEnd;
         int b = (int)wave_min_u32((uint32_t)nxt);
-        // this lane's output row is row `col` of the tile (position -1 when
-        // that row is not walked now)
-        const int tq = __shfl(tm, col);
+        // this lane's output row in sub-tile sb is row 16 * sb + col of the
+        // tile (position -1 when that row is not walked now)
+        int tq[SUB];
+#pragma unroll
+        for (int sb = 0; sb < SUB; ++sb) tq[sb] = __shfl(tm, 16 * sb + col);
         while (b != kTileEnd) {
             const bool hit = nxt == b;
             const int pos = hit ? cur : -1;
@@ -802,7 +816,9 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
                 const int v = cur < m ? lst[cur] : -1;
                 nxt = v >= 0 && v < bhi ? v : kTileEnd;
             }
-            const int pq = __shfl(pos, col);           // -1 unless row `col` kept b
+            int pq[SUB];                               // -1 unless that row kept b
+#pragma unroll
+            for (int sb = 0; sb < SUB; ++sb) pq[sb] = __shfl(pos, 16 * sb + col);
             const uint16_t* kb = keys + (koff + ((int64_t)b << LB)) * kDim + 8 * kg;
             const int bend = ((b + 1) << LB) - 1;     // last token of block b
             bf16x8_t k0[KT], k1[KT];
@@ -828,28 +844,33 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
             const int bn = (int)wave_min_u32((uint32_t)nxt);
             const bool seen = bend <= tmin;           // no walked row masks a token of b
             // keys as the A operand: lane l receives keys 4*(l/16)..+4 of
-            // each 16-key tile for query row l%16.  The KT tiles are
-            // independent accumulations, issued back to back.
-            f32x4_t c[KT];
+            // each 16-key tile for query row l%16 of the sub-tile.  The
+            // tiles are independent accumulations, issued back to back.
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-                c[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[kt], a0, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            for (int sb = 0; sb < SUB; ++sb) {
+                f32x4_t c[KT];
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) c[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[kt], a1, c[kt], 0, 0, 0);
-            if (pq >= 0) {
-                uint32_t* urow = ukeys + (row0 + col) * N + ((int64_t)pq << LB) + 4 * kg;
+                for (int kt = 0; kt < KT; ++kt)
+                    c[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[kt], a0[sb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0,
+                                                                    0, 0);
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt) {
-                    uint4 o = make_uint4(score_key(c[kt][0]), score_key(c[kt][1]), score_key(c[kt][2]),
-                                         score_key(c[kt][3]));
-                    if (!seen) {
-                        const int j = (b << LB) + kt * 16 + 4 * kg;
-                        o.x = j + 0 <= tq ? o.x : 0u;
-                        o.y = j + 1 <= tq ? o.y : 0u;
-                        o.z = j + 2 <= tq ? o.z : 0u;
-                        o.w = j + 3 <= tq ? o.w : 0u;
+                for (int kt = 0; kt < KT; ++kt)
+                    c[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[kt], a1[sb], c[kt], 0, 0, 0);
+                if (pq[sb] >= 0) {
+                    uint32_t* urow = ukeys + (row0 + 16 * sb + col) * N + ((int64_t)pq[sb] << LB) + 4 * kg;
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt) {
+                        uint4 o = make_uint4(score_key(c[kt][0]), score_key(c[kt][1]), score_key(c[kt][2]),
+                                             score_key(c[kt][3]));
+                        if (!seen) {
+                            const int j = (b << LB) + kt * 16 + 4 * kg;
+                            o.x = j + 0 <= tq[sb] ? o.x : 0u;
+                            o.y = j + 1 <= tq[sb] ? o.y : 0u;
+                            o.z = j + 2 <= tq[sb] ? o.z : 0u;
+                            o.w = j + 3 <= tq[sb] ? o.w : 0u;
+                        }
+                        *reinterpret_cast<uint4*>(urow + kt * 16) = o;
                     }
-                    *reinterpret_cast<uint4*>(urow + kt * 16) = o;
                 }
             }
             b = bn;
@@ -857,20 +878,21 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
     }
 }
 
-hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m,
-                                     int64_t Mmax, const RowInfo* rinfo, const int32_t* sel, uint32_t* ukeys,
-                                     hipStream_t stream, Timing t)
+template <int SUB>
+hipError_t launch_tile_sub(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m,
+                           int64_t Mmax, const RowInfo* rinfo, const int32_t* sel, uint32_t* ukeys,
+                           hipStream_t stream, Timing t)
 {
     // enough waves to fill the chip: split each tile's blocks into ranges
-    const int64_t ntiles = (nq + kTileQueries - 1) / kTileQueries;
+    const int64_t ntiles = (nq + kTileQueries * SUB - 1) / (kTileQueries * SUB);
     const int64_t want = std::max<int64_t>(1, (kTileTargetWaves + ntiles - 1) / ntiles);
     const int64_t range = std::max<int64_t>(1, (Mmax + want - 1) / want);
     const int64_t nranges = (Mmax + range - 1) / range;
     const dim3 grid((unsigned)ntiles, (unsigned)((nranges + kTileWaves - 1) / kTileWaves));
     const dim3 block(64 * kTileWaves);
-    const size_t lds = (size_t)kTileQueries * m * sizeof(int32_t);
+    const size_t lds = (size_t)kTileQueries * SUB * m * sizeof(int32_t);
 #define HISA_T2(LB_) \
-    if (lb == LB_) return launch_kl(stage2_tile_kernel<LB_>, grid, block, lds, stream, t.start, t.stop, qm.queries, keys, q0, nq, m, (int)range, rinfo, sel, ukeys)
+    if (lb == LB_) return launch_kl(stage2_tile_kernel<LB_, SUB>, grid, block, lds, stream, t.start, t.stop, qm.queries, keys, q0, nq, m, (int)range, rinfo, sel, ukeys)
     HISA_T2(4);
     HISA_T2(5);
     HISA_T2(6);
@@ -878,6 +900,20 @@ hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, 
     HISA_T2(8);
 #undef HISA_T2
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m,
+                                     int64_t Mmax, const RowInfo* rinfo, const int32_t* sel, uint32_t* ukeys,
+                                     hipStream_t stream, Timing t)
+{
+    // as many 16-query sub-tiles per wave (up to 4, all 64 lanes) as the
+    // lists of kept blocks leave room for in LDS
+    const size_t per16 = (size_t)kTileQueries * m * sizeof(int32_t);
+    if (4 * per16 <= kTileListBytes)
+        return launch_tile_sub<4>(qm, keys, q0, nq, lb, m, Mmax, rinfo, sel, ukeys, stream, t);
+    if (2 * per16 <= kTileListBytes)
+        return launch_tile_sub<2>(qm, keys, q0, nq, lb, m, Mmax, rinfo, sel, ukeys, stream, t);
+    return launch_tile_sub<1>(qm, keys, q0, nq, lb, m, Mmax, rinfo, sel, ukeys, stream, t);
 }
 
 // Top-k of rows of N ranking keys, one workgroup per row; out rows start at

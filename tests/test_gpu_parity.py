@@ -150,6 +150,23 @@ def test_index_small_grid(L, B, m, k, iid):
         _check_phase(w, cache, ph, k, m, flat, label="grid%d" % L)
 
 
+@pytest.mark.parametrize("B,m,k", [(16, 1024, 2048), (16, 500, 1000), (32, 300, 4000)])
+def test_many_queries_long_kept_lists(B, m, k):
+    """Enough queries for the matrix-core token scores, with kept-block
+    lists long enough that a wave serves one (m = 1024), two (m = 500) or
+    four (m = 300) 16-query sub-tiles."""
+    print("long kept lists B=%d m=%d k=%d" % (B, m, k), flush=True)
+    dv = _dev()
+    L = 20000
+    pos = np.arange(3, L, 33, dtype=np.int64)       # 606 queries, every block size of row
+    w = synth.chunked_prefill(L=L, seed=29, B=B, m=m, k=k, q_positions=pos)
+    cache = dv.DeviceCache(w, B=B)
+    cache.pool()
+    g = np.random.default_rng(B + m)
+    rows = sorted(set([0, 1, 15, 16, 63, 64, len(pos) - 1] + list(g.choice(len(pos), 80, replace=False))))
+    _check_phase(w, cache, w.phases[0], k, m, False, rows=rows, label="longlists")
+
+
 def test_small_workspace_forces_chunks():
     print("chunked workspace", flush=True)
     dv = _dev()
