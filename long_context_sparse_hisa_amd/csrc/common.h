@@ -178,7 +178,11 @@ __device__ __forceinline__ int block_sum(int v, int* scratch)
     return tot;
 }
 
-__device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
+// How many lanes below this one have their bit set in b (v_mbcnt).
+__device__ __forceinline__ int count_below(uint64_t b)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
 
 // ---- query metadata ----------------------------------------------------------
 

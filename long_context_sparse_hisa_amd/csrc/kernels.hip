@@ -918,7 +918,11 @@ hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, 
 
 // Top-k of rows of N ranking keys, one workgroup per row; out rows start at
 // out_idx / out_scores (the caller offsets them).  sel: slot -> token map.
-template <int NT, int ITEMS>
+// WAVE_BLK (sel given, B >= 64): the 64 slots of one item lie in one kept
+// block, so an item's token is a wave-uniform base plus the lane, and the
+// wave reads its kept blocks once (lane j holds the j-th block of its slot
+// range) instead of one LDS lookup per emitted key.
+template <int NT, int ITEMS, bool WAVE_BLK>
 __global__ __launch_bounds__(NT) void topk_rows_kernel(const uint32_t* ukeys, int N, int k, const int32_t* sel, int m,
                                                        int lb, int32_t* out_idx, float* out_scores)
 {
@@ -950,10 +954,26 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(const uint32_t* ukeys, in
     int32_t* orow = out_idx + row * k;
     float* scrow = out_scores ? out_scores + row * k : nullptr;
     const Threshold th = wg_bucket_select<NT, ITEMS>(key, k, sm);
-    const int total = wg_emit_selected<NT, ITEMS>(key, th, sm, k, [&](int slot, uint32_t kk, int rank) {
-        orow[rank] = sel ? (s_list[slot >> lb] << lb) + (slot & ((1 << lb) - 1)) : slot;
-        if (scrow) scrow[rank] = key_score(kk);
-    });
+    int total;
+    if constexpr (WAVE_BLK) {
+        const int lane = lane_id();
+        const int sh = lb - 6;                             // item -> kept block: (wave item) >> sh
+        const int g0 = __builtin_amdgcn_readfirstlane(wave_id()) * ITEMS;   // the wave's first item (scalar)
+        const int j0 = g0 >> sh;
+        const int mask = (1 << lb) - 1;
+        const int myblk = j0 + lane < m ? s_list[j0 + lane] : 0;
+        total = wg_emit_selected_items<NT, ITEMS>(key, th, sm, k, [&](int it, uint32_t kk, int rank) {
+            const int g = g0 + it;
+            const int base = (__builtin_amdgcn_readlane(myblk, (g >> sh) - j0) << lb) + ((g << 6) & mask);
+            orow[(uint32_t)rank] = base + lane;
+            if (scrow) scrow[(uint32_t)rank] = key_score(kk);
+        });
+    } else {
+        total = wg_emit_selected<NT, ITEMS>(key, th, sm, k, [&](int slot, uint32_t kk, int rank) {
+            orow[rank] = sel ? (s_list[slot >> lb] << lb) + (slot & ((1 << lb) - 1)) : slot;
+            if (scrow) scrow[rank] = key_score(kk);
+        });
+    }
     for (int r = total + threadIdx.x; r < k; r += NT) {
         orow[r] = -1;
         if (scrow) scrow[r] = __builtin_nanf("");
@@ -965,8 +985,11 @@ static hipError_t launch_topk_rows_items(const uint32_t* ukeys, int64_t nrows, i
                                          int m, int lb, int32_t* out_idx, float* out_scores, hipStream_t stream,
                                          Timing t)
 {
-    return launch_k(topk_rows_kernel<NT, ITEMS>, dim3((unsigned)nrows), dim3(NT), stream, t.start, t.stop, ukeys, N, k,
-                    sel, m, lb, out_idx, out_scores);
+    if (sel && lb >= 6)
+        return launch_k(topk_rows_kernel<NT, ITEMS, true>, dim3((unsigned)nrows), dim3(NT), stream, t.start, t.stop,
+                        ukeys, N, k, sel, m, lb, out_idx, out_scores);
+    return launch_k(topk_rows_kernel<NT, ITEMS, false>, dim3((unsigned)nrows), dim3(NT), stream, t.start, t.stop,
+                    ukeys, N, k, sel, m, lb, out_idx, out_scores);
 }
 
 // ---- block-only selection: the kept blocks expanded -------------------------
@@ -1567,8 +1590,8 @@ __global__ __launch_bounds__(kThreads) void radix_emit_kernel(const uint32_t* uk
             sg += wc[0][v];
             se += wc[1][v];
         }
-        const int pg = og + __popcll(mg & lanemask_lt());
-        const int pe = oe + __popcll(me & lanemask_lt());
+        const int pg = og + count_below(mg);
+        const int pe = oe + count_below(me);
         int pos = -1;
         if (gt) pos = pg + min(pe, need_eq);
         else if (eq && pe < need_eq) pos = pg + pe;

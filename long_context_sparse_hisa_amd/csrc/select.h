@@ -385,16 +385,17 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
     return th;
 }
 
-// Hand every selected key to emit(slot, key, rank), rank = its position in
-// ascending slot order among the selected, for ranks below `limit` (a
-// guard: a consistent threshold never selects more than the n asked for).
-// Returns how many were selected, at most limit.
+// Hand every selected key to emit(it, key, rank) (item it of this thread,
+// slot slot_of<ITEMS>(it)), rank = its position in ascending slot order
+// among the selected, for ranks below `limit` (a guard: a consistent
+// threshold never selects more than the n asked for).  Returns how many
+// were selected, at most limit.
 // One barrier: each wave knows the counts of its own slots from ballots and
 // only needs the totals of the waves before it.  No barrier at the end:
 // synchronise before reusing the shared memory.
 template <int NT, int ITEMS, class Emit>
-HISA_INLINE int wg_emit_selected(const uint32_t (&key)[ITEMS], const Threshold& th, BucketSmem<NT>& sm, int limit,
-                                 Emit emit)
+HISA_INLINE int wg_emit_selected_items(const uint32_t (&key)[ITEMS], const Threshold& th, BucketSmem<NT>& sm,
+                                       int limit, Emit emit)
 {
     constexpr int NW = NT / 64;
     const int w = wave_id();
@@ -418,7 +419,6 @@ HISA_INLINE int wg_emit_selected(const uint32_t (&key)[ITEMS], const Threshold& 
         tg += g;
         te += q;
     }
-    const uint64_t lt = lanemask_lt();
     if (th.all || te <= th.need_eq) {
         // every key equal to the threshold is taken: selected = key >= T
         // (or every nonzero key), ranked by one ballot per item
@@ -428,8 +428,8 @@ HISA_INLINE int wg_emit_selected(const uint32_t (&key)[ITEMS], const Threshold& 
         for (int it = 0; it < ITEMS; ++it) {
             const bool take = key[it] >= lo;
             const uint64_t b = __ballot(take);
-            const int rank = r + __popcll(b & lt);
-            if (take && rank < limit) emit(slot_of<ITEMS>(it), key[it], rank);
+            const int rank = r + count_below(b);
+            if (take && rank < limit) emit(it, key[it], rank);
             r += __popcll(b);
         }
         return min(limit, tg + te);
@@ -440,14 +440,23 @@ HISA_INLINE int wg_emit_selected(const uint32_t (&key)[ITEMS], const Threshold& 
         const bool eq = key[it] == th.T;
         const uint64_t bg = __ballot(gt);
         const uint64_t be = __ballot(eq);
-        const int pg = rg + __popcll(bg & lt);
-        const int pe = re + __popcll(be & lt);
+        const int pg = rg + count_below(bg);
+        const int pe = re + count_below(be);
         const int rank = gt ? pg + min(pe, th.need_eq) : pg + pe;
-        if ((gt || (eq && pe < th.need_eq)) && rank < limit) emit(slot_of<ITEMS>(it), key[it], rank);
+        if ((gt || (eq && pe < th.need_eq)) && rank < limit) emit(it, key[it], rank);
         rg += __popcll(bg);
         re += __popcll(be);
     }
     return min(limit, tg + min(te, th.need_eq));
+}
+
+// The same with emit(slot, key, rank).
+template <int NT, int ITEMS, class Emit>
+HISA_INLINE int wg_emit_selected(const uint32_t (&key)[ITEMS], const Threshold& th, BucketSmem<NT>& sm, int limit,
+                                 Emit emit)
+{
+    return wg_emit_selected_items<NT, ITEMS>(key, th, sm, limit,
+                                             [&](int it, uint32_t kk, int rank) { emit(slot_of<ITEMS>(it), kk, rank); });
 }
 
 // ---- wave-level select -------------------------------------------------------------
@@ -521,7 +530,6 @@ template <int ITEMS, class Emit>
 HISA_INLINE int wave_select(const uint32_t (&key)[ITEMS], int n, WaveSmem& ws, Emit emit)
 {
     const int lane = lane_id();
-    const uint64_t lt = lanemask_lt();
     if (n <= 0) return 0;
     int nvalid = 0;
     uint32_t kmax = 0u, kmin1 = 0xffffffffu;
@@ -592,7 +600,7 @@ HISA_INLINE int wave_select(const uint32_t (&key)[ITEMS], int n, WaveSmem& ws, E
                     const bool mem = key[it] && bin(key[it]) == bstar;
                     const uint64_t b = __ballot(mem);
                     if (mem) {
-                        const int p = base + __popcll(b & lt);
+                        const int p = base + count_below(b);
                         ws.list_key[p] = key[it];
                         ws.list_slot[p] = it * 64 + lane;
                     }
@@ -623,10 +631,10 @@ HISA_INLINE int wave_select(const uint32_t (&key)[ITEMS], int n, WaveSmem& ws, E
         const bool gt = th.all ? key[it] >= lo : key[it] > th.T;
         const bool is_eq = !th.all && key[it] == th.T;
         const uint64_t bg = __ballot(gt), be = __ballot(is_eq);
-        const int pe = eq + __popcll(be & lt);
+        const int pe = eq + count_below(be);
         const bool take = gt || (is_eq && pe < th.need_eq);
         const uint64_t bt = __ballot(take);
-        if (take) emit(it * 64 + lane, key[it], rank + __popcll(bt & lt));
+        if (take) emit(it * 64 + lane, key[it], rank + count_below(bt));
         rank += __popcll(bt);
         eq += __popcll(be);
         (void)bg;
