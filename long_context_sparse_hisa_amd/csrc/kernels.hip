@@ -918,11 +918,13 @@ hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, 
 
 // Top-k of rows of N ranking keys, one workgroup per row; out rows start at
 // out_idx / out_scores (the caller offsets them).  sel: slot -> token map.
-// WAVE_BLK (sel given, B >= 64): the 64 slots of one item lie in one kept
-// block, so an item's token is a wave-uniform base plus the lane, and the
-// wave reads its kept blocks once (lane j holds the j-th block of its slot
-// range) instead of one LDS lookup per emitted key.
-template <int NT, int ITEMS, bool WAVE_BLK>
+// WAVE_BLK (sel given, B >= 64, so N and the row's candidate count are
+// multiples of 64): the 64 slots of one item lie in one kept block, so an
+// item's token is a wave-uniform base plus the lane, the wave reads its
+// kept blocks once (lane j holds the j-th block of its slot range) instead
+// of one LDS lookup per emitted key, and the bounds of an item are scalar
+// tests.  SCORES: out_scores is written.
+template <int NT, int ITEMS, bool WAVE_BLK, bool SCORES>
 __global__ __launch_bounds__(NT) void topk_rows_kernel(const uint32_t* ukeys, int N, int k, const int32_t* sel, int m,
                                                        int lb, int32_t* out_idx, float* out_scores)
 {
@@ -930,53 +932,65 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(const uint32_t* ukeys, in
     __shared__ int32_t s_list[kMaxKept];                   // the row's kept blocks
     const int64_t row = blockIdx.x;
     const uint32_t* src = ukeys + row * N;
-    // the keys and the kept-block list load together; slots of -1 list
-    // entries (a suffix of the list) hold no candidate and are masked after
-    uint32_t key[ITEMS];
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-        const int s = slot_of<ITEMS>(it);
-        key[it] = s < N ? src[s] : 0u;
-    }
-    if (sel) {
-        int cnt = 0;
-        for (int i = lane_id(); i < m; i += 64) {
-            const int32_t v = sel[row * m + i];
-            cnt += v >= 0;
-            if (wave_id() == 0) s_list[i] = v;
-        }
-        const int n = min(N, wave_sum(cnt) << lb);
-#pragma unroll
-        for (int it = 0; it < ITEMS; ++it)
-            if (slot_of<ITEMS>(it) >= n) key[it] = 0u;
-    }
-    // the select's barriers publish s_list before anything is emitted
+    const int lane = lane_id();
+    const int g0 = __builtin_amdgcn_readfirstlane(wave_id()) * ITEMS;   // the wave's first item (scalar)
     int32_t* orow = out_idx + row * k;
-    float* scrow = out_scores ? out_scores + row * k : nullptr;
-    const Threshold th = wg_bucket_select<NT, ITEMS>(key, k, sm);
+    float* scrow = SCORES ? out_scores + row * k : nullptr;
     int total;
     if constexpr (WAVE_BLK) {
-        const int lane = lane_id();
         const int sh = lb - 6;                             // item -> kept block: (wave item) >> sh
-        const int g0 = __builtin_amdgcn_readfirstlane(wave_id()) * ITEMS;   // the wave's first item (scalar)
         const int j0 = g0 >> sh;
         const int mask = (1 << lb) - 1;
-        const int myblk = j0 + lane < m ? s_list[j0 + lane] : 0;
+        // every item loads (items past the row re-read its last 64 slots)
+        // and is masked after by a scalar: slots of -1 list entries (a
+        // suffix of the list) and past N hold no candidate
+        uint32_t key[ITEMS];
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) key[it] = src[min((g0 + it) << 6, N - 64) + lane];
+        const int myblk = j0 + lane < m ? sel[row * m + j0 + lane] : 0;
+        int cnt = 0;
+        for (int i = lane; i < m; i += 64) cnt += sel[row * m + i] >= 0;
+        const int n = min(N, wave_sum(cnt) << lb);
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) key[it] &= ((g0 + it) << 6) < n ? 0xffffffffu : 0u;
+        const Threshold th = wg_bucket_select<NT, ITEMS>(key, k, sm);
         total = wg_emit_selected_items<NT, ITEMS>(key, th, sm, k, [&](int it, uint32_t kk, int rank) {
             const int g = g0 + it;
             const int base = (__builtin_amdgcn_readlane(myblk, (g >> sh) - j0) << lb) + ((g << 6) & mask);
             orow[(uint32_t)rank] = base + lane;
-            if (scrow) scrow[(uint32_t)rank] = key_score(kk);
+            if constexpr (SCORES) scrow[(uint32_t)rank] = key_score(kk);
         });
     } else {
+        // the keys and the kept-block list load together; slots of -1 list
+        // entries (a suffix of the list) hold no candidate and are masked after
+        uint32_t key[ITEMS];
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int s = slot_of<ITEMS>(it);
+            key[it] = s < N ? src[s] : 0u;
+        }
+        if (sel) {
+            int cnt = 0;
+            for (int i = lane; i < m; i += 64) {
+                const int32_t v = sel[row * m + i];
+                cnt += v >= 0;
+                if (wave_id() == 0) s_list[i] = v;
+            }
+            const int n = min(N, wave_sum(cnt) << lb);
+#pragma unroll
+            for (int it = 0; it < ITEMS; ++it)
+                if (slot_of<ITEMS>(it) >= n) key[it] = 0u;
+        }
+        // the select's barriers publish s_list before anything is emitted
+        const Threshold th = wg_bucket_select<NT, ITEMS>(key, k, sm);
         total = wg_emit_selected<NT, ITEMS>(key, th, sm, k, [&](int slot, uint32_t kk, int rank) {
             orow[rank] = sel ? (s_list[slot >> lb] << lb) + (slot & ((1 << lb) - 1)) : slot;
-            if (scrow) scrow[rank] = key_score(kk);
+            if constexpr (SCORES) scrow[rank] = key_score(kk);
         });
     }
     for (int r = total + threadIdx.x; r < k; r += NT) {
         orow[r] = -1;
-        if (scrow) scrow[r] = __builtin_nanf("");
+        if constexpr (SCORES) scrow[r] = __builtin_nanf("");
     }
 }
 
@@ -985,11 +999,15 @@ static hipError_t launch_topk_rows_items(const uint32_t* ukeys, int64_t nrows, i
                                          int m, int lb, int32_t* out_idx, float* out_scores, hipStream_t stream,
                                          Timing t)
 {
-    if (sel && lb >= 6)
-        return launch_k(topk_rows_kernel<NT, ITEMS, true>, dim3((unsigned)nrows), dim3(NT), stream, t.start, t.stop,
-                        ukeys, N, k, sel, m, lb, out_idx, out_scores);
-    return launch_k(topk_rows_kernel<NT, ITEMS, false>, dim3((unsigned)nrows), dim3(NT), stream, t.start, t.stop,
-                    ukeys, N, k, sel, m, lb, out_idx, out_scores);
+#define HISA_TR(W_, S_) \
+    return launch_k(topk_rows_kernel<NT, ITEMS, W_, S_>, dim3((unsigned)nrows), dim3(NT), stream, t.start, t.stop, \
+                    ukeys, N, k, sel, m, lb, out_idx, out_scores)
+    const bool wave_blk = sel && lb >= 6;
+    if (wave_blk && out_scores) HISA_TR(true, true);
+    if (wave_blk) HISA_TR(true, false);
+    if (out_scores) HISA_TR(false, true);
+    HISA_TR(false, false);
+#undef HISA_TR
 }
 
 // ---- block-only selection: the kept blocks expanded -------------------------

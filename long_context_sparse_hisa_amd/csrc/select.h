@@ -229,9 +229,8 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
     for (int it = 0; it < ITEMS; ++it) {
         kmax = max(kmax, key[it]);
         kmin1 = min(kmin1, key[it] - 1u);     // an empty slot wraps to the top
-        nz += key[it] != 0u;
+        nz += __popcll(__ballot(key[it] != 0u));
     }
-    nz = wave_sum(nz);
     kmax = wave_max_u32(kmax);
     kmin1 = wave_min_u32(kmin1);
     if (lane_id() == 0) {

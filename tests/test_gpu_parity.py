@@ -150,11 +150,14 @@ def test_index_small_grid(L, B, m, k, iid):
         _check_phase(w, cache, ph, k, m, flat, label="grid%d" % L)
 
 
-@pytest.mark.parametrize("B,m,k", [(16, 1024, 2048), (16, 500, 1000), (32, 300, 4000)])
+@pytest.mark.parametrize("B,m,k", [(16, 1024, 2048), (16, 500, 1000), (32, 300, 4000), (128, 128, 4096),
+                                   (64, 256, 3000)])
 def test_many_queries_long_kept_lists(B, m, k):
     """Enough queries for the matrix-core token scores, with kept-block
-    lists long enough that a wave serves one (m = 1024), two (m = 500) or
-    four (m = 300) 16-query sub-tiles."""
+    lists long enough that a wave serves one (m = 1024), two (m = 500, 256)
+    or four (m = 300, 128) 16-query sub-tiles; the last two also take the
+    16,384-candidate rows of the 512-thread top-k with per-wave token
+    bases (B >= 64)."""
     print("long kept lists B=%d m=%d k=%d" % (B, m, k), flush=True)
     dv = _dev()
     L = 20000
@@ -165,6 +168,31 @@ def test_many_queries_long_kept_lists(B, m, k):
     g = np.random.default_rng(B + m)
     rows = sorted(set([0, 1, 15, 16, 63, 64, len(pos) - 1] + list(g.choice(len(pos), 80, replace=False))))
     _check_phase(w, cache, w.phases[0], k, m, False, rows=rows, label="longlists")
+
+
+@pytest.mark.parametrize("kind,B,m,k", [("prefill", 128, 8, 256), ("prefill", 32, 12, 300), ("prefill", 64, 128, 4096),
+                                         ("decode", 128, 16, 512), ("decode", 32, 40, 900)])
+def test_indices_without_scores_equal_with_scores(kind, B, m, k):
+    """The index rows do not depend on whether the optional scores are
+    written (the calls the benchmark times request none); the rows with
+    scores are checked against the oracle elsewhere."""
+    print("no-scores %s B=%d m=%d k=%d" % (kind, B, m, k), flush=True)
+    dv = _dev()
+    if kind == "prefill":
+        w = synth.chunked_prefill(L=9000, seed=31, B=B, m=m, k=k, q_positions=np.arange(0, 9000, 7))
+    else:
+        w = synth.decode_batch(nseq=6, L=20000, seed=31, B=B, m=m, k=k)
+    cache = dv.DeviceCache(w, B=B)
+    cache.pool()
+    ph = w.phases[0]
+    for flat in (False, True):
+        a = dv.IndexCall(cache, ph.queries, ph.q_pos, ph.q_seq, k=k, m=m, flat=flat)
+        b = dv.IndexCall(cache, ph.queries, ph.q_pos, ph.q_seq, k=k, m=m, flat=flat, scores=False)
+        a.run()
+        b.run()
+        ia = a.results()[0]
+        ib = b.results()[0]
+        assert np.array_equal(ia, ib), "%s flat=%s: rows differ without scores" % (kind, flat)
 
 
 def test_small_workspace_forces_chunks():
