@@ -280,42 +280,38 @@ static hipError_t launch_stage1_items(const QueryMeta& qm, const uint16_t* reps,
                     q0, lb, m, Mmax, sigma, sel, rinfo, out_blocks);
 }
 
-// Many queries (prefill): 16 consecutive query rows form a tile, scored
-// against the representatives on the bf16 MFMA (16 blocks x 16 rows per
-// pair of v_mfma_f32_16x16x32_bf16).  WT waves share a tile: each computes
-// the tile's scores (cheap) but keeps only its own rows r = wt (mod WT) in
-// its LDS, kS1RowsPerPass at a time, and selects their top-m with the
-// barrier-free wave select.  WT grows when there are few tiles, so the
-// selects still fill the chip.  Rows of a tile in different sequences are
-// handled one sequence at a time.  ITEMS = 64-slot groups per row: block b
-// is slot b.
+// Many queries (prefill): 16 consecutive query rows form a tile, one
+// workgroup of WT waves per tile.  The waves score the tile's rows against
+// the representatives on the bf16 MFMA together (the 16-block tiles dealt
+// round-robin, 16 blocks x 16 rows per pair of v_mfma_f32_16x16x32_bf16)
+// into the workgroup's LDS, so a representative is read once per query
+// tile; then wave w selects the top-m of rows w, w+WT, ... with the
+// barrier-free wave select.  WT grows when tiles are few, so the selects
+// still fill the chip.  Rows of a tile in different sequences are handled
+// one sequence at a time.  ITEMS = 64-slot groups per row: block b is slot b.
 
-constexpr int kS1TileWaves = 2;               // waves per workgroup
 constexpr int kS1TileMaxBlocks = 1024;
 constexpr int64_t kS1TargetWaves = 4096;
+constexpr int kS1MaxWaves = 16;
 
-__host__ __device__ constexpr int s1_rows_per_pass(int items) { return items <= 4 ? 16 : 64 / items; }
 __host__ __device__ constexpr int s1_row_stride(int items) { return 64 * items + 16; }   // floats; +16 spreads banks
-__host__ __device__ constexpr size_t s1_wave_lds(int items)
+__host__ __device__ constexpr size_t s1_tile_lds(int items, int wt)
 {
-    return (size_t)s1_rows_per_pass(items) * s1_row_stride(items) * sizeof(float) + sizeof(WaveSmem);
+    return (size_t)16 * s1_row_stride(items) * sizeof(float) + (size_t)wt * sizeof(WaveSmem);
 }
 
 template <int ITEMS>
-__global__ __launch_bounds__(64 * kS1TileWaves) void stage1_tile_kernel(QueryMeta qm, const uint16_t* reps, int64_t q0,
-                                                                        int64_t nq, int lb, int m, int WT, int32_t* sel,
-                                                                        RowInfo* rinfo, int32_t* out_blocks)
+__global__ __launch_bounds__(64 * kS1MaxWaves) void stage1_tile_kernel(QueryMeta qm, const uint16_t* reps, int64_t q0,
+                                                                       int64_t nq, int lb, int m, int32_t* sel,
+                                                                       RowInfo* rinfo, int32_t* out_blocks)
 {
     extern __shared__ __align__(16) float s_dyn[];
-    constexpr int R = s1_rows_per_pass(ITEMS);
     constexpr int RS = s1_row_stride(ITEMS);
+    const int WT = (int)(blockDim.x >> 6);
     const int w = wave_id(), lane = lane_id();
-    float* sc = s_dyn + w * (s1_wave_lds(ITEMS) / sizeof(float));
-    WaveSmem& ws = *reinterpret_cast<WaveSmem*>(sc + R * RS);
-    const int64_t gw = (int64_t)blockIdx.x * kS1TileWaves + w;
-    const int wt = (int)(gw % WT);
-    const int64_t row0 = (gw / WT) * 16;
-    if (row0 >= nq) return;
+    float* sc = s_dyn;                                   // [16][RS]: the tile's block scores
+    WaveSmem& ws = reinterpret_cast<WaveSmem*>(s_dyn + 16 * RS)[w];
+    const int64_t row0 = (int64_t)blockIdx.x * 16;
     const int nrows = (int)min<int64_t>(16, nq - row0);
     const int r = lane & 15;
     QueryInfo qi;
@@ -327,11 +323,10 @@ __global__ __launch_bounds__(64 * kS1TileWaves) void stage1_tile_kernel(QueryMet
     if (lane < 16 && r < nrows) {
         qi = query_info(q0 + row0 + r, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq,
                         qm.max_len);
-        if (wt == 0) rinfo[row0 + r] = RowInfo{qi.key_off, qi.valid ? qi.t : -1};
+        if (w == 0) rinfo[row0 + r] = RowInfo{qi.key_off, qi.valid ? qi.t : -1};
     }
-    const bool own = lane < 16 && r < nrows && r % WT == wt;
     // invalid rows keep no block
-    for (uint64_t iv = __ballot(own && !qi.valid); iv; iv &= iv - 1) {
+    for (uint64_t iv = __ballot(lane < 16 && r < nrows && r % WT == w && !qi.valid); iv; iv &= iv - 1) {
         const int rr = (int)__builtin_ctzll(iv);
         for (int i = lane; i < m; i += 64) {
             sel[(row0 + rr) * m + i] = -1;
@@ -346,79 +341,71 @@ __global__ __launch_bounds__(64 * kS1TileWaves) void stage1_tile_kernel(QueryMet
         a1 = *reinterpret_cast<const bf16x8_t*>(qrow + 32);
     }
     const int c_own = qi.valid ? (int)(qi.t >> lb) : -1;
-    uint64_t pending = __ballot(own && qi.valid);
+    // every wave computes the same row infos, so the loop below is uniform
+    // over the workgroup
+    const bool act = lane < 16 && r < nrows && qi.valid;
+    uint64_t pending = __ballot(act);
     while (pending) {
         const int lead = (int)__builtin_ctzll(pending);
         const int s = __builtin_amdgcn_readlane(qi.seq, lead);
-        const bool mine = own && qi.valid && qi.seq == s;
+        const bool mine = act && qi.seq == s;
         const uint64_t mine_rows = __ballot(mine);
         pending &= ~mine_rows;
         const int64_t rep_off = ((int64_t)__builtin_amdgcn_readlane((int)(qi.rep_off >> 32), lead) << 32) |
                                 (uint32_t)__builtin_amdgcn_readlane((int)qi.rep_off, lead);
         const int cmax = (int)wave_max_u32(mine ? (uint32_t)c_own : 0u);
-        // own rows are wt, wt+WT, ...: own index i = row / WT
-        const int nown = (16 - wt + WT - 1) / WT;
-        for (int i0 = 0; i0 < nown; i0 += R) {
-            bool any = false;
-            for (int i = i0; i < i0 + R && i < nown; ++i) any |= (mine_rows >> (wt + i * WT)) & 1ull;
-            if (!any) continue;
-            // scores of blocks 0 .. cmax for own rows i0 .. i0+R-1: the
-            // representatives are the A operand, so lane l receives blocks
-            // 4*(l/16)..+4 of the tile for query row l%16 and stores them as
-            // one 16-byte vector
-            const int iq = col / WT - i0;
-            const bool keep = col % WT == wt && iq >= 0 && iq < R;
-            for (int bt = 0; bt * 16 <= cmax; ++bt) {
-                const int b = bt * 16 + col;
-                bf16x8_t b0 = {}, b1 = {};
-                if (b <= cmax) {
-                    const uint16_t* rp = reps + (rep_off + b) * kDim + 8 * kg;
-                    b0 = *reinterpret_cast<const bf16x8_t*>(rp);
-                    b1 = *reinterpret_cast<const bf16x8_t*>(rp + 32);
-                }
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, a0, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, a1, acc, 0, 0, 0);
-                if (keep) *reinterpret_cast<f32x4_t*>(sc + iq * RS + bt * 16 + 4 * kg) = acc;
+        // scores of blocks 0 .. cmax: the representatives are the A
+        // operand, so lane l receives blocks 4*(l/16)..+4 of the 16-block
+        // tile for query row l%16 and stores them as one 16-byte vector
+        for (int bt = w; bt * 16 <= cmax; bt += WT) {
+            const int b = bt * 16 + col;
+            bf16x8_t b0 = {}, b1 = {};
+            if (b <= cmax) {
+                const uint16_t* rp = reps + (rep_off + b) * kDim + 8 * kg;
+                b0 = *reinterpret_cast<const bf16x8_t*>(rp);
+                b1 = *reinterpret_cast<const bf16x8_t*>(rp + 32);
             }
-            wave_lds_fence();
-            for (int i = i0; i < i0 + R && i < nown; ++i) {
-                const int rr = wt + i * WT;
-                if (!((mine_rows >> rr) & 1ull)) continue;
-                const int cr = __builtin_amdgcn_readlane(c_own, rr);
-                int32_t* srow = sel + (row0 + rr) * m;
-                int32_t* orow = out_blocks ? out_blocks + (q0 + row0 + rr) * m : nullptr;
-                if (cr + 1 <= m) {
-                    for (int j = lane; j < m; j += 64) {
-                        const int32_t v = j <= cr ? j : -1;
-                        srow[j] = v;
-                        if (orow) orow[j] = v;
-                    }
-                    continue;
-                }
-                uint32_t key[ITEMS];
-#pragma unroll
-                for (int it = 0; it < ITEMS; ++it) {
-                    const int b = it * 64 + lane;
-                    key[it] = (b >= 1 && b <= cr - 2) ? score_key(sc[(i - i0) * RS + b]) : 0u;
-                }
-                wave_select<ITEMS>(key, m - 3, ws, [&](int slot, uint32_t, int rank) {
-                    srow[1 + rank] = slot;
-                    if (orow) orow[1 + rank] = slot;
-                });
-                if (lane == 0) {
-                    srow[0] = 0;
-                    srow[m - 2] = cr - 1;
-                    srow[m - 1] = cr;
-                    if (orow) {
-                        orow[0] = 0;
-                        orow[m - 2] = cr - 1;
-                        orow[m - 1] = cr;
-                    }
-                }
-            }
-            wave_lds_fence();
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, a0, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, a1, acc, 0, 0, 0);
+            *reinterpret_cast<f32x4_t*>(sc + col * RS + bt * 16 + 4 * kg) = acc;
         }
+        __syncthreads();
+        for (int rr = w; rr < 16; rr += WT) {
+            if (!((mine_rows >> rr) & 1ull)) continue;
+            const int cr = __builtin_amdgcn_readlane(c_own, rr);
+            int32_t* srow = sel + (row0 + rr) * m;
+            int32_t* orow = out_blocks ? out_blocks + (q0 + row0 + rr) * m : nullptr;
+            if (cr + 1 <= m) {
+                for (int j = lane; j < m; j += 64) {
+                    const int32_t v = j <= cr ? j : -1;
+                    srow[j] = v;
+                    if (orow) orow[j] = v;
+                }
+                continue;
+            }
+            uint32_t key[ITEMS];
+#pragma unroll
+            for (int it = 0; it < ITEMS; ++it) {
+                const int b = it * 64 + lane;
+                key[it] = (b >= 1 && b <= cr - 2) ? score_key(sc[rr * RS + b]) : 0u;
+            }
+            wave_select<ITEMS>(key, m - 3, ws, [&](int slot, uint32_t, int rank) {
+                srow[1 + rank] = slot;
+                if (orow) orow[1 + rank] = slot;
+            });
+            if (lane == 0) {
+                srow[0] = 0;
+                srow[m - 2] = cr - 1;
+                srow[m - 1] = cr;
+                if (orow) {
+                    orow[0] = 0;
+                    orow[m - 2] = cr - 1;
+                    orow[m - 1] = cr;
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -429,11 +416,9 @@ static hipError_t launch_stage1_tile_items(const QueryMeta& qm, const uint16_t* 
 {
     const int64_t tiles = (nq + 15) / 16;
     int WT = 1;
-    while (WT < 16 && tiles * WT < kS1TargetWaves) WT *= 2;
-    const int64_t waves = tiles * WT;
-    const dim3 grid((unsigned)((waves + kS1TileWaves - 1) / kS1TileWaves));
-    return launch_kl(stage1_tile_kernel<ITEMS>, grid, dim3(64 * kS1TileWaves), kS1TileWaves * s1_wave_lds(ITEMS),
-                     stream, t.start, t.stop, qm, reps, q0, nq, lb, m, WT, sel, rinfo, out_blocks);
+    while (WT < kS1MaxWaves && tiles * WT < kS1TargetWaves) WT *= 2;
+    return launch_kl(stage1_tile_kernel<ITEMS>, dim3((unsigned)tiles), dim3(64 * WT), s1_tile_lds(ITEMS, WT), stream,
+                     t.start, t.stop, qm, reps, q0, nq, lb, m, sel, rinfo, out_blocks);
 }
 
 hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
