@@ -178,6 +178,15 @@ __device__ __forceinline__ int block_sum(int v, int* scratch)
     return tot;
 }
 
+// A raw buffer resource over `bytes` bytes from p (word 3 as CDNA
+// expects for untyped dword access).  Loads through it take a vector
+// offset and a scalar offset, so a wave's per-item addresses cost no
+// vector instructions.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 // How many lanes below this one have their bit set in b (v_mbcnt).
 __device__ __forceinline__ int count_below(uint64_t b)
 {

@@ -909,6 +909,9 @@ hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, 
 // kept blocks once (lane j holds the j-th block of its slot range) instead
 // of one LDS lookup per emitted key, and the bounds of an item are scalar
 // tests.  SCORES: out_scores is written.
+template <int NT>
+constexpr bool kTopkBufferIo = NT < 1024;    // see the WAVE_BLK loads below
+
 template <int NT, int ITEMS, bool WAVE_BLK, bool SCORES>
 __global__ __launch_bounds__(NT) void topk_rows_kernel(const uint32_t* ukeys, int N, int k, const int32_t* sel, int m,
                                                        int lb, int32_t* out_idx, float* out_scores)
@@ -926,12 +929,23 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(const uint32_t* ukeys, in
         const int sh = lb - 6;                             // item -> kept block: (wave item) >> sh
         const int j0 = g0 >> sh;
         const int mask = (1 << lb) - 1;
-        // every item loads (items past the row re-read its last 64 slots)
+        // Every item loads (items past the row re-read its last 64 slots)
         // and is masked after by a scalar: slots of -1 list entries (a
-        // suffix of the list) and past N hold no candidate
+        // suffix of the list) and past N hold no candidate.  The many-rows
+        // shapes, bound by instruction issue, load and store through buffer
+        // resources (the lane is the vector offset, the item's slot a
+        // scalar one: no vector address arithmetic); the 1024-thread shape
+        // for few rows keeps plain loads, measured slightly faster there.
         uint32_t key[ITEMS];
+        if constexpr (kTopkBufferIo<NT>) {
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, (uint32_t)N * 4u);
 #pragma unroll
-        for (int it = 0; it < ITEMS; ++it) key[it] = src[min((g0 + it) << 6, N - 64) + lane];
+            for (int it = 0; it < ITEMS; ++it)
+                key[it] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, min((g0 + it) << 6, N - 64) * 4, 0);
+        } else {
+#pragma unroll
+            for (int it = 0; it < ITEMS; ++it) key[it] = src[min((g0 + it) << 6, N - 64) + lane];
+        }
         const int myblk = j0 + lane < m ? sel[row * m + j0 + lane] : 0;
         int cnt = 0;
         for (int i = lane; i < m; i += 64) cnt += sel[row * m + i] >= 0;
@@ -939,10 +953,14 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(const uint32_t* ukeys, in
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) key[it] &= ((g0 + it) << 6) < n ? 0xffffffffu : 0u;
         const Threshold th = wg_bucket_select<NT, ITEMS>(key, k, sm);
+        const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(orow, (uint32_t)k * 4u);
         total = wg_emit_selected_items<NT, ITEMS>(key, th, sm, k, [&](int it, uint32_t kk, int rank) {
             const int g = g0 + it;
             const int base = (__builtin_amdgcn_readlane(myblk, (g >> sh) - j0) << lb) + ((g << 6) & mask);
-            orow[(uint32_t)rank] = base + lane;
+            if constexpr (kTopkBufferIo<NT>)
+                __builtin_amdgcn_raw_buffer_store_b32(base + lane, ro, rank * 4, 0, 0);
+            else
+                orow[(uint32_t)rank] = base + lane;
             if constexpr (SCORES) scrow[(uint32_t)rank] = key_score(kk);
         });
     } else {

@@ -23,6 +23,16 @@ HISA_INLINE int slot_of(int it)
 
 // ---- workgroup scans for NT threads ------------------------------------------
 
+// Makes the compiler treat the keys as new values (no instruction): lane
+// masks computed from them before this point are not kept live across it
+// in scalar registers.
+template <int ITEMS>
+HISA_INLINE void opaque_keys(uint32_t (&key)[ITEMS])
+{
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) asm volatile("" : "+v"(key[it]));
+}
+
 template <int NT>
 HISA_INLINE int wg_incl_scan(int v, int* scratch)
 {
@@ -393,10 +403,13 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
 // only needs the totals of the waves before it.  No barrier at the end:
 // synchronise before reusing the shared memory.
 template <int NT, int ITEMS, class Emit>
-HISA_INLINE int wg_emit_selected_items(const uint32_t (&key)[ITEMS], const Threshold& th, BucketSmem<NT>& sm,
+HISA_INLINE int wg_emit_selected_items(const uint32_t (&key_in)[ITEMS], const Threshold& th, BucketSmem<NT>& sm,
                                        int limit, Emit emit)
 {
     constexpr int NW = NT / 64;
+    uint32_t key[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) key[it] = key_in[it];
     const int w = wave_id();
     int wg = 0, we = 0;
 #pragma unroll
@@ -409,6 +422,7 @@ HISA_INLINE int wg_emit_selected_items(const uint32_t (&key)[ITEMS], const Thres
         sm.wave_tot[1][w] = we;
     }
     __syncthreads();
+    opaque_keys(key);
     int rg = 0, re = 0, tg = 0, te = 0;
 #pragma unroll
     for (int v = 0; v < NW; ++v) {
