@@ -716,7 +716,7 @@ constexpr int64_t kTileTargetWaves = 16384;
 // kernel's occupancy) fit in the 160 KB of LDS
 constexpr size_t kTileListBytes = 80 * 1024;
 
-template <int LB, int SUB>
+template <int LB, int SUB, int P>
 __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint16_t* queries, const uint16_t* keys,
                                                                       int64_t q0, int64_t nq, int m, int range,
                                                                       const RowInfo* rinfo, const int32_t* sel,
@@ -724,7 +724,9 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
 {
     // SUB sub-tiles of 16 query rows per wave: every key block loaded from
     // L2 feeds SUB MFMA tiles, so the union walk reads each block once per
-    // 16 * SUB queries
+    // 16 * SUB queries.  A block is taken in P pieces of KT/P key tiles,
+    // and the next piece (of this block or the next one) is loaded while
+    // the current one is on the MFMA.
     constexpr int TQ = kTileQueries * SUB;
     extern __shared__ int32_t s_sel[];            // [TQ][m] kept-block lists of the tile's rows
     constexpr int B = 1 << LB;
@@ -776,6 +778,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
             a1[sb] = *reinterpret_cast<const bf16x8_t*>(qrow + 32);
         }
     }
+    constexpr int KP = KT / P;                    // key tiles per piece
     while (pending) {
         const int lead = (int)__builtin_ctzll(pending);
         const int64_t koff = ((int64_t)__builtin_amdgcn_readlane((int)(ri.key_off >> 32), lead) << 32) |
@@ -787,37 +790,26 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
         const int tm = mine ? t32 : -1;
         int cur = first;
         int nxt = mine ? lst[first] : kTileEnd;
-        int b = (int)wave_min_u32((uint32_t)nxt);
         // this lane's output row in sub-tile sb is row 16 * sb + col of the
         // tile (position -1 when that row is not walked now)
         int tq[SUB];
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) tq[sb] = __shfl(tm, 16 * sb + col);
-        while (b != kTileEnd) {
-            const bool hit = nxt == b;
-            const int pos = hit ? cur : -1;
-            if (hit) {
-                ++cur;
-                const int v = cur < m ? lst[cur] : -1;
-                nxt = v >= 0 && v < bhi ? v : kTileEnd;
-            }
-            int pq[SUB];                               // -1 unless that row kept b
-#pragma unroll
-            for (int sb = 0; sb < SUB; ++sb) pq[sb] = __shfl(pos, 16 * sb + col);
+        // piece p of block b: key tiles p*KP .. p*KP+KP-1 (keys past the
+        // walked rows' last position read as zero)
+        auto load_piece = [&](int b, int p, bf16x8_t (&k0)[KP], bf16x8_t (&k1)[KP]) {
             const uint16_t* kb = keys + (koff + ((int64_t)b << LB)) * kDim + 8 * kg;
-            const int bend = ((b + 1) << LB) - 1;     // last token of block b
-            bf16x8_t k0[KT], k1[KT];
-            if (bend <= tmax) {                       // every key of the block exists
+            if (((b + 1) << LB) - 1 <= tmax) {           // every key of the block exists
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt) {
-                    const int jj = kt * 16 + col;
+                for (int kt = 0; kt < KP; ++kt) {
+                    const int jj = (p * KP + kt) * 16 + col;
                     k0[kt] = *reinterpret_cast<const bf16x8_t*>(kb + jj * kDim);
                     k1[kt] = *reinterpret_cast<const bf16x8_t*>(kb + jj * kDim + 32);
                 }
             } else {
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt) {
-                    const int jj = kt * 16 + col;
+                for (int kt = 0; kt < KP; ++kt) {
+                    const int jj = (p * KP + kt) * 16 + col;
                     k0[kt] = bf16x8_t{};
                     k1[kt] = bf16x8_t{};
                     if ((b << LB) + jj <= tmax) {
@@ -826,42 +818,105 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
                     }
                 }
             }
-            const int bn = (int)wave_min_u32((uint32_t)nxt);
-            const bool seen = bend <= tmin;           // no walked row masks a token of b
-            // keys as the A operand: lane l receives keys 4*(l/16)..+4 of
-            // each 16-key tile for query row l%16 of the sub-tile.  The
-            // tiles are independent accumulations, issued back to back.
+        };
+        // per block: advance the cursors of the rows that kept it; pq[sb]
+        // is the list position for this lane's row of sub-tile sb (-1 unless
+        // that row kept b)
+        int b = (int)wave_min_u32((uint32_t)nxt), bn = kTileEnd;
+        int pq[SUB];
+        bool seen = true;
+        auto enter_block = [&]() {
+            const bool hit = nxt == b;
+            const int pos = hit ? cur : -1;
+            if (hit) {
+                ++cur;
+                const int v = cur < m ? lst[cur] : -1;
+                nxt = v >= 0 && v < bhi ? v : kTileEnd;
+            }
+#pragma unroll
+            for (int sb = 0; sb < SUB; ++sb) pq[sb] = __shfl(pos, 16 * sb + col);
+            bn = (int)wave_min_u32((uint32_t)nxt);
+            seen = ((b + 1) << LB) - 1 <= tmin;           // no walked row masks a token of b
+        };
+        // keys as the A operand: lane l receives keys 4*(l/16)..+4 of each
+        // 16-key tile for query row l%16 of the sub-tile; the tiles are
+        // independent accumulations, issued back to back
+        auto score_piece = [&](int p, const bf16x8_t (&k0)[KP], const bf16x8_t (&k1)[KP]) {
 #pragma unroll
             for (int sb = 0; sb < SUB; ++sb) {
-                f32x4_t c[KT];
+                f32x4_t c[KP];
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
+                for (int kt = 0; kt < KP; ++kt)
                     c[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[kt], a0[sb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0,
                                                                     0, 0);
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
+                for (int kt = 0; kt < KP; ++kt)
                     c[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[kt], a1[sb], c[kt], 0, 0, 0);
                 if (pq[sb] >= 0) {
                     uint32_t* urow = ukeys + (row0 + 16 * sb + col) * N + ((int64_t)pq[sb] << LB) + 4 * kg;
 #pragma unroll
-                    for (int kt = 0; kt < KT; ++kt) {
+                    for (int kt = 0; kt < KP; ++kt) {
                         uint4 o = make_uint4(score_key(c[kt][0]), score_key(c[kt][1]), score_key(c[kt][2]),
                                              score_key(c[kt][3]));
                         if (!seen) {
-                            const int j = (b << LB) + kt * 16 + 4 * kg;
+                            const int j = (b << LB) + (p * KP + kt) * 16 + 4 * kg;
                             o.x = j + 0 <= tq[sb] ? o.x : 0u;
                             o.y = j + 1 <= tq[sb] ? o.y : 0u;
                             o.z = j + 2 <= tq[sb] ? o.z : 0u;
                             o.w = j + 3 <= tq[sb] ? o.w : 0u;
                         }
-                        *reinterpret_cast<uint4*>(urow + kt * 16) = o;
+                        *reinterpret_cast<uint4*>(urow + (p * KP + kt) * 16) = o;
                     }
                 }
             }
-            b = bn;
+        };
+        if (b == kTileEnd) continue;
+        if constexpr (P == 1) {
+            // whole blocks, one at a time
+            while (b != kTileEnd) {
+                enter_block();
+                bf16x8_t k0[KP], k1[KP];
+                load_piece(b, 0, k0, k1);
+                score_piece(0, k0, k1);
+                b = bn;
+            }
+            continue;
+        }
+        enter_block();
+        bf16x8_t x0[KP], x1[KP], y0[KP], y1[KP];
+        load_piece(b, 0, x0, x1);
+        int p = 0;
+        // one work item: score piece p of block b from (c0, c1) while the
+        // next item's keys load into (n0, n1); false when the walk ends
+        auto item = [&](const bf16x8_t (&c0)[KP], const bf16x8_t (&c1)[KP], bf16x8_t (&n0)[KP],
+                        bf16x8_t (&n1)[KP]) {
+            const bool last_piece = p + 1 == P;
+            const int b2 = last_piece ? bn : b;
+            const int p2 = last_piece ? 0 : p + 1;
+            if (b2 != kTileEnd) load_piece(b2, p2, n0, n1);
+            score_piece(p, c0, c1);
+            if (last_piece) {
+                b = bn;
+                if (b == kTileEnd) return false;
+                enter_block();
+            }
+            p = p2;
+            return true;
+        };
+        while (item(x0, x1, y0, y1) && item(y0, y1, x0, x1)) {
         }
     }
 }
+
+// Pieces per key block in the tile walk: a piece of KT/P key tiles loads
+// while the previous one is scored.  Kept-block lists that are sparse in
+// the block range (a tile's rows share few blocks, so the walk visits many
+// blocks for few stores each) are bound by the load latency of each block
+// and walk in pieces of one key tile; dense ones are bound by the stores and
+// walk whole blocks (measured: 128K chunk 185 -> 167 us, 32K prefill 311
+// against 411 us in pieces).
+template <int LB, int SPARSE>
+constexpr int kTilePieces = SPARSE ? (1 << LB) / 16 : 1;
 
 template <int SUB>
 hipError_t launch_tile_sub(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m,
@@ -876,8 +931,10 @@ hipError_t launch_tile_sub(const QueryMeta& qm, const uint16_t* keys, int64_t q0
     const dim3 grid((unsigned)ntiles, (unsigned)((nranges + kTileWaves - 1) / kTileWaves));
     const dim3 block(64 * kTileWaves);
     const size_t lds = (size_t)kTileQueries * SUB * m * sizeof(int32_t);
+    const bool sparse = Mmax >= 8 * (int64_t)m;
 #define HISA_T2(LB_) \
-    if (lb == LB_) return launch_kl(stage2_tile_kernel<LB_, SUB>, grid, block, lds, stream, t.start, t.stop, qm.queries, keys, q0, nq, m, (int)range, rinfo, sel, ukeys)
+    if (lb == LB_) return sparse ? launch_kl(stage2_tile_kernel<LB_, SUB, kTilePieces<LB_, 1>>, grid, block, lds, stream, t.start, t.stop, qm.queries, keys, q0, nq, m, (int)range, rinfo, sel, ukeys) \
+                                 : launch_kl(stage2_tile_kernel<LB_, SUB, kTilePieces<LB_, 0>>, grid, block, lds, stream, t.start, t.stop, qm.queries, keys, q0, nq, m, (int)range, rinfo, sel, ukeys)
     HISA_T2(4);
     HISA_T2(5);
     HISA_T2(6);

@@ -170,6 +170,25 @@ def test_many_queries_long_kept_lists(B, m, k):
     _check_phase(w, cache, w.phases[0], k, m, False, rows=rows, label="longlists")
 
 
+@pytest.mark.parametrize("B,m,k", [(32, 40, 1000), (64, 16, 900), (128, 16, 2000), (256, 8, 1500), (16, 60, 700)])
+def test_many_queries_sparse_kept_lists(B, m, k):
+    """Matrix-core token scores where the kept lists cover a small part of
+    the block range (at least 8 blocks per kept block), which the tile walk
+    takes in pieces of one 16-key tile with the next piece loading while
+    one is scored (B = 16 has a single tile per block)."""
+    print("sparse kept lists B=%d m=%d k=%d" % (B, m, k), flush=True)
+    dv = _dev()
+    L = 20000
+    assert (L + B - 1) // B >= 8 * m
+    pos = np.arange(5, L, 31, dtype=np.int64)       # 645 queries
+    w = synth.chunked_prefill(L=L, seed=33, B=B, m=m, k=k, q_positions=pos)
+    cache = dv.DeviceCache(w, B=B)
+    cache.pool()
+    g = np.random.default_rng(B * 7 + m)
+    rows = sorted(set([0, 1, 15, 16, 63, 64, len(pos) - 1] + list(g.choice(len(pos), 80, replace=False))))
+    _check_phase(w, cache, w.phases[0], k, m, False, rows=rows, label="sparselists")
+
+
 @pytest.mark.parametrize("kind,B,m,k", [("prefill", 128, 8, 256), ("prefill", 32, 12, 300), ("prefill", 64, 128, 4096),
                                          ("decode", 128, 16, 512), ("decode", 32, 40, 900)])
 def test_indices_without_scores_equal_with_scores(kind, B, m, k):
