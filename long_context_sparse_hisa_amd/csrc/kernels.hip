@@ -498,11 +498,12 @@ constexpr int kScorePasses = kStage2SlotsPerWg / kScoreRowsPerPass;
 // list entry, then every pass's key part (row 0 of the sequence stands in
 // for a masked slot).
 template <class Kept, class Row>
-HISA_INLINE void score_slots(const uint16_t* qrow, Row row_of, int64_t t, int lb, int N, Kept kept, uint32_t* urow)
+HISA_INLINE void score_slots(const uint16_t* qrow, Row row_of, int64_t t, int lb, int N, Kept kept, uint32_t* urow,
+                             int chunk)
 {
     const int sub = threadIdx.x & 7;              // which 16 bytes of a row
     const int grp = threadIdx.x >> 3;             // which row of a pass
-    const int beg = blockIdx.y * kStage2SlotsPerWg + grp;
+    const int beg = chunk * kStage2SlotsPerWg + grp;
     const uint4 qv = reinterpret_cast<const uint4*>(qrow)[sub];
     int32_t blk[kScorePasses];
 #pragma unroll
@@ -542,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void stage2_score_kernel(const uint16_t* 
     const int32_t* srow = sel + row * m;
     const RowInfo ri = rinfo[row];
     score_slots(queries + (q0 + row) * kDim, [&](int64_t j) { return keys + (ri.key_off + j) * kDim; }, ri.t, lb, N,
-                [&](int i) { return srow[i]; }, ukeys + row * N);
+                [&](int i) { return srow[i]; }, ukeys + row * N, blockIdx.y);
 }
 
 // Few queries with at most kStage1FusedMax blocks: stage 1 and the token
@@ -555,7 +556,8 @@ __global__ __launch_bounds__(kThreads) void stage2_score_kernel(const uint16_t* 
 // the query's sequence.
 template <int ITEMS, class Source>
 HISA_INLINE void decode_fused_body(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t row, int lb, int m,
-                                   int32_t* sel, RowInfo* rinfo, int32_t* out_blocks, uint32_t* ukeys, Source source)
+                                   int groups, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks, uint32_t* ukeys,
+                                   Source source)
 {
     __shared__ BucketSmem<kThreads> sm;
     __shared__ int32_t s_kept[kMaxKept];
@@ -592,18 +594,26 @@ HISA_INLINE void decode_fused_body(const QueryMeta& qm, const uint16_t* reps, in
             if (out_blocks) out_blocks[i * m + r] = s_kept[r];
         }
     }
+    // the workgroup's `groups` chunks of kStage2SlotsPerWg slots, one after
+    // the other (more than one when queries are many: fewer redundant
+    // selections)
     const int N = m << lb;
-    score_slots(qm.queries + i * kDim, source(qi), qi.valid ? qi.t : -1, lb, N, [&](int e) { return s_kept[e]; },
-                ukeys + row * N);
+    for (int g = 0; g < groups; ++g) {
+        const int chunk = (int)blockIdx.y * groups + g;
+        if (chunk * kStage2SlotsPerWg >= N) break;
+        score_slots(qm.queries + i * kDim, source(qi), qi.valid ? qi.t : -1, lb, N, [&](int e) { return s_kept[e]; },
+                    ukeys + row * N, chunk);
+    }
 }
 
 template <int ITEMS>
 __global__ __launch_bounds__(kThreads) void decode_fused_kernel(QueryMeta qm, const uint16_t* reps,
                                                                 const uint16_t* keys, int64_t q0, int lb, int m,
-                                                                int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
-                                                                uint32_t* ukeys)
+                                                                int groups, int32_t* sel, RowInfo* rinfo,
+                                                                int32_t* out_blocks, uint32_t* ukeys)
 {
-    decode_fused_body<ITEMS>(qm, reps, q0, blockIdx.x, lb, m, sel, rinfo, out_blocks, ukeys, [&](const QueryInfo& qi) {
+    decode_fused_body<ITEMS>(qm, reps, q0, blockIdx.x, lb, m, groups, sel, rinfo, out_blocks, ukeys,
+                             [&](const QueryInfo& qi) {
         return [=](int64_t j) { return keys + (qi.key_off + j) * kDim; };
     });
 }
@@ -619,8 +629,9 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(QueryMeta qm, co
 template <int ITEMS>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(QueryMeta qm, uint16_t* reps, uint16_t* keys,
                                                                const uint16_t* new_keys, int B, DecodeJobs jobs,
-                                                               int njobs, int splits, int lb, int m, int32_t* sel,
-                                                               RowInfo* rinfo, int32_t* out_blocks, uint32_t* ukeys)
+                                                               int njobs, int splits, int groups, int lb, int m,
+                                                               int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
+                                                               uint32_t* ukeys)
 {
     if ((int)blockIdx.x < njobs) {
         const PoolJob& job = jobs.j[blockIdx.x];
@@ -628,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(QueryMeta qm, uin
         return;
     }
     if ((int)blockIdx.y >= splits) return;       // rows of the grid kept for two-block appends
-    decode_fused_body<ITEMS>(qm, reps, 0, blockIdx.x - njobs, lb, m, sel, rinfo, out_blocks, ukeys,
+    decode_fused_body<ITEMS>(qm, reps, 0, blockIdx.x - njobs, lb, m, groups, sel, rinfo, out_blocks, ukeys,
                              [&](const QueryInfo& qi) {
         // an invalid query reads no key; job 0 (or a zero padding job)
         // keeps its row functor in bounds
@@ -642,15 +653,28 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(QueryMeta qm, uin
     });
 }
 
+// Slot chunks per workgroup in the fused decode launches: one (every
+// workgroup selects the query's blocks itself and scores 512 slots) until
+// the launch has work for four workgroups per CU, then more, so that large
+// batches repeat the selection less.
+inline int decode_groups(int64_t nq, int chunks)
+{
+    int g = 1;
+    while (g < chunks && nq * chunks / (2 * g) >= 1024) g *= 2;
+    return g;
+}
+
 template <int ITEMS>
 static hipError_t launch_decode_fused_items(const QueryMeta& qm, const uint16_t* reps, const uint16_t* keys,
                                             int64_t q0, int64_t nq, int lb, int m, int32_t* sel, RowInfo* rinfo,
                                             int32_t* out_blocks, uint32_t* ukeys, hipStream_t stream, Timing t)
 {
     const int N = m << lb;
-    const dim3 grid((unsigned)nq, (unsigned)((N + kStage2SlotsPerWg - 1) / kStage2SlotsPerWg));
+    const int chunks = (N + kStage2SlotsPerWg - 1) / kStage2SlotsPerWg;
+    const int groups = decode_groups(nq, chunks);
+    const dim3 grid((unsigned)nq, (unsigned)((chunks + groups - 1) / groups));
     return launch_k(decode_fused_kernel<ITEMS>, grid, dim3(kThreads), stream, t.start, t.stop, qm, reps, keys, q0, lb,
-                    m, sel, rinfo, out_blocks, ukeys);
+                    m, groups, sel, rinfo, out_blocks, ukeys);
 }
 
 hipError_t launch_decode_step(const QueryMeta& qm, uint16_t* reps, uint16_t* keys, const uint16_t* new_keys, int B,
@@ -660,7 +684,9 @@ hipError_t launch_decode_step(const QueryMeta& qm, uint16_t* reps, uint16_t* key
     DecodeJobs dj;
     for (int i = 0; i < kDecodeJobs; ++i) dj.j[i] = i < njobs ? jobs[i] : PoolJob{0, 0, 0, 0, 0, 0, 0, 0};
     const int N = m << lb;
-    const int splits = (N + kStage2SlotsPerWg - 1) / kStage2SlotsPerWg;
+    const int chunks = (N + kStage2SlotsPerWg - 1) / kStage2SlotsPerWg;
+    const int groups = decode_groups(nq, chunks);
+    const int splits = (chunks + groups - 1) / groups;
     int rows = splits;                                // an append touches at most two blocks
     for (int i = 0; i < njobs; ++i) rows = std::max<int>(rows, jobs[i].nblk);
     const dim3 grid((unsigned)(nq + njobs), (unsigned)rows);
@@ -668,7 +694,7 @@ hipError_t launch_decode_step(const QueryMeta& qm, uint16_t* reps, uint16_t* key
 #define HISA_DS(N_)                                                                                             \
     if (per <= N_)                                                                                              \
     return launch_k(decode_step_kernel<N_>, grid, dim3(kThreads), stream, t.start, t.stop, qm, reps, keys, new_keys, \
-                    B, dj, njobs, splits, lb, m, sel, rinfo, out_blocks, ukeys)
+                    B, dj, njobs, splits, groups, lb, m, sel, rinfo, out_blocks, ukeys)
     HISA_DS(1);
     HISA_DS(2);
     HISA_DS(4);

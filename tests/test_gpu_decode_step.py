@@ -119,3 +119,34 @@ def test_long_rows_fold_the_append_into_the_block_scores(n_new):
                      np.array([after[0] - 1, after[1] - 1, 150_000], np.int64), np.array([0, 1, 1], np.int32))
     a, b = _pair(w, 128, before, new, ph, 2048, 16)
     _same(a, b, "300K n_new=%d" % n_new)
+
+
+def test_many_queries_per_sequence_share_selections():
+    """160 queries over 8 sequences (20 each, m*B = 8192): the fused launch
+    gives each workgroup two 512-slot chunks; equal to the two calls, and
+    sampled rows equal the oracle."""
+    print("decode step 8 x 20 queries", flush=True)
+    g = np.random.default_rng(75)
+    w = synth.decode_batch(nseq=8, L=20_000, seed=76, B=128, m=64, k=2048, spare=3)
+    before = np.full(8, 20_000, np.int64)
+    new = synth.to_bf16(g.standard_normal((8, 3, synth.D)).astype(np.float32))
+    after = before + 3
+    q_seq = np.repeat(np.arange(8, dtype=np.int32), 20)
+    q_pos = np.concatenate([np.concatenate([[a - 1, a - 3], g.integers(9000, a - 1, 18)]) for a in after])
+    queries = synth.to_bf16(g.standard_normal((160, synth.D)).astype(np.float32))
+    ph = synth.Phase("p", queries, q_pos.astype(np.int64), q_seq)
+    a, b = _pair(w, 128, before, new, ph, 2048, 64)
+    _same(a, b, "8 x 20 queries")
+    idx, sc, blk = b[0], b[1], b[2]
+    check_all_rows_properties(idx, blk, ph.q_pos, 128, 64, 2048, False)
+    # the oracle's keys come from the host: the cache's keys with the new
+    # rows placed after each sequence
+    keys_of = []
+    for s in range(8):
+        o = int(w.seq_key_off[s])
+        keys_of.append(np.concatenate([w.keys[o:o + int(before[s])], new[s]]))
+    reps = [oracle.pool(keys_of[s], 128) for s in range(8)]
+    rows = list(range(0, 160, 7)) + [1, 159]
+    counts = check_rows(rows, ph.queries, ph.q_pos, lambda i: keys_of[int(q_seq[i])], lambda i: reps[int(q_seq[i])],
+                        128, 64, 2048, idx, sc, blk, False, "step8x20")
+    print("decode step 8x20 vs oracle", counts, flush=True)
