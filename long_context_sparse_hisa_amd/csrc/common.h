@@ -93,8 +93,10 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double v)
 __device__ __forceinline__ uint32_t score_key(float f)
 {
     // negative: invert every bit; otherwise set the top bit.  Key 0 stays
-    // free for "no candidate" (only the all-ones NaN would map to it).
-    const uint32_t u = __float_as_uint(f);
+    // free for "no candidate" (only the all-ones NaN would map to it).  -0
+    // takes +0's key: the two compare equal, so they tie (lower index first)
+    const uint32_t u0 = __float_as_uint(f);
+    const uint32_t u = u0 == 0x80000000u ? 0u : u0;
     const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
     return max(key, 1u);
 }

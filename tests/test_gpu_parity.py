@@ -275,6 +275,33 @@ def test_degenerate_ties_pick_lowest_indices():
             assert np.array_equal(idx[0], np.arange(100))
 
 
+def test_signed_zero_scores_tie():
+    """Scores -0.0 and +0.0 compare equal, so the two tie and the lower
+    index goes first (the oracle sorts the fp32 values).  Query all ones;
+    keys all -1 except five rows of +1 (scores 64), row 20 of -0.0 (score
+    -0.0: every product is -0) and row 30 of +0.0 (score +0.0); k = 6 takes
+    the five positives and one zero, which must be row 20."""
+    print("signed zeros", flush=True)
+    dv = _dev()
+    L, B = 600, 64
+    keys = np.full((L, synth.D), synth.to_bf16(np.float32(-1.0)), np.uint16)
+    keys[10:15] = synth.to_bf16(np.float32(1.0))
+    keys[20] = 0x8000                                      # bf16 -0.0
+    keys[30] = 0x0000                                      # bf16 +0.0
+    q = np.full((1, synth.D), synth.to_bf16(np.float32(1.0)), np.uint16)
+    w = synth.Workload("zeros", keys, np.zeros(1, np.int64), np.array([L], np.int64),
+                       np.array([L], np.int64), B, 10, 6)
+    ph = synth.Phase("p", q, np.array([L - 1], np.int64), np.zeros(1, np.int32))
+    cache = dv.DeviceCache(w, B=B)
+    cache.pool()
+    want = np.array([10, 11, 12, 13, 14, 20], np.int32)
+    o_idx = oracle.flat_query(q[0], keys, L - 1, 6)[0]
+    assert np.array_equal(np.sort(o_idx), want), o_idx
+    for flat in (False, True):
+        idx, sc, _ = _run(cache, ph, 6, 10, flat)
+        assert np.array_equal(np.sort(idx[0]), want), (flat, idx[0])
+
+
 def test_hisa_with_m_covering_every_block_equals_flat():
     """With m covering every causal block HISA is the flat indexer: its rows
     must pass the parity rule against the oracle's flat result, and where

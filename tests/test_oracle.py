@@ -335,3 +335,25 @@ def test_mog_generator_is_deterministic():
     b = synth.decode_batch(nseq=2, L=512, seed=2)
     assert synth.sha256(a.keys, a.phases[0].queries) == synth.sha256(b.keys, b.phases[0].queries)
     assert np.all(np.abs(synth.from_bf16(a.keys)) < 16)
+
+
+def test_signed_zero_scores_tie_to_lower_index():
+    """-0.0 and +0.0 are equal fp32 values: a key whose every product is -0
+    (score -0.0) ties with one of score +0.0, and the lower index is taken.
+    Expected rows written by hand."""
+    L = 600
+    keys = np.full((L, synth.D), synth.to_bf16(np.float32(-1.0)), np.uint16)
+    keys[10:15] = synth.to_bf16(np.float32(1.0))
+    keys[20] = 0x8000                                      # bf16 -0.0
+    keys[30] = 0x0000                                      # bf16 +0.0
+    q = np.full(synth.D, synth.to_bf16(np.float32(1.0)), np.uint16)
+    want = [10, 11, 12, 13, 14, 20]
+    idx, sc, _ = oracle.flat_query(q, keys, L - 1, 6)
+    assert sorted(idx.tolist()) == want
+    assert sc[list(idx).index(20)] == 0.0
+    idx, _, _ = oracle.hisa_query(q, keys, oracle.pool(keys, 64), L - 1, 64, 10, 6)[:3]
+    assert sorted(idx.tolist()) == want
+    # with the zeros swapped the +0 row is the lower one
+    keys[20], keys[30] = 0x0000, 0x8000
+    idx, _, _ = oracle.flat_query(q, keys, L - 1, 6)
+    assert sorted(idx.tolist()) == want
