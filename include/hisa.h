@@ -48,7 +48,8 @@
  *   j <= t; block b is causal iff b*B <= t; with c = t / B the forced blocks
  *   are 0, c-1 and c, counted among the m kept blocks; if c+1 <= m every
  *   causal block is kept.  Scores are fp32 sums of exact bf16 products.
- *   Ties at the m-th block / k-th token go to the lower block / token index.
+ *   Ties at the m-th block / k-th token go to the lower block / token index
+ *   (scores compare as fp32 values, so -0.0 ties with +0.0).
  *
  * Output layout (identical for HISA and flat):
  *   out_idx[i*k + r]: the selected token indices of query i, relative to the
