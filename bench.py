@@ -133,8 +133,8 @@ def flat_stage_bytes(q_pos, k):
 # ---- measured HBM traffic ----------------------------------------------------------
 
 # kernel symbol that carries each stage
-STAGE_KERNEL = {"block_stage": ("stage1_select_kernel",),
-                "token_scores": ("stage2_score_kernel", "stage2_tile_kernel"),
+STAGE_KERNEL = {"block_stage": ("stage1_select_kernel", "stage1_tile_kernel", "block_score"),
+                "token_scores": ("select_score_kernel", "stage2_tile_kernel"),
                 "token_topk": ("topk_rows_kernel",),
                 "select_and_scores": ("decode_fused_kernel", "decode_step_kernel"),
                 "flat_scores": ("flat_score_kernel", "flat_score_mfma_kernel")}

@@ -257,16 +257,22 @@ int hisa_index(const hisa_index_args* a, void* stream_)
             // launch (recorded as stage 1)
             err = launch_decode_fused(qm, a->reps, a->keys, q0, nc, lb, a->m, Mmax, sel, rinfo, a->out_blocks, ukeys,
                                       stream, stage_timing(a, last, 1));
+        } else if (split) {
+            // few queries, many blocks: the representative scores over many
+            // workgroups, then the selection and the token scores in one
+            // launch (the selection recorded with the token scores)
+            err = launch_block_scores(qm, a->reps, q0, nc, lb, Mmax, sigma, stream, stage_timing(a, last, 0));
+            if (err == hipSuccess)
+                err = launch_select_scores(qm, a->keys, q0, nc, lb, a->m, Mmax, sigma, sel, rinfo, a->out_blocks,
+                                           ukeys, stream, stage_timing(a, last, 1));
         } else {
             err = launch_stage1(qm, a->reps, q0, nc, lb, a->m, Mmax, sigma, sel, rinfo, a->out_blocks, stream,
                                 stage_timing(a, last, 0));
-            // token scores into ukeys: few queries split each row over several
-            // workgroups, many queries share key loads 16 at a time on the MFMA
+            // token scores into ukeys: many queries share key loads up to 64
+            // at a time on the MFMA
             if (err == hipSuccess)
-                err = split ? launch_stage2_split_scores(qm, a->keys, q0, nc, lb, a->m, rinfo, sel, ukeys, stream,
-                                                         stage_timing(a, last, 1))
-                            : launch_stage2_tile_scores(qm, a->keys, q0, nc, lb, a->m, Mmax, rinfo, sel, ukeys,
-                                                        stream, stage_timing(a, last, 1));
+                err = launch_stage2_tile_scores(qm, a->keys, q0, nc, lb, a->m, Mmax, rinfo, sel, ukeys, stream,
+                                                stage_timing(a, last, 1));
         }
         if (err == hipSuccess)
             err = launch_topk_small(ukeys, nc, a->m << lb, a->k, sel, a->m, lb, a->out_idx + q0 * a->k,
@@ -300,7 +306,8 @@ int hisa_decode_step(const hisa_index_args* a, const hisa_seq* seqs, const uint1
     const bool fuse = foldable && Mmax <= kStage1FusedMax;
     if (foldable && !fuse) {
         // more than 2048 blocks: the append joins the block-score launch,
-        // then the selection, the token scores and the top-k as in hisa_index
+        // then the selection with the token scores and the top-k as in
+        // hisa_index
         const Layout L = layout_for(a, 0, chunk);
         hipStream_t stream = static_cast<hipStream_t>(stream_);
         const int lb = log2_of(a->B);
@@ -318,11 +325,11 @@ int hisa_decode_step(const hisa_index_args* a, const hisa_seq* seqs, const uint1
         int32_t* sel = at<int32_t>(a->workspace, L.sel);
         RowInfo* rinfo = at<RowInfo>(a->workspace, L.rinfo);
         uint32_t* ukeys = at<uint32_t>(a->workspace, L.ukeys);
-        hipError_t err = launch_stage1(qm, a->reps, 0, a->nq, lb, a->m, Mmax, sigma, sel, rinfo, a->out_blocks, stream,
-                                       stage_timing(a, true, 0), &app);
+        hipError_t err = launch_block_scores(qm, a->reps, 0, a->nq, lb, Mmax, sigma, stream, stage_timing(a, true, 0),
+                                             &app);
         if (err == hipSuccess)
-            err = launch_stage2_split_scores(qm, a->keys, 0, a->nq, lb, a->m, rinfo, sel, ukeys, stream,
-                                             stage_timing(a, true, 1));
+            err = launch_select_scores(qm, a->keys, 0, a->nq, lb, a->m, Mmax, sigma, sel, rinfo, a->out_blocks, ukeys,
+                                       stream, stage_timing(a, true, 1));
         if (err == hipSuccess)
             err = launch_topk_small(ukeys, a->nq, a->m << lb, a->k, sel, a->m, lb, a->out_idx, a->out_scores, stream,
                                     stage_timing(a, true, 2));

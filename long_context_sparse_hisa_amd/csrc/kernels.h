@@ -77,6 +77,20 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
                          hipStream_t stream, Timing t = {},
                          const struct StepAppend* app = nullptr);
 
+// The representative scores alone into sigma [nq, Mmax] (free candidates
+// 1 .. c-2 of each query), with a decode step's append folded in when app
+// is given; launch_select_scores then selects and scores the tokens.
+hipError_t launch_block_scores(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb,
+                               int64_t Mmax, float* sigma, hipStream_t stream, Timing t = {},
+                               const struct StepAppend* app = nullptr);
+
+// Few queries with more than kStage1FusedMax blocks: the selection from
+// sigma and the token scores in one launch (every workgroup of a query
+// selects the kept blocks itself); writes sel, rinfo, out_blocks and ukeys.
+hipError_t launch_select_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m,
+                                int64_t Mmax, const float* sigma, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
+                                uint32_t* ukeys, hipStream_t stream, Timing t = {});
+
 // HISA stage 2 for many queries: 16 query rows per wave scored on the
 // MFMA against the union of their kept blocks, into ukeys [nq, m*B] (only
 // the kept blocks' slots are written); launch_topk_small then selects.
@@ -100,11 +114,9 @@ hipError_t launch_decode_step(const QueryMeta& qm, uint16_t* reps, uint16_t* key
                               RowInfo* rinfo, int32_t* out_blocks, uint32_t* ukeys, hipStream_t stream, Timing t = {});
 
 // HISA stage 2 for few queries: kStage2SlotsPerWg candidate slots per
-// workgroup scored into ukeys [nq, m*B]; launch_topk_small then selects.
+// workgroup scored into ukeys [nq, m*B] (inside the fused decode and
+// select-and-score launches); launch_topk_small then selects.
 constexpr int kStage2SlotsPerWg = 512;
-hipError_t launch_stage2_split_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb,
-                                      int m, const RowInfo* rinfo, const int32_t* sel, uint32_t* ukeys,
-                                      hipStream_t stream, Timing t = {});
 
 // Flat: ranking keys of the visible keys into ukeys [nq, Lmax].  mfma: 16
 // query rows per tile on the matrix cores, otherwise one thread per

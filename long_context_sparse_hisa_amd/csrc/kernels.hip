@@ -421,6 +421,25 @@ static hipError_t launch_stage1_tile_items(const QueryMeta& qm, const uint16_t* 
                      t.start, t.stop, qm, reps, q0, nq, lb, m, sel, rinfo, out_blocks);
 }
 
+hipError_t launch_block_scores(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb,
+                               int64_t Mmax, float* sigma, hipStream_t stream, Timing t, const StepAppend* app)
+{
+    if (app) {
+        DecodeJobs dj;
+        int rows = 1;
+        for (int i = 0; i < kDecodeJobs; ++i) {
+            dj.j[i] = i < app->njobs ? app->jobs[i] : PoolJob{0, 0, 0, 0, 0, 0, 0, 0};
+            if (i < app->njobs) rows = std::max<int>(rows, app->jobs[i].nblk);
+        }
+        dim3 grid((unsigned)std::max<int64_t>((Mmax + kThreads - 1) / kThreads, rows), (unsigned)(nq + app->njobs));
+        return launch_k(block_score_append_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm,
+                        const_cast<uint16_t*>(reps), app->keys, app->new_keys, app->B, dj, app->njobs, q0, lb, Mmax,
+                        sigma);
+    }
+    dim3 grid((unsigned)((Mmax + kThreads - 1) / kThreads), (unsigned)nq);
+    return launch_k(block_score_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm, reps, q0, lb, Mmax, sigma);
+}
+
 hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
                          int64_t Mmax, float* sigma, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
                          hipStream_t stream, Timing t, const StepAppend* app)
@@ -449,23 +468,7 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
 #undef HISA_S1F
         return hipErrorInvalidValue;
     }
-    hipError_t err;
-    if (app) {
-        DecodeJobs dj;
-        int rows = 1;
-        for (int i = 0; i < kDecodeJobs; ++i) {
-            dj.j[i] = i < app->njobs ? app->jobs[i] : PoolJob{0, 0, 0, 0, 0, 0, 0, 0};
-            if (i < app->njobs) rows = std::max<int>(rows, app->jobs[i].nblk);
-        }
-        dim3 grid((unsigned)std::max<int64_t>((Mmax + kThreads - 1) / kThreads, rows), (unsigned)(nq + app->njobs));
-        err = launch_k(block_score_append_kernel, grid, dim3(kThreads), stream, t.start, nullptr, qm,
-                       const_cast<uint16_t*>(reps), app->keys, app->new_keys, app->B, dj, app->njobs, q0, lb, Mmax,
-                       sigma);
-    } else {
-        dim3 grid((unsigned)((Mmax + kThreads - 1) / kThreads), (unsigned)nq);
-        err = launch_k(block_score_kernel, grid, dim3(kThreads), stream, t.start, nullptr, qm, reps, q0, lb, Mmax,
-                       sigma);
-    }
+    const hipError_t err = launch_block_scores(qm, reps, q0, nq, lb, Mmax, sigma, stream, Timing{t.start, nullptr}, app);
     if (err != hipSuccess) return err;
     // 1024 threads select among up to 16384 scores, 16 per thread
     const int64_t per = (Mmax + 1023) / 1024;
@@ -490,17 +493,16 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
 // bytes, so every wave load is 1 KiB of whole rows; the eight partial dots
 // are summed across the lanes with DPP.  The top-k follows in
 // topk_rows_kernel.
-constexpr int kScoreRowsPerPass = kThreads / 8;
-constexpr int kScorePasses = kStage2SlotsPerWg / kScoreRowsPerPass;
-
-// The slots of this workgroup: kept(i) gives entry i of the row's kept list.
-// Two round trips when the list is in memory, no branches: every pass's
-// list entry, then every pass's key part (row 0 of the sequence stands in
-// for a masked slot).
-template <class Kept, class Row>
+// The slots of this workgroup (NT threads): kept(i) gives entry i of the
+// row's kept list.  Two round trips when the list is in memory, no
+// branches: every pass's list entry, then every pass's key part (row 0 of
+// the sequence stands in for a masked slot).
+template <int NT = kThreads, class Kept, class Row>
 HISA_INLINE void score_slots(const uint16_t* qrow, Row row_of, int64_t t, int lb, int N, Kept kept, uint32_t* urow,
                              int chunk)
 {
+    constexpr int kScoreRowsPerPass = NT / 8;
+    constexpr int kScorePasses = kStage2SlotsPerWg / kScoreRowsPerPass;
     const int sub = threadIdx.x & 7;              // which 16 bytes of a row
     const int grp = threadIdx.x >> 3;             // which row of a pass
     const int beg = chunk * kStage2SlotsPerWg + grp;
@@ -534,16 +536,72 @@ HISA_INLINE void score_slots(const uint16_t* qrow, Row row_of, int64_t t, int lb
     }
 }
 
-__global__ __launch_bounds__(kThreads) void stage2_score_kernel(const uint16_t* queries, const uint16_t* keys,
-                                                                int64_t q0, int lb, int m, const RowInfo* rinfo,
-                                                                const int32_t* sel, uint32_t* ukeys)
+// Few queries with more than kStage1FusedMax blocks: the representative
+// scores come from block_score_kernel (sigma); this launch does the rest of
+// stage 1 and the token scores.  Every workgroup of a query (1024 threads)
+// selects the kept blocks from the query's scores itself - the same
+// selection in each, a few KiB of L2 reads - then scores its own
+// kStage2SlotsPerWg slots; workgroup 0 of the query also writes the kept
+// list, the row info and out_blocks.
+template <int ITEMS>
+__global__ __launch_bounds__(1024) void select_score_kernel(QueryMeta qm, const uint16_t* keys, int64_t q0, int lb,
+                                                            int m, int64_t Mmax, const float* sigma, int32_t* sel,
+                                                            RowInfo* rinfo, int32_t* out_blocks, uint32_t* ukeys)
 {
+    constexpr int NT = 1024;
+    __shared__ BucketSmem<NT> sm;
+    __shared__ int32_t s_kept[kMaxKept];
     const int64_t row = blockIdx.x;
+    const int64_t i = q0 + row;
+    const QueryInfo qi =
+        query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
+    const int64_t c = qi.valid ? qi.t >> lb : -1;
+    if (!qi.valid || c + 1 <= m) {
+        for (int r = threadIdx.x; r < m; r += NT) s_kept[r] = r <= c ? r : -1;
+    } else {
+        const float* sg = sigma + row * Mmax;
+        uint32_t key[ITEMS];
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int64_t b = slot_of<ITEMS>(it);
+            key[it] = (b >= 1 && b <= c - 2) ? score_key(sg[b]) : 0u;
+        }
+        const Threshold th = wg_bucket_select<NT, ITEMS>(key, m - 3, sm);
+        wg_emit_selected<NT, ITEMS>(key, th, sm, m - 3, [&](int slot, uint32_t, int rank) { s_kept[1 + rank] = slot; });
+        if (threadIdx.x == 0) {
+            s_kept[0] = 0;
+            s_kept[m - 2] = (int32_t)(c - 1);
+            s_kept[m - 1] = (int32_t)c;
+        }
+    }
+    __syncthreads();
+    if (blockIdx.y == 0) {
+        if (threadIdx.x == 0) rinfo[row] = RowInfo{qi.key_off, qi.valid ? qi.t : -1};
+        for (int r = threadIdx.x; r < m; r += NT) {
+            sel[row * m + r] = s_kept[r];
+            if (out_blocks) out_blocks[i * m + r] = s_kept[r];
+        }
+    }
     const int N = m << lb;
-    const int32_t* srow = sel + row * m;
-    const RowInfo ri = rinfo[row];
-    score_slots(queries + (q0 + row) * kDim, [&](int64_t j) { return keys + (ri.key_off + j) * kDim; }, ri.t, lb, N,
-                [&](int i) { return srow[i]; }, ukeys + row * N, blockIdx.y);
+    score_slots<NT>(qm.queries + i * kDim, [&](int64_t j) { return keys + (qi.key_off + j) * kDim; },
+                    qi.valid ? qi.t : -1, lb, N, [&](int e) { return s_kept[e]; }, ukeys + row * N, blockIdx.y);
+}
+
+hipError_t launch_select_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m,
+                                int64_t Mmax, const float* sigma, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
+                                uint32_t* ukeys, hipStream_t stream, Timing t)
+{
+    const int N = m << lb;
+    const dim3 grid((unsigned)nq, (unsigned)((N + kStage2SlotsPerWg - 1) / kStage2SlotsPerWg));
+    const int64_t per = (Mmax + 1023) / 1024;
+#define HISA_SS(N_) \
+    if (per <= N_) return launch_k(select_score_kernel<N_>, grid, dim3(1024), stream, t.start, t.stop, qm, keys, q0, lb, m, Mmax, sigma, sel, rinfo, out_blocks, ukeys)
+    HISA_SS(2);
+    HISA_SS(4);
+    HISA_SS(8);
+    HISA_SS(16);
+#undef HISA_SS
+    return hipErrorInvalidValue;
 }
 
 // Few queries with at most kStage1FusedMax blocks: stage 1 and the token
@@ -1177,16 +1235,6 @@ hipError_t launch_topk_small(const uint32_t* ukeys, int64_t nrows, int N, int k,
     HISA_TK(16);
 #undef HISA_TK
     return hipErrorInvalidValue;
-}
-
-hipError_t launch_stage2_split_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb,
-                                      int m, const RowInfo* rinfo, const int32_t* sel, uint32_t* ukeys,
-                                      hipStream_t stream, Timing t)
-{
-    const int N = m << lb;
-    dim3 grid((unsigned)nq, (unsigned)((N + kStage2SlotsPerWg - 1) / kStage2SlotsPerWg));
-    return launch_k(stage2_score_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm.queries, keys, q0, lb, m,
-                    rinfo, sel, ukeys);
 }
 
 // ---- flat indexer: every key ------------------------------------------------
