@@ -144,8 +144,8 @@ template <int NT>
 struct BucketSmem {
     static constexpr int NW = NT / 64;
     int hist[kBins + 1];                      // the extra bin counts the empty slots
-    uint32_t list_key[kListCap];
-    int list_slot[kListCap];
+    alignas(16) uint32_t list_key[kListCap];  // 16-byte aligned: read four at a time
+    alignas(16) int list_slot[kListCap];
     uint32_t red[3][NW];
     int wave_tot[2][NW];
     int misc[8];
@@ -349,42 +349,32 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
     __syncthreads();
     // rank of member j in (key desc, slot asc) order; the member of rank
     // need-1 is the threshold key, and the equal keys before it plus itself
-    // are the copies of it to take.  Up to 64 members: wave 0 holds one per
-    // lane and compares against the others by readlane, without LDS round
-    // trips; more: every thread ranks its members from LDS.
-    if (c <= 64) {
-        if (wave_id() == 0) {
-            const int l = lane_id();
-            const uint32_t kj = l < c ? sm.list_key[l] : 0u;
-            const int sj = l < c ? sm.list_slot[l] : 0;
-            int r = 0, eq_before = 0;
-            for (int i = 0; i < c; ++i) {
-                const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)kj, i);
-                const int si = __builtin_amdgcn_readlane(sj, i);
-                const bool before = ki == kj && si < sj;
-                r += (ki > kj) || before;
-                eq_before += before;
-            }
-            if (l < c && r == need - 1) {
-                sm.misc[6] = (int)kj;
-                sm.misc[7] = eq_before + 1;
-            }
+    // are the copies of it to take.  Thread j ranks member j against all c
+    // members, read four at a time as broadcast 16-byte LDS loads (several
+    // in flight); up to 64 members this is wave 0 alone.
+    for (int j = threadIdx.x; j < c; j += NT) {
+        const uint32_t kj = sm.list_key[j];
+        const int sj = sm.list_slot[j];
+        int r = 0, eq_before = 0;
+        auto step = [&](uint32_t ki, int si) {
+            const bool before = ki == kj && si < sj;
+            r += (ki > kj) || before;
+            eq_before += before;
+        };
+        int i = 0;
+#pragma unroll 4
+        for (; i + 4 <= c; i += 4) {
+            const uint4 kv = *reinterpret_cast<const uint4*>(sm.list_key + i);
+            const int4 sv = *reinterpret_cast<const int4*>(sm.list_slot + i);
+            step(kv.x, sv.x);
+            step(kv.y, sv.y);
+            step(kv.z, sv.z);
+            step(kv.w, sv.w);
         }
-    } else {
-        for (int j = threadIdx.x; j < c; j += NT) {
-            const uint32_t kj = sm.list_key[j];
-            const int sj = sm.list_slot[j];
-            int r = 0, eq_before = 0;
-            for (int i = 0; i < c; ++i) {
-                const uint32_t ki = sm.list_key[i];
-                const bool before = ki == kj && sm.list_slot[i] < sj;
-                r += (ki > kj) || before;
-                eq_before += before;
-            }
-            if (r == need - 1) {
-                sm.misc[6] = (int)kj;
-                sm.misc[7] = eq_before + 1;
-            }
+        for (; i < c; ++i) step(sm.list_key[i], sm.list_slot[i]);
+        if (r == need - 1) {
+            sm.misc[6] = (int)kj;
+            sm.misc[7] = eq_before + 1;
         }
     }
     __syncthreads();
@@ -484,8 +474,8 @@ constexpr int kWaveBins = 256;
 
 struct WaveSmem {
     int hist[kWaveBins];
-    uint32_t list_key[64];
-    int list_slot[64];
+    alignas(16) uint32_t list_key[64];        // 16-byte aligned: read four at a time
+    alignas(16) int list_slot[64];
 };
 
 // Exact n-th largest nonzero key by four 8-bit passes (n <= count of
@@ -623,12 +613,22 @@ HISA_INLINE int wave_select(const uint32_t (&key)[ITEMS], int n, WaveSmem& ws, E
                 const uint32_t kj = lane < c ? ws.list_key[lane] : 0u;
                 const int sj = lane < c ? ws.list_slot[lane] : 0;
                 int r = 0, eq_before = 0;
-                for (int i = 0; i < c; ++i) {
-                    const uint32_t ki = ws.list_key[i];
-                    const bool before = ki == kj && ws.list_slot[i] < sj;
+                auto step = [&](uint32_t ki, int si) {
+                    const bool before = ki == kj && si < sj;
                     r += (ki > kj) || before;
                     eq_before += before;
+                };
+                int i = 0;
+#pragma unroll 4
+                for (; i + 4 <= c; i += 4) {   // broadcast 16-byte LDS loads, several in flight
+                    const uint4 kv = *reinterpret_cast<const uint4*>(ws.list_key + i);
+                    const int4 sv = *reinterpret_cast<const int4*>(ws.list_slot + i);
+                    step(kv.x, sv.x);
+                    step(kv.y, sv.y);
+                    step(kv.z, sv.z);
+                    step(kv.w, sv.w);
                 }
+                for (; i < c; ++i) step(ws.list_key[i], ws.list_slot[i]);
                 const int J = (int)__builtin_ctzll(__ballot(lane < c && r == need - 1));
                 th.T = (uint32_t)__builtin_amdgcn_readlane((int)kj, J);
                 th.need_eq = __builtin_amdgcn_readlane(eq_before, J) + 1;
