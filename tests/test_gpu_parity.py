@@ -553,3 +553,26 @@ def test_many_queries_packed_sequences(force_fallback):
     max_len = 262144 if force_fallback else None
     for flat in (False, True):
         _check_phase(w, cache, ph, k, m, flat, label="manypacked", props=False, max_len=max_len)
+
+
+@pytest.mark.parametrize("n_out", [16, 300])
+def test_outlier_scores_stretch_the_bins(n_out):
+    """A few keys along each decode query (score about 6 |q|^2, far above
+    the rest) stretch the selects' bins, so the threshold bin holds well
+    over 64 members (ranked through the member list); 300 outliers per
+    sequence also put them among the kept tokens."""
+    print("outliers %d" % n_out, flush=True)
+    dv = _dev()
+    w = synth.decode_batch(nseq=4, L=20000, seed=35, B=128, m=64, k=2048)
+    keys = w.keys.copy()
+    g = np.random.default_rng(36 + n_out)
+    for s in range(4):
+        o = int(w.seq_key_off[s])
+        q = synth.from_bf16(w.phases[0].queries[s])
+        pos = g.choice(int(w.seq_len[s]) - 1, n_out, replace=False)
+        keys[o + pos] = synth.to_bf16((6.0 * q).astype(np.float32))
+    w2 = synth.Workload("outliers", keys, w.seq_key_off, w.seq_len, w.seq_cap, 128, 64, 2048)
+    cache = dv.DeviceCache(w2, B=128)
+    cache.pool()
+    for flat in (False, True):
+        _check_phase(w2, cache, w.phases[0], 2048, 64, flat, label="outliers%d" % n_out)
