@@ -62,8 +62,8 @@ struct QueryMeta {
 // lb = log2(B).
 constexpr int64_t kStage1FusedMax = 2048;
 // A decode step's append, folded into the first launch of the path for
-// more than 2048 blocks (launch_stage1's block scores): one job per
-// sequence, at most kDecodeJobs.
+// more than 2048 blocks (the block scores, launch_block_scores): one job
+// per sequence, at most kDecodeJobs.
 struct StepAppend {
     uint16_t* keys;
     const uint16_t* new_keys;
@@ -74,8 +74,7 @@ struct StepAppend {
 
 hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
                          int64_t Mmax, float* sigma, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
-                         hipStream_t stream, Timing t = {},
-                         const struct StepAppend* app = nullptr);
+                         hipStream_t stream, Timing t = {});
 
 // The representative scores alone into sigma [nq, Mmax] (free candidates
 // 1 .. c-2 of each query), with a decode step's append folded in when app

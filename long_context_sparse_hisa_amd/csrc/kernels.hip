@@ -442,7 +442,7 @@ hipError_t launch_block_scores(const QueryMeta& qm, const uint16_t* reps, int64_
 
 hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
                          int64_t Mmax, float* sigma, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
-                         hipStream_t stream, Timing t, const StepAppend* app)
+                         hipStream_t stream, Timing t)
 {
     if (nq >= kManyRows && Mmax <= kS1TileMaxBlocks) {
         // many queries: MFMA block scores, wave-level top-m
@@ -468,7 +468,7 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
 #undef HISA_S1F
         return hipErrorInvalidValue;
     }
-    const hipError_t err = launch_block_scores(qm, reps, q0, nq, lb, Mmax, sigma, stream, Timing{t.start, nullptr}, app);
+    const hipError_t err = launch_block_scores(qm, reps, q0, nq, lb, Mmax, sigma, stream, Timing{t.start, nullptr});
     if (err != hipSuccess) return err;
     // 1024 threads select among up to 16384 scores, 16 per thread
     const int64_t per = (Mmax + 1023) / 1024;
