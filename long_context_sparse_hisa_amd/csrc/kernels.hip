@@ -291,7 +291,7 @@ static hipError_t launch_stage1_items(const QueryMeta& qm, const uint16_t* reps,
 // one sequence at a time.  ITEMS = 64-slot groups per row: block b is slot b.
 
 constexpr int kS1TileMaxBlocks = 1024;
-constexpr int64_t kS1TargetWaves = 4096;
+constexpr int64_t kS1TargetWaves = 8192;   // measured: 32K prefill stage 1 34 -> 28 us against 4096
 constexpr int kS1MaxWaves = 16;
 
 __host__ __device__ constexpr int s1_row_stride(int items) { return 64 * items + 16; }   // floats; +16 spreads banks
