@@ -150,3 +150,30 @@ def test_many_queries_per_sequence_share_selections():
     counts = check_rows(rows, ph.queries, ph.q_pos, lambda i: keys_of[int(q_seq[i])], lambda i: reps[int(q_seq[i])],
                         128, 64, 2048, idx, sc, blk, False, "step8x20")
     print("decode step 8x20 vs oracle", counts, flush=True)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_steps_equal_two_calls(seed):
+    """Seeded random decode steps: block size, sequence count and lengths,
+    appended keys (up to B, so the fused launch takes them), queries on old
+    and new positions; bit for bit equal to append + index."""
+    g = np.random.default_rng(500 + seed)
+    B = int(g.choice([16, 32, 64, 128, 256]))
+    nseq = int(g.integers(1, 9))
+    n_new = int(g.integers(1, B + 1))
+    before = g.integers(0, 5000, nseq).astype(np.int64)
+    m = int(g.integers(3, 40))
+    m = min(m, 16384 // B)
+    k = int(min(g.integers(1, m * B + 1), 2048))
+    print("random step %d: B=%d nseq=%d n_new=%d m=%d k=%d" % (seed, B, nseq, n_new, m, k), flush=True)
+    w = synth.decode_batch(nseq=nseq, L=int(before.max()) + 1, seed=600 + seed, B=B, m=m, k=k, spare=n_new)
+    new = synth.to_bf16(g.standard_normal((nseq, n_new, synth.D)).astype(np.float32))
+    after = before + n_new
+    nq = int(g.integers(1, 3 * nseq + 1))
+    q_seq = g.integers(0, nseq, nq).astype(np.int32)
+    q_pos = np.array([g.integers(0, after[s]) for s in q_seq], np.int64)
+    q_pos[: min(nq, nseq)] = after[q_seq[: min(nq, nseq)]] - 1
+    queries = synth.to_bf16(g.standard_normal((nq, synth.D)).astype(np.float32))
+    ph = synth.Phase("p", queries, q_pos, q_seq)
+    a, b = _pair(w, B, before, new, ph, k, m)
+    _same(a, b, "random step %d" % seed)
