@@ -498,58 +498,43 @@ __global__ __launch_bounds__(kLsaFillThreads) void lsa_fill_kernel(const int32_t
         if (brow) brow[r] = used;
     }
     __syncthreads();
-    // emit: thread t owns words [t * wper, (t + 1) * wper) and counts their
-    // keys; then every output slot e (strided over the threads, so the
-    // stores coalesce) finds its owner by binary search over the owners'
-    // first slots and its pool key by counting set bits
+    // emit: thread t owns words [t * wper, (t + 1) * wper); after a scan of
+    // their set-bit counts it lists their pool keys, ascending, in LDS (over
+    // the rank arrays, which are free now: at most 4 pool keys per bucket,
+    // so at most 4 * P2 of them); then every output slot e (strided over
+    // the threads, so the stores coalesce) reads its pool key from the list,
+    // the slots past the partial pool key shifted by the keys it lacks
     const int wper = (words + kLsaFillThreads - 1) / kLsaFillThreads;
     const int pg = s_part_g, pn = s_part_n;
     int cnt = 0;
     for (int j = 0; j < wper; ++j) {
         const int wi = t * wper + j;
-        if (wi < words) cnt += kLsaPool * __popc(bits[wi]);
+        if (wi < words) cnt += __popc(bits[wi]);
     }
-    if (pg >= 0 && (pg >> 5) >= t * wper && (pg >> 5) < (t + 1) * wper) cnt -= kLsaPool - pn;
     const int incl = wg_incl_scan<kLsaFillThreads>(cnt, s_scan);
-    int* first = reinterpret_cast<int*>(skey);            // [threads] first slot of each owner
-    first[t] = incl - cnt;
+    int* list = reinterpret_cast<int*>(skey);
+    int o = incl - cnt;
+    for (int j = 0; j < wper; ++j) {
+        const int wi = t * wper + j;
+        if (wi >= words) break;
+        uint32_t b = bits[wi];
+        while (b) {
+            const int g = wi * 32 + __builtin_ctz(b);
+            b &= b - 1u;
+            if (o < 4 * P2) list[o] = g;
+            if (g == pg) s_part_g = o;       // the partial pool key's ordinal
+            ++o;
+        }
+    }
     if (t == kLsaFillThreads - 1) s_scan[0] = incl;
     __syncthreads();
-    const int total = s_scan[0];
+    const int ip = pg >= 0 ? s_part_g : -1;
+    const int nkeys = min(s_scan[0], 4 * P2);
+    const int total = min(kLsaPool * nkeys - (ip >= 0 ? kLsaPool - pn : 0), k);
     for (int e = t; e < total; e += kLsaFillThreads) {
-        int lo = 0, hi = kLsaFillThreads - 1;             // last owner whose first slot is <= e
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (first[mid] <= e) lo = mid;
-            else hi = mid - 1;
-        }
-        int rem = e - first[lo];
-        int pos = -1;
-        for (int j = 0; j < wper && pos < 0; ++j) {
-            const int wi = lo * wper + j;
-            const uint32_t b = bits[wi];
-            const bool part = pg >= 0 && (pg >> 5) == wi;
-            const int c = kLsaPool * __popc(b) - (part ? kLsaPool - pn : 0);
-            if (rem >= c) {
-                rem -= c;
-                continue;
-            }
-            // set bit number i of the word holds slot rem; the partial pool
-            // key (if it is in this word and before, or is that bit and rem
-            // runs past its keys) shifts the count by the keys it lacks
-            int i = rem / kLsaPool;
-            if (part) {
-                const int ip = __popc(b & ((1u << (pg & 31)) - 1u));       // its ordinal
-                if (ip < i || (ip == i && rem - kLsaPool * ip >= pn)) {
-                    rem += kLsaPool - pn;
-                    i = rem / kLsaPool;
-                }
-            }
-            uint32_t x = b;
-            for (int q = 0; q < i; ++q) x &= x - 1;
-            pos = kLsaPool * (wi * 32 + __builtin_ctz(x)) + rem % kLsaPool;
-        }
-        orow[e] = pos;
+        int x = e;
+        if (ip >= 0 && e >= kLsaPool * ip + pn) x += kLsaPool - pn;
+        orow[e] = kLsaPool * list[x / kLsaPool] + x % kLsaPool;
     }
     for (int e = total + t; e < k; e += kLsaFillThreads) orow[e] = -1;
 }
