@@ -149,23 +149,29 @@ def kernel_source_hash(root):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(root, workload, stage):
+def measured_traffic(root, workload, stage, fused_step=False):
     """HBM bytes per dispatch of a stage's kernel from the PMC summary under
     profiles/ (FETCH_SIZE and WRITE_SIZE scaled by a known-size copy), or
-    None when there is none or the kernel sources changed since."""
+    None when there is none or the kernel sources changed since.
+    fused_step: the step runs hisa_decode_step, whose selection-and-scores
+    kernel is decode_step_kernel rather than decode_fused_kernel."""
     import glob
     sym = STAGE_KERNEL.get(stage.split("/")[-1])
     if sym is None:
         return None
+    if fused_step:
+        sym = tuple(sorted(sym, key=lambda x: x != "decode_step_kernel"))
     for path in glob.glob(os.path.join(root, "profiles", "*_hbm_traffic.md")):
         lines = open(path).read().splitlines()
         sha = [l.split("=", 1)[1].strip() for l in lines if l.startswith("source_sha256")]
         if not sha or sha[0] != kernel_source_hash(root):
             continue
-        for l in lines:
-            f = l.split("\t")
-            if len(f) == 4 and f[0] == "traffic" and f[1] == workload and any(x in f[2] for x in sym):
-                return float(f[3])
+        rows = [l.split("\t") for l in lines]
+        rows = [f for f in rows if len(f) == 4 and f[0] == "traffic" and f[1] == workload]
+        for x in sym:                      # the first symbol with a line wins
+            for f in rows:
+                if x in f[2]:
+                    return float(f[3])
     return None
 
 
@@ -794,7 +800,8 @@ def main():
                    "replicas": R, "B": S.B, "m": S.m, "k": S.k},
         "roofline": {"bound": bound, "kernel": kern, "achieved": achieved, "peak": peak,
                      "unit": unit, "frac": achieved / peak,
-                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)), args.workload, kern),
+                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)), args.workload, kern,
+                                                 fused_step=S.fused_step),
                      ("algorithmic_flops_per_launch" if bound == "mfma" else "algorithmic_bytes_per_launch"): work,
                      "avg_launch_ms": h_stage[kern]},
         "cpu_baseline": cpu,

@@ -39,3 +39,23 @@ def test_row_overlap():
     # row 0: 2 shared of 6 distinct, 2 of 4 flat; row 1 identical; row 2 empty on both sides
     assert abs(iou - (2 / 6 + 1 + 1) / 3) < 1e-12
     assert abs(rec - (0.5 + 1 + 1) / 3) < 1e-12
+
+
+def test_traffic_lookup_takes_the_kernel_the_step_runs(tmp_path):
+    src = tmp_path / "long_context_sparse_hisa_amd" / "csrc"
+    src.mkdir(parents=True)
+    (src / "k.hip").write_text("// kernels\n")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    sha = bench.kernel_source_hash(str(tmp_path))
+    (prof / "w_hbm_traffic.md").write_text(
+        "source_sha256 = %s\n" % sha
+        + "traffic\tw\tvoid hisa::decode_fused_kernel<1>(x)\t100\n"
+        + "traffic\tw\tvoid hisa::decode_step_kernel<1>(x)\t200\n")
+    root = str(tmp_path)
+    assert bench.measured_traffic(root, "w", "decode/select_and_scores", fused_step=True) == 200.0
+    assert bench.measured_traffic(root, "w", "decode/select_and_scores") == 100.0
+    assert bench.measured_traffic(root, "other", "decode/select_and_scores") is None
+    # a changed kernel source voids the figure
+    (src / "k.hip").write_text("// kernels, edited\n")
+    assert bench.measured_traffic(root, "w", "decode/select_and_scores", fused_step=True) is None
