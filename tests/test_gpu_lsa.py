@@ -165,7 +165,8 @@ def test_planted_groups_become_buckets():
     _check_build(w, cache, lsa, "planted")
 
 
-@pytest.mark.parametrize("p,k", [(1, 1), (7, 33), (64, 256), (300, 2048), (513, 3000), (2048, 5000)])
+@pytest.mark.parametrize("p,k", [(1, 1), (7, 33), (64, 256), (256, 2045), (300, 2048), (513, 3000), (700, 2047),
+                                 (2048, 5000)])
 def test_query_grid(p, k):
     print("lsa query p=%d k=%d" % (p, k), flush=True)
     L = 8192
