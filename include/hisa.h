@@ -210,7 +210,12 @@ int hisa_flat_index(const hisa_index_args* a, void* stream);
  * block-score launch (stage events 0, 1, 2 as in hisa_index).  Either way
  * the blocks the append re-pools are the queries' forced last two, whose
  * representatives stage 1 never scores.  Otherwise the two calls run one
- * after the other.
+ * after the other.  The append is folded in only when the lengths the
+ * queries see are known to be the appended ones: a->seq_len is given, or
+ * (one sequence, seq_len NULL) max_len == seqs[0].len + n_new.  A device
+ * length larger than len + n_new breaks that precondition: in the folded
+ * launch a query at or past len + n_new of its sequence then gets a -1 row
+ * (where the two calls would index it).
  * Errors: those of hisa_index and hisa_append_keys; INVALID_ARG also when
  *         an appended length exceeds max_len.
  */

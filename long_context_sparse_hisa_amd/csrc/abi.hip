@@ -301,8 +301,14 @@ int hisa_decode_step(const hisa_index_args* a, const hisa_seq* seqs, const uint1
     const int64_t chunk = a->nq > 0 ? chunk_for(a, 0, a->workspace_bytes) : 1;
     if (chunk < 1) return HISA_ERR_WORKSPACE;
     const int64_t Mmax = hisa_Mmax(a);
+    // Without device lengths every query may sit anywhere below max_len;
+    // the append is folded into the index's launch only when that bound is
+    // the appended length (the launch treats positions at or past a
+    // sequence's appended length as invalid, which the two calls would not
+    // when max_len is larger).
+    const bool lengths_known = a->seq_len != nullptr || (n_new > 0 && a->max_len == seqs[0].len + n_new);
     const bool foldable = n_new > 0 && a->nq > 0 && hisa_split(a) && n_new <= a->B && a->nseq <= kDecodeJobs &&
-                          chunk >= a->nq;
+                          chunk >= a->nq && lengths_known;
     const bool fuse = foldable && Mmax <= kStage1FusedMax;
     if (foldable && !fuse) {
         // more than 2048 blocks: the append joins the block-score launch,

@@ -177,3 +177,117 @@ def test_random_steps_equal_two_calls(seed):
     ph = synth.Phase("p", queries, q_pos, q_seq)
     a, b = _pair(w, B, before, new, ph, k, m)
     _same(a, b, "random step %d" % seed)
+
+
+def test_decode_32k_x16_indices_only_against_oracle():
+    """The configuration the bench times: hisa_decode_step on the 32K
+    decode batch with out_scores and out_blocks NULL (the indices-only
+    top-k), every row against the oracle directly."""
+    print("decode step 32K x16, indices only", flush=True)
+    from long_context_sparse_hisa_amd import device
+    from parity import check_batch
+    w = synth.decode_batch()
+    before = w.seq_len - 1
+    new = np.stack([w.keys[int(o) + int(L) - 1][None] for o, L in zip(w.seq_key_off, w.seq_len)])
+    ph = w.phases[0]
+    cache = device.DeviceCache(w, B=128)
+    cache.set_lengths(before)
+    cache.pool()
+    call = device.IndexCall(cache, ph.queries, ph.q_pos, ph.q_seq, k=w.k, m=w.m, scores=False, blocks=False,
+                            one_chunk_limit=16 << 30)
+    assert call.out_scores is None and call.out_blocks is None
+    cache.decode_step(call, new)
+    idx, sc, blk = call.results()
+    assert sc is None and blk is None
+    reps_list = [oracle.pool(w.keys[int(o):int(o) + int(L)], 128) for o, L in zip(w.seq_key_off, w.seq_len)]
+    reps = np.concatenate(reps_list)
+    rep_off = np.arange(16, dtype=np.int64) * 256
+
+    def K_of(i):
+        o = int(w.seq_key_off[i])
+        return w.keys[o:o + int(w.seq_len[i])]
+
+    counts = check_batch(ph, w.keys, w.seq_len, w.seq_key_off, reps, rep_off, 128, w.m, w.k, idx, None, None,
+                         False, K_of, lambda i: reps_list[i], "step-indices")
+    print("decode step indices only vs oracle", counts, flush=True)
+    assert counts["exact"] + counts["excused"] == 16
+
+
+def _one_seq_step(fused, keys0, L0, new, queries, q_pos, max_len, B, m, k, lengths_dev):
+    """One sequence: pool L0 keys, then append + index (fused: one
+    hisa_decode_step call) with the given device lengths (None: NULL)."""
+    from long_context_sparse_hisa_amd import device, hisa
+    dev = "cuda:0"
+    keys = device.to_dev(keys0, dev)
+    reps = torch.zeros(((keys0.shape[0] + B - 1) // B, synth.D), dtype=torch.int16, device=dev)
+    hisa.hisa_pool_blocks(keys[:L0], B, reps[:(L0 + B - 1) // B])
+    qd = device.to_dev(queries, dev)
+    pd = device.to_dev(q_pos, dev)
+    nq = len(q_pos)
+    out_idx = torch.empty((nq, k), dtype=torch.int32, device=dev)
+    out_sc = torch.empty((nq, k), dtype=torch.float32, device=dev)
+    out_blk = torch.empty((nq, m), dtype=torch.int32, device=dev)
+    seq_len = None if lengths_dev is None else device.to_dev(np.array([lengths_dev], np.int64), dev)
+    a = hisa.make_args(qd, pd, keys, k, reps=reps, seq_len=seq_len, max_len=max_len, B=B, m=m, out_idx=out_idx,
+                       out_scores=out_sc, out_blocks=out_blk)
+    want, _, whole = hisa.hisa_workspace_bytes(a, False, all_queries=True)
+    ws = torch.empty(whole, dtype=torch.uint8, device=dev)
+    a = hisa.make_args(qd, pd, keys, k, reps=reps, seq_len=seq_len, max_len=max_len, B=B, m=m, out_idx=out_idx,
+                       out_scores=out_sc, out_blocks=out_blk, workspace=ws)
+    nk = device.to_dev(new[None], dev)
+    seqs = [(0, 0, L0, keys0.shape[0])]
+    if fused:
+        hisa.hisa_decode_step(a, seqs, nk)
+    else:
+        hisa.hisa_append_keys(keys, reps, seqs, nk, B)
+        hisa.hisa_index(a)
+    torch.cuda.synchronize()
+    return (out_idx.cpu().numpy(), out_sc.cpu().numpy(), out_blk.cpu().numpy(), keys.cpu().numpy(),
+            reps.cpu().numpy())
+
+
+@pytest.mark.parametrize("L0", [3000, 300_000])
+def test_decode_step_lengths_null_beyond_append(L0):
+    """No device lengths (one sequence, lengths = max_len) with max_len past
+    the appended length: the step must equal append + index bit for bit,
+    also for queries past the new keys (the call takes the two-call path)."""
+    print("decode step, NULL lengths, L0=%d" % L0, flush=True)
+    g = np.random.default_rng(90 + L0 % 7)
+    B, m, k, n_new = 128, 16, 512, 3
+    cap = L0 + 2000
+    keys0 = np.zeros((cap, synth.D), np.uint16)
+    keys0[:L0] = synth.to_bf16(g.standard_normal((L0, synth.D)).astype(np.float32))
+    new = synth.to_bf16(g.standard_normal((n_new, synth.D)).astype(np.float32))
+    q_pos = np.array([L0 + n_new - 1, L0 + n_new, L0 + 1500, L0 // 2], np.int64)
+    queries = synth.to_bf16(g.standard_normal((4, synth.D)).astype(np.float32))
+    two = _one_seq_step(False, keys0, L0, new, queries, q_pos, cap, B, m, k, None)
+    one = _one_seq_step(True, keys0, L0, new, queries, q_pos, cap, B, m, k, None)
+    for x, y, what in zip(two, one, ("idx", "scores", "blocks", "keys", "reps")):
+        assert np.array_equal(x, y, equal_nan=True), what
+    assert np.all(one[0][2] >= -1) and one[0][2][0] >= 0       # the far query is indexed, as two calls do
+
+
+@pytest.mark.parametrize("L0", [3000, 300_000])
+def test_decode_step_inconsistent_lengths_give_empty_rows(L0):
+    """Device lengths larger than the appended length (a caller error the
+    host cannot see): when the append is folded into the index's launch, a
+    query at or past the appended length gets a -1 row instead of reading
+    representatives the append is rewriting; the other rows, keys and
+    representatives equal append + index."""
+    print("decode step, inconsistent lengths, L0=%d" % L0, flush=True)
+    g = np.random.default_rng(95 + L0 % 7)
+    B, m, k, n_new = 128, 16, 512, 3
+    cap = L0 + 2000
+    keys0 = np.zeros((cap, synth.D), np.uint16)
+    keys0[:L0] = synth.to_bf16(g.standard_normal((L0, synth.D)).astype(np.float32))
+    new = synth.to_bf16(g.standard_normal((n_new, synth.D)).astype(np.float32))
+    q_pos = np.array([L0 + n_new - 1, L0 + n_new + 700, L0 // 2], np.int64)
+    queries = synth.to_bf16(g.standard_normal((3, synth.D)).astype(np.float32))
+    lengths = L0 + n_new + 1000
+    two = _one_seq_step(False, keys0, L0, new, queries, q_pos, cap, B, m, k, lengths)
+    one = _one_seq_step(True, keys0, L0, new, queries, q_pos, cap, B, m, k, lengths)
+    assert np.all(one[0][1] == -1) and np.all(one[2][1] == -1)
+    for r in (0, 2):
+        for x, y in zip(two[:3], one[:3]):
+            assert np.array_equal(x[r], y[r], equal_nan=True)
+    assert np.array_equal(two[3], one[3]) and np.array_equal(two[4], one[4])
