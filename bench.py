@@ -76,24 +76,28 @@ def log(*a):
 # ---- algorithmic traffic per stage ------------------------------------------------
 
 def hisa_stage_bytes(q_pos, B, m, k):
-    """Algorithmic HBM bytes of the two HISA stages for queries at q_pos
-    (d = 64: a key or representative row is 128 bytes).  Block stage: the
-    query, its causal representatives, the kept-block list out.  Token
-    stage: the query, the kept list, the candidate keys, int32 indices out."""
+    """Algorithmic HBM bytes of the HISA stages for queries at q_pos (d = 64:
+    a key or representative row is 128 bytes): inputs read once and the
+    call's required output, no workspace traffic (kept-block lists and
+    candidate scores passed between kernels are not counted).  Block stage:
+    the query and its causal representatives.  Token stage: the query and
+    the candidate keys of its kept blocks.  Top-k: the int32 indices out."""
     q_pos = np.asarray(q_pos, np.int64)
     nb = q_pos // B + 1                                  # causal blocks
     kept = np.minimum(nb, m)
     cand = np.minimum(kept * B, q_pos + 1)                # <= m*B candidate tokens
+    block = (128 + nb * 128).sum()
+    token = (128 + cand * 128).sum()
+    out = len(q_pos) * k * 4
     return {
-        "block_stage": float((128 + nb * 128 + 2 * m * 4).sum()),
-        # few queries: scores go to a workspace row, then the top-k reads it
-        "token_scores": float((128 + m * 4 + cand * 128 + m * B * 4).sum()),
-        "token_topk": float(len(q_pos) * (m * B * 4 + m * 4 + k * 4)),
-        # stage 1 and the token scores as one kernel (few queries)
-        "select_and_scores": float((128 + nb * 128 + 2 * m * 4).sum() + (128 + m * 4 + cand * 128 + m * B * 4).sum()),
-        # the token stage without the workspace round trip: query, kept
-        # list and candidate keys in, indices out
-        "token_ideal": float((128 + m * 4 + cand * 128 + k * 4).sum()),
+        "block_stage": float(block),
+        "token_scores": float(token),
+        "token_topk": float(out),
+        # stage 1 and the token scores as one kernel (few queries): the
+        # query once, its representatives and its candidate keys
+        "select_and_scores": float(block + (cand * 128).sum()),
+        # the whole path of these queries
+        "token_ideal": float(block + (cand * 128).sum() + out),
     }
 
 
@@ -120,13 +124,14 @@ def stage_roofline(name, ms, nq, flops, nbytes):
 
 
 def flat_stage_bytes(q_pos, k):
-    """Flat: the scores stage reads every visible key and writes its score;
-    the top-k stage reads the scores and writes int32 indices."""
+    """Flat: the scores stage reads the query and every visible key; the
+    top-k stage writes the int32 indices (the score rows between them are
+    workspace traffic, not counted)."""
     q_pos = np.asarray(q_pos, np.int64)
     n = q_pos + 1
     return {
-        "flat_scores": float((n * 128 + 128 + n * 4).sum()),
-        "flat_topk": float((n * 4).sum() + len(n) * k * 4),
+        "flat_scores": float((n * 128 + 128).sum()),
+        "flat_topk": float(len(n) * k * 4),
     }
 
 
@@ -389,14 +394,7 @@ class LsaLeg:
             with torch.cuda.graph(g):
                 self.run(r)
             graphs.append(g)
-        for i in range(warmup):
-            graphs[i % n].replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            graphs[(warmup + i) % n].replay()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps * 1e3
+        return replay_timed(graphs, steps, warmup, torch, spg=1) * 1e3
 
 
 def attention_kernel_ms(S, A, nsteps, torch):
@@ -445,20 +443,33 @@ def capture_graphs(S, flat, torch, attn=None):
     return graphs
 
 
-def time_method(S, flat, steps, warmup, torch, attn=None):
-    """Wall time of `steps` graph replays (one step each, rotating over the
-    replicas), bracketed by device synchronisation."""
-    graphs = capture_graphs(S, flat, torch, attn)
-    spg = STEPS_PER_GRAPH
-    n = max(1, steps // spg)                # replays of spg steps each, consecutive replays on fresh replicas
+def replay_timed(graphs, steps, warmup, torch, spg=None):
+    """Seconds per replay-step over `steps` replays of the captured graphs
+    (rotating, consecutive replays on fresh replicas).  Every graph is
+    replayed once before the warmup and the timed region, so that no timed
+    replay is a graph's first launch (whose upload and first dispatch cost
+    more than a steady-state replay)."""
+    n = len(graphs)
+    spg = STEPS_PER_GRAPH if spg is None else spg
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // spg)
     for i in range(max(1, warmup // spg)):
-        graphs[(i * spg) % S.replicas].replay()
+        graphs[i % n].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(n):
-        graphs[((warmup + i) * spg) % S.replicas].replay()
+    for i in range(reps):
+        graphs[(warmup // spg + i) % n].replay()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * steps / (n * spg)
+    return (time.perf_counter() - t0) / (reps * spg)
+
+
+def time_method(S, flat, steps, warmup, torch, attn=None):
+    """Milliseconds per step: graph replays (one step each, rotating over
+    the replicas), bracketed by device synchronisation."""
+    graphs = capture_graphs(S, flat, torch, attn)
+    return replay_timed(graphs, steps, warmup, torch) * 1e3
 
 
 def stage_times(S, flat, nsteps, torch):
@@ -535,7 +546,7 @@ def sweep_m(S, ms, steps, warmup, torch):
             out.append(ic.out_idx[torch.from_numpy(pick).to(ic.out_idx.device)].cpu().numpy())
         return np.concatenate(out)
 
-    f_ms = time_method(S, True, steps, warmup, torch) / steps * 1e3
+    f_ms = time_method(S, True, steps, warmup, torch)
     S.step(0, True, sp)
     torch.cuda.synchronize()
     flat_rows = rows_of(S.calls[True])
@@ -547,7 +558,7 @@ def sweep_m(S, ms, steps, warmup, torch):
         log("sweep: %s m=%d k=%d" % ("block-only" if block_only else "hisa", m, k))
         S.calls[False] = S.build_calls(False, m, k, block_only=block_only)
         S.block_only = block_only
-        ms_step = time_method(S, False, steps, warmup, torch) / steps * 1e3
+        ms_step = time_method(S, False, steps, warmup, torch)
         S.step(0, False, sp)
         torch.cuda.synchronize()
         iou, rec = row_overlap(rows_of(S.calls[False]), flat_rows)
@@ -558,48 +569,198 @@ def sweep_m(S, ms, steps, warmup, torch):
     return f_ms, points
 
 
-def cpu_baseline(S, seconds, oracle):
-    """The oracle on the same step, repeated for about `seconds`."""
-    w = S.w
-    B, m, k = S.B, S.m, S.k
-    lens = S.cache.seq_len
-    reps = np.zeros((w.total_rep_rows(B), 64), np.uint16)
-    rep_off = w.seq_rep_off(B)
-    for s in range(w.nseq):
-        o = int(w.seq_key_off[s])
-        r = oracle.pool(w.keys[o:o + int(lens[s])], B)
-        reps[rep_off[s]:rep_off[s] + len(r)] = r
-    # prefill steps are far beyond a few seconds of CPU work: time an evenly
-    # spaced sample of at most 256 queries per phase instead
+def oracle_rate(w, lens, n_new, B, m, k, flat, seconds, oracle, max_q=256):
+    """Queries per second of the oracle on the phases of workload w (keys
+    of sequence s: the first lens[s] rows at w.seq_key_off[s]), repeated
+    for about `seconds`.  A phase of more than max_q queries is sampled
+    (evenly spaced queries).  n_new > 0: every repetition first re-pools
+    the blocks the step's append touched, as the step does.  Returns
+    (queries/s, repetitions, queries per repetition, whether the sample is
+    the whole step, seconds)."""
+    reps = None
+    if not flat:
+        reps = np.zeros((w.total_rep_rows(B), 64), np.uint16)
+        rep_off = w.seq_rep_off(B)
+        for s in range(w.nseq):
+            o = int(w.seq_key_off[s])
+            r = oracle.pool(w.keys[o:o + int(lens[s])], B)
+            reps[rep_off[s]:rep_off[s] + len(r)] = r
+    else:
+        rep_off = None
     sample = []
-    for ph in S.phases:
+    for ph in w.phases:
         nq = len(ph.q_pos)
-        pick = np.unique(np.linspace(0, nq - 1, min(nq, 256)).astype(np.int64))
+        pick = np.unique(np.linspace(0, nq - 1, min(nq, max_q)).astype(np.int64))
         sample.append((ph, pick))
     nsample = sum(len(p) for _, p in sample)
+    whole = nsample == sum(len(ph.q_pos) for ph in w.phases)
     n = 0
     t0 = time.perf_counter()
     while True:
-        if S.append_src is not None:                   # re-pool the blocks the append touches
-            n_new = S.append_src.shape[1]
+        if n_new and not flat:                          # re-pool the blocks the append touches
             for s in range(w.nseq):
                 o = int(w.seq_key_off[s])
                 L = int(lens[s])
                 oracle.pool_range(w.keys[o:o + L], B, (L - n_new) // B, (L + B - 1) // B,
                                   reps[rep_off[s]:rep_off[s] + (L + B - 1) // B])
         for ph, pick in sample:
-            oracle.index_batch(False, ph.queries[pick], ph.q_pos[pick], w.keys, k, reps=reps,
+            oracle.index_batch(flat, ph.queries[pick], ph.q_pos[pick], w.keys, k, reps=reps,
                                q_seq=ph.q_seq[pick], seq_key_off=w.seq_key_off, seq_rep_off=rep_off,
                                seq_len=lens, B=B, m=m)
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    whole = nsample == S.q_per_step
-    what = ("the whole step" if whole else "%d evenly spaced queries of the step" % nsample)
-    return {"value": n * nsample / el, "unit": "queries/s", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": "%d repetitions of %s (%s), HISA oracle, %.1f s" % (n, what, S.desc, el)}
+    return n * nsample / el, n, nsample, whole, el
+
+
+def host_facts():
+    """The host the oracle runs on: logical CPUs, the ones this process may
+    use, the CPU model and OMP_NUM_THREADS."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def cpu_baseline(S, seconds, oracle, extras=True):
+    """The oracle (HISA) on the same step, repeated for about `seconds`;
+    with extras also the flat oracle on the same sample and the HISA
+    oracle on one core over the 4K tiny prefill."""
+    n_new = 0 if S.append_src is None else int(S.append_src.shape[1])
+    w = S.w
+    w_ph = w.phases
+    w.phases = S.phases
+    try:
+        v, n, nsample, whole, el = oracle_rate(w, S.cache.seq_len, n_new, S.B, S.m, S.k, False, seconds, oracle)
+        what = ("the whole step" if whole else "%d evenly spaced queries of the step" % nsample)
+        out = {"value": v, "unit": "queries/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": "%d repetitions of %s (%s), HISA oracle, %.1f s" % (n, what, S.desc, el)}
+        out.update(host_facts())
+        if extras:
+            fv, fn, fns, fwhole, fel = oracle_rate(w, S.cache.seq_len, 0, S.B, S.m, S.k, True,
+                                                   max(1.0, seconds / 3), oracle)
+            out["flat_oracle"] = {"value": fv, "unit": "queries/s", "cores": oracle.threads(),
+                                  "sample": "%d repetitions of the same %d queries, %.1f s" % (fn, fns, fel)}
+    finally:
+        w.phases = w_ph
+    if extras:
+        from long_context_sparse_hisa_amd import synth
+        tw = synth.tiny_prefill()
+        oracle.set_threads(1)
+        try:
+            tv, tn, tns, _, tel = oracle_rate(tw, tw.seq_len, 0, tw.B, tw.m, tw.k, False, max(1.0, seconds / 3),
+                                              oracle)
+        finally:
+            oracle.set_threads(out["cores"])
+        out["one_core_tiny_prefill_4k"] = {
+            "value": tv, "unit": "queries/s", "cores": 1,
+            "sample": "%d repetitions of %d evenly spaced queries of the 4096-query causal prefill (4096 i.i.d. "
+                      "N(0,1) keys, B=128 m=8 k=256), HISA oracle, %.1f s" % (tn, tns, tel)}
+    return out
+
+
+def measure(S, args, torch, label):
+    """Time HISA and the flat indexer on setup S: graph-replayed steps
+    (HISA's decode steps also as two calls), per-kernel event times, the
+    roofline of each method's dominant kernel and the step's algorithmic
+    bytes.  Returns the summary dict."""
+    log("%s: timing HISA: %d warmup + %d graph-replayed steps" % (label, args.warmup, args.steps))
+    h_ms = time_method(S, False, args.steps, args.warmup, torch)
+    two_ms = None
+    if S.fused_step:
+        log("%s: timing HISA as two calls (append, then index)" % label)
+        S.fused_step = False
+        two_ms = time_method(S, False, args.steps, args.warmup, torch)
+        S.fused_step = True
+    log("%s: timing flat: %d warmup + %d graph-replayed steps" % (label, args.warmup, args.steps))
+    f_ms = time_method(S, True, args.steps, args.warmup, torch)
+    nst = max(4, min(args.stage_steps, S.replicas * 4))
+    log("%s: per-stage HIP-event timing over %d eager steps each" % (label, nst))
+    h_stage = stage_times(S, False, nst, torch)
+    f_stage = stage_times(S, True, nst, torch)
+    qps = S.q_per_step / (h_ms * 1e-3)
+    fqps = S.q_per_step / (f_ms * 1e-3)
+
+    stage_bytes = {}
+    for ph in S.phases:
+        for nm, b in hisa_stage_bytes(ph.q_pos, S.B, S.m, S.k).items():
+            stage_bytes["%s/%s" % (ph.name, nm)] = b
+        for nm, b in flat_stage_bytes(ph.q_pos, S.k).items():
+            stage_bytes["%s/%s" % (ph.name, nm)] = b
+    stage_fl, stage_nq = {}, {}
+    for ph in S.phases:
+        for nm, f in stage_flops(ph.q_pos, S.B, S.m).items():
+            stage_fl["%s/%s" % (ph.name, nm)] = f
+            stage_nq["%s/%s" % (ph.name, nm)] = len(ph.q_pos)
+    # the append: the new rows read and written, the touched blocks' other
+    # rows read, their representatives written
+    app_bytes = 0
+    if S.append_src is not None:
+        n_new = S.append_src.shape[1]
+        for sq in S.seqs:
+            L0 = int(sq[2])
+            b0, b1 = L0 // S.B, (L0 + n_new - 1) // S.B
+            old_rows = L0 - b0 * S.B                       # rows of the first touched block already there
+            app_bytes += 2 * n_new * 128 + old_rows * 128 + (b1 - b0 + 1) * 128
+    if S.fused_step:
+        # the decode step's first launch also runs the append
+        for n in list(stage_bytes):
+            if n.endswith("/select_and_scores") or (n.endswith("/block_stage") and S.max_len // S.B > 2048):
+                stage_bytes[n] += app_bytes
+    kern = max((n for n in h_stage if n in stage_bytes), key=lambda n: h_stage[n])
+    bound, achieved, peak, unit, work = stage_roofline(kern, h_stage[kern], stage_nq.get(kern, 0),
+                                                       stage_fl.get(kern, 0.0), stage_bytes[kern])
+    fkern = max((n for n in f_stage if n in stage_bytes), key=lambda n: f_stage[n])
+    fbound, f_achieved, fpeak, funit, fwork = stage_roofline(fkern, f_stage[fkern], stage_nq.get(fkern, 0),
+                                                             stage_fl.get(fkern, 0.0), stage_bytes[fkern])
+    # algorithmic bytes of a whole step: every query's representatives,
+    # candidate keys and output, plus the append
+    h_step_bytes = sum(b for n, b in stage_bytes.items() if n.endswith("/token_ideal")) + app_bytes
+    f_step_bytes = sum(b for n, b in stage_bytes.items() if n.split("/")[-1] in STAGES_FLAT) + app_bytes
+
+    def per_kernel(stage):
+        return {n: {"avg_ms": v, "algorithmic_bytes": stage_bytes.get(n),
+                    "gbps": (stage_bytes[n] / (v * 1e-3) / 1e9) if n in stage_bytes and v > 0 else None}
+                for n, v in stage.items()}
+
+    return {
+        "workload": S.name, "description": S.desc, "queries_per_step": S.q_per_step, "replicas": S.replicas,
+        "B": S.B, "m": S.m, "k": S.k,
+        "hisa": {"ms_per_step": h_ms, "queries_per_s": qps, "step_bytes": h_step_bytes,
+                 "hbm_gbps_step": h_step_bytes / (h_ms * 1e-3) / 1e9, "kernels": per_kernel(h_stage),
+                 "two_calls_ms_per_step": two_ms},
+        "flat": {"ms_per_step": f_ms, "queries_per_s": fqps, "step_bytes": f_step_bytes,
+                 "hbm_gbps_step": f_step_bytes / (f_ms * 1e-3) / 1e9, "kernels": per_kernel(f_stage),
+                 "dominant": {"kernel": fkern, "bound": fbound, "achieved": f_achieved, "peak": fpeak,
+                              "unit": funit, "frac": f_achieved / fpeak,
+                              ("algorithmic_flops_per_launch" if fbound == "mfma" else
+                               "algorithmic_bytes_per_launch"): fwork, "avg_launch_ms": f_stage[fkern]}},
+        "speedup_vs_flat": f_ms / h_ms,
+        "roofline": {"bound": bound, "kernel": kern, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak,
+                     ("algorithmic_flops_per_launch" if bound == "mfma" else "algorithmic_bytes_per_launch"): work,
+                     "avg_launch_ms": h_stage[kern]},
+    }
+
+
+# workloads reported beside the default one, so that one run covers the
+# 32K, 128K and 1M contexts and the large decode batch
+CONTEXT_WORKLOADS = ("decode_32k_x256", "long_context_128k", "long_decode_1m")
+DEFAULT_REPLICAS = {"decode_32k_x16": 64, "decode_32k_x64": 16, "decode_32k_x256": 4, "long_decode_1m": 256,
+                    "decode_varlen_x64": 16, "chunked_prefill_32k": 1, "long_context_128k": 1,
+                    "tiny_prefill_4k": 1}
 
 
 def main():
@@ -616,6 +777,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attention", action="store_true", help="skip the sparse-attention leg")
     ap.add_argument("--no-lsa", action="store_true", help="skip the LSA-Flat leg")
+    ap.add_argument("--no-contexts", action="store_true",
+                    help="skip the 32K x 256, 128K and 1M workloads reported beside the default one")
     ap.add_argument("--steps-per-graph", type=int, default=1,
                     help="consecutive steps captured in one graph (1: one replay per step, the serving form)")
     ap.add_argument("--lsa-replicas", type=int, default=8, help="copies of the LSA bucket cache rotated over")
@@ -652,12 +815,8 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
         return
     hisa.lib()
-    # replicas rotate about 4 GiB of keys so the 256 MB MALL cannot serve
-    # repeated decode steps
-    default_rep = {"decode_32k_x16": 64, "decode_32k_x64": 16, "decode_32k_x256": 4, "long_decode_1m": 256,
-                   "decode_varlen_x64": 16,
-                   "chunked_prefill_32k": 1, "long_context_128k": 1, "tiny_prefill_4k": 1}
-    R = args.replicas or default_rep[args.workload]
+    root = os.path.dirname(os.path.abspath(__file__))
+    R = args.replicas or DEFAULT_REPLICAS[args.workload]
     log("setting up %s with %d replicas" % (args.workload, R))
     S = Setup(args.workload, R, hisa, synth, device, torch)
     if args.sweep_m:
@@ -670,82 +829,29 @@ def main():
                                      "1024 evenly spaced rows per phase, F the flat indexer's row",
                           "points": points}), flush=True)
         return
-    log("timing HISA: %d warmup + %d graph-replayed steps" % (args.warmup, args.steps))
-    h_el = time_method(S, False, args.steps, args.warmup, torch)
-    two_ms = None
-    if S.fused_step:
-        log("timing HISA as two calls (append, then index)")
-        S.fused_step = False
-        two_ms = time_method(S, False, args.steps, args.warmup, torch) / args.steps * 1e3
-        S.fused_step = True
-    log("timing flat: %d warmup + %d graph-replayed steps" % (args.warmup, args.steps))
-    f_el = time_method(S, True, args.steps, args.warmup, torch)
-    nst = max(4, min(args.stage_steps, S.replicas * 4))
-    log("per-stage HIP-event timing over %d eager steps each" % nst)
-    h_stage = stage_times(S, False, nst, torch)
-    f_stage = stage_times(S, True, nst, torch)
-    h_ms = h_el / args.steps * 1e3
-    f_ms = f_el / args.steps * 1e3
-    qps = S.q_per_step * args.steps / h_el
-    fqps = S.q_per_step * args.steps / f_el
-
-    # roofline of the dominant HISA kernel
-    stage_bytes = {}
-    for ph in S.phases:
-        for nm, b in hisa_stage_bytes(ph.q_pos, S.B, S.m, S.k).items():
-            stage_bytes["%s/%s" % (ph.name, nm)] = b
-        for nm, b in flat_stage_bytes(ph.q_pos, S.k).items():
-            stage_bytes["%s/%s" % (ph.name, nm)] = b
-    stage_fl, stage_nq = {}, {}
-    for ph in S.phases:
-        for nm, f in stage_flops(ph.q_pos, S.B, S.m).items():
-            stage_fl["%s/%s" % (ph.name, nm)] = f
-            stage_nq["%s/%s" % (ph.name, nm)] = len(ph.q_pos)
-    if S.fused_step:
-        # the decode step's launch also appends: new rows written, touched
-        # blocks read, their representatives written
-        n_new = S.append_src.shape[1]
-        blocks = sum((int(sq[2]) + n_new - 1) // S.B - int(sq[2]) // S.B + 1 for sq in S.seqs)
-        app_bytes = len(S.seqs) * n_new * 128 + blocks * (S.B * 128 + 128)
-        for n in list(stage_bytes):
-            if n.endswith("/select_and_scores"):
-                stage_bytes[n] += app_bytes
-    kern = max((n for n in h_stage if n in stage_bytes), key=lambda n: h_stage[n])
-    bound, achieved, peak, unit, work = stage_roofline(kern, h_stage[kern], stage_nq.get(kern, 0),
-                                                       stage_fl.get(kern, 0.0), stage_bytes[kern])
-    fkern = max((n for n in f_stage if n in stage_bytes), key=lambda n: f_stage[n])
-    fbound, f_achieved, fpeak, funit, _ = stage_roofline(fkern, f_stage[fkern], stage_nq.get(fkern, 0),
-                                                         stage_fl.get(fkern, 0.0), stage_bytes[fkern])
-    # algorithmic bytes of a whole step: every stage's per-query traffic
-    # (no workspace round trips) plus the append (new rows written, touched
-    # blocks re-read, representatives written)
-    append_rows = 0 if S.append_src is None else S.append_src.shape[0] * S.append_src.shape[1]
-    h_step_bytes = sum(b for n, b in stage_bytes.items() if n.split("/")[-1] in ("block_stage", "token_ideal"))
-    f_step_bytes = sum(b for n, b in stage_bytes.items() if n.split("/")[-1] in STAGES_FLAT)
-    h_step_bytes += append_rows * 128 * 2
-    f_step_bytes += append_rows * 128 * 2
-
-    def per_kernel(stage):
-        return {n: {"avg_ms": v, "algorithmic_bytes": stage_bytes.get(n),
-                    "gbps": (stage_bytes[n] / (v * 1e-3) / 1e9) if n in stage_bytes and v > 0 else None}
-                for n, v in stage.items()}
+    res = measure(S, args, torch, args.workload)
+    h_ms = res["hisa"]["ms_per_step"]
+    f_ms = res["flat"]["ms_per_step"]
+    roof = dict(res["roofline"])
+    roof["traffic"] = measured_traffic(root, args.workload, roof["kernel"], fused_step=S.fused_step)
 
     attention = None
     if args.workload in ATTN_WORKLOADS and not args.no_attention:
         log("attention leg: inputs and %d replicas" % args.attn_replicas)
         A = AttentionLeg(S, args.attn_replicas, device, synth, torch)
-        a_ms = attention_kernel_ms(S, A, max(8, nst), torch)
+        a_ms = attention_kernel_ms(S, A, max(8, min(args.stage_steps, S.replicas * 4)), torch)
         n_valid = int((A.calls[False][0].idx >= 0).sum().item())
         a_bytes = A.algorithmic_bytes(n_valid)
         log("timing index + attention steps (HISA, flat)")
-        ha_ms = time_method(S, False, args.steps, args.warmup, torch, A) / args.steps * 1e3
-        fa_ms = time_method(S, True, args.steps, args.warmup, torch, A) / args.steps * 1e3
+        ha_ms = time_method(S, False, args.steps, args.warmup, torch, A)
+        fa_ms = time_method(S, True, args.steps, args.warmup, torch, A)
         a_gbps = a_bytes / (a_ms * 1e-3) / 1e9
         attention = {"description": A.desc, "kernels": "attn_partial_kernel + attn_combine_kernel",
                      "avg_call_ms": a_ms, "algorithmic_bytes": a_bytes, "gbps": a_gbps,
                      "frac_of_hbm_peak": a_gbps / HBM_PEAK_GBPS,
                      "ms_per_step_hisa_plus_attention": ha_ms, "ms_per_step_flat_plus_attention": fa_ms,
                      "speedup_vs_flat": fa_ms / ha_ms}
+        del A
 
     lsa = None
     if args.workload in LSA_WORKLOADS and not args.no_lsa:
@@ -775,6 +881,7 @@ def main():
                "note": "a step is the same key append as HISA's and flat's steps, then the search; a sequence "
                        "completes a block every 512 decode steps, so the build adds "
                        "build_us_per_decode_step_amortized per step"}
+        del Lg
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -782,9 +889,32 @@ def main():
         log("timing the CPU oracle for about %.0f s" % args.cpu_seconds)
         cpu = cpu_baseline(S, args.cpu_seconds, oracle)
 
+    contexts = None
+    if args.workload == "decode_32k_x16" and not args.no_contexts:
+        contexts = {args.workload: {"hisa_ms_per_step": h_ms, "flat_ms_per_step": f_ms,
+                                    "speedup_vs_flat": res["speedup_vs_flat"], "see": "the top-level fields"}}
+        del S
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        for name in CONTEXT_WORKLOADS:
+            log("setting up %s with %d replicas" % (name, DEFAULT_REPLICAS[name]))
+            S2 = Setup(name, DEFAULT_REPLICAS[name], hisa, synth, device, torch)
+            r = measure(S2, args, torch, name)
+            r["roofline"]["traffic"] = measured_traffic(root, name, r["roofline"]["kernel"],
+                                                        fused_step=S2.fused_step)
+            if not args.no_cpu_baseline:
+                import oracle
+                log("%s: timing the CPU oracle for about %.0f s" % (name, max(1.0, args.cpu_seconds / 3)))
+                r["cpu_baseline"] = cpu_baseline(S2, max(1.0, args.cpu_seconds / 3), oracle, extras=False)
+                r["cpu_baseline"]["flat_oracle"] = None
+            contexts[name] = r
+            del S2
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+
     out = {
         "metric": "indexer queries/s + HBM GB/s at 32K/128K/1M ctx; HISA vs flat-DSA speedup",
-        "value": qps,
+        "value": res["hisa"]["queries_per_s"],
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -795,31 +925,26 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "description": S.desc, "queries_per_step": S.q_per_step,
+        "config": {"workload": args.workload, "description": res["description"],
+                   "queries_per_step": res["queries_per_step"],
                    "outputs": "int32 top-k indices (the optional scores and kept-block lists are not requested)",
-                   "replicas": R, "B": S.B, "m": S.m, "k": S.k},
-        "roofline": {"bound": bound, "kernel": kern, "achieved": achieved, "peak": peak,
-                     "unit": unit, "frac": achieved / peak,
-                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)), args.workload, kern,
-                                                 fused_step=S.fused_step),
-                     ("algorithmic_flops_per_launch" if bound == "mfma" else "algorithmic_bytes_per_launch"): work,
-                     "avg_launch_ms": h_stage[kern]},
+                   "replicas": R, "B": res["B"], "m": res["m"], "k": res["k"]},
+        "roofline": roof,
         "cpu_baseline": cpu,
-        "step_bytes": h_step_bytes,
-        "hbm_gbps_step": h_step_bytes / (h_ms * 1e-3) / 1e9,
-        "kernels": per_kernel(h_stage),
-        "flat": {"value": fqps, "unit": "queries/s", "ms_per_step": f_ms, "kernels": per_kernel(f_stage),
-                 "step_bytes": f_step_bytes,
-                 "hbm_gbps_step": f_step_bytes / (f_ms * 1e-3) / 1e9,
-                 "dominant": {"kernel": fkern, "bound": fbound, "achieved": f_achieved, "unit": funit,
-                              "frac": f_achieved / fpeak}},
-        "speedup_vs_flat": f_ms / h_ms,
-        "hisa_two_calls_ms_per_step": two_ms,
+        "step_bytes": res["hisa"]["step_bytes"],
+        "hbm_gbps_step": res["hisa"]["hbm_gbps_step"],
+        "kernels": res["hisa"]["kernels"],
+        "flat": dict(res["flat"], value=res["flat"]["queries_per_s"], unit="queries/s"),
+        "speedup_vs_flat": res["speedup_vs_flat"],
+        "hisa_two_calls_ms_per_step": res["hisa"]["two_calls_ms_per_step"],
         "step_note": ("HISA decode steps are one hisa_decode_step call (the append in the same launch as the block "
                       "selection and token scores); hisa_two_calls_ms_per_step is the same step as append + index, "
-                      "the form the flat indexer's step takes" if two_ms is not None else None),
+                      "the form the flat indexer's step takes"
+                      if res["hisa"]["two_calls_ms_per_step"] is not None else None),
+        "timing_note": "every captured graph is replayed once before the warmup and the timed replays",
         "attention": attention,
         "lsa_flat": lsa,
+        "contexts": contexts,
     }
     print(json.dumps(out), flush=True)
 

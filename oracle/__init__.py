@@ -75,6 +75,7 @@ def _load():
             lib.oracle_bf16_round.argtypes = [ctypes.c_double]
             lib.oracle_bf16_round.restype = ctypes.c_uint16
             lib.oracle_threads.restype = ctypes.c_int
+            lib.oracle_set_threads.argtypes = [_I32]
             _lib = lib
     return _lib
 
@@ -92,6 +93,11 @@ def _u16(a) -> np.ndarray:
 
 def threads() -> int:
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of later oracle calls from this thread (timing only)."""
+    _load().oracle_set_threads(int(n))
 
 
 def bf16_round(v: float) -> int:

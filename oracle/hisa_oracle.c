@@ -473,5 +473,16 @@ int oracle_threads(void)
 #endif
 }
 
+/* Threads later parallel regions of the calling thread use (n >= 1); the
+ * timing harness sets 1 for its single-core figure.  Not arithmetic. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Exposed for the tests: the rounding rule used for representatives. */
 uint16_t oracle_bf16_round(double v) { return bf16_round_nearest_even(v); }

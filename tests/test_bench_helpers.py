@@ -5,20 +5,26 @@ import bench
 
 
 def test_stage_bytes_decode_32k():
-    # one decode query at 32767: 256 representatives, 64 kept blocks of 128 keys
+    # one decode query at 32767: 256 representatives, 64 kept blocks of 128
+    # keys; only inputs read once and the int32 output count (no workspace)
     b = bench.hisa_stage_bytes(np.array([32767]), 128, 64, 2048)
-    assert b["block_stage"] == 128 + 256 * 128 + 2 * 64 * 4
-    assert b["token_ideal"] == 128 + 64 * 4 + 8192 * 128 + 2048 * 4
-    assert b["token_topk"] == 8192 * 4 + 64 * 4 + 2048 * 4
+    assert b["block_stage"] == 128 + 256 * 128
+    assert b["token_scores"] == 128 + 8192 * 128
+    assert b["select_and_scores"] == 128 + 256 * 128 + 8192 * 128
+    assert b["token_ideal"] == 128 + 256 * 128 + 8192 * 128 + 2048 * 4
+    assert b["token_topk"] == 2048 * 4
+    # the 16-sequence decode batch: 17.30 MB of representatives, keys and queries
+    b16 = bench.hisa_stage_bytes(np.full(16, 32767), 128, 64, 2048)
+    assert b16["select_and_scores"] == 16 * (128 + (256 + 8192) * 128) == 17303552
     f = bench.flat_stage_bytes(np.array([32767, 32767]), 2048)
-    assert f["flat_scores"] == 2 * (32768 * 132 + 128)
-    assert f["flat_topk"] == 2 * (32768 * 4 + 2048 * 4)
+    assert f["flat_scores"] == 2 * (32768 * 128 + 128)
+    assert f["flat_topk"] == 2 * 2048 * 4
 
 
 def test_stage_bytes_early_queries_are_causal():
     b = bench.hisa_stage_bytes(np.array([0, 200]), 128, 64, 16)
     # query 0 sees one block and one key, query 200 two blocks and 201 keys
-    assert b["token_ideal"] == 2 * (128 + 64 * 4 + 16 * 4) + (1 + 201) * 128
+    assert b["token_ideal"] == 2 * (128 + 16 * 4) + (1 + 2) * 128 + (1 + 201) * 128
 
 
 def test_stage_flops_and_bound():
