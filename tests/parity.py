@@ -127,6 +127,11 @@ def check_all_rows_properties(g_idx, g_blk, q_pos, B, m, k, flat, seq_len=None):
         assert np.all(g_blk[:, 0] == 0), "first block not kept"
         last = g_blk[np.arange(nq), nb - 1]
         assert np.all(last == c), "own block not kept"
+        # the block before the query's own is forced too: second to last of
+        # the ascending list whenever it exists
+        has_prev = c >= 1
+        prev = g_blk[np.arange(nq), np.maximum(nb - 2, 0)]
+        assert np.all(prev[has_prev] == c[has_prev] - 1), "block c-1 not kept"
         # tokens sit inside kept blocks
         M = int(q_pos.max()) // B + 2
         kept = np.zeros((nq, M), bool)
@@ -138,3 +143,30 @@ def check_all_rows_properties(g_idx, g_blk, q_pos, B, m, k, flat, seq_len=None):
         assert inside.all(), "token outside kept blocks"
         cand = np.where(g_blk >= 0, np.minimum(B, q_pos[:, None] - g_blk * B + 1), 0).sum(1)
         assert np.all(nvalid == np.minimum(k, cand)), "hisa row count"
+
+
+def check_batch(ph, keys, lens, seq_key_off, reps, rep_off, B, m, k, g_idx, g_sc, g_blk, flat, K_of, R_of,
+                label=""):
+    """Every row of a phase against one batched oracle call: rows whose
+    indices (and kept blocks) equal the oracle's exactly pass, with every
+    exported score within TOL of the oracle's fp64 value; the other rows go
+    through the per-row tolerance rule of check_query.  Returns counts per
+    verdict."""
+    o_idx, o_sc, o_blk = oracle.index_batch(flat, ph.queries, ph.q_pos, keys, k, reps=reps, q_seq=ph.q_seq,
+                                            seq_key_off=seq_key_off, seq_rep_off=rep_off, seq_len=lens, B=B, m=m)
+    same = np.all(g_idx == o_idx, axis=1)
+    if not flat and g_blk is not None:
+        same &= np.all(g_blk == o_blk, axis=1)
+    if g_sc is not None:
+        v = same[:, None] & (o_idx >= 0)
+        err = np.abs(np.where(v, g_sc.astype(np.float64) - o_sc, 0.0))
+        if err.max() > TOL:
+            r = int(np.argmax(err.max(1)))
+            raise Mismatch("%s row %d: score error %.3g > %g" % (label, r, err[r].max(), TOL))
+    counts = {"exact": int(same.sum()), "excused": 0}
+    rest = np.nonzero(~same)[0]
+    if len(rest):
+        c = check_rows(rest, ph.queries, ph.q_pos, K_of, R_of, B, m, k, g_idx, g_sc, g_blk, flat, label)
+        counts["exact"] += c["exact"]
+        counts["excused"] += c["excused"]
+    return counts

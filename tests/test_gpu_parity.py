@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 from long_context_sparse_hisa_amd import synth
-from parity import check_all_rows_properties, check_rows
+from parity import check_all_rows_properties, check_batch, check_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -399,30 +399,58 @@ def test_decode_varlen_x64_full():
         _check_phase(w, cache, w.phases[0], w.k, w.m, flat, label="varlen")
 
 
-def test_chunked_prefill_32k_sampled():
-    print("chunked prefill 32K", flush=True)
+def _check_phase_all(w, cache, ph, k, m, flat, label="", **kw):
+    """Every row of a phase against one batched oracle call (exact rows
+    pass at once, the rest through the per-row tolerance rule), plus the
+    vectorised row properties."""
+    idx, sc, blk = _run(cache, ph, k, m, flat, **kw)
+    B = cache.B
+    lens = np.asarray(cache.seq_len, np.int64)
+    check_all_rows_properties(idx, blk, ph.q_pos, B, m, k, flat)
+    reps_list = None if flat else _oracle_reps(w, B, lens)
+    reps = None if flat else np.concatenate(reps_list)
+    rep_off = None if flat else np.concatenate([[0], np.cumsum([len(r) for r in reps_list])[:-1]]).astype(np.int64)
+
+    def K_of(i):
+        s = int(ph.q_seq[i])
+        o = int(w.seq_key_off[s])
+        return w.keys[o:o + int(lens[s])]
+
+    def R_of(i):
+        return reps_list[int(ph.q_seq[i])]
+
+    counts = check_batch(ph, w.keys, lens, w.seq_key_off, reps, rep_off, B, m, k, idx, sc, blk, flat, K_of, R_of,
+                         label)
+    print(label, "flat" if flat else "hisa", "all rows", counts, flush=True)
+    assert counts["exact"] + counts["excused"] == len(ph.q_pos)
+    return idx, sc, blk
+
+
+def test_chunked_prefill_32k_all_rows():
+    """All 32768 causal queries of the 32K prefill, every row against the
+    oracle (HISA and flat)."""
+    print("chunked prefill 32K, all rows", flush=True)
     dv = _dev()
     w = synth.chunked_prefill()
     cache = dv.DeviceCache(w)
     cache.pool()
-    g = np.random.default_rng(28)
-    rows = sorted(set([0, 1, 127, 128, 8191, 32767] + list(g.choice(32768, 120, replace=False))))
     for flat in (False, True):
-        _check_phase(w, cache, w.phases[0], w.k, w.m, flat, rows=rows, label="cfg3")
+        _check_phase_all(w, cache, w.phases[0], w.k, w.m, flat, label="cfg3")
 
 
-def test_long_context_128k():
-    print("long context 128K", flush=True)
+def test_long_context_128k_all_rows():
+    """The 128K context: every row of the 4096-query chunk and of the
+    32-query decode batch against the oracle; the flat rows of the decode
+    batch hold every planted needle."""
+    print("long context 128K, all rows", flush=True)
     dv = _dev()
     w = synth.long_context()
     cache = dv.DeviceCache(w)
     cache.pool()
-    g = np.random.default_rng(29)
     chunk, dec = w.phases
-    rows = sorted(set([0, 4095] + list(g.choice(4096, 40, replace=False))))
     for flat in (False, True):
-        _check_phase(w, cache, chunk, w.k, w.m, flat, rows=rows, label="cfg4chunk")
-        idx, _, _ = _check_phase(w, cache, dec, w.k, w.m, flat, label="cfg4decode")
+        _check_phase_all(w, cache, chunk, w.k, w.m, flat, label="cfg4chunk")
+        idx, _, _ = _check_phase_all(w, cache, dec, w.k, w.m, flat, label="cfg4decode")
         if flat:
             assert set(w.needles.tolist()) <= set(idx[0].tolist())
 
