@@ -189,6 +189,26 @@ int hisa_workspace_bytes(const hisa_index_args* a, int flat, size_t* bytes, size
 int hisa_index(const hisa_index_args* a, void* stream);
 
 /*
+ * hisa_index_static -- hisa_index for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same results, with the library's own device
+ * scratch in place of a caller workspace.  a->workspace and
+ * a->workspace_bytes are ignored; nothing is allocated.
+ *   The scratch is a static device array of HISA_STATIC_SCRATCH_BYTES per
+ *   GPU, held from the first call on that GPU until the process ends.  Its
+ *   contents need not start at any value.  Every call on one GPU uses the
+ *   same array, so calls that may overlap on one GPU (different streams,
+ *   threads or processes' shared contexts) race: serialise them.  Queries
+ *   that do not fit at once run in chunks, in order, on `stream`.
+ *   The stream must belong to the current device.
+ * Errors: those of hisa_index, HISA_ERR_WORKSPACE when one query's scratch
+ *         would exceed HISA_STATIC_SCRATCH_BYTES (not reachable within the
+ *         limits above), HISA_ERR_HIP when the scratch cannot be located.
+ */
+#define HISA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int hisa_index_static(const hisa_index_args* a, void* stream);
+
+/*
  * hisa_flat_index -- the flat DSA indexer: every visible key scored, top-k
  * ("DSA" section of the video summary).  B, m, reps and out_blocks are
  * ignored.  Same errors as hisa_index, less those about B and m.

@@ -6,10 +6,18 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "kernels.h"
 
 using namespace hisa;
+
+// Device scratch of hisa_index_static: one copy per GPU the library runs
+// on, held until the process ends.  Host code never uses this name as an
+// address: static_scratch() looks the array up once per device and every
+// launch takes that address.
+static __device__ __align__(256) unsigned char scratch[HISA_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -160,6 +168,30 @@ Timing stage_timing(const hisa_index_args* a, bool last_chunk, int s)
     return t;
 }
 
+// Address of the current device's copy of `scratch` (looked up on the
+// first call on that device, with the device current); nullptr on error.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int static_scratch(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return HISA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return HISA_ERR_UNSUPPORTED;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HISA_ERR_HIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return HISA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -281,6 +313,23 @@ int hisa_index(const hisa_index_args* a, void* stream_)
         if (err != hipSuccess) return HISA_ERR_HIP;
     }
     return HISA_OK;
+}
+
+int hisa_index_static(const hisa_index_args* a, void* stream)
+{
+    const int rc = validate_index(a, 0);
+    if (rc != HISA_OK) return rc;
+    if (a->nq == 0) return HISA_OK;
+    // one query's regions must fit; more queries than fit at once run in
+    // chunks, as hisa_index does with a small workspace
+    if (layout_for(a, 0, 1).total > HISA_STATIC_SCRATCH_BYTES) return HISA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    const int src = static_scratch(&ws);
+    if (src != HISA_OK) return src;
+    hisa_index_args b = *a;
+    b.workspace = ws;
+    b.workspace_bytes = HISA_STATIC_SCRATCH_BYTES;
+    return hisa_index(&b, stream);
 }
 
 int hisa_decode_step(const hisa_index_args* a, const hisa_seq* seqs, const uint16_t* new_keys, int64_t n_new,

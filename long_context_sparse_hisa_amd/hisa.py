@@ -89,6 +89,7 @@ def lib():
                                            ctypes.POINTER(ctypes.c_size_t),
                                            ctypes.POINTER(ctypes.c_size_t)]
         L.hisa_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
+        L.hisa_index_static.argtypes = [ctypes.POINTER(hisa_index_args), _P]
         L.hisa_flat_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
         L.hisa_block_index.argtypes = [ctypes.POINTER(hisa_index_args), _P]
         L.hisa_decode_step.argtypes = [ctypes.POINTER(hisa_index_args), ctypes.POINTER(hisa_seq), _P,
@@ -204,6 +205,12 @@ def hisa_workspace_bytes(args: hisa_index_args, flat: bool = False, all_queries:
 
 def hisa_index(args: hisa_index_args, stream=None):
     _check(lib().hisa_index(ctypes.byref(args), _stream(stream)), "hisa_index")
+
+
+def hisa_index_static(args: hisa_index_args, stream=None):
+    """hisa_index on the library's own device scratch (args.workspace is
+    ignored; nothing is allocated)."""
+    _check(lib().hisa_index_static(ctypes.byref(args), _stream(stream)), "hisa_index_static")
 
 
 def hisa_flat_index(args: hisa_index_args, stream=None):
