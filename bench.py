@@ -755,6 +755,58 @@ def measure(S, args, torch, label):
     }
 
 
+# The supplementary block-scoring shape: the last 32,768 positions of a
+# 1,048,576-key MoG sequence (8,192 blocks of 128), all indexed in one call.
+SUPP_L = 1 << 20
+SUPP_NQ = 32768
+SUPP_SEED = 13
+
+
+def supplementary_block_scoring(nsteps, torch, hisa_mod, device_mod, synth):
+    """Block scoring at 32,768 queries x 8,192 representatives (about 34
+    GFLOP of causal pairs), a shape large enough for the matrix-core
+    fraction to be read, outside the pages' configurations.  One hisa_index
+    call indexes every query (B=128, m=64, k=2048); stage 0 is the
+    representative scores on the MFMA (into a row per query) plus the top-m
+    select from those rows, timed with the library's stage events over
+    `nsteps` eager calls.  No flat indexer: its score rows would take
+    128 GiB."""
+    pos = np.arange(SUPP_L - SUPP_NQ, SUPP_L, dtype=np.int64)
+    w = synth.chunked_prefill(L=SUPP_L, seed=SUPP_SEED, q_positions=pos)
+    cache = device_mod.DeviceCache(w)
+    cache.pool()
+    ph = w.phases[0]
+    ic = device_mod.IndexCall(cache, ph.queries, ph.q_pos, ph.q_seq, k=w.k, m=w.m, scores=False, blocks=False,
+                              one_chunk_limit=16 << 30)
+    ic.run()
+    torch.cuda.synchronize()
+    evs = [hisa_mod.StageEvents() for _ in range(nsteps)]
+    torch.cuda._sleep(int(2.0e7))
+    for e in evs:
+        e.attach(ic.args)
+        ic.run()
+    torch.cuda.synchronize()
+    ic.args.stage_events = None
+    st = {nm: float(np.mean([e.stage_ms(i) for e in evs])) for i, nm in enumerate(STAGES_HISA)}
+    flops = stage_flops(pos, w.B, w.m)["block_stage"]
+    tflops = flops / (st["block_stage"] * 1e-3) / 1e12
+    nvalid = int((ic.out_idx >= 0).sum().item())
+    del ic, cache
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"label": "supplementary: not a configuration of the pages",
+            "description": "%d queries at positions %d..%d of one %d-key MoG sequence (d=64 bf16; B=%d, so "
+                           "8,064-8,192 causal blocks per query), m=%d, k=%d, all in one hisa_index call"
+                           % (SUPP_NQ, SUPP_L - SUPP_NQ, SUPP_L - 1, SUPP_L, w.B, w.m, w.k),
+            "causal_block_pairs": int((pos // w.B + 1).sum()), "block_flops": flops,
+            "stage_ms": st, "call_ms": float(sum(st.values())),
+            "block_stage": {"kernels": "block_score_tile_kernel (bf16 MFMA, scores into a row per query) + "
+                                       "stage1_select_kernel (top-m from each row)",
+                            "achieved_tflops": tflops, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                            "frac": tflops / MFMA_BF16_PEAK_TFLOPS},
+            "valid_indices": nvalid, "steps": nsteps}
+
+
 # workloads reported beside the default one, so that one run covers the
 # 32K, 128K and 1M contexts and the large decode batch
 CONTEXT_WORKLOADS = ("decode_32k_x256", "long_context_128k", "long_decode_1m")
@@ -779,6 +831,10 @@ def main():
     ap.add_argument("--no-lsa", action="store_true", help="skip the LSA-Flat leg")
     ap.add_argument("--no-contexts", action="store_true",
                     help="skip the 32K x 256, 128K and 1M workloads reported beside the default one")
+    ap.add_argument("--no-supplementary", action="store_true",
+                    help="skip the supplementary block-scoring shape (32768 queries x 8192 representatives)")
+    ap.add_argument("--supplementary-only", action="store_true",
+                    help="only the supplementary block-scoring shape")
     ap.add_argument("--steps-per-graph", type=int, default=1,
                     help="consecutive steps captured in one graph (1: one replay per step, the serving form)")
     ap.add_argument("--lsa-replicas", type=int, default=8, help="copies of the LSA bucket cache rotated over")
@@ -816,6 +872,11 @@ def main():
         return
     hisa.lib()
     root = os.path.dirname(os.path.abspath(__file__))
+    if args.supplementary_only:
+        log("supplementary block-scoring shape: %d queries x %d representatives" % (SUPP_NQ, SUPP_L // 128))
+        print(json.dumps(supplementary_block_scoring(max(4, min(args.stage_steps, 8)), torch, hisa, device, synth)),
+              flush=True)
+        return
     R = args.replicas or DEFAULT_REPLICAS[args.workload]
     log("setting up %s with %d replicas" % (args.workload, R))
     S = Setup(args.workload, R, hisa, synth, device, torch)
@@ -912,6 +973,11 @@ def main():
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
 
+    supplementary = None
+    if args.workload == "decode_32k_x16" and not args.no_contexts and not args.no_supplementary:
+        log("supplementary block-scoring shape: %d queries x %d representatives" % (SUPP_NQ, SUPP_L // 128))
+        supplementary = supplementary_block_scoring(max(4, min(args.stage_steps, 8)), torch, hisa, device, synth)
+
     out = {
         "metric": "indexer queries/s + HBM GB/s at 32K/128K/1M ctx; HISA vs flat-DSA speedup",
         "value": res["hisa"]["queries_per_s"],
@@ -945,6 +1011,7 @@ def main():
         "attention": attention,
         "lsa_flat": lsa,
         "contexts": contexts,
+        "supplementary_block_scoring": supplementary,
     }
     print(json.dumps(out), flush=True)
 

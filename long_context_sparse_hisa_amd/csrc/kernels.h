@@ -76,9 +76,11 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
                          int64_t Mmax, float* sigma, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
                          hipStream_t stream, Timing t = {});
 
-// The representative scores alone into sigma [nq, Mmax] (free candidates
-// 1 .. c-2 of each query), with a decode step's append folded in when app
-// is given; launch_select_scores then selects and scores the tokens.
+// The representative scores alone into sigma [nq, Mmax] (at least the free
+// candidates 1 .. c-2 of each query; slot 0 flags the query as one to
+// index), with a decode step's append folded in when app is given;
+// launch_select_scores or the stage-1 select then selects.  Many queries
+// are scored on the matrix cores, few one thread per score.
 hipError_t launch_block_scores(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb,
                                int64_t Mmax, float* sigma, hipStream_t stream, Timing t = {},
                                const struct StepAppend* app = nullptr);

@@ -227,11 +227,18 @@ __global__ __launch_bounds__(NT) void stage1_select_kernel(QueryMeta qm, const u
                           : 0u;
         }
     } else {
-        const float* sg = sigma + row * Mmax;
+        // every item loads (through a buffer resource: the lane is the
+        // vector offset, the item a scalar one, and slots past the row read
+        // as zero), then the slots outside 1 .. c-2 are masked
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(sigma + row * Mmax, (uint32_t)Mmax * 4u);
+        const int w0 = __builtin_amdgcn_readfirstlane(wave_id()) * ITEMS;
+        const int lane = lane_id();
+        const int hi = (int)(c - 2);
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
-            const int64_t b = slot_of<ITEMS>(it);
-            key[it] = (b >= 1 && b <= c - 2) ? score_key(sg[b]) : 0u;
+            const int b = ((w0 + it) << 6) + lane;            // slot_of<ITEMS>(it)
+            const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, (w0 + it) * 256, 0));
+            key[it] = (b >= 1 && b <= hi) ? score_key(v) : 0u;
         }
     }
     const Threshold th = wg_bucket_select<NT, ITEMS>(key, m - 3, sm);
@@ -401,6 +408,110 @@ static hipError_t launch_stage1_tile_items(const QueryMeta& qm, const uint16_t* 
                      t.start, t.stop, qm, reps, q0, nq, lb, m, sel, rinfo, out_blocks);
 }
 
+// Many queries with more blocks than stage1_tile_kernel holds in LDS: the
+// representative scores on the bf16 MFMA into sigma [nq, Mmax], for
+// stage1_select_kernel to select from.  A wave takes 64 consecutive query
+// rows (four 16-row sub-tiles, the B operands, loaded once) and a range of
+// 16-block tiles; each representative tile it loads (the A operand) feeds
+// the two v_mfma_f32_16x16x32_bf16 of every sub-tile (d = 64).  Lane l
+// receives blocks 4*(l/16)..+4 of the tile for query row l%16 of a
+// sub-tile and stores them as one 16-byte vector.  Tiles past the largest
+// causal block of the walked rows are not scored; rows of several
+// sequences are walked one sequence at a time.  Slot 0 of a valid row
+// holds 1 instead of block 0's score (block 0 is forced, never a free
+// candidate; select_score_kernel reads the flag).
+constexpr int kBsRows = 64;
+constexpr int kBsWaves = 4;
+constexpr int64_t kBsTargetWaves = 8192;
+
+__global__ __launch_bounds__(64 * kBsWaves) void block_score_tile_kernel(QueryMeta qm, const uint16_t* reps,
+                                                                         int64_t q0, int64_t nq, int lb, int64_t Mmax,
+                                                                         int range, float* sigma)
+{
+    const int lane = lane_id();
+    const int64_t row0 = (int64_t)blockIdx.x * kBsRows;
+    const int nrows = (int)min<int64_t>(kBsRows, nq - row0);
+    const int ntile = (int)((Mmax + 15) / 16);
+    const int bt0 = ((int)blockIdx.y * kBsWaves + wave_id()) * range;
+    if (bt0 >= ntile) return;
+    const int bt1 = min(bt0 + range, ntile);
+    QueryInfo qi;
+    qi.valid = false;
+    qi.seq = -1;
+    qi.t = -1;
+    qi.key_off = 0;
+    qi.rep_off = 0;
+    if (lane < nrows)
+        qi = query_info(q0 + row0 + lane, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq,
+                        qm.max_len);
+    const int c_own = qi.valid ? (int)(qi.t >> lb) : 0;
+    const int col = lane & 15, kg = lane >> 4;
+    bf16x8_t a0[4], a1[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+        a0[sb] = bf16x8_t{};
+        a1[sb] = bf16x8_t{};
+        if (16 * sb + col < nrows) {
+            const uint16_t* qrow = qm.queries + (q0 + row0 + 16 * sb + col) * kDim + 8 * kg;
+            a0[sb] = *reinterpret_cast<const bf16x8_t*>(qrow);
+            a1[sb] = *reinterpret_cast<const bf16x8_t*>(qrow + 32);
+        }
+    }
+    const bool vec = (Mmax & 3) == 0;                  // 16-byte aligned score rows
+    uint64_t pending = __ballot(qi.valid);
+    while (pending) {
+        const int lead = (int)__builtin_ctzll(pending);
+        const int s = __builtin_amdgcn_readlane(qi.seq, lead);
+        const bool mine = qi.valid && qi.seq == s;
+        const uint64_t mrows = __ballot(mine);
+        pending &= ~mrows;
+        const int64_t rep_off = ((int64_t)__builtin_amdgcn_readlane((int)(qi.rep_off >> 32), lead) << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane((int)qi.rep_off, lead);
+        const int cmax = (int)wave_max_u32(mine ? (uint32_t)c_own : 0u);
+        const int tend = min(bt1, cmax / 16 + 1);
+        for (int bt = bt0; bt < tend; ++bt) {
+            const int b = bt * 16 + col;
+            bf16x8_t r0 = {}, r1 = {};
+            if (b <= cmax) {
+                const uint16_t* rp = reps + (rep_off + b) * kDim + 8 * kg;
+                r0 = *reinterpret_cast<const bf16x8_t*>(rp);
+                r1 = *reinterpret_cast<const bf16x8_t*>(rp + 32);
+            }
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                if (((mrows >> (16 * sb)) & 0xffffull) == 0) continue;      // uniform: no walked row here
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r0, a0[sb], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r1, a1[sb], acc, 0, 0, 0);
+                if (!((mrows >> (16 * sb + col)) & 1ull)) continue;
+                const int j = bt * 16 + 4 * kg;
+                if (j == 0) acc[0] = 1.0f;
+                float* dst = sigma + (row0 + 16 * sb + col) * Mmax + j;
+                if (vec && j + 3 < Mmax) {
+                    *reinterpret_cast<f32x4_t*>(dst) = acc;
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (j + v < Mmax) dst[v] = acc[v];
+                }
+            }
+        }
+    }
+}
+
+static hipError_t launch_block_scores_tile(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb,
+                                           int64_t Mmax, float* sigma, hipStream_t stream, Timing t)
+{
+    const int64_t qtiles = (nq + kBsRows - 1) / kBsRows;
+    const int64_t ntile = (Mmax + 15) / 16;
+    const int64_t want = std::max<int64_t>(1, (kBsTargetWaves + qtiles - 1) / qtiles);
+    const int64_t range = std::max<int64_t>(1, (ntile + want - 1) / want);
+    const int64_t nranges = (ntile + range - 1) / range;
+    const dim3 grid((unsigned)qtiles, (unsigned)((nranges + kBsWaves - 1) / kBsWaves));
+    return launch_k(block_score_tile_kernel, grid, dim3(64 * kBsWaves), stream, t.start, t.stop, qm, reps, q0, nq, lb,
+                    Mmax, (int)range, sigma);
+}
+
 hipError_t launch_block_scores(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb,
                                int64_t Mmax, float* sigma, hipStream_t stream, Timing t, const StepAppend* app)
 {
@@ -416,6 +527,8 @@ hipError_t launch_block_scores(const QueryMeta& qm, const uint16_t* reps, int64_
                         const_cast<uint16_t*>(reps), app->keys, app->new_keys, app->B, dj, app->njobs, q0, lb, Mmax,
                         sigma);
     }
+    // many queries: the scores on the matrix cores; few: one thread per score
+    if (nq >= kManyRows) return launch_block_scores_tile(qm, reps, q0, nq, lb, Mmax, sigma, stream, t);
     dim3 grid((unsigned)((Mmax + kThreads - 1) / kThreads), (unsigned)nq);
     return launch_k(block_score_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm, reps, q0, lb, Mmax, sigma);
 }
@@ -450,6 +563,18 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
     }
     const hipError_t err = launch_block_scores(qm, reps, q0, nq, lb, Mmax, sigma, stream, Timing{t.start, nullptr});
     if (err != hipSuccess) return err;
+    if (nq >= kManyRows) {
+        // many rows: 32 scores per thread in 256- or 512-thread workgroups,
+        // several per CU hiding each other's barriers
+        if (Mmax <= 4096)
+            return launch_stage1_items<256, 16, false>(qm, reps, q0, nq, lb, m, Mmax, sigma, sel, rinfo, out_blocks,
+                                                       stream, nullptr, t.stop);
+        if (Mmax <= 8192)
+            return launch_stage1_items<256, 32, false>(qm, reps, q0, nq, lb, m, Mmax, sigma, sel, rinfo, out_blocks,
+                                                       stream, nullptr, t.stop);
+        return launch_stage1_items<512, 32, false>(qm, reps, q0, nq, lb, m, Mmax, sigma, sel, rinfo, out_blocks,
+                                                   stream, nullptr, t.stop);
+    }
     // 1024 threads select among up to 16384 scores, 16 per thread
     const int64_t per = (Mmax + 1023) / 1024;
 #define HISA_S1S(N) \

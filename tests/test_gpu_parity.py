@@ -583,6 +583,83 @@ def test_many_queries_packed_sequences(force_fallback):
         _check_phase(w, cache, ph, k, m, flat, label="manypacked", props=False, max_len=max_len)
 
 
+@pytest.mark.parametrize("kind", ["mog", "quantized", "constant"])
+def test_many_rows_topk_ties(kind):
+    """Hundreds of prefill rows of up to 8,192 candidates (B = 128, m = 64,
+    k = 2048) through the many-row top-k (one 256-thread workgroup per row):
+    plain keys; scores from five values only (block and token ties across
+    the threshold, resolved by the lower index); one score for every key
+    (the lowest blocks and tokens win).  The early positions keep every
+    causal block."""
+    print("many-row top-k %s" % kind, flush=True)
+    dv = _dev()
+    L, B, m, k = 20000, 128, 64, 2048
+    pos = np.concatenate([np.arange(2100, 5400, 97), np.arange(9001, L, 37)]).astype(np.int64)
+    w = synth.chunked_prefill(L=L, seed=41, B=B, m=m, k=k, q_positions=pos)
+    keys, queries = w.keys, w.phases[0].queries
+    if kind != "mog":
+        g = np.random.default_rng(42)
+        kf = np.zeros((L, synth.D), np.float32)
+        if kind == "quantized":
+            kf[:, :4] = g.choice([-1.0, 1.0], size=(L, 4))
+        else:
+            kf[:, :4] = 1.0
+        keys = synth.to_bf16(kf)
+        qf = np.zeros((len(pos), synth.D), np.float32)
+        qf[:, :4] = 1.0
+        queries = synth.to_bf16(qf)
+    w2 = synth.Workload(kind, keys, w.seq_key_off, w.seq_len, w.seq_cap, B, m, k)
+    ph = synth.Phase("p", queries, pos, np.zeros(len(pos), np.int32))
+    cache = dv.DeviceCache(w2, B=B)
+    cache.pool()
+    idx, _, _ = _check_phase(w2, cache, ph, k, m, False, label="pf-" + kind)
+    if kind == "constant":
+        # every score ties: the lowest blocks and, inside them, the lowest tokens
+        t = int(pos[-1])
+        c = t // B
+        blocks = list(range(0, m - 2)) + [c - 1, c]
+        want = np.concatenate([np.arange(b * B, b * B + B) for b in blocks])[:k]
+        assert np.array_equal(idx[-1], want)
+
+
+@pytest.mark.parametrize("nq", [320, 600])
+def test_many_queries_long_rows(nq):
+    """Hundreds of queries with more representatives than the stage-1 tile
+    kernel holds (2,345 blocks of 128 over 300,100 keys; a count not
+    divisible by four, so the last scores of a row are stored one by one):
+    the representative scores on the matrix cores into a row per query,
+    then the selection from those rows (one workgroup per query for 600
+    queries; with 320, the selection fused with the token scores)."""
+    print("long rows nq=%d" % nq, flush=True)
+    dv = _dev()
+    L, B, m, k = 300100, 128, 64, 2048
+    g = np.random.default_rng(43 + nq)
+    pos = np.sort(g.choice(np.arange(200000, L), nq, replace=False)).astype(np.int64)
+    pos[-1] = L - 1
+    w = synth.chunked_prefill(L=L, seed=44, B=B, m=m, k=k, q_positions=pos)
+    cache = dv.DeviceCache(w, B=B)
+    cache.pool()
+    _check_phase(w, cache, w.phases[0], k, m, False, label="longrows%d" % nq)
+
+
+def test_supplementary_block_scoring_shape_sampled():
+    """The supplementary block-scoring shape at full size: the last 32,768
+    positions of a 1,048,576-key MoG sequence in one call (8,064-8,192
+    causal blocks per query, scored on the matrix cores into a row per
+    query).  Every row's properties; 48 rows (the first, the last and 46
+    random ones) against the oracle."""
+    print("supplementary 32768 x 8192", flush=True)
+    dv = _dev()
+    L, nq = 1 << 20, 32768
+    pos = np.arange(L - nq, L, dtype=np.int64)
+    w = synth.chunked_prefill(L=L, seed=13, q_positions=pos)
+    cache = dv.DeviceCache(w)
+    cache.pool()
+    g = np.random.default_rng(45)
+    rows = sorted(set([0, nq - 1] + list(g.choice(nq, 46, replace=False))))
+    _check_phase(w, cache, w.phases[0], w.k, w.m, False, rows=rows, label="supp", one_chunk_limit=16 << 30)
+
+
 @pytest.mark.parametrize("n_out", [16, 300])
 def test_outlier_scores_stretch_the_bins(n_out):
     """A few keys along each decode query (score about 6 |q|^2, far above
