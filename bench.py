@@ -60,6 +60,7 @@ STAGES_HISA = ("block_stage", "token_scores", "token_topk")
 STAGES_FLAT = ("flat_scores", "flat_topk")
 SPLIT_BELOW = 512               # fewer queries: the token stage splits each query over workgroups
 FUSED_MAX_BLOCKS = 2048         # ... and with at most this many blocks stage 1 joins it in one kernel
+DECODE_FOLD_MAX_SEQS = 64       # a decode step folds its append into the first launch for this many sequences
 
 
 def hisa_stage_names(nq, max_len, B):
@@ -714,8 +715,10 @@ def measure(S, args, torch, label):
             b0, b1 = L0 // S.B, (L0 + n_new - 1) // S.B
             old_rows = L0 - b0 * S.B                       # rows of the first touched block already there
             app_bytes += 2 * n_new * 128 + old_rows * 128 + (b1 - b0 + 1) * 128
-    if S.fused_step:
-        # the decode step's first launch also runs the append
+    if S.fused_step and S.cache.nseq <= DECODE_FOLD_MAX_SEQS:
+        # the decode step's first launch also runs the append (the library
+        # folds it for up to 64 sequences; beyond, the append is a launch
+        # of its own inside the same call)
         for n in list(stage_bytes):
             if n.endswith("/select_and_scores") or (n.endswith("/block_stage") and S.max_len // S.B > 2048):
                 stage_bytes[n] += app_bytes
