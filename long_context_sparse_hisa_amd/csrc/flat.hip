@@ -179,9 +179,9 @@ hipError_t launch_flat_scores(const QueryMeta& qm, const uint16_t* keys, int64_t
 // candidates stay in token order, so every output is ascending.
 
 template <int NT, int ITEMS, bool TO_CAND>
-__global__ __launch_bounds__(NT) void flat_select_kernel(QueryMeta qm, int64_t q0, const uint32_t* ukeys,
-                                                         int64_t Lmax, int SL, int k, int K1, uint32_t* cand_key,
-                                                         int32_t* cand_tok, int32_t* out_idx, float* out_scores)
+HISA_INLINE void flat_select_body(const QueryMeta& qm, int64_t q0, const uint32_t* ukeys, int64_t Lmax, int SL,
+                                  int k, int K1, uint32_t* cand_key, int32_t* cand_tok, int32_t* out_idx,
+                                  float* out_scores)
 {
     __shared__ BucketSmem<NT> sm;
     const int64_t row = blockIdx.x;
@@ -192,12 +192,13 @@ __global__ __launch_bounds__(NT) void flat_select_kernel(QueryMeta qm, int64_t q
     const int64_t beg = (int64_t)g * SL;
     const int64_t n = max<int64_t>(0, min<int64_t>(SL, n_row - beg));
     const uint32_t* src = ukeys + row * Lmax + beg;
+    // every item loads through a buffer resource of the slice's n keys (the
+    // lane is the vector offset, the item a scalar one; past n reads 0)
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, (uint32_t)n * 4u);
+    const int w0 = __builtin_amdgcn_readfirstlane(wave_id()) * ITEMS;
     uint32_t key[ITEMS];
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-        const int s = slot_of<ITEMS>(it);
-        key[it] = s < n ? src[s] : 0u;
-    }
+    for (int it = 0; it < ITEMS; ++it) key[it] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_id() * 4, (w0 + it) * 256, 0);
     const int want = TO_CAND ? K1 : k;
     const Threshold th = wg_bucket_select<NT, ITEMS>(key, want, sm);
     if (TO_CAND) {
@@ -229,9 +230,8 @@ __global__ __launch_bounds__(NT) void flat_select_kernel(QueryMeta qm, int64_t q
 // [g*G, (g+1)*G) of S_in (G*K1 keys) and keeps the top K1 (TO_CAND) or
 // writes the final top-k.
 template <int NT, int ITEMS, bool TO_CAND>
-__global__ __launch_bounds__(NT) void cand_select_kernel(int64_t q0, const uint32_t* in_key, const int32_t* in_tok,
-                                                         int S_in, int G, int k, int K1, uint32_t* out_key,
-                                                         int32_t* out_tok, int32_t* out_idx, float* out_scores)
+HISA_INLINE void cand_select_body(int64_t q0, const uint32_t* in_key, const int32_t* in_tok, int S_in, int G, int k,
+                                  int K1, uint32_t* out_key, int32_t* out_tok, int32_t* out_idx, float* out_scores)
 {
     __shared__ BucketSmem<NT> sm;
     const int64_t row = blockIdx.x;
@@ -240,12 +240,11 @@ __global__ __launch_bounds__(NT) void cand_select_kernel(int64_t q0, const uint3
     const int n = max(0, min(G, S_in - s0)) * K1;
     const uint32_t* kin = in_key + ((int64_t)row * S_in + s0) * K1;
     const int32_t* tin = in_tok + ((int64_t)row * S_in + s0) * K1;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(kin, (uint32_t)n * 4u);     // past n reads 0
+    const int w0 = __builtin_amdgcn_readfirstlane(wave_id()) * ITEMS;
     uint32_t key[ITEMS];
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-        const int s = slot_of<ITEMS>(it);
-        key[it] = s < n ? kin[s] : 0u;
-    }
+    for (int it = 0; it < ITEMS; ++it) key[it] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_id() * 4, (w0 + it) * 256, 0);
     const Threshold th = wg_bucket_select<NT, ITEMS>(key, TO_CAND ? K1 : k, sm);
     if (TO_CAND) {
         uint32_t* ok = out_key + (row * gridDim.y + g) * K1;
@@ -272,16 +271,61 @@ __global__ __launch_bounds__(NT) void cand_select_kernel(int64_t q0, const uint3
     }
 }
 
+template <int NT, int ITEMS, bool TO_CAND>
+__global__ __launch_bounds__(NT) void flat_select_kernel(QueryMeta qm, int64_t q0, const uint32_t* ukeys,
+                                                         int64_t Lmax, int SL, int k, int K1, uint32_t* cand_key,
+                                                         int32_t* cand_tok, int32_t* out_idx, float* out_scores)
+{
+    flat_select_body<NT, ITEMS, TO_CAND>(qm, q0, ukeys, Lmax, SL, k, K1, cand_key, cand_tok, out_idx, out_scores);
+}
+
+template <int NT, int ITEMS, bool TO_CAND>
+__global__ __launch_bounds__(NT) void cand_select_kernel(int64_t q0, const uint32_t* in_key, const int32_t* in_tok,
+                                                         int S_in, int G, int k, int K1, uint32_t* out_key,
+                                                         int32_t* out_tok, int32_t* out_idx, float* out_scores)
+{
+    cand_select_body<NT, ITEMS, TO_CAND>(q0, in_key, in_tok, S_in, G, k, K1, out_key, out_tok, out_idx, out_scores);
+}
+
+// The 512-thread forms (many rows, 32 keys per thread) held to six waves per
+// SIMD, as the HISA top-k's many-row form: three slices share a CU instead
+// of one (150 VGPRs) and hide each other's barrier and LDS latency
+// (measured, 32K prefill: level selects 3.47 -> 2.95 ms; four waves per
+// SIMD 3.51 ms).
+template <int NT, int ITEMS, bool TO_CAND>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 8))) void flat_select_many_kernel(
+    QueryMeta qm, int64_t q0, const uint32_t* ukeys, int64_t Lmax, int SL, int k, int K1, uint32_t* cand_key,
+    int32_t* cand_tok, int32_t* out_idx, float* out_scores)
+{
+    flat_select_body<NT, ITEMS, TO_CAND>(qm, q0, ukeys, Lmax, SL, k, K1, cand_key, cand_tok, out_idx, out_scores);
+}
+
+template <int NT, int ITEMS, bool TO_CAND>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 8))) void cand_select_many_kernel(
+    int64_t q0, const uint32_t* in_key, const int32_t* in_tok, int S_in, int G, int k, int K1, uint32_t* out_key,
+    int32_t* out_tok, int32_t* out_idx, float* out_scores)
+{
+    cand_select_body<NT, ITEMS, TO_CAND>(q0, in_key, in_tok, S_in, G, k, K1, out_key, out_tok, out_idx, out_scores);
+}
+
 template <int NT, int ITEMS>
 static hipError_t launch_flat_level(const QueryMeta& qm, int64_t q0, int64_t nq, const uint32_t* ukeys, int64_t Lmax,
                                     int SL, int S, int k, int K1, uint32_t* ck, int32_t* ct, int32_t* out_idx,
                                     float* out_scores, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1)
 {
-    if (S > 1)
-        return launch_k(flat_select_kernel<NT, ITEMS, true>, dim3((unsigned)nq, (unsigned)S), dim3(NT), stream, ev0,
+    if constexpr (NT == 512) {
+        if (S > 1)
+            return launch_k(flat_select_many_kernel<NT, ITEMS, true>, dim3((unsigned)nq, (unsigned)S), dim3(NT),
+                            stream, ev0, ev1, qm, q0, ukeys, Lmax, SL, k, K1, ck, ct, out_idx, out_scores);
+        return launch_k(flat_select_many_kernel<NT, ITEMS, false>, dim3((unsigned)nq, 1u), dim3(NT), stream, ev0,
                         ev1, qm, q0, ukeys, Lmax, SL, k, K1, ck, ct, out_idx, out_scores);
-    return launch_k(flat_select_kernel<NT, ITEMS, false>, dim3((unsigned)nq, 1u), dim3(NT), stream, ev0, ev1, qm, q0,
-                    ukeys, Lmax, SL, k, K1, ck, ct, out_idx, out_scores);
+    } else {
+        if (S > 1)
+            return launch_k(flat_select_kernel<NT, ITEMS, true>, dim3((unsigned)nq, (unsigned)S), dim3(NT), stream,
+                            ev0, ev1, qm, q0, ukeys, Lmax, SL, k, K1, ck, ct, out_idx, out_scores);
+        return launch_k(flat_select_kernel<NT, ITEMS, false>, dim3((unsigned)nq, 1u), dim3(NT), stream, ev0, ev1, qm,
+                        q0, ukeys, Lmax, SL, k, K1, ck, ct, out_idx, out_scores);
+    }
 }
 
 template <int NT, int ITEMS>
@@ -289,11 +333,19 @@ static hipError_t launch_cand_level(int64_t q0, int64_t nq, const uint32_t* ik, 
                                     int S_out, int k, int K1, uint32_t* ok, int32_t* otok, int32_t* out_idx,
                                     float* out_scores, hipStream_t stream, hipEvent_t ev1)
 {
-    if (S_out > 1)
-        return launch_k(cand_select_kernel<NT, ITEMS, true>, dim3((unsigned)nq, (unsigned)S_out), dim3(NT), stream,
-                        nullptr, ev1, q0, ik, itok, S_in, G, k, K1, ok, otok, out_idx, out_scores);
-    return launch_k(cand_select_kernel<NT, ITEMS, false>, dim3((unsigned)nq, 1u), dim3(NT), stream, nullptr, ev1, q0,
-                    ik, itok, S_in, G, k, K1, ok, otok, out_idx, out_scores);
+    if constexpr (NT == 512) {
+        if (S_out > 1)
+            return launch_k(cand_select_many_kernel<NT, ITEMS, true>, dim3((unsigned)nq, (unsigned)S_out), dim3(NT),
+                            stream, nullptr, ev1, q0, ik, itok, S_in, G, k, K1, ok, otok, out_idx, out_scores);
+        return launch_k(cand_select_many_kernel<NT, ITEMS, false>, dim3((unsigned)nq, 1u), dim3(NT), stream, nullptr,
+                        ev1, q0, ik, itok, S_in, G, k, K1, ok, otok, out_idx, out_scores);
+    } else {
+        if (S_out > 1)
+            return launch_k(cand_select_kernel<NT, ITEMS, true>, dim3((unsigned)nq, (unsigned)S_out), dim3(NT),
+                            stream, nullptr, ev1, q0, ik, itok, S_in, G, k, K1, ok, otok, out_idx, out_scores);
+        return launch_k(cand_select_kernel<NT, ITEMS, false>, dim3((unsigned)nq, 1u), dim3(NT), stream, nullptr, ev1,
+                        q0, ik, itok, S_in, G, k, K1, ok, otok, out_idx, out_scores);
+    }
 }
 
 FlatPlan flat_plan(int64_t nq, int64_t Lmax, int k)
