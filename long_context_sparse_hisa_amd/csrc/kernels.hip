@@ -219,12 +219,15 @@ __global__ __launch_bounds__(NT) void stage1_select_kernel(QueryMeta qm, const u
     if (FUSED) {
         uint32_t q[32];
         load_query(qm.queries + i * kDim, q);
+        // every item scores a representative (outside 1 .. c-2 the nearest
+        // free one; c >= m >= 3 here), masked after: no branch around loads
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
             const int64_t b = slot_of<ITEMS>(it);
-            key[it] = (b >= 1 && b <= c - 2)
-                          ? score_key(dot64_packed(q, reinterpret_cast<const uint4*>(reps + (qi.rep_off + b) * kDim)))
-                          : 0u;
+            const int64_t bc = min<int64_t>(max<int64_t>(b, 1), c - 2);
+            const uint32_t kk =
+                score_key(dot64_packed(q, reinterpret_cast<const uint4*>(reps + (qi.rep_off + bc) * kDim)));
+            key[it] = (b >= 1 && b <= c - 2) ? kk : 0u;
         }
     } else {
         // every item loads (through a buffer resource: the lane is the
@@ -666,12 +669,18 @@ __global__ __launch_bounds__(1024) void select_score_kernel(QueryMeta qm, const 
     if (!qi.valid || c + 1 <= m) {
         for (int r = threadIdx.x; r < m; r += NT) s_kept[r] = r <= c ? r : -1;
     } else {
-        const float* sg = sigma + row * Mmax;
+        // every item loads (buffer resource over the row: the lane is the
+        // vector offset, the item a scalar one), then slots outside 1 .. c-2
+        // are masked
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(sigma + row * Mmax, (uint32_t)Mmax * 4u);
+        const int w0 = __builtin_amdgcn_readfirstlane(wave_id()) * ITEMS;
+        const int hi = (int)(c - 2);
         uint32_t key[ITEMS];
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
-            const int64_t b = slot_of<ITEMS>(it);
-            key[it] = (b >= 1 && b <= c - 2) ? score_key(sg[b]) : 0u;
+            const int b = ((w0 + it) << 6) + lane_id();
+            const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, lane_id() * 4, (w0 + it) * 256, 0));
+            key[it] = (b >= 1 && b <= hi) ? score_key(v) : 0u;
         }
         const Threshold th = wg_bucket_select<NT, ITEMS>(key, m - 3, sm);
         wg_emit_selected<NT, ITEMS>(key, th, sm, m - 3, [&](int slot, uint32_t, int rank) { s_kept[1 + rank] = slot; });
