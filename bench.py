@@ -139,7 +139,7 @@ def flat_stage_bytes(q_pos, k):
 # ---- measured HBM traffic ----------------------------------------------------------
 
 # kernel symbol that carries each stage
-STAGE_KERNEL = {"block_stage": ("stage1_select_kernel", "stage1_tile_kernel", "block_score"),
+STAGE_KERNEL = {"block_stage": ("stage1_select_kernel", "stage1_select_many_kernel", "stage1_tile_kernel", "block_score"),
                 "token_scores": ("select_score_kernel", "stage2_tile_kernel"),
                 "token_topk": ("topk_rows_kernel", "topk_rows_many_kernel"),
                 "select_and_scores": ("decode_fused_kernel", "decode_step_kernel"),
@@ -804,7 +804,7 @@ def supplementary_block_scoring(nsteps, torch, hisa_mod, device_mod, synth):
             "causal_block_pairs": int((pos // w.B + 1).sum()), "block_flops": flops,
             "stage_ms": st, "call_ms": float(sum(st.values())),
             "block_stage": {"kernels": "block_score_tile_kernel (bf16 MFMA, scores into a row per query) + "
-                                       "stage1_select_kernel (top-m from each row)",
+                                       "stage1_select_many_kernel (top-m from each row)",
                             "achieved_tflops": tflops, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                             "frac": tflops / MFMA_BF16_PEAK_TFLOPS},
             "valid_indices": nvalid, "steps": nsteps}

@@ -187,9 +187,9 @@ __global__ __launch_bounds__(kThreads) void block_score_append_kernel(QueryMeta 
 // representatives itself; otherwise it reads the scores from sigma.
 
 template <int NT, int ITEMS, bool FUSED>
-__global__ __launch_bounds__(NT) void stage1_select_kernel(QueryMeta qm, const uint16_t* reps, int64_t q0, int lb,
-                                                           int m, int64_t Mmax, const float* sigma, int32_t* sel,
-                                                           RowInfo* rinfo, int32_t* out_blocks)
+HISA_INLINE void stage1_select_body(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int lb, int m,
+                                    int64_t Mmax, const float* sigma, int32_t* sel, RowInfo* rinfo,
+                                    int32_t* out_blocks)
 {
     __shared__ BucketSmem<NT> sm;
     const int64_t row = blockIdx.x;
@@ -262,12 +262,35 @@ __global__ __launch_bounds__(NT) void stage1_select_kernel(QueryMeta qm, const u
 }
 
 template <int NT, int ITEMS, bool FUSED>
+__global__ __launch_bounds__(NT) void stage1_select_kernel(QueryMeta qm, const uint16_t* reps, int64_t q0, int lb,
+                                                           int m, int64_t Mmax, const float* sigma, int32_t* sel,
+                                                           RowInfo* rinfo, int32_t* out_blocks)
+{
+    stage1_select_body<NT, ITEMS, FUSED>(qm, reps, q0, lb, m, Mmax, sigma, sel, rinfo, out_blocks);
+}
+
+// The select from sigma for many rows of 32 scores per thread, held to six
+// waves per SIMD like the many-row token top-k (148 VGPRs otherwise: three
+// rows per CU instead of six).
+template <int NT, int ITEMS, bool FUSED>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 8))) void stage1_select_many_kernel(
+    QueryMeta qm, const uint16_t* reps, int64_t q0, int lb, int m, int64_t Mmax, const float* sigma, int32_t* sel,
+    RowInfo* rinfo, int32_t* out_blocks)
+{
+    stage1_select_body<NT, ITEMS, FUSED>(qm, reps, q0, lb, m, Mmax, sigma, sel, rinfo, out_blocks);
+}
+
+template <int NT, int ITEMS, bool FUSED, bool MANY = false>
 static hipError_t launch_stage1_items(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb,
                                       int m, int64_t Mmax, const float* sigma, int32_t* sel, RowInfo* rinfo,
                                       int32_t* out_blocks, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1)
 {
-    return launch_k(stage1_select_kernel<NT, ITEMS, FUSED>, dim3((unsigned)nq), dim3(NT), stream, ev0, ev1, qm, reps,
-                    q0, lb, m, Mmax, sigma, sel, rinfo, out_blocks);
+    if constexpr (MANY)
+        return launch_k(stage1_select_many_kernel<NT, ITEMS, FUSED>, dim3((unsigned)nq), dim3(NT), stream, ev0, ev1,
+                        qm, reps, q0, lb, m, Mmax, sigma, sel, rinfo, out_blocks);
+    else
+        return launch_k(stage1_select_kernel<NT, ITEMS, FUSED>, dim3((unsigned)nq), dim3(NT), stream, ev0, ev1, qm,
+                        reps, q0, lb, m, Mmax, sigma, sel, rinfo, out_blocks);
 }
 
 // Many queries (prefill): 16 consecutive query rows form a tile, one
@@ -573,8 +596,8 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
             return launch_stage1_items<256, 16, false>(qm, reps, q0, nq, lb, m, Mmax, sigma, sel, rinfo, out_blocks,
                                                        stream, nullptr, t.stop);
         if (Mmax <= 8192)
-            return launch_stage1_items<256, 32, false>(qm, reps, q0, nq, lb, m, Mmax, sigma, sel, rinfo, out_blocks,
-                                                       stream, nullptr, t.stop);
+            return launch_stage1_items<256, 32, false, true>(qm, reps, q0, nq, lb, m, Mmax, sigma, sel, rinfo,
+                                                             out_blocks, stream, nullptr, t.stop);
         return launch_stage1_items<512, 32, false>(qm, reps, q0, nq, lb, m, Mmax, sigma, sel, rinfo, out_blocks,
                                                    stream, nullptr, t.stop);
     }
