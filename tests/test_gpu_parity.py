@@ -660,6 +660,37 @@ def test_supplementary_block_scoring_shape_sampled():
     _check_phase(w, cache, w.phases[0], w.k, w.m, False, rows=rows, label="supp", one_chunk_limit=16 << 30)
 
 
+@pytest.mark.parametrize("B,m,k", [(64, 12, 500), (128, 64, 2048), (16, 40, 640)])
+def test_few_hundred_packed_queries(B, m, k):
+    """A few hundred queries (300, fewer than 512: every query split over
+    several workgroups) over packed sequences of ragged lengths with invalid
+    queries mixed in, with at most 2048 blocks: the fused selection and
+    token scores, then the many-row top-k."""
+    print("few hundred packed B=%d m=%d k=%d" % (B, m, k), flush=True)
+    dv = _dev()
+    nseq = 9
+    g = np.random.default_rng(B * 3 + m)
+    lens = g.integers(300, 6000, nseq).astype(np.int64)
+    w = synth.decode_batch(nseq=nseq, L=int(lens.max()), seed=46, B=B, m=m, k=k)
+    cache = dv.DeviceCache(w, B=B)
+    cache.set_lengths(lens)
+    cache.pool()
+    nq = 300
+    q_seq = g.integers(0, nseq, nq).astype(np.int32)
+    q_pos = (g.random(nq) * lens[q_seq]).astype(np.int64)
+    q_pos[::37] = lens[q_seq[::37]] + 5                 # past the sequence: invalid, a -1 row
+    queries = synth.to_bf16(g.standard_normal((nq, synth.D)).astype(np.float32))
+    ph = synth.Phase("p", queries, q_pos, q_seq)
+    bad = np.zeros(nq, bool)
+    bad[::37] = True
+    for flat in (False, True):
+        idx, sc, blk = _run(cache, ph, k, m, flat)
+        assert np.all(idx[bad] == -1) and np.all(np.isnan(sc[bad]))
+        if not flat:
+            assert np.all(blk[bad] == -1)
+        _check_phase(w, cache, ph, k, m, flat, rows=np.nonzero(~bad)[0], label="fewhundred", props=False)
+
+
 @pytest.mark.parametrize("n_out", [16, 300])
 def test_outlier_scores_stretch_the_bins(n_out):
     """A few keys along each decode query (score about 6 |q|^2, far above
