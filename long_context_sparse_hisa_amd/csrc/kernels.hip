@@ -397,11 +397,14 @@ __global__ __launch_bounds__(64 * kS1MaxWaves) void stage1_tile_kernel(QueryMeta
                 }
                 continue;
             }
+            // every item reads its score (b < 64 * ITEMS lies inside the LDS
+            // row) and is masked after: no branch around the reads
             uint32_t key[ITEMS];
 #pragma unroll
             for (int it = 0; it < ITEMS; ++it) {
                 const int b = it * 64 + lane;
-                key[it] = (b >= 1 && b <= cr - 2) ? score_key(sc[rr * RS + b]) : 0u;
+                const uint32_t kk = score_key(sc[rr * RS + b]);
+                key[it] = (b >= 1 && b <= cr - 2) ? kk : 0u;
             }
             wave_select<ITEMS>(key, m - 3, ws, [&](int slot, uint32_t, int rank) {
                 srow[1 + rank] = slot;
