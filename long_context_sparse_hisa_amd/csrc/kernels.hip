@@ -1264,12 +1264,13 @@ HISA_INLINE void topk_rows_body(const uint32_t* ukeys, int N, int k, const int32
     } else {
         // the keys and the kept-block list load together; slots of -1 list
         // entries (a suffix of the list) hold no candidate and are masked after
+        // every item loads through a buffer resource of the row's N keys
+        // (the lane is the vector offset, the item a scalar one; slots past
+        // N read 0)
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, (uint32_t)N * 4u);
         uint32_t key[ITEMS];
 #pragma unroll
-        for (int it = 0; it < ITEMS; ++it) {
-            const int s = slot_of<ITEMS>(it);
-            key[it] = s < N ? src[s] : 0u;
-        }
+        for (int it = 0; it < ITEMS; ++it) key[it] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, (g0 + it) * 256, 0);
         if (sel) {
             int cnt = 0;
             for (int i = lane; i < m; i += 64) {
