@@ -65,3 +65,20 @@ def test_traffic_lookup_takes_the_kernel_the_step_runs(tmp_path):
     # a changed kernel source voids the figure
     (src / "k.hip").write_text("// kernels, edited\n")
     assert bench.measured_traffic(root, "w", "decode/select_and_scores", fused_step=True) is None
+
+
+def test_stage_names_follow_the_library_split():
+    # few queries with at most 2048 blocks: stage 1 and the token scores are
+    # one kernel (stage 1 of the events); otherwise three stages
+    assert bench.hisa_stage_names(16, 32768, 128) == {1: "select_and_scores", 2: "token_topk"}
+    assert bench.hisa_stage_names(256, 32768, 128) == {1: "select_and_scores", 2: "token_topk"}
+    assert bench.hisa_stage_names(16, 1 << 20, 128) == dict(enumerate(bench.STAGES_HISA))
+    assert bench.hisa_stage_names(4096, 32768, 128) == dict(enumerate(bench.STAGES_HISA))
+
+
+def test_many_row_kernels_carry_their_stage():
+    # the many-row forms of the top-k and of the select from scores are
+    # looked up under their stages like the plain forms
+    assert any("topk_rows_many_kernel" == s for s in bench.STAGE_KERNEL["token_topk"])
+    assert any("stage1_select_many_kernel" == s for s in bench.STAGE_KERNEL["block_stage"])
+    assert bench.DECODE_FOLD_MAX_SEQS == 64
