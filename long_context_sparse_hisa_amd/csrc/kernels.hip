@@ -438,17 +438,17 @@ static hipError_t launch_stage1_tile_items(const QueryMeta& qm, const uint16_t* 
 }
 
 // Many queries with more blocks than stage1_tile_kernel holds in LDS: the
-// representative scores on the bf16 MFMA into sigma [nq, Mmax], for
-// stage1_select_kernel to select from.  A wave takes 64 consecutive query
-// rows (four 16-row sub-tiles, the B operands, loaded once) and a range of
-// 16-block tiles; each representative tile it loads (the A operand) feeds
-// the two v_mfma_f32_16x16x32_bf16 of every sub-tile (d = 64).  Lane l
-// receives blocks 4*(l/16)..+4 of the tile for query row l%16 of a
-// sub-tile and stores them as one 16-byte vector.  Tiles past the largest
-// causal block of the walked rows are not scored; rows of several
-// sequences are walked one sequence at a time.  Slot 0 of a valid row
-// holds 1 instead of block 0's score (block 0 is forced, never a free
-// candidate; select_score_kernel reads the flag).
+// representative scores on the bf16 MFMA into sigma [nq, Mmax], for the
+// stage-1 select (or select_score_kernel) to select from.  A wave takes 64
+// consecutive query rows (four 16-row sub-tiles, the B operands, loaded
+// once) and a range of 16-block tiles; each representative tile it loads
+// (the A operand) feeds the two v_mfma_f32_16x16x32_bf16 of every sub-tile
+// (d = 64).  Lane l receives blocks 4*(l/16)..+4 of the tile for query row
+// l%16 of a sub-tile and stores them as one 16-byte vector.  Tiles past the
+// largest causal block of the walked rows are not scored; rows of several
+// sequences are walked one sequence at a time.  Slot 0 of a valid row holds
+// 1 instead of block 0's score (block 0 is forced, never a free candidate;
+// select_score_kernel reads the flag).
 constexpr int kBsRows = 64;
 constexpr int kBsWaves = 4;
 constexpr int64_t kBsTargetWaves = 8192;
