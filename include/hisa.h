@@ -141,7 +141,9 @@ typedef struct hisa_index_args {
     const int64_t* seq_rep_off;  /* [nseq] first rep row of each sequence; NULL if nseq == 1: 0 */
     const int64_t* seq_len;      /* [nseq] keys in each sequence; NULL if nseq == 1: max_len */
     int32_t nseq;                /* >= 1 */
-    int64_t max_len;             /* HOST bound: every seq_len <= max_len <= HISA_MAX_LEN */
+    int64_t max_len;             /* HOST bound: every seq_len <= max_len <= HISA_MAX_LEN;
+                                    HISA also ceil(max_len / B) <= HISA_MAX_CANDIDATES
+                                    blocks (2M keys at B = 128, 256K at B = 16) */
     int32_t d;                   /* 64 */
     int32_t B;                   /* block size (HISA), power of two in [16, 256] */
     int32_t m;                   /* kept blocks (HISA), 3 <= m, m*B <= HISA_MAX_CANDIDATES */
@@ -183,8 +185,8 @@ int hisa_workspace_bytes(const hisa_index_args* a, int flat, size_t* bytes, size
  * the kept blocks, top-k (stage-1 and stage-2 paragraphs of the HISA
  * summary).
  * Errors: INVALID_ARG (null required pointer, nq < 0, nseq < 1, m < 3,
- *         k < 1, m*B < k, max_len < 1), UNSUPPORTED (d, B, k, m*B or
- *         max_len beyond the limits above), WORKSPACE.
+ *         k < 1, m*B < k, max_len < 1), UNSUPPORTED (d, B, k, m*B,
+ *         max_len or its block count beyond the limits above), WORKSPACE.
  */
 int hisa_index(const hisa_index_args* a, void* stream);
 

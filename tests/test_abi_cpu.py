@@ -67,6 +67,7 @@ def _rc(fn, a):
     ("nseq", 2, hisa.HISA_ERR_INVALID_ARG),        # several sequences need offsets
     ("max_len", 0, hisa.HISA_ERR_INVALID_ARG),
     ("max_len", (1 << 30) + 1, hisa.HISA_ERR_UNSUPPORTED),
+    ("max_len", 16384 * 128 + 1, hisa.HISA_ERR_UNSUPPORTED),  # 16385 blocks of 128
     ("queries", None, hisa.HISA_ERR_INVALID_ARG),
     ("reps", None, hisa.HISA_ERR_INVALID_ARG),
     ("out_idx", None, hisa.HISA_ERR_INVALID_ARG),

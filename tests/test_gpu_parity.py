@@ -642,6 +642,27 @@ def test_many_queries_long_rows(nq):
     _check_phase(w, cache, w.phases[0], k, m, False, label="longrows%d" % nq)
 
 
+@pytest.mark.parametrize("nq", [12, 600])
+def test_largest_block_count(nq):
+    """A sequence of exactly the most blocks the index calls accept (16,384
+    blocks of 16 over 262,144 keys): the last query sees every block.  With
+    12 queries each gets its own score row; with 600 the many-row
+    selection takes rows of 16,384 scores.  Sampled rows, HISA and flat,
+    against the oracle."""
+    print("largest block count nq=%d" % nq, flush=True)
+    dv = _dev()
+    L, B, m, k = 262144, 16, 64, 512
+    g = np.random.default_rng(46 + nq)
+    pos = np.sort(g.choice(np.arange(1000, L), nq, replace=False)).astype(np.int64)
+    pos[-1] = L - 1
+    w = synth.chunked_prefill(L=L, seed=47, B=B, m=m, k=k, q_positions=pos)
+    cache = dv.DeviceCache(w, B=B)
+    cache.pool()
+    rows = sorted(set([0, nq - 1] + list(g.choice(nq, min(nq, 30), replace=False))))
+    for flat in (False, True):
+        _check_phase(w, cache, w.phases[0], k, m, flat, rows=rows, label="maxblocks%d" % nq)
+
+
 def test_supplementary_block_scoring_shape_sampled():
     """The supplementary block-scoring shape at full size: the last 32,768
     positions of a 1,048,576-key MoG sequence in one call (8,064-8,192
