@@ -146,6 +146,36 @@ STAGE_KERNEL = {"block_stage": ("stage1_select_kernel", "stage1_select_many_kern
                 "flat_scores": ("flat_score_kernel", "flat_score_mfma_kernel")}
 
 
+def stream_ceiling(n, torch, reps=20):
+    """HBM bandwidth of plain streaming kernels over n bytes, timed with HIP
+    events on torch's stream (launch cost is negligible at this size): full
+    reads (a sum, a maximum and a matrix-vector product over n bytes of
+    float32), a device-to-device copy and an elementwise dst = src + 1 (n
+    read + n written each), and a fill (n written)."""
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    mat = src.view(-1, 4096)
+    vec = torch.ones(4096, dtype=torch.float32, device="cuda:0")
+    out = {"bytes": n, "repeats": reps, "peak_gbps": HBM_PEAK_GBPS}
+    for name, fn, moved in (("read_sum", lambda: src.sum(), n), ("read_amax", lambda: src.amax(), n),
+                            ("read_gemv", lambda: torch.mv(mat, vec), n),
+                            ("copy", lambda: dst.copy_(src), 2 * n),
+                            ("add_one", lambda: torch.add(src, 1.0, out=dst), 2 * n),
+                            ("write_fill", lambda: dst.fill_(2.0), n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": ms, "gbps": moved / ms / 1e6, "frac": moved / ms / 1e6 / HBM_PEAK_GBPS}
+    return out
+
+
 def kernel_source_hash(root):
     import glob
     import hashlib
@@ -848,6 +878,9 @@ def main():
                     help="copies of the attention keys and values rotated over")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device (a known-size reference for HBM counters)")
+    ap.add_argument("--stream-ceiling", type=int, default=0, metavar="MIB",
+                    help="only time plain streaming kernels over MIB MiB (a full read, a copy): the HBM "
+                         "bandwidth simple kernels reach on this GPU, beside the 8 TB/s peak")
     args = ap.parse_args()
     global STEPS_PER_GRAPH
     STEPS_PER_GRAPH = max(1, args.steps_per_graph)
@@ -872,6 +905,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
+        return
+    if args.stream_ceiling:
+        print(json.dumps(stream_ceiling(args.stream_ceiling << 20, torch)), flush=True)
         return
     hisa.lib()
     root = os.path.dirname(os.path.abspath(__file__))
