@@ -663,6 +663,27 @@ def test_largest_block_count(nq):
         _check_phase(w, cache, w.phases[0], k, m, flat, rows=rows, label="maxblocks%d" % nq)
 
 
+@pytest.mark.parametrize("nq", [8, 600])
+def test_largest_k(nq):
+    """The largest k the index calls accept, 16,384, equal to m*B (128
+    blocks of 128): HISA returns every visible token of its kept blocks, and
+    the flat indexer the 16,384 best of up to 40,000 keys.  Few queries (one
+    workgroup per row of 16,384 candidates) and many (the many-row forms).
+    Sampled rows, HISA and flat, against the oracle."""
+    print("largest k nq=%d" % nq, flush=True)
+    dv = _dev()
+    L, B, m, k = 40000, 128, 128, 16384
+    g = np.random.default_rng(48 + nq)
+    pos = np.sort(g.choice(np.arange(100, L), nq, replace=False)).astype(np.int64)
+    pos[-1] = L - 1
+    w = synth.chunked_prefill(L=L, seed=49, B=B, m=m, k=k, q_positions=pos)
+    cache = dv.DeviceCache(w, B=B)
+    cache.pool()
+    rows = sorted(set([0, nq - 1] + list(g.choice(nq, min(nq, 24), replace=False))))
+    for flat in (False, True):
+        _check_phase(w, cache, w.phases[0], k, m, flat, rows=rows, label="maxk%d" % nq)
+
+
 def test_supplementary_block_scoring_shape_sampled():
     """The supplementary block-scoring shape at full size: the last 32,768
     positions of a 1,048,576-key MoG sequence in one call (8,064-8,192
