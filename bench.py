@@ -720,6 +720,12 @@ def measure(S, args, torch, label):
     nst = max(4, min(args.stage_steps, S.replicas * 4))
     log("%s: per-stage HIP-event timing over %d eager steps each" % (label, nst))
     h_stage = stage_times(S, False, nst, torch)
+    h_stage_two = None
+    if S.fused_step:
+        # the append and the index kernels apart: the two-call form
+        S.fused_step = False
+        h_stage_two = stage_times(S, False, nst, torch)
+        S.fused_step = True
     f_stage = stage_times(S, True, nst, torch)
     qps = S.q_per_step / (h_ms * 1e-3)
     fqps = S.q_per_step / (f_ms * 1e-3)
@@ -764,16 +770,19 @@ def measure(S, args, torch, label):
     f_step_bytes = sum(b for n, b in stage_bytes.items() if n.split("/")[-1] in STAGES_FLAT) + app_bytes
 
     def per_kernel(stage):
-        return {n: {"avg_ms": v, "algorithmic_bytes": stage_bytes.get(n),
-                    "gbps": (stage_bytes[n] / (v * 1e-3) / 1e9) if n in stage_bytes and v > 0 else None}
-                for n, v in stage.items()}
+        out = {}
+        for n, v in stage.items():
+            b = app_bytes if n == "append" and app_bytes else stage_bytes.get(n)
+            out[n] = {"avg_ms": v, "algorithmic_bytes": b, "gbps": (b / (v * 1e-3) / 1e9) if b and v > 0 else None}
+        return out
 
     return {
         "workload": S.name, "description": S.desc, "queries_per_step": S.q_per_step, "replicas": S.replicas,
         "B": S.B, "m": S.m, "k": S.k,
         "hisa": {"ms_per_step": h_ms, "queries_per_s": qps, "step_bytes": h_step_bytes,
                  "hbm_gbps_step": h_step_bytes / (h_ms * 1e-3) / 1e9, "kernels": per_kernel(h_stage),
-                 "two_calls_ms_per_step": two_ms},
+                 "two_calls_ms_per_step": two_ms,
+                 "two_calls_kernels": per_kernel(h_stage_two) if h_stage_two is not None else None},
         "flat": {"ms_per_step": f_ms, "queries_per_s": fqps, "step_bytes": f_step_bytes,
                  "hbm_gbps_step": f_step_bytes / (f_ms * 1e-3) / 1e9, "kernels": per_kernel(f_stage),
                  "dominant": {"kernel": fkern, "bound": fbound, "achieved": f_achieved, "peak": fpeak,
@@ -1085,6 +1094,7 @@ def main():
         "flat": dict(res["flat"], value=res["flat"]["queries_per_s"], unit="queries/s"),
         "speedup_vs_flat": res["speedup_vs_flat"],
         "hisa_two_calls_ms_per_step": res["hisa"]["two_calls_ms_per_step"],
+        "hisa_two_calls_kernels": res["hisa"]["two_calls_kernels"],
         "step_note": ("HISA decode steps are one hisa_decode_step call (the append in the same launch as the block "
                       "selection and token scores); hisa_two_calls_ms_per_step is the same step as append + index, "
                       "the form the flat indexer's step takes"
