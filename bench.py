@@ -851,7 +851,7 @@ def supplementary_block_scoring(nsteps, torch, hisa_mod, device_mod, synth):
 
 # workloads reported beside the default one, so that one run covers the
 # 32K, 128K and 1M contexts and the large decode batch
-CONTEXT_WORKLOADS = ("decode_32k_x256", "long_context_128k", "long_decode_1m")
+CONTEXT_WORKLOADS = ("decode_32k_x256", "chunked_prefill_32k", "long_context_128k", "long_decode_1m")
 DEFAULT_REPLICAS = {"decode_32k_x16": 64, "decode_32k_x64": 16, "decode_32k_x256": 4, "long_decode_1m": 256,
                     "decode_varlen_x64": 16, "chunked_prefill_32k": 1, "long_context_128k": 1,
                     "tiny_prefill_4k": 1}
@@ -872,7 +872,8 @@ def main():
     ap.add_argument("--no-attention", action="store_true", help="skip the sparse-attention leg")
     ap.add_argument("--no-lsa", action="store_true", help="skip the LSA-Flat leg")
     ap.add_argument("--no-contexts", action="store_true",
-                    help="skip the 32K x 256, 128K and 1M workloads reported beside the default one")
+                    help="only the named workload: skip the 32K x 256, 32K prefill, 128K and 1M workloads "
+                         "reported beside the default one, its warm-cache timing and the streaming peak")
     ap.add_argument("--no-supplementary", action="store_true",
                     help="skip the supplementary block-scoring shape (32768 queries x 8192 representatives)")
     ap.add_argument("--supplementary-only", action="store_true",
@@ -997,7 +998,7 @@ def main():
         del Lg
 
     warm = None
-    if args.workload == "decode_32k_x16" and R > 1 and not args.no_warm:
+    if args.workload == "decode_32k_x16" and R > 1 and not args.no_warm and not args.no_contexts:
         # the same steps on one copy of the key cache (64 MiB), which stays
         # in the 256 MB last-level cache from one step to the next
         log("warm-cache leg: one replica")
@@ -1047,7 +1048,7 @@ def main():
         supplementary = supplementary_block_scoring(max(4, min(args.stage_steps, 8)), torch, hisa, device, synth)
 
     stream_peak = None
-    if not args.no_stream_peak:
+    if not args.no_stream_peak and not args.no_contexts:
         # after every timed region: what plain streaming kernels reach on this
         # GPU, beside the published peak, for the HBM rooflines
         log("plain streaming kernels over 4 GiB")
