@@ -76,6 +76,15 @@ def log(*a):
 
 # ---- algorithmic traffic per stage ------------------------------------------------
 
+def visible_candidates(q_pos, B, m):
+    """Candidate tokens a query at t scores: every causal key when all its
+    causal blocks are kept, otherwise m-1 whole earlier blocks and the
+    t % B + 1 visible keys of its own block (always kept)."""
+    q_pos = np.asarray(q_pos, np.int64)
+    nb = q_pos // B + 1
+    return np.where(nb <= m, q_pos + 1, (m - 1) * B + q_pos % B + 1)
+
+
 def hisa_stage_bytes(q_pos, B, m, k):
     """Algorithmic HBM bytes of the HISA stages for queries at q_pos (d = 64:
     a key or representative row is 128 bytes): inputs read once and the
@@ -85,8 +94,7 @@ def hisa_stage_bytes(q_pos, B, m, k):
     the candidate keys of its kept blocks.  Top-k: the int32 indices out."""
     q_pos = np.asarray(q_pos, np.int64)
     nb = q_pos // B + 1                                  # causal blocks
-    kept = np.minimum(nb, m)
-    cand = np.minimum(kept * B, q_pos + 1)                # <= m*B candidate tokens
+    cand = visible_candidates(q_pos, B, m)                # <= m*B candidate tokens
     block = (128 + nb * 128).sum()
     token = (128 + cand * 128).sum()
     out = len(q_pos) * k * 4
@@ -104,11 +112,11 @@ def hisa_stage_bytes(q_pos, B, m, k):
 
 def stage_flops(q_pos, B, m):
     """Algorithmic flops of the contractions: 2*64 per (query, row) pair
-    over the causal representatives (block stage), the kept candidates
-    (token stage) and every visible key (flat scores)."""
+    over the causal representatives (block stage), the visible candidates
+    of the kept blocks (token stage) and every visible key (flat scores)."""
     q_pos = np.asarray(q_pos, np.int64)
     nb = q_pos // B + 1
-    cand = np.minimum(np.minimum(nb, m) * B, q_pos + 1)
+    cand = visible_candidates(q_pos, B, m)
     return {"block_stage": float(128 * nb.sum()), "token_scores": float(128 * cand.sum()),
             "flat_scores": float(128 * (q_pos + 1).sum())}
 
@@ -736,11 +744,18 @@ def measure(S, args, torch, label):
             stage_bytes["%s/%s" % (ph.name, nm)] = b
         for nm, b in flat_stage_bytes(ph.q_pos, S.k).items():
             stage_bytes["%s/%s" % (ph.name, nm)] = b
-    stage_fl, stage_nq = {}, {}
+    stage_fl, stage_nq, stage_pairs = {}, {}, {}
     for ph in S.phases:
-        for nm, f in stage_flops(ph.q_pos, S.B, S.m).items():
+        fl = stage_flops(ph.q_pos, S.B, S.m)
+        for nm, f in fl.items():
             stage_fl["%s/%s" % (ph.name, nm)] = f
             stage_nq["%s/%s" % (ph.name, nm)] = len(ph.q_pos)
+        # (query, row) pairs each stage works through: causal representatives,
+        # kept candidates, every visible key
+        cand, vis = fl["token_scores"] / 128, fl["flat_scores"] / 128
+        for nm, v in (("block_stage", fl["block_stage"] / 128), ("token_scores", cand), ("select_and_scores", cand),
+                      ("token_topk", cand), ("flat_scores", vis), ("flat_topk", vis)):
+            stage_pairs["%s/%s" % (ph.name, nm)] = v
     # the append: the new rows read and written, the touched blocks' other
     # rows read, their representatives written
     app_bytes = 0
@@ -773,7 +788,9 @@ def measure(S, args, torch, label):
         out = {}
         for n, v in stage.items():
             b = app_bytes if n == "append" and app_bytes else stage_bytes.get(n)
-            out[n] = {"avg_ms": v, "algorithmic_bytes": b, "gbps": (b / (v * 1e-3) / 1e9) if b and v > 0 else None}
+            p = stage_pairs.get(n)
+            out[n] = {"avg_ms": v, "algorithmic_bytes": b, "gbps": (b / (v * 1e-3) / 1e9) if b and v > 0 else None,
+                      "pairs": p, "pairs_per_s": (p / (v * 1e-3)) if p and v > 0 else None}
         return out
 
     return {

@@ -27,6 +27,15 @@ def test_stage_bytes_early_queries_are_causal():
     assert b["token_ideal"] == 2 * (128 + 16 * 4) + (1 + 2) * 128 + (1 + 201) * 128
 
 
+def test_visible_candidates():
+    # every causal key while all causal blocks are kept; past that, m-1 whole
+    # blocks and the visible part of the query's own block
+    c = bench.visible_candidates(np.array([0, 200, 8191, 8192, 10000, 32767]), 128, 64)
+    assert c.tolist() == [1, 201, 8192, 63 * 128 + 1, 63 * 128 + 10000 % 128 + 1, 8192]
+    # the whole 32K causal prefill: 233,324,544 (query, candidate) pairs
+    assert int(bench.visible_candidates(np.arange(32768), 128, 64).sum()) == 233324544
+
+
 def test_stage_flops_and_bound():
     f = bench.stage_flops(np.array([32767, 200]), 128, 64)
     assert f["block_stage"] == 128 * (256 + 2)
