@@ -1065,7 +1065,7 @@ def main():
         supplementary = supplementary_block_scoring(max(4, min(args.stage_steps, 8)), torch, hisa, device, synth)
 
     stream_peak = None
-    if not args.no_stream_peak and not args.no_contexts:
+    if args.workload == "decode_32k_x16" and not args.no_stream_peak and not args.no_contexts:
         # after every timed region: what plain streaming kernels reach on this
         # GPU, beside the published peak, for the HBM rooflines
         log("plain streaming kernels over 4 GiB")

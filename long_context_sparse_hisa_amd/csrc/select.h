@@ -65,6 +65,7 @@ struct Threshold {
     uint32_t T;      // the n-th largest key (0 when every candidate is taken)
     int need_eq;     // how many keys equal to T are taken, lowest slots first
     bool all;        // n >= number of candidates: take every nonzero key
+    bool eq_all = false;   // known: every key equal to T is taken (the selection is key >= T)
 };
 
 // ---- radix select (exact fallback) ----------------------------------------------
@@ -148,7 +149,7 @@ struct BucketSmem {
     alignas(16) int list_slot[kListCap];
     uint32_t red[3][NW];
     int wave_tot[2][NW];
-    int misc[8];
+    int misc[9];
     RadixSmem<NT> radix;
 };
 
@@ -328,6 +329,7 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
         th.T = klo;
         th.need_eq = c;
         th.all = false;
+        th.eq_all = true;
         return th;
     }
     const uint32_t span = khi1 - klo;
@@ -355,11 +357,12 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
     for (int j = threadIdx.x; j < c; j += NT) {
         const uint32_t kj = sm.list_key[j];
         const int sj = sm.list_slot[j];
-        int r = 0, eq_before = 0;
+        int r = 0, eq_before = 0, eq_n = 0;
         auto step = [&](uint32_t ki, int si) {
             const bool before = ki == kj && si < sj;
             r += (ki > kj) || before;
             eq_before += before;
+            eq_n += ki == kj;
         };
         int i = 0;
 #pragma unroll 4
@@ -375,12 +378,14 @@ HISA_INLINE Threshold wg_bucket_select(const uint32_t (&key)[ITEMS], int n, Buck
         if (r == need - 1) {
             sm.misc[6] = (int)kj;
             sm.misc[7] = eq_before + 1;
+            sm.misc[8] = eq_n;
         }
     }
     __syncthreads();
     th.T = (uint32_t)sm.misc[6];
     th.need_eq = sm.misc[7];
     th.all = false;
+    th.eq_all = sm.misc[8] == sm.misc[7];   // no copy of T after the last one taken
     return th;
 }
 
@@ -401,11 +406,40 @@ HISA_INLINE int wg_emit_selected_items(const uint32_t (&key_in)[ITEMS], const Th
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) key[it] = key_in[it];
     const int w = wave_id();
+    if (th.all || th.eq_all) {
+        // the selection is key >= lo: one count per item, and each wave
+        // only needs the totals of the waves before it
+        const uint32_t lo = th.all ? 1u : th.T;
+        int wg = 0;
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) wg += __popcll(__ballot(key[it] >= lo));
+        if (lane_id() == 0) sm.wave_tot[0][w] = wg;
+        __syncthreads();
+        opaque_keys(key);
+        int r = 0, tg = 0;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+            const int g = sm.wave_tot[0][v];
+            r += v < w ? g : 0;
+            tg += g;
+        }
+        r = __builtin_amdgcn_readfirstlane(r);
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const bool take = key[it] >= lo;
+            const uint64_t b = __ballot(take);
+            const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)b, (uint32_t)r));
+            if (take && rank < limit) emit(it, key[it], rank);
+            r += __popcll(b);
+        }
+        return min(limit, tg);
+    }
     int wg = 0, we = 0;
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
         wg += __popcll(__ballot(key[it] > th.T));
-        we += __popcll(__ballot(!th.all && key[it] == th.T));
+        we += __popcll(__ballot(key[it] == th.T));
     }
     if (lane_id() == 0) {
         sm.wave_tot[0][w] = wg;
@@ -422,16 +456,18 @@ HISA_INLINE int wg_emit_selected_items(const uint32_t (&key_in)[ITEMS], const Th
         tg += g;
         te += q;
     }
-    if (th.all || te <= th.need_eq) {
-        // every key equal to the threshold is taken: selected = key >= T
-        // (or every nonzero key), ranked by one ballot per item
-        const uint32_t lo = th.all ? 1u : th.T;
+    rg = __builtin_amdgcn_readfirstlane(rg);
+    re = __builtin_amdgcn_readfirstlane(re);
+    if (te <= th.need_eq) {
+        // every key equal to the threshold is taken: selected = key >= T,
+        // ranked by one ballot per item
         int r = rg + re;
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
-            const bool take = key[it] >= lo;
+            const bool take = key[it] >= th.T;
             const uint64_t b = __ballot(take);
-            const int rank = r + count_below(b);
+            const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)b, (uint32_t)r));
             if (take && rank < limit) emit(it, key[it], rank);
             r += __popcll(b);
         }
