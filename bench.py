@@ -20,8 +20,12 @@ the sparse attention that consumes the indices (one head of dimension 128,
 bf16 queries, keys and values drawn i.i.d. N(0, 1)), timed alone and as
 index + attention steps over HISA's and over the flat indexer's output.
 
-The timed region replays one captured HIP graph per step (per replica):
-the step's kernels without host work in between.  Per-kernel durations come
+Each method's steps are timed in two launch forms and the faster counts,
+for HISA and flat alike: eager, the library calls queued back to back on
+one stream with the host ahead of the GPU (the GPU sets the pace when it is
+the slower side), and one captured HIP graph replayed per step (which wins
+where a call's host work outweighs its kernels); `--launch eager|graph`
+times one form only.  Per-kernel durations come
 from HIP start / stop events attached to the kernel dispatches of a
 separate run of eager steps (queued behind a sleep kernel so they run back
 to back); the roofline object is computed from the kernel with the largest
@@ -30,7 +34,9 @@ average duration.
 from __future__ import annotations
 
 import argparse
+import contextlib
 import ctypes
+import gc
 import json
 import os
 import sys
@@ -272,6 +278,7 @@ class Setup:
         if self.append_src is not None:
             self.seqs = [(c.seq_key_off[s], c.seq_rep_off[s], c.seq_len[s], c.seq_cap[s])
                          for s in range(c.nseq)]
+            self.seq_arr = hisa_mod.seq_array(self.seqs)      # marshalled once, reused every step
             c.append(self.append_src, update_lengths=True)   # lengths the queries see
         torch.cuda.synchronize()
         self.phases = w.phases if name != "long_decode_1m" else w.phases[:1]
@@ -318,13 +325,12 @@ class Setup:
                 events[0].attach(a)
             else:
                 a.stage_events = None
-            h.hisa_decode_step(a, self.seqs, self.append_src)
+            h.hisa_decode_step(a, self.seq_arr, self.append_src, stream)
             return
         if self.append_src is not None:
             if append_events is not None:
                 h._hiprt().hipEventRecord(append_events[0], stream)
-            h.hisa_append_keys(self.keys[r], self.reps[r], self.seqs, self.append_src, self.B,
-                               self.torch.cuda.current_stream())
+            h.hisa_append_keys(self.keys[r], self.reps[r], self.seq_arr, self.append_src, self.B, stream)
             if append_events is not None:
                 h._hiprt().hipEventRecord(append_events[1], stream)
         for p, (ic, per_rep) in enumerate(self.calls[flat]):
@@ -333,7 +339,7 @@ class Setup:
                 events[p].attach(a)
             else:
                 a.stage_events = None
-            (h.hisa_flat_index if flat else h.hisa_block_index if self.block_only else h.hisa_index)(a)
+            (h.hisa_flat_index if flat else h.hisa_block_index if self.block_only else h.hisa_index)(a, stream)
 
 
 class AttentionLeg:
@@ -415,7 +421,7 @@ class LsaLeg:
         S = self.S
         if S.append_src is not None:
             rr = r % S.replicas
-            S.h.hisa_append_keys(S.keys[rr], S.reps[rr], S.seqs, S.append_src, S.B)
+            S.h.hisa_append_keys(S.keys[rr], S.reps[rr], S.seq_arr, S.append_src, S.B)
         S.h.hisa_lsa_index(self.calls[r % self.replicas][0])
 
     def time_steps(self, steps, warmup):
@@ -426,14 +432,34 @@ class LsaLeg:
             self.run(0)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        graphs = []
         n = max(self.replicas, self.S.replicas)
-        for r in range(n):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+        out = []
+        if LAUNCH in ("graph", "best"):
+            graphs = []
+            for r in range(n):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    self.run(r)
+                graphs.append(g)
+            out.append(replay_timed(graphs, steps, warmup, torch, spg=1) * 1e3)
+            del graphs
+        if LAUNCH in ("eager", "best"):
+            # as eager_timed: every replica once, the warmup, then the timed
+            # steps back to back
+            for r in range(n):
                 self.run(r)
-            graphs.append(g)
-        return replay_timed(graphs, steps, warmup, torch, spg=1) * 1e3
+            torch.cuda.synchronize()
+            gc.collect()
+            for i in range(warmup):
+                self.run(i % n)
+            torch.cuda.synchronize()
+            with no_gc():
+                t0 = time.perf_counter()
+                for i in range(steps):
+                    self.run((warmup + i) % n)
+                torch.cuda.synchronize()
+                out.append((time.perf_counter() - t0) / steps * 1e3)
+        return min(out)
 
 
 def attention_kernel_ms(S, A, nsteps, torch):
@@ -453,6 +479,24 @@ def attention_kernel_ms(S, A, nsteps, torch):
 
 
 STEPS_PER_GRAPH = 1
+# How timed steps are launched: "eager" (each step's calls queued back to
+# back on the stream, the host running ahead of the GPU), "graph" (one
+# captured HIP graph replayed per step) or "best" (both, the faster counts:
+# eager wins where the GPU is the slower side, graphs where the host work
+# of a call outweighs its kernels)
+LAUNCH = "best"
+
+
+@contextlib.contextmanager
+def no_gc():
+    """Python's garbage collector off inside a timed region, so that no
+    collection pause lands among the timed steps (callers collect before
+    their warmup, which then brings the GPU back to its steady state)."""
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
 
 
 def capture_graphs(S, flat, torch, attn=None):
@@ -493,22 +537,67 @@ def replay_timed(graphs, steps, warmup, torch, spg=None):
     for g in graphs:
         g.replay()
     torch.cuda.synchronize()
+    gc.collect()
     reps = max(1, steps // spg)
     for i in range(max(1, warmup // spg)):
         graphs[i % n].replay()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(reps):
-        graphs[(warmup // spg + i) % n].replay()
+    with no_gc():
+        t0 = time.perf_counter()
+        for i in range(reps):
+            graphs[(warmup // spg + i) % n].replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / (reps * spg)
+
+
+def eager_timed(S, flat, steps, warmup, torch, attn=None):
+    """Seconds per step over `steps` steps whose calls are queued back to
+    back on the current stream (rotating over the replicas; the host runs
+    ahead of the GPU, so the GPU sets the pace when it is the slower side).
+    Every replica takes one step before the warmup and the timed region, so
+    that no timed step is the first on its replica."""
+    st = torch.cuda.current_stream().cuda_stream
+
+    def one(r):
+        S.step(r, flat, st)
+        if attn is not None:
+            attn.run(r, flat)
+
+    for r in range(S.replicas):
+        one(r)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / (reps * spg)
+    gc.collect()
+    for i in range(warmup):
+        one(i % S.replicas)
+    torch.cuda.synchronize()
+    with no_gc():
+        t0 = time.perf_counter()
+        for i in range(steps):
+            one((warmup + i) % S.replicas)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
 
 
-def time_method(S, flat, steps, warmup, torch, attn=None):
-    """Milliseconds per step: graph replays (one step each, rotating over
-    the replicas), bracketed by device synchronisation."""
-    graphs = capture_graphs(S, flat, torch, attn)
-    return replay_timed(graphs, steps, warmup, torch) * 1e3
+def time_forms(S, flat, steps, warmup, torch, attn=None, launch=None):
+    """{launch form: milliseconds per step}, rotating over the replicas,
+    bracketed by device synchronisation, for the forms `launch` (default
+    LAUNCH) asks for: eager steps queued back to back, one graph replay per
+    step, or both."""
+    mode = launch or LAUNCH
+    out = {}
+    for form in (("eager", "graph") if mode == "best" else (mode,)):
+        if form == "graph":
+            graphs = capture_graphs(S, flat, torch, attn)
+            out[form] = replay_timed(graphs, steps, warmup, torch) * 1e3
+            del graphs
+        else:
+            out[form] = eager_timed(S, flat, steps, warmup, torch, attn) * 1e3
+    return out
+
+
+def time_method(S, flat, steps, warmup, torch, attn=None, launch=None):
+    """Milliseconds per step in the faster of the launch forms asked for."""
+    return min(time_forms(S, flat, steps, warmup, torch, attn, launch).values())
 
 
 def stage_times(S, flat, nsteps, torch):
@@ -516,7 +605,7 @@ def stage_times(S, flat, nsteps, torch):
     start / stop HIP events the library records with each stage's kernel
     dispatches (the kernels' own execution time).  A sleep kernel holds the
     GPU while the host queues the steps, so the kernels run back to back as
-    in the graph-replayed steps."""
+    in the timed steps."""
     h = S.h
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -573,7 +662,7 @@ def row_overlap(a, b):
 def sweep_m(S, ms, steps, warmup, torch):
     """HISA at each m (k fixed) and block-only selection at the same token
     budget (m = k/B) and at HISA's candidate set (the workload's m): time
-    per step (graph replays) and overlap with the flat indexer's rows."""
+    per step and overlap with the flat indexer's rows."""
     sp = torch.cuda.current_stream().cuda_stream
     nrow = 1024                                      # rows compared (evenly spaced)
 
@@ -711,20 +800,22 @@ def cpu_baseline(S, seconds, oracle, extras=True):
 
 
 def measure(S, args, torch, label):
-    """Time HISA and the flat indexer on setup S: graph-replayed steps
-    (HISA's decode steps also as two calls), per-kernel event times, the
+    """Time HISA and the flat indexer on setup S: timed steps (HISA's
+    decode steps also as two calls), per-kernel event times, the
     roofline of each method's dominant kernel and the step's algorithmic
     bytes.  Returns the summary dict."""
-    log("%s: timing HISA: %d warmup + %d graph-replayed steps" % (label, args.warmup, args.steps))
-    h_ms = time_method(S, False, args.steps, args.warmup, torch)
+    log("%s: timing HISA: %d warmup + %d steps (launch: %s)" % (label, args.warmup, args.steps, LAUNCH))
+    h_forms = time_forms(S, False, args.steps, args.warmup, torch)
+    h_ms = min(h_forms.values())
     two_ms = None
     if S.fused_step:
         log("%s: timing HISA as two calls (append, then index)" % label)
         S.fused_step = False
         two_ms = time_method(S, False, args.steps, args.warmup, torch)
         S.fused_step = True
-    log("%s: timing flat: %d warmup + %d graph-replayed steps" % (label, args.warmup, args.steps))
-    f_ms = time_method(S, True, args.steps, args.warmup, torch)
+    log("%s: timing flat: %d warmup + %d steps (launch: %s)" % (label, args.warmup, args.steps, LAUNCH))
+    f_forms = time_forms(S, True, args.steps, args.warmup, torch)
+    f_ms = min(f_forms.values())
     nst = max(4, min(args.stage_steps, S.replicas * 4))
     log("%s: per-stage HIP-event timing over %d eager steps each" % (label, nst))
     h_stage = stage_times(S, False, nst, torch)
@@ -796,11 +887,13 @@ def measure(S, args, torch, label):
     return {
         "workload": S.name, "description": S.desc, "queries_per_step": S.q_per_step, "replicas": S.replicas,
         "B": S.B, "m": S.m, "k": S.k,
-        "hisa": {"ms_per_step": h_ms, "queries_per_s": qps, "step_bytes": h_step_bytes,
+        "hisa": {"ms_per_step": h_ms, "launch_forms_ms_per_step": h_forms, "queries_per_s": qps,
+                 "step_bytes": h_step_bytes,
                  "hbm_gbps_step": h_step_bytes / (h_ms * 1e-3) / 1e9, "kernels": per_kernel(h_stage),
                  "two_calls_ms_per_step": two_ms,
                  "two_calls_kernels": per_kernel(h_stage_two) if h_stage_two is not None else None},
-        "flat": {"ms_per_step": f_ms, "queries_per_s": fqps, "step_bytes": f_step_bytes,
+        "flat": {"ms_per_step": f_ms, "launch_forms_ms_per_step": f_forms, "queries_per_s": fqps,
+                 "step_bytes": f_step_bytes,
                  "hbm_gbps_step": f_step_bytes / (f_ms * 1e-3) / 1e9, "kernels": per_kernel(f_stage),
                  "dominant": {"kernel": fkern, "bound": fbound, "achieved": f_achieved, "peak": fpeak,
                               "unit": funit, "frac": f_achieved / fpeak,
@@ -895,8 +988,11 @@ def main():
                     help="skip the supplementary block-scoring shape (32768 queries x 8192 representatives)")
     ap.add_argument("--supplementary-only", action="store_true",
                     help="only the supplementary block-scoring shape")
+    ap.add_argument("--launch", choices=("best", "eager", "graph"), default="best",
+                    help="timed steps launched eagerly back to back, as one graph replay per step, or both with "
+                         "the faster counted (default)")
     ap.add_argument("--steps-per-graph", type=int, default=1,
-                    help="consecutive steps captured in one graph (1: one replay per step, the serving form)")
+                    help="with --launch graph: consecutive steps captured in one graph (1: one replay per step)")
     ap.add_argument("--lsa-replicas", type=int, default=8, help="copies of the LSA bucket cache rotated over")
     ap.add_argument("--sweep-m", default=None, metavar="M1,M2,...",
                     help="instead of the default line: HISA at each m and block-only selection, time per "
@@ -913,8 +1009,9 @@ def main():
                     help="only time plain streaming kernels over MIB MiB (a full read, a copy): the HBM "
                          "bandwidth simple kernels reach on this GPU, beside the 8 TB/s peak")
     args = ap.parse_args()
-    global STEPS_PER_GRAPH
+    global STEPS_PER_GRAPH, LAUNCH
     STEPS_PER_GRAPH = max(1, args.steps_per_graph)
+    LAUNCH = args.launch
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the indexer here runs on a single MI355X and has no "
@@ -1117,7 +1214,15 @@ def main():
                       "selection and token scores); hisa_two_calls_ms_per_step is the same step as append + index, "
                       "the form the flat indexer's step takes"
                       if res["hisa"]["two_calls_ms_per_step"] is not None else None),
-        "timing_note": "every captured graph is replayed once before the warmup and the timed replays",
+        "timing_note": {"best": "each method's steps are timed in two launch forms and the faster counts, for HISA "
+                                "and flat alike (launch_forms_ms_per_step holds both): eager, the calls queued back "
+                                "to back on one stream with the host ahead of the GPU, every replica taking one "
+                                "untimed step first; and one captured HIP graph replayed per step, every graph "
+                                "replayed once first. The garbage collector is off inside timed regions.",
+                        "eager": "steps launched eagerly, back to back on one stream; every replica takes one "
+                                 "untimed step before the warmup and the timed steps",
+                        "graph": "one captured graph replayed per step; every graph is replayed once before the "
+                                 "warmup and the timed replays"}[LAUNCH],
         "warm": warm,
         "attention": attention,
         "lsa_flat": lsa,

@@ -140,9 +140,22 @@ def _dev(t, what: str, nbytes_per_elem=None):
 
 
 def _stream(stream):
+    """A torch stream, a raw hipStream_t handle (int), or None for torch's
+    current stream."""
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def seq_array(seqs):
+    """The host hisa_seq array of the append calls from (key_off, rep_off,
+    len, capacity) tuples; an existing hisa_seq array is returned as it is
+    (build it once to keep per-call marshalling out of a decode loop)."""
+    if isinstance(seqs, ctypes.Array) and seqs._type_ is hisa_seq:
+        return seqs
+    return (hisa_seq * max(1, len(seqs)))(*[hisa_seq(*map(int, s)) for s in seqs])
 
 
 def hisa_pool_blocks(keys, B: int, reps, stream=None):
@@ -155,7 +168,7 @@ def hisa_pool_blocks(keys, B: int, reps, stream=None):
 def hisa_append_keys(keys, reps, seqs, new_keys, B: int, stream=None):
     """Append new_keys [nseq, n_new, 64] to each sequence; seqs is a list of
     (key_off, rep_off, len, capacity) with the lengths before the append."""
-    arr = (hisa_seq * max(1, len(seqs)))(*[hisa_seq(*map(int, s)) for s in seqs])
+    arr = seq_array(seqs)
     n_new = new_keys.shape[1] if new_keys.dim() == 3 else new_keys.shape[0]
     rc = lib().hisa_append_keys(_dev(keys, "keys", 2), _dev(reps, "reps", 2), arr, len(seqs),
                                 _dev(new_keys, "new_keys", 2), n_new, keys.shape[-1], B,
@@ -220,7 +233,7 @@ def hisa_flat_index(args: hisa_index_args, stream=None):
 def hisa_decode_step(args: hisa_index_args, seqs, new_keys, stream=None):
     """Append new_keys [nseq, n_new, 64] to every sequence (seqs: host
     (key_off, rep_off, len before, capacity) per sequence) and index."""
-    arr = (hisa_seq * max(1, len(seqs)))(*[hisa_seq(*map(int, s)) for s in seqs])
+    arr = seq_array(seqs)
     n_new = 0 if new_keys is None else (new_keys.shape[1] if new_keys.dim() == 3 else new_keys.shape[0])
     rc = lib().hisa_decode_step(ctypes.byref(args), arr, _dev(new_keys, "new_keys", 2), n_new, _stream(stream))
     _check(rc, "hisa_decode_step")

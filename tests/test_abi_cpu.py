@@ -221,3 +221,13 @@ def test_decode_step_validation(lib):
     assert lib.hisa_decode_step(ctypes.byref(a), seqs, None, 5, None) == hisa.HISA_ERR_INVALID_ARG
     assert lib.hisa_decode_step(ctypes.byref(a), seqs, P(FAKE), 5, None) == hisa.HISA_ERR_WORKSPACE
     assert lib.hisa_decode_step(ctypes.byref(_args(d=32)), seqs, P(FAKE), 5, None) == hisa.HISA_ERR_UNSUPPORTED
+
+
+def test_seq_array_marshalling():
+    # tuples become hisa_seq rows; an array already built passes through as it is
+    arr = hisa.seq_array([(0, 0, 100, 128), (128, 1, 7, 64)])
+    assert len(arr) == 2
+    assert (arr[1].key_off, arr[1].rep_off, arr[1].len, arr[1].capacity) == (128, 1, 7, 64)
+    assert hisa.seq_array(arr) is arr
+    # a raw stream handle is passed on unchanged
+    assert hisa._stream(0x1234).value == 0x1234
