@@ -1208,6 +1208,7 @@ def main():
         "kernels": res["hisa"]["kernels"],
         "flat": dict(res["flat"], value=res["flat"]["queries_per_s"], unit="queries/s"),
         "speedup_vs_flat": res["speedup_vs_flat"],
+        "hisa_launch_forms_ms_per_step": res["hisa"]["launch_forms_ms_per_step"],
         "hisa_two_calls_ms_per_step": res["hisa"]["two_calls_ms_per_step"],
         "hisa_two_calls_kernels": res["hisa"]["two_calls_kernels"],
         "step_note": ("HISA decode steps are one hisa_decode_step call (the append in the same launch as the block "
