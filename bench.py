@@ -919,9 +919,11 @@ def supplementary_block_scoring(nsteps, torch, hisa_mod, device_mod, synth):
     GFLOP of causal pairs), a shape large enough for the matrix-core
     fraction to be read, outside the pages' configurations.  One hisa_index
     call indexes every query (B=128, m=64, k=2048); stage 0 is the
-    representative scores on the MFMA (into a row per query) plus the top-m
-    select from those rows, timed with the library's stage events over
-    `nsteps` eager calls.  No flat indexer: its score rows would take
+    block scores on the MFMA and the top-m select (two walks over the
+    representatives, no score row in memory), timed with the library's
+    stage events over `nsteps` eager calls; its fraction counts each causal
+    (query, block) pair's 128 flops once, though the two walks issue them
+    twice.  No flat indexer: its score rows would take
     128 GiB."""
     pos = np.arange(SUPP_L - SUPP_NQ, SUPP_L, dtype=np.int64)
     w = synth.chunked_prefill(L=SUPP_L, seed=SUPP_SEED, q_positions=pos)
@@ -952,8 +954,11 @@ def supplementary_block_scoring(nsteps, torch, hisa_mod, device_mod, synth):
                            % (SUPP_NQ, SUPP_L - SUPP_NQ, SUPP_L - 1, SUPP_L, w.B, w.m, w.k),
             "causal_block_pairs": int((pos // w.B + 1).sum()), "block_flops": flops,
             "stage_ms": st, "call_ms": float(sum(st.values())),
-            "block_stage": {"kernels": "block_score_tile_kernel (bf16 MFMA, scores into a row per query) + "
-                                       "stage1_select_many_kernel (top-m from each row)",
+            "block_stage": {"kernels": "block_select_tile_kernel (two bf16 MFMA walks over the representatives, "
+                                       "no score row in memory: a per-row threshold, then the exact top-m of the "
+                                       "blocks at or above it) + stage1_fixup_kernel (rows that list cannot "
+                                       "certify, selected from scratch)",
+                            "mfma_flops_issued": 2 * flops,
                             "achieved_tflops": tflops, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                             "frac": tflops / MFMA_BF16_PEAK_TFLOPS},
             "valid_indices": nvalid, "steps": nsteps}

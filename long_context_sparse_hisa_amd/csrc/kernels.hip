@@ -187,12 +187,11 @@ __global__ __launch_bounds__(kThreads) void block_score_append_kernel(QueryMeta 
 // representatives itself; otherwise it reads the scores from sigma.
 
 template <int NT, int ITEMS, bool FUSED>
-HISA_INLINE void stage1_select_body(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int lb, int m,
-                                    int64_t Mmax, const float* sigma, int32_t* sel, RowInfo* rinfo,
+HISA_INLINE void stage1_select_body(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t row, int lb,
+                                    int m, int64_t Mmax, const float* sigma, int32_t* sel, RowInfo* rinfo,
                                     int32_t* out_blocks)
 {
     __shared__ BucketSmem<NT> sm;
-    const int64_t row = blockIdx.x;
     const int64_t i = q0 + row;
     const QueryInfo qi =
         query_info(i, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq, qm.max_len);
@@ -266,7 +265,7 @@ __global__ __launch_bounds__(NT) void stage1_select_kernel(QueryMeta qm, const u
                                                            int m, int64_t Mmax, const float* sigma, int32_t* sel,
                                                            RowInfo* rinfo, int32_t* out_blocks)
 {
-    stage1_select_body<NT, ITEMS, FUSED>(qm, reps, q0, lb, m, Mmax, sigma, sel, rinfo, out_blocks);
+    stage1_select_body<NT, ITEMS, FUSED>(qm, reps, q0, blockIdx.x, lb, m, Mmax, sigma, sel, rinfo, out_blocks);
 }
 
 // The select from sigma for many rows of 32 scores per thread, held to six
@@ -277,7 +276,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6, 8))) void
     QueryMeta qm, const uint16_t* reps, int64_t q0, int lb, int m, int64_t Mmax, const float* sigma, int32_t* sel,
     RowInfo* rinfo, int32_t* out_blocks)
 {
-    stage1_select_body<NT, ITEMS, FUSED>(qm, reps, q0, lb, m, Mmax, sigma, sel, rinfo, out_blocks);
+    stage1_select_body<NT, ITEMS, FUSED>(qm, reps, q0, blockIdx.x, lb, m, Mmax, sigma, sel, rinfo, out_blocks);
 }
 
 template <int NT, int ITEMS, bool FUSED, bool MANY = false>
@@ -562,6 +561,472 @@ hipError_t launch_block_scores(const QueryMeta& qm, const uint16_t* reps, int64_
     return launch_k(block_score_kernel, grid, dim3(kThreads), stream, t.start, t.stop, qm, reps, q0, lb, Mmax, sigma);
 }
 
+// ---- many queries, many blocks: block scores and top-m, no score row -------
+// Rows with more blocks than stage1_tile_kernel holds, when m - 3 is at most
+// kBfMaxFree.  The representative scores are never written: a workgroup of
+// kBfWaves waves takes kBfRows consecutive query rows (four 16-row MFMA
+// sub-tiles; queries are the A operand, representatives the B operand, so
+// lane l receives rows 4*(l/16)+v, v = 0..3, of each sub-tile against block
+// 16*bt + l%16), and wave w walks the 16-block tiles w, w+kBfWaves, ...
+// twice:
+//  1. every lane keeps, for each row it holds, the kBfTrack largest scores of
+//     the free blocks in its column (one max and kBfTrack-1 med3 per score).
+//     The four waves' lists are merged per (row, column) through LDS, and
+//     theta_r is the (m-3)-th largest of the row's 16*kBfTrack merged
+//     values, so at least m-3 free blocks score >= theta_r.
+//  2. the scores again; every free block with !(score < theta_r) is listed
+//     (ranking key, block) in the row's LDS list.
+// A row whose list holds between m-3 and kBfCap blocks, none scoring NaN,
+// then holds every block of its top m-3: a block left out scores below
+// theta_r, below every listed one, and m-3 are listed.  So the exact top
+// m-3 of the list (ties to the lower block) is the row's selection, found by
+// the wave select over the list in ascending block order (a bitmap of the
+// listed blocks gives each its place).  Any other row is marked by
+// sel[row][0] = -2 and selected again from scratch by stage1_fixup_kernel.
+constexpr int kBfRows = 64;
+constexpr int kBfWaves = 4;
+constexpr int kBfTrack = 6;
+constexpr int kBfSeg = 32;                   // list entries of one row from one wave
+constexpr int kBfCap = kBfWaves * kBfSeg;
+constexpr int kBfMaxFree = 64;
+constexpr int kBfMaxBlocks = 16384;
+constexpr int kBfWords = kBfMaxBlocks / 32;
+
+struct BfWave {
+    alignas(16) uint32_t bm[kBfWords];   // the listed blocks of one row as bits
+    int pre[kBfWords];                   // listed blocks before each word
+    uint32_t skey[kBfCap];               // the list in ascending block order
+    int32_t sblk[kBfCap];
+    WaveSmem ws;
+};
+
+struct BfSmem {
+    union {
+        float xch[kBfWaves][4][kBfTrack][64];   // walk-1 lists on their way to the wave that merges them
+        struct {
+            float score[kBfWaves][kBfRows][kBfSeg];   // the blocks a wave lists for a row
+            int16_t blk[kBfWaves][kBfRows][kBfSeg];
+        } lst;
+    } u;
+    float theta[kBfRows];
+    int cnt[kBfWaves][kBfRows];         // blocks each wave listed for a row (more than kBfSeg: overflow)
+    int hi[kBfRows];          // last free block of each walked row (-1: not walked now)
+    BfWave pw[kBfWaves];
+};
+
+// The T largest of t and x, descending (t is descending): T medians of
+// three, the first against the largest finite float (a median against +inf
+// would be compiled as a maximum with its operands canonicalised, three
+// instructions).  An infinite score may enter as that float; the lists only
+// set a threshold, and a row the threshold does not certify is reselected.
+template <int T>
+HISA_INLINE void track_insert(float (&t)[T], float x)
+{
+#pragma unroll
+    for (int i = T - 1; i >= 1; --i) t[i] = __builtin_amdgcn_fmed3f(t[i - 1], t[i], x);
+    t[0] = __builtin_amdgcn_fmed3f(t[0], x, 3.40282347e38f);
+}
+
+// Sum over the 16 lanes of each row of the wave (DPP row rotations).
+HISA_INLINE int row_sum16(int v)
+{
+    uint32_t x = (uint32_t)v;
+    x += dpp_u32<0x128>(x);          // row_ror:8
+    x += dpp_u32<0x124>(x);          // row_ror:4
+    x += dpp_u32<0x122>(x);          // row_ror:2
+    x += dpp_u32<0x121>(x);          // row_ror:1
+    return (int)x;
+}
+
+HISA_INLINE bool nan_key(uint32_t k) { return k > 0xff800000u || k < 0x007fffffu; }
+
+__global__ __launch_bounds__(64 * kBfWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void block_select_tile_kernel(QueryMeta qm, const uint16_t* reps,
+                                                                          int64_t q0, int64_t nq, int lb, int m,
+                                                                          int32_t* sel, RowInfo* rinfo,
+                                                                          int32_t* out_blocks)
+{
+    extern __shared__ __align__(16) unsigned char s_raw[];
+    BfSmem& S = *reinterpret_cast<BfSmem*>(s_raw);
+    const int w = wave_id(), lane = lane_id();
+    const int col = lane & 15, kg = lane >> 4;
+    const int64_t row0 = (int64_t)blockIdx.x * kBfRows;
+    const int nrows = (int)min<int64_t>(kBfRows, nq - row0);
+    const int mf = m - 3;
+    // lane r holds the info of row r (every wave the same, so the loops
+    // below are uniform over the workgroup)
+    QueryInfo qi;
+    qi.valid = false;
+    qi.seq = -1;
+    qi.t = -1;
+    qi.key_off = 0;
+    qi.rep_off = 0;
+    if (lane < nrows) {
+        qi = query_info(q0 + row0 + lane, qm.q_pos, qm.q_seq, qm.seq_key_off, qm.seq_rep_off, qm.seq_len, qm.nseq,
+                        qm.max_len);
+        if (w == 0) rinfo[row0 + lane] = RowInfo{qi.key_off, qi.valid ? qi.t : -1};
+    }
+    const int c_own = qi.valid ? (int)(qi.t >> lb) : -1;
+    // invalid rows keep no block, rows with c + 1 <= m every causal block
+    for (uint64_t sv = __ballot(lane < nrows && c_own + 1 <= m && (lane & 3) == w); sv; sv &= sv - 1) {
+        const int rr = (int)__builtin_ctzll(sv);
+        const int cr = __builtin_amdgcn_readlane(c_own, rr);
+        for (int j = lane; j < m; j += 64) {
+            const int32_t v = j <= cr ? j : -1;
+            sel[(row0 + rr) * m + j] = v;
+            if (out_blocks) out_blocks[(q0 + row0 + rr) * m + j] = v;
+        }
+    }
+    bf16x8_t a0[4], a1[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+        a0[sb] = bf16x8_t{};
+        a1[sb] = bf16x8_t{};
+        if (16 * sb + col < nrows) {
+            const uint16_t* qrow = qm.queries + (q0 + row0 + 16 * sb + col) * kDim + 8 * kg;
+            a0[sb] = *reinterpret_cast<const bf16x8_t*>(qrow);
+            a1[sb] = *reinterpret_cast<const bf16x8_t*>(qrow + 32);
+        }
+    }
+    const bool act = lane < nrows && c_own + 1 > m;
+    uint64_t pending = __ballot(act);
+    while (pending) {
+        // the rows of one sequence at a time
+        const int lead = (int)__builtin_ctzll(pending);
+        const int s = __builtin_amdgcn_readlane(qi.seq, lead);
+        const bool mine = act && qi.seq == s;
+        const uint64_t mrows = __ballot(mine);
+        pending &= ~mrows;
+        const int64_t rep_off = ((int64_t)__builtin_amdgcn_readlane((int)(qi.rep_off >> 32), lead) << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane((int)qi.rep_off, lead);
+        // free blocks of a row: 1 .. hi (hi = -1: not walked now)
+        const int hi_own = mine ? c_own - 2 : -1;
+        if (w == 0) S.hi[lane] = hi_own;          // read by the tiles that need a mask
+        __syncthreads();
+        const int hmax = (int)wave_max_u32(mine ? (uint32_t)hi_own : 0u);
+        // tiles 1 .. tint lie inside every walked row's free blocks: scored
+        // without a mask (rows not walked now are scored too and ignored:
+        // their theta is +inf); tile 0 and tiles past tint are masked
+        const int hmin = (int)wave_min_u32(mine ? (uint32_t)hi_own : 0x7fffffffu);
+        const int tint = (hmin + 1) / 16 - 1;
+        const int ntile = hmax / 16 + 1;
+        // representative rows 0 .. hmax through a buffer resource: every
+        // load is issued unconditionally (rows past hmax read as zero and are
+        // masked like any block outside a row's free range), so the next
+        // tile's loads stay in flight while the current one is scored
+        const __amdgpu_buffer_rsrc_t rrs = buffer_rsrc(reps + rep_off * kDim, (uint32_t)(hmax + 1) * 128u);
+        auto load_rep = [&](int bt, bf16x8_t& r0, bf16x8_t& r1) {
+            const uint32_t off = (uint32_t)(bt * 16 + col) * 128u + 16u * (uint32_t)kg;
+            r0 = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rrs, off, 0, 0));
+            r1 = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rrs, off + 64u, 0, 0));
+        };
+
+        // the scores of tile bt for the four sub-tiles
+        auto tile_scores = [&](const bf16x8_t& r0, const bf16x8_t& r1, f32x4_t (&acc)[4]) {
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                acc[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                acc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[sb], r0, acc[sb], 0, 0, 0);
+                acc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[sb], r1, acc[sb], 0, 0, 0);
+            }
+        };
+        // this wave's tiles: bt = w (mod kBfWaves); interior ones first,
+        // then the masked ones (tile 0 and those past tint)
+        const int ib = w == 0 ? kBfWaves : w;          // first interior tile of the wave
+        const int eb = tint < w ? w : w + ((tint - w) / kBfWaves + 1) * kBfWaves;   // first tile past tint
+        auto edge_tile = [&](int i) {                  // i-th masked tile of the wave, or -1
+            if (w == 0) {
+                if (i == 0) return 0;
+                --i;
+            }
+            const int bt = max(eb, w == 0 ? kBfWaves : w) + i * kBfWaves;
+            return bt < ntile ? bt : -1;
+        };
+
+        // walk 1: the kBfTrack largest free scores per (row, column)
+        float tr[4][4][kBfTrack];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int t = 0; t < kBfTrack; ++t) tr[sb][v][t] = -__builtin_inff();
+        {
+            bf16x8_t n0, n1;
+            load_rep(ib, n0, n1);
+            for (int bt = ib; bt <= tint; bt += kBfWaves) {
+                const bf16x8_t r0 = n0, r1 = n1;
+                load_rep(bt + kBfWaves, n0, n1);
+                f32x4_t acc[4];
+                tile_scores(r0, r1, acc);
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) track_insert(tr[sb][v], acc[sb][v]);
+            }
+            for (int i = 0;; ++i) {
+                const int bt = edge_tile(i);
+                if (bt < 0) break;
+                bf16x8_t r0, r1;
+                load_rep(bt, r0, r1);
+                f32x4_t acc[4];
+                tile_scores(r0, r1, acc);
+                const int b = bt * 16 + col;
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int h = S.hi[16 * sb + 4 * kg + v];
+                        track_insert(tr[sb][v], (b >= 1 && b <= h) ? acc[sb][v] : -__builtin_inff());
+                    }
+            }
+        }
+        // merge: in round r wave w sends its lists of sub-tile (w + r) % 4
+        // and merges those of sub-tile w from wave (w - r) % 4
+#pragma unroll
+        for (int r = 1; r < kBfWaves; ++r) {
+            const int out_sb = (w + r) & 3;
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                if (sb != out_sb) continue;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+#pragma unroll
+                    for (int t = 0; t < kBfTrack; ++t) S.u.xch[w][v][t][lane] = tr[sb][v][t];
+            }
+            __syncthreads();
+            const int from = (w - r) & 3;
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                if (sb != w) continue;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+#pragma unroll
+                    for (int t = 0; t < kBfTrack; ++t) track_insert(tr[sb][v], S.u.xch[from][v][t][lane]);
+            }
+            __syncthreads();
+        }
+        // theta of the rows of sub-tile w: the mf-th largest ranking key of
+        // the 16 lanes' merged lists, bit by bit from the top
+        uint32_t kk[4][kBfTrack];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            if (sb != w) continue;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int t = 0; t < kBfTrack; ++t) kk[v][t] = score_key(tr[sb][v][t]);
+        }
+        uint32_t p[4] = {0u, 0u, 0u, 0u};
+        for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint32_t cand = p[v] | (1u << bit);
+                int cnt = 0;
+#pragma unroll
+                for (int t = 0; t < kBfTrack; ++t) cnt += kk[v][t] >= cand;
+                if (row_sum16(cnt) >= mf) p[v] = cand;
+            }
+        }
+        if (col == 0) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * w + 4 * kg + v;
+                S.theta[r] = ((mrows >> r) & 1ull) ? key_score(p[v]) : __builtin_inff();
+            }
+        }
+        __syncthreads();
+
+        // walk 2: list every free block scoring at least theta, in this
+        // wave's segment of the row's list; a lane's place comes from the
+        // ballot of its 16-lane group (the lanes of one row), no atomics
+        float th[4][4];
+        int cnt[4][4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                th[sb][v] = S.theta[16 * sb + 4 * kg + v];
+                cnt[sb][v] = 0;
+            }
+        const uint32_t gm_lo = kg == 0 ? 0x0000ffffu : (kg == 1 ? 0xffff0000u : 0u);
+        const uint32_t gm_hi = kg == 2 ? 0x0000ffffu : (kg == 3 ? 0xffff0000u : 0u);
+        auto list_tile = [&](const f32x4_t (&acc)[4], int b, bool masked) {
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float x = acc[sb][v];
+                    bool take = !(x < th[sb][v]);
+                    if (masked) take = take && b >= 1 && b <= S.hi[16 * sb + 4 * kg + v];
+                    const uint64_t M = __ballot(take);
+                    if (M == 0) continue;
+                    const uint32_t lo = (uint32_t)M & gm_lo, hi = (uint32_t)(M >> 32) & gm_hi;
+                    const int pos = cnt[sb][v] + (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+                    if (take && pos < kBfSeg) {
+                        const int r = 16 * sb + 4 * kg + v;
+                        S.u.lst.score[w][r][pos] = x;
+                        S.u.lst.blk[w][r][pos] = (int16_t)b;
+                    }
+                    cnt[sb][v] += __popc(lo) + __popc(hi);
+                }
+        };
+        {
+            bf16x8_t n0, n1;
+            load_rep(ib, n0, n1);
+            for (int bt = ib; bt <= tint; bt += kBfWaves) {
+                const bf16x8_t r0 = n0, r1 = n1;
+                load_rep(bt + kBfWaves, n0, n1);
+                f32x4_t acc[4];
+                tile_scores(r0, r1, acc);
+                list_tile(acc, bt * 16 + col, false);
+            }
+            for (int i = 0;; ++i) {
+                const int bt = edge_tile(i);
+                if (bt < 0) break;
+                bf16x8_t r0, r1;
+                load_rep(bt, r0, r1);
+                f32x4_t acc[4];
+                tile_scores(r0, r1, acc);
+                list_tile(acc, bt * 16 + col, true);
+            }
+        }
+        if (col == 0) {
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) S.cnt[w][16 * sb + 4 * kg + v] = cnt[sb][v];
+        }
+        __syncthreads();
+
+        // each listed row: wave w takes rows w, w + 4, ...
+        BfWave& P = S.pw[w];
+        for (uint64_t mv = mrows & (0x1111111111111111ull << w); mv; mv &= mv - 1) {
+            const int r = (int)__builtin_ctzll(mv);
+            int nw[kBfWaves], n = 0, nmax = 0;
+#pragma unroll
+            for (int v = 0; v < kBfWaves; ++v) {
+                nw[v] = __builtin_amdgcn_readfirstlane(S.cnt[v][r]);
+                n += nw[v];
+                nmax = max(nmax, nw[v]);
+            }
+            const int cr = __builtin_amdgcn_readlane(c_own, r);
+            int32_t* srow = sel + (row0 + r) * m;
+            int32_t* orow = out_blocks ? out_blocks + (q0 + row0 + r) * m : nullptr;
+            bool ok = n >= mf && nmax <= kBfSeg;
+            uint32_t k0 = 0u, k1 = 0u;
+            int b0 = 0, b1 = 0;
+            if (ok) {
+                // entry e: the segments one after the other
+                const int p1 = nw[0], p2 = p1 + nw[1], p3 = p2 + nw[2];
+                auto load_entry = [&](int e, uint32_t& kk, int& bb) {
+                    const int v = (e >= p1) + (e >= p2) + (e >= p3);
+                    const int base = v == 0 ? 0 : (v == 1 ? p1 : (v == 2 ? p2 : p3));
+                    kk = score_key(S.u.lst.score[v][r][e - base]);
+                    bb = S.u.lst.blk[v][r][e - base];
+                };
+                if (lane < n) load_entry(lane, k0, b0);
+                if (lane + 64 < n) load_entry(lane + 64, k1, b1);
+                ok = __ballot((lane < n && nan_key(k0)) || (lane + 64 < n && nan_key(k1))) == 0;
+            }
+            if (!ok) {
+                if (lane == 0) srow[0] = -2;
+                continue;
+            }
+            // place of each listed block in ascending block order
+#pragma unroll
+            for (int i = 0; i < kBfWords / 64; ++i) P.bm[lane + 64 * i] = 0u;
+            wave_lds_fence();
+            if (lane < n) atomicOr(&P.bm[b0 >> 5], 1u << (b0 & 31));
+            if (lane + 64 < n) atomicOr(&P.bm[b1 >> 5], 1u << (b1 & 31));
+            wave_lds_fence();
+            constexpr int kPer = kBfWords / 64;   // words of lane l: kPer*l ..
+            int pc[kPer];
+            int tot = 0;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                pc[j] = tot;
+                tot += __popc(P.bm[kPer * lane + j]);
+            }
+            const int ex = wave_incl_scan(tot) - tot;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) P.pre[kPer * lane + j] = ex + pc[j];
+            wave_lds_fence();
+            if (lane < n) {
+                const int sl = P.pre[b0 >> 5] + __popc(P.bm[b0 >> 5] & ((1u << (b0 & 31)) - 1u));
+                P.skey[sl] = k0;
+                P.sblk[sl] = b0;
+            }
+            if (lane + 64 < n) {
+                const int sl = P.pre[b1 >> 5] + __popc(P.bm[b1 >> 5] & ((1u << (b1 & 31)) - 1u));
+                P.skey[sl] = k1;
+                P.sblk[sl] = b1;
+            }
+            wave_lds_fence();
+            uint32_t key2[2];
+            key2[0] = lane < n ? P.skey[lane] : 0u;
+            key2[1] = lane + 64 < n ? P.skey[lane + 64] : 0u;
+            wave_select<2>(key2, mf, P.ws, [&](int slot, uint32_t, int rank) {
+                const int32_t blk = P.sblk[slot];
+                srow[1 + rank] = blk;
+                if (orow) orow[1 + rank] = blk;
+            });
+            if (lane == 0) {
+                srow[0] = 0;
+                srow[m - 2] = cr - 1;
+                srow[m - 1] = cr;
+                if (orow) {
+                    orow[0] = 0;
+                    orow[m - 2] = cr - 1;
+                    orow[m - 1] = cr;
+                }
+            }
+            wave_lds_fence();
+        }
+        __syncthreads();
+    }
+}
+
+// Rows block_select_tile_kernel marked (sel[row][0] = -2): selected from
+// scratch, one row at a time by the workgroup of the row's tile (1024
+// threads score the representatives and run the workgroup select).
+template <int ITEMS>
+__global__ __launch_bounds__(1024) void stage1_fixup_kernel(QueryMeta qm, const uint16_t* reps, int64_t q0,
+                                                            int64_t nq, int lb, int m, int32_t* sel, RowInfo* rinfo,
+                                                            int32_t* out_blocks)
+{
+    const int64_t row0 = (int64_t)blockIdx.x * kBfRows;
+    const int64_t r = row0 + lane_id();
+    uint64_t fl = __ballot(r < nq && sel[r * m] == -2);
+    __syncthreads();                  // every wave has read the marks before any row is rewritten
+    while (fl) {
+        const int rr = (int)__builtin_ctzll(fl);
+        fl &= fl - 1;
+        stage1_select_body<1024, ITEMS, true>(qm, reps, q0, row0 + rr, lb, m, 0, nullptr, sel, rinfo, out_blocks);
+        __syncthreads();
+    }
+}
+
+static hipError_t launch_block_select(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb,
+                                      int m, int64_t Mmax, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
+                                      hipStream_t stream, Timing t)
+{
+    const int64_t tiles = (nq + kBfRows - 1) / kBfRows;
+    hipError_t err = launch_kl(block_select_tile_kernel, dim3((unsigned)tiles), dim3(64 * kBfWaves), sizeof(BfSmem),
+                               stream, t.start, nullptr, qm, reps, q0, nq, lb, m, sel, rinfo, out_blocks);
+    if (err != hipSuccess) return err;
+    const int64_t per = (Mmax + 1023) / 1024;
+#define HISA_FX(N_)                                                                                              \
+    if (per <= N_)                                                                                               \
+    return launch_k(stage1_fixup_kernel<N_>, dim3((unsigned)tiles), dim3(1024), stream, nullptr, t.stop, qm, reps, \
+                    q0, nq, lb, m, sel, rinfo, out_blocks)
+    HISA_FX(2);
+    HISA_FX(4);
+    HISA_FX(8);
+    HISA_FX(16);
+#undef HISA_FX
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, int64_t nq, int lb, int m,
                          int64_t Mmax, float* sigma, int32_t* sel, RowInfo* rinfo, int32_t* out_blocks,
                          hipStream_t stream, Timing t)
@@ -578,6 +1043,9 @@ hipError_t launch_stage1(const QueryMeta& qm, const uint16_t* reps, int64_t q0, 
         HISA_S1T(16);
 #undef HISA_S1T
     }
+    if (nq >= kManyRows && Mmax <= kBfMaxBlocks && m - 3 >= 1 && m - 3 <= kBfMaxFree)
+        // many queries, many blocks: MFMA walks, no score row in memory
+        return launch_block_select(qm, reps, q0, nq, lb, m, Mmax, sel, rinfo, out_blocks, stream, t);
     if (Mmax <= kStage1FusedMax) {
         // 256 threads score up to 2048 representatives, 8 per thread
         const int64_t per = (Mmax + 255) / 256;

@@ -626,10 +626,11 @@ def test_many_rows_topk_ties(kind):
 def test_many_queries_long_rows(nq):
     """Hundreds of queries with more representatives than the stage-1 tile
     kernel holds (2,345 blocks of 128 over 300,100 keys; a count not
-    divisible by four, so the last scores of a row are stored one by one):
-    the representative scores on the matrix cores into a row per query,
-    then the selection from those rows (one workgroup per query for 600
-    queries; with 320, the selection fused with the token scores)."""
+    divisible by four): with 600 queries the two MFMA walks that select
+    without a score row; with 320 (fewer than 512, every query split over
+    several workgroups) the representative scores into a row per query
+    (the last scores of a row stored one by one), then the selection fused
+    with the token scores."""
     print("long rows nq=%d" % nq, flush=True)
     dv = _dev()
     L, B, m, k = 300100, 128, 64, 2048
@@ -646,8 +647,8 @@ def test_many_queries_long_rows(nq):
 def test_largest_block_count(nq):
     """A sequence of exactly the most blocks the index calls accept (16,384
     blocks of 16 over 262,144 keys): the last query sees every block.  With
-    12 queries each gets its own score row; with 600 the many-row
-    selection takes rows of 16,384 scores.  Sampled rows, HISA and flat,
+    12 queries each gets its own score row; with 600 the two MFMA walks
+    select from 16,384 blocks per row.  Sampled rows, HISA and flat,
     against the oracle."""
     print("largest block count nq=%d" % nq, flush=True)
     dv = _dev()
@@ -687,8 +688,7 @@ def test_largest_k(nq):
 def test_supplementary_block_scoring_shape_sampled():
     """The supplementary block-scoring shape at full size: the last 32,768
     positions of a 1,048,576-key MoG sequence in one call (8,064-8,192
-    causal blocks per query, scored on the matrix cores into a row per
-    query).  Every row's properties; 48 rows (the first, the last and 46
+    causal blocks per query, selected by the two MFMA walks).  Every row's properties; 48 rows (the first, the last and 46
     random ones) against the oracle."""
     print("supplementary 32768 x 8192", flush=True)
     dv = _dev()
