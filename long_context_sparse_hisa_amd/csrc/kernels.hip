@@ -1503,28 +1503,18 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
         int tq[SUB];
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) tq[sb] = __shfl(tm, 16 * sb + col);
-        // piece p of block b: key tiles p*KP .. p*KP+KP-1 (keys past the
-        // walked rows' last position read as zero)
+        // piece p of block b: key tiles p*KP .. p*KP+KP-1, through a buffer
+        // resource over the sequence's keys 0 .. tmax (keys past the walked
+        // rows' last position read as zero): every load is issued
+        // unconditionally, so a prefetched piece stays in flight while the
+        // current one is on the MFMA
+        const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(keys + koff * kDim, (uint32_t)(tmax + 1) * 128u);
         auto load_piece = [&](int b, int p, bf16x8_t (&k0)[KP], bf16x8_t (&k1)[KP]) {
-            const uint16_t* kb = keys + (koff + ((int64_t)b << LB)) * kDim + 8 * kg;
-            if (((b + 1) << LB) - 1 <= tmax) {           // every key of the block exists
 #pragma unroll
-                for (int kt = 0; kt < KP; ++kt) {
-                    const int jj = (p * KP + kt) * 16 + col;
-                    k0[kt] = *reinterpret_cast<const bf16x8_t*>(kb + jj * kDim);
-                    k1[kt] = *reinterpret_cast<const bf16x8_t*>(kb + jj * kDim + 32);
-                }
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < KP; ++kt) {
-                    const int jj = (p * KP + kt) * 16 + col;
-                    k0[kt] = bf16x8_t{};
-                    k1[kt] = bf16x8_t{};
-                    if ((b << LB) + jj <= tmax) {
-                        k0[kt] = *reinterpret_cast<const bf16x8_t*>(kb + jj * kDim);
-                        k1[kt] = *reinterpret_cast<const bf16x8_t*>(kb + jj * kDim + 32);
-                    }
-                }
+            for (int kt = 0; kt < KP; ++kt) {
+                const uint32_t off = (uint32_t)((b << LB) + (p * KP + kt) * 16 + col) * 128u + 16u * (uint32_t)kg;
+                k0[kt] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+                k1[kt] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64u, 0, 0));
             }
         };
         // per block: advance the cursors of the rows that kept it; pq[sb]
@@ -1601,7 +1591,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void stage2_tile_kernel(const uint
             const bool last_piece = p + 1 == P;
             const int b2 = last_piece ? bn : b;
             const int p2 = last_piece ? 0 : p + 1;
-            if (b2 != kTileEnd) load_piece(b2, p2, n0, n1);
+            load_piece(b2 != kTileEnd ? b2 : b, p2, n0, n1);   // past the walk's end: a harmless reload
             score_piece(p, c0, c1);
             if (last_piece) {
                 b = bn;
