@@ -153,7 +153,8 @@ def flat_stage_bytes(q_pos, k):
 # ---- measured HBM traffic ----------------------------------------------------------
 
 # kernel symbol that carries each stage
-STAGE_KERNEL = {"block_stage": ("stage1_select_kernel", "stage1_select_many_kernel", "stage1_tile_kernel", "block_score"),
+STAGE_KERNEL = {"block_stage": ("stage1_select_kernel", "stage1_select_many_kernel", "stage1_tile_kernel",
+                                "block_select_tile_kernel", "block_score"),
                 "token_scores": ("select_score_kernel", "stage2_tile_kernel"),
                 "token_topk": ("topk_rows_kernel", "topk_rows_many_kernel"),
                 "select_and_scores": ("decode_fused_kernel", "decode_step_kernel"),
