@@ -57,9 +57,11 @@ struct QueryMeta {
 
 // HISA stage 1: block scores, causal + forced top-m.  sel [nq, m] (the
 // chunk's rows) and rinfo [nq]; out_blocks (nullable) gets the same rows at query offset
-// q0.  Queries with at most kStage1FusedMax blocks are scored by the
-// selecting workgroup; longer ones go through sigma [nq, Mmax].
-// lb = log2(B).
+// q0.  Many queries (>= kManyRows) are scored on the matrix cores: up to
+// 1024 blocks into LDS tiles, more blocks (m - 3 <= 64) by two walks that
+// keep no score row; otherwise queries with at most kStage1FusedMax blocks
+// are scored by the selecting workgroup and longer ones go through sigma
+// [nq, Mmax].  lb = log2(B).
 constexpr int64_t kStage1FusedMax = 2048;
 // A decode step's append, folded into the first launch of the path for
 // more than 2048 blocks (the block scores, launch_block_scores): one job
