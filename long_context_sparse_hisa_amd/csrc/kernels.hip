@@ -1643,10 +1643,180 @@ hipError_t launch_tile_sub(const QueryMeta& qm, const uint16_t* keys, int64_t q0
     return hipErrorInvalidValue;
 }
 
+// ---- token scores of sparse kept lists, block-major ------------------------
+// Many queries of one sequence whose kept lists are sparse in the block range
+// (8m <= Mmax <= 32m: a 64-row tile of the union walk would score most of
+// the blocks it walks for only a few of its rows).  Workgroup (x, y) takes
+// the kGatherRows query rows of tile x and the BR blocks of range y.  Every
+// row's list (ascending, m <= kGatherMaxM entries, loaded by one thread as
+// 16-byte vectors) gives the (row, list position) pairs whose block lies in
+// the range; they are grouped by block in LDS (a count, a scan, a scatter).
+// Each wave then takes blocks of the range: the block's keys are the A
+// operand (lane l: key l%16 of each 16-key tile, dims 8*(l/16)..+8 of each
+// half of d, through a buffer resource over the sequence's keys up to the
+// tile's last position: keys past it read as zero), its keepers the B
+// operand, 16 at a time, two v_mfma_f32_16x16x32_bf16 per 16-key tile as in
+// the union walk; lane l receives keys 4*(l/16)..+4 of each tile for keeper
+// l%16 and stores them as one 16-byte vector into the keeper's slots, key 0
+// for tokens after its position.  Every kept (row, block) pair is scored
+// once, and each slot is written by one workgroup.
+constexpr int kGatherRows = 256;
+constexpr int kGatherMaxM = 64;
+
+__host__ __device__ constexpr size_t gather_lds(int BR, int m)
+{
+    return sizeof(int32_t) * ((size_t)(BR + 1) + BR + (size_t)kGatherRows * (m < BR ? m : BR) + kGatherRows + 8);
+}
+
+template <int LB>
+__global__ __launch_bounds__(kGatherRows) void stage2_gather_kernel(const uint16_t* queries, const uint16_t* keys,
+                                                                    int64_t q0, int64_t nq, int m, int BR,
+                                                                    const RowInfo* rinfo, const int32_t* sel,
+                                                                    uint32_t* ukeys)
+{
+    constexpr int B = 1 << LB;
+    constexpr int KT = B / 16;
+    extern __shared__ __align__(16) int32_t s_g[];
+    int* off = s_g;                                   // [BR + 1]: keepers per block, then their offsets
+    int* cur = off + (BR + 1);                        // [BR]: scatter cursors
+    int32_t* ent = cur + BR;                          // keepers grouped by block: (row << 10) | list position
+    int* trow = ent + kGatherRows * min(m, BR);       // [kGatherRows]: each row's position (-1: none)
+    int* misc = trow + kGatherRows;                   // [0]: largest position, [1..2]: key offset
+    const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+    const int64_t row0 = (int64_t)blockIdx.x * kGatherRows;
+    const int nrows = (int)min<int64_t>(kGatherRows, nq - row0);
+    const int blo = (int)blockIdx.y * BR, bhi = blo + BR;
+    const int N = m << LB;
+    for (int i = tid; i <= BR; i += kGatherRows) off[i] = 0;
+    // thread tid: row tid of the tile, its list in registers
+    RowInfo ri{0, -1};
+    if (tid < nrows) ri = rinfo[row0 + tid];
+    const bool valid = ri.t >= 0;
+    trow[tid] = valid ? (int)ri.t : -1;
+    int4 lst[kGatherMaxM / 4];
+#pragma unroll
+    for (int i = 0; i < kGatherMaxM / 4; ++i) {
+        lst[i] = make_int4(-1, -1, -1, -1);
+        if (valid && 4 * i < m) lst[i] = reinterpret_cast<const int4*>(sel + (row0 + tid) * m)[i];
+    }
+    const uint32_t tmax = wave_max_u32(valid ? (uint32_t)ri.t : 0u);
+    if (lane == 0) misc[4 + w] = (int)tmax;
+    if (valid) {
+        misc[1] = (int)(ri.key_off & 0xffffffff);     // every valid row of the call has the same key offset
+        misc[2] = (int)(ri.key_off >> 32);
+    }
+    __syncthreads();
+    auto in_range = [&](int v) { return v >= blo && v < bhi; };
+#pragma unroll
+    for (int i = 0; i < kGatherMaxM / 4; ++i) {
+        const int v[4] = {lst[i].x, lst[i].y, lst[i].z, lst[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (in_range(v[e])) atomicAdd(&off[v[e] - blo], 1);
+    }
+    __syncthreads();
+    if (w == 0) {
+        // exclusive scan of the counts (BR <= 64: one wave)
+        const int c = lane < BR ? off[lane] : 0;
+        const int incl = wave_incl_scan(c);
+        if (lane < BR) {
+            off[lane] = incl - c;
+            cur[lane] = incl - c;
+        }
+        if (lane == 63) off[BR] = incl;
+        if (lane == 0) misc[0] = (int)max(max((uint32_t)misc[4], (uint32_t)misc[5]), max((uint32_t)misc[6], (uint32_t)misc[7]));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kGatherMaxM / 4; ++i) {
+        const int v[4] = {lst[i].x, lst[i].y, lst[i].z, lst[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (in_range(v[e])) ent[atomicAdd(&cur[v[e] - blo], 1)] = (tid << 10) | (4 * i + e);
+    }
+    __syncthreads();
+    if (off[BR] == 0) return;                         // uniform: no kept block in this range
+    const int64_t koff = ((int64_t)misc[2] << 32) | (uint32_t)misc[1];
+    const int tlast = misc[0];
+    const int col = lane & 15, kg = lane >> 4;
+    const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(keys + koff * kDim, (uint32_t)(tlast + 1) * 128u);
+    for (int j = w; j < BR; j += kWaves) {
+        const int e0 = off[j], nk = off[j + 1] - e0;
+        if (nk == 0) continue;
+        const int b = blo + j;
+        bf16x8_t k0[KT], k1[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            const uint32_t o = (uint32_t)((b << LB) + kt * 16 + col) * 128u + 16u * (uint32_t)kg;
+            k0[kt] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(krs, o, 0, 0));
+            k1[kt] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(krs, o + 64u, 0, 0));
+        }
+        for (int g = 0; g < nk; g += 16) {
+            // keeper g + col of the block (a clamped one past the last loads
+            // a valid row and stores nothing)
+            const bool have = g + col < nk;
+            const int e = ent[e0 + min(g + col, nk - 1)];
+            const int rl = e >> 10, p = e & 1023;
+            const uint16_t* qrow = queries + (q0 + row0 + rl) * kDim + 8 * kg;
+            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(qrow);
+            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(qrow + 32);
+            f32x4_t c[KT];
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+                c[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[kt], a0, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) c[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[kt], a1, c[kt], 0, 0, 0);
+            if (have) {
+                const int t = trow[rl];
+                uint32_t* urow = ukeys + (row0 + rl) * N + ((int64_t)p << LB) + 4 * kg;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) {
+                    const int jj = (b << LB) + kt * 16 + 4 * kg;
+                    uint4 o = make_uint4(score_key(c[kt][0]), score_key(c[kt][1]), score_key(c[kt][2]),
+                                         score_key(c[kt][3]));
+                    o.x = jj + 0 <= t ? o.x : 0u;
+                    o.y = jj + 1 <= t ? o.y : 0u;
+                    o.z = jj + 2 <= t ? o.z : 0u;
+                    o.w = jj + 3 <= t ? o.w : 0u;
+                    *reinterpret_cast<uint4*>(urow + kt * 16) = o;
+                }
+            }
+        }
+    }
+}
+
+static hipError_t launch_stage2_gather(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb,
+                                       int m, int64_t Mmax, const RowInfo* rinfo, const int32_t* sel, uint32_t* ukeys,
+                                       hipStream_t stream, Timing t)
+{
+    // about 512 workgroups, ranges of BR blocks (a power of two, 4 .. 64):
+    // measured on the 128K chunk (4,096 rows, 1,024 blocks) 66 us at 512,
+    // 73 at 256, 85 at 1024, 101 at 2048 (each workgroup reads its rows'
+    // whole lists, so more workgroups repeat that more)
+    const int64_t tiles = (nq + kGatherRows - 1) / kGatherRows;
+    int BR = 4;
+    while (BR < 64 && tiles * ((Mmax + BR - 1) / BR) > 512) BR *= 2;
+    const dim3 grid((unsigned)tiles, (unsigned)((Mmax + BR - 1) / BR));
+    const size_t lds = gather_lds(BR, m);
+#define HISA_G2(LB_) \
+    if (lb == LB_) return launch_kl(stage2_gather_kernel<LB_>, grid, dim3(kGatherRows), lds, stream, t.start, t.stop, qm.queries, keys, q0, nq, m, BR, rinfo, sel, ukeys)
+    HISA_G2(4);
+    HISA_G2(5);
+    HISA_G2(6);
+    HISA_G2(7);
+    HISA_G2(8);
+#undef HISA_G2
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, int64_t q0, int64_t nq, int lb, int m,
                                      int64_t Mmax, const RowInfo* rinfo, const int32_t* sel, uint32_t* ukeys,
                                      hipStream_t stream, Timing t)
 {
+    // sparse lists of one sequence: block-major, every kept pair scored once
+    if (qm.nseq == 1 && nq >= kManyRows && m <= kGatherMaxM && m % 4 == 0 && Mmax >= 8 * (int64_t)m &&
+        Mmax <= 32 * (int64_t)m)
+        return launch_stage2_gather(qm, keys, q0, nq, lb, m, Mmax, rinfo, sel, ukeys, stream, t);
     // as many 16-query sub-tiles per wave (up to 4, all 64 lanes) as the
     // lists of kept blocks leave room for in LDS
     const size_t per16 = (size_t)kTileQueries * m * sizeof(int32_t);
