@@ -155,7 +155,7 @@ def flat_stage_bytes(q_pos, k):
 # kernel symbol that carries each stage
 STAGE_KERNEL = {"block_stage": ("stage1_select_kernel", "stage1_select_many_kernel", "stage1_tile_kernel",
                                 "block_select_tile_kernel", "block_score"),
-                "token_scores": ("select_score_kernel", "stage2_tile_kernel"),
+                "token_scores": ("select_score_kernel", "stage2_tile_kernel", "stage2_gather_kernel"),
                 "token_topk": ("topk_rows_kernel", "topk_rows_many_kernel"),
                 "select_and_scores": ("decode_fused_kernel", "decode_step_kernel"),
                 "flat_scores": ("flat_score_kernel", "flat_score_mfma_kernel")}
