@@ -1645,8 +1645,10 @@ hipError_t launch_tile_sub(const QueryMeta& qm, const uint16_t* keys, int64_t q0
 
 // ---- token scores of sparse kept lists, block-major ------------------------
 // Many queries of one sequence whose kept lists are sparse in the block range
-// (8m <= Mmax <= 32m: a 64-row tile of the union walk would score most of
-// the blocks it walks for only a few of its rows).  Workgroup (x, y) takes
+// (8m <= Mmax <= 128m: a 64-row tile of the union walk would score most of
+// the blocks it walks for only a few of its rows; measured 152 -> 66 us at
+// Mmax = 16m, 2.90 -> 1.75 ms at 128m, where a tile's block has about two
+// keepers).  Workgroup (x, y) takes
 // the kGatherRows query rows of tile x and the BR blocks of range y.  Every
 // row's list (ascending, m <= kGatherMaxM entries, loaded by one thread as
 // 16-byte vectors) gives the (row, list position) pairs whose block lies in
@@ -1815,7 +1817,7 @@ hipError_t launch_stage2_tile_scores(const QueryMeta& qm, const uint16_t* keys, 
 {
     // sparse lists of one sequence: block-major, every kept pair scored once
     if (qm.nseq == 1 && nq >= kManyRows && m <= kGatherMaxM && m % 4 == 0 && Mmax >= 8 * (int64_t)m &&
-        Mmax <= 32 * (int64_t)m)
+        Mmax <= 128 * (int64_t)m)
         return launch_stage2_gather(qm, keys, q0, nq, lb, m, Mmax, rinfo, sel, ukeys, stream, t);
     // as many 16-query sub-tiles per wave (up to 4, all 64 lanes) as the
     // lists of kept blocks leave room for in LDS

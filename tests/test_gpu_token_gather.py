@@ -1,5 +1,5 @@
 """Token scores of sparse kept lists, block-major (many queries of one
-sequence, 8m <= blocks <= 32m, m <= 64 and a multiple of 4): each kept
+sequence, 8m <= blocks <= 128m, m <= 64 and a multiple of 4): each kept
 (row, block) pair scored once by the workgroup that holds the block's
 keepers.  Every row against the oracle, through the C ABI."""
 import numpy as np
@@ -53,16 +53,18 @@ def _check_all(w, cache, ph, k, m, label, bad=None):
     assert counts["exact"] + counts["excused"] == len(ph.q_pos)
 
 
-@pytest.mark.parametrize("L,B,m,k", [(20000, 32, 40, 1000), (60000, 64, 32, 1500), (32768, 16, 64, 1024)])
+@pytest.mark.parametrize("L,B,m,k", [(20000, 32, 40, 1000), (60000, 64, 32, 1500), (32768, 16, 64, 1024),
+                                     (131072, 16, 64, 1024)])
 def test_gather_every_row_with_invalid_queries(L, B, m, k):
     """700 queries (a ragged last tile of 188 rows) at random positions of
     one MoG sequence, one in 13 past the sequence's end (a -1 row), the
     first few keeping every causal block; the last shape sits at the
-    largest block count the block-major form takes (32m)."""
+    largest block count the block-major form takes (128m: about two
+    keepers per block and tile)."""
     print("gather L=%d B=%d m=%d k=%d" % (L, B, m, k), flush=True)
     dv = _dev()
     Mb = (L + B - 1) // B
-    assert 8 * m <= Mb <= 32 * m and m % 4 == 0
+    assert 8 * m <= Mb <= 128 * m and m % 4 == 0
     g = np.random.default_rng(L + m)
     nq = 700
     pos = np.sort(g.choice(np.arange(L), nq, replace=False)).astype(np.int64)
