@@ -568,17 +568,23 @@ hipError_t launch_block_scores(const QueryMeta& qm, const uint16_t* reps, int64_
 // sub-tiles; queries are the A operand, representatives the B operand, so
 // lane l receives rows 4*(l/16)+v, v = 0..3, of each sub-tile against block
 // 16*bt + l%16), and wave w walks the 16-block tiles w, w+kBfWaves, ...
-// twice:
+// (representatives through a buffer resource, the next tile loading while
+// one is scored; tiles inside every walked row's free range unmasked, tile 0
+// and the last ones masked) twice:
 //  1. every lane keeps, for each row it holds, the kBfTrack largest scores of
-//     the free blocks in its column (one max and kBfTrack-1 med3 per score).
+//     the free blocks in its column (kBfTrack medians of three per score).
 //     The four waves' lists are merged per (row, column) through LDS, and
 //     theta_r is the (m-3)-th largest of the row's 16*kBfTrack merged
-//     values, so at least m-3 free blocks score >= theta_r.
+//     values (found bit by bit over their ranking keys), so at least m-3
+//     free blocks score >= theta_r when those values are real scores.
 //  2. the scores again; every free block with !(score < theta_r) is listed
-//     (ranking key, block) in the row's LDS list.
-// A row whose list holds between m-3 and kBfCap blocks, none scoring NaN,
-// then holds every block of its top m-3: a block left out scores below
-// theta_r, below every listed one, and m-3 are listed.  So the exact top
+//     (score, block) in this wave's kBfSeg-entry segment of the row's LDS
+//     list, its place given by the ballot of the row's 16 lanes.
+// A row whose list holds at least m-3 blocks, no segment overflowing and
+// none scoring NaN, then holds every block of its top m-3: a block left out
+// scores below theta_r, below every listed one, and m-3 are listed (this
+// holds whatever theta_r is, so the first walk only has to make it tight).
+// So the exact top
 // m-3 of the list (ties to the lower block) is the row's selection, found by
 // the wave select over the list in ascending block order (a bitmap of the
 // listed blocks gives each its place).  Any other row is marked by
