@@ -91,3 +91,10 @@ def test_many_row_kernels_carry_their_stage():
     assert any("topk_rows_many_kernel" == s for s in bench.STAGE_KERNEL["token_topk"])
     assert any("stage1_select_many_kernel" == s for s in bench.STAGE_KERNEL["block_stage"])
     assert bench.DECODE_FOLD_MAX_SEQS == 64
+
+
+def test_long_row_kernels_carry_their_stage():
+    # the two-walk block selection and the block-major token scores are
+    # looked up under their stages, so the line finds their traffic
+    assert "block_select_tile_kernel" in bench.STAGE_KERNEL["block_stage"]
+    assert "stage2_gather_kernel" in bench.STAGE_KERNEL["token_scores"]
