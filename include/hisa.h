@@ -151,7 +151,9 @@ typedef struct hisa_index_args {
     int32_t* out_idx;            /* [nq, k] */
     float* out_scores;           /* [nq, k] or NULL */
     int32_t* out_blocks;         /* [nq, m] or NULL (HISA only) */
-    void* workspace;             /* device scratch owned by the caller */
+    void* workspace;             /* device scratch owned by the caller, 16-byte aligned
+                                    (HISA_ERR_INVALID_ARG otherwise: the kernels move it
+                                    as 16-byte vectors) */
     size_t workspace_bytes;      /* its size; see hisa_workspace_bytes */
     void* const* stage_events;   /* NULL, or 2 * HISA_STAGES hipEvent_t handles (profiling aid,
                                     created with timing enabled).  Events 2s and 2s+1 record

@@ -27,6 +27,9 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// The kernels read and write workspace regions as 16-byte vectors.
+inline bool ws_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 static_assert(kMaxKept * kMinB == HISA_MAX_CANDIDATES, "kept-block bound of the kernels");
 inline bool valid_B(int B) { return B >= kMinB && B <= kMaxB && (B & (B - 1)) == 0; }
 
@@ -268,6 +271,7 @@ int hisa_index(const hisa_index_args* a, void* stream_)
     if (rc != HISA_OK) return rc;
     if (a->nq == 0) return HISA_OK;
     if (!a->workspace) return HISA_ERR_WORKSPACE;
+    if (!ws_aligned(a->workspace)) return HISA_ERR_INVALID_ARG;
     const int64_t chunk = chunk_for(a, 0, a->workspace_bytes);
     if (chunk < 1) return HISA_ERR_WORKSPACE;
     const Layout L = layout_for(a, 0, chunk);
@@ -347,6 +351,7 @@ int hisa_decode_step(const hisa_index_args* a, const hisa_seq* seqs, const uint1
     }
     if (n_new > 0 && (int64_t)a->nseq * n_new > INT32_MAX) return HISA_ERR_INVALID_ARG;
     if (a->nq > 0 && !a->workspace) return HISA_ERR_WORKSPACE;
+    if (a->nq > 0 && !ws_aligned(a->workspace)) return HISA_ERR_INVALID_ARG;
     const int64_t chunk = a->nq > 0 ? chunk_for(a, 0, a->workspace_bytes) : 1;
     if (chunk < 1) return HISA_ERR_WORKSPACE;
     const int64_t Mmax = hisa_Mmax(a);
@@ -429,6 +434,7 @@ int hisa_block_index(const hisa_index_args* a, void* stream_)
     if ((int64_t)a->k != (int64_t)a->m * a->B || a->out_scores) return HISA_ERR_INVALID_ARG;
     if (a->nq == 0) return HISA_OK;
     if (!a->workspace) return HISA_ERR_WORKSPACE;
+    if (!ws_aligned(a->workspace)) return HISA_ERR_INVALID_ARG;
     const int64_t chunk = chunk_for(a, 0, a->workspace_bytes);
     if (chunk < 1) return HISA_ERR_WORKSPACE;
     const Layout L = layout_for(a, 0, chunk);
@@ -458,6 +464,7 @@ int hisa_flat_index(const hisa_index_args* a, void* stream_)
     if (rc != HISA_OK) return rc;
     if (a->nq == 0) return HISA_OK;
     if (!a->workspace) return HISA_ERR_WORKSPACE;
+    if (!ws_aligned(a->workspace)) return HISA_ERR_INVALID_ARG;
     const int64_t chunk = chunk_for(a, 1, a->workspace_bytes);
     if (chunk < 1) return HISA_ERR_WORKSPACE;
     const Layout L = layout_for(a, 1, chunk);

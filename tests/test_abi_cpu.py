@@ -231,3 +231,18 @@ def test_seq_array_marshalling():
     assert hisa.seq_array(arr) is arr
     # a raw stream handle is passed on unchanged
     assert hisa._stream(0x1234).value == 0x1234
+
+
+def test_workspace_must_be_16_byte_aligned(lib):
+    # the kernels read and write the workspace as 16-byte vectors: a
+    # misaligned one is refused before any launch
+    a = _args(max_len=200)
+    want, least, whole = hisa.hisa_workspace_bytes(a, all_queries=True)
+    bad = _args(max_len=200, workspace=FAKE + 4, workspace_bytes=whole)
+    assert _rc(lib.hisa_index, bad) == hisa.HISA_ERR_INVALID_ARG
+    assert _rc(lib.hisa_block_index, bad) == hisa.HISA_ERR_INVALID_ARG
+    fw, fl = hisa.hisa_workspace_bytes(a, flat=True)
+    assert _rc(lib.hisa_flat_index, _args(max_len=200, workspace=FAKE + 8, workspace_bytes=fw)) == \
+        hisa.HISA_ERR_INVALID_ARG
+    seqs = (hisa.hisa_seq * 1)(hisa.hisa_seq(0, 0, 100, 200))
+    assert lib.hisa_decode_step(ctypes.byref(bad), seqs, ctypes.c_void_p(FAKE), 5, None) == hisa.HISA_ERR_INVALID_ARG
